@@ -1,0 +1,285 @@
+"""Pins for the CPU oracle.
+
+Each test checks the oracle against something other than itself: values
+worked by hand from the definition (tests/golden/), closed forms the text
+states in prose, an exact rational brute force, NumPy's own IEEE casts, or an
+algebraic invariant.  The checks are chosen so that a plausible slip in the
+oracle (swapped denominators, a wrong sign, a wrong pairing order, a dropped
+carry, a segment leak, a wrong rounding mode) fails at least one of them.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import exact
+from oracle.rounding import round_to_format
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)["examples"]
+
+
+# ---------------------------------------------------------------- worked examples
+
+@pytest.mark.parametrize("ex", _golden(), ids=lambda e: e["name"])
+def test_golden_exact(ex):
+    vecs = [[Fraction(v) for v in vec] for vec in ex["inputs"]]
+    fn = exact.adasum_tree if ex["schedule"] == "tree" else exact.adasum_chain
+    res, coeffs, _ = fn(vecs)
+    assert res == [Fraction(v) for v in ex["result"]]
+    assert [(ca, cb) for ca, cb in coeffs] == [(Fraction(a), Fraction(b)) for a, b in ex["coeffs"]]
+
+
+@pytest.mark.parametrize("ex", _golden(), ids=lambda e: e["name"])
+def test_golden_fp64(ex):
+    vecs = [np.array([float(Fraction(v)) for v in vec]) for vec in ex["inputs"]]
+    fn = oracle.adasum_tree if ex["schedule"] == "tree" else oracle.adasum_chain
+    res, coeffs, _ = fn(vecs)
+    np.testing.assert_allclose(res, [float(Fraction(v)) for v in ex["result"]], rtol=1e-14, atol=1e-15)
+    for (ca, cb), (ga, gb) in zip(coeffs, ex["coeffs"]):
+        assert abs(ca - float(Fraction(ga))) <= 1e-14 and abs(cb - float(Fraction(gb))) <= 1e-14
+
+
+def test_tree_and_chain_differ():
+    # the operator is not associative: the pairing order matters
+    g = [np.array(v, dtype=float) for v in ([1, 0], [1, 1], [0, 2], [-1, 1])]
+    t, _, _ = oracle.adasum_tree(g)
+    c, _, _ = oracle.adasum_chain(g)
+    assert np.max(np.abs(t - c)) > 0.1
+
+
+# ---------------------------------------------------------------- properties from the text
+
+def test_orthogonal_inputs_sum():
+    rng = np.random.default_rng(1)
+    for K in (2, 3, 5, 8, 16):
+        q, _ = np.linalg.qr(rng.standard_normal((40, K)))
+        vecs = [q[:, k] * rng.uniform(0.1, 10.0) for k in range(K)]
+        res, coeffs, _ = oracle.adasum_tree(vecs)
+        np.testing.assert_allclose(res, np.sum(vecs, axis=0), rtol=0, atol=1e-12)
+        assert oracle.orthogonality(vecs, [0, 40])[0] == pytest.approx(1.0, abs=1e-12)
+
+
+def test_parallel_pair_average_any_norms():
+    rng = np.random.default_rng(2)
+    u = rng.standard_normal(17)
+    for lam, mu in ((1.0, 2.0), (3.0, -0.5), (-2.0, -7.0), (5.0, -5.0), (1e-3, 1e3)):
+        res, _, _ = oracle.adasum_pair(lam * u, mu * u)
+        np.testing.assert_allclose(res, 0.5 * (lam + mu) * u, rtol=1e-12, atol=1e-12)
+
+
+def test_identical_inputs_return_input():
+    rng = np.random.default_rng(3)
+    g = rng.standard_normal(33)
+    for K in (1, 2, 3, 4, 7, 16, 64):
+        res, _, _ = oracle.adasum_tree([g] * K)
+        np.testing.assert_allclose(res, g, rtol=1e-13, atol=1e-14)
+    # the orthogonality ratio of K equal gradients is 1/K (1/64 at K = 64)
+    assert oracle.orthogonality([g] * 64, [0, 33])[0] == pytest.approx(1 / 64, rel=1e-12)
+
+
+def test_mean_of_two_sequential_orders():
+    # Emulating b1 then b2 scales g2 by (1 - g1.g2/|g2|^2); the other order
+    # scales g1 by (1 - g1.g2/|g1|^2); the operator is the mean of the two.
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        g1, g2 = rng.standard_normal(9), rng.standard_normal(9) + 0.5
+        d = g1 @ g2
+        s12 = g1 + (1 - d / (g2 @ g2)) * g2
+        s21 = g2 + (1 - d / (g1 @ g1)) * g1
+        res, _, _ = oracle.adasum_pair(g1, g2)
+        np.testing.assert_allclose(res, 0.5 * (s12 + s21), rtol=1e-12, atol=1e-12)
+
+
+def test_zero_norm_is_plain_sum():
+    b = np.array([1.0, -2.0, 3.5])
+    z = np.zeros(3)
+    res, cf, _ = oracle.adasum_pair(z, b)
+    assert np.array_equal(res, b) and cf == (1.0, 1.0)
+    res, cf, _ = oracle.adasum_pair(b, z)
+    assert np.array_equal(res, b) and cf == (1.0, 1.0)
+    res, cf, _ = oracle.adasum_pair(z, z)
+    assert np.array_equal(res, z) and cf == (1.0, 1.0)
+
+
+def test_not_elementwise():
+    # changing one coordinate of one input changes the other coordinates of
+    # the result, which an elementwise reduction could never do
+    a = np.array([1.0, 2.0, 3.0])
+    b = np.array([0.5, -1.0, 2.0])
+    r0, _, _ = oracle.adasum_pair(a, b)
+    a2 = a.copy()
+    a2[0] += 1.0
+    r1, _, _ = oracle.adasum_pair(a2, b)
+    assert np.all(np.abs(r1[1:] - r0[1:]) > 1e-6)
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("K", range(1, 9))
+def test_fp64_matches_exact_bruteforce(K):
+    rng = np.random.default_rng(100 + K)
+    for trial in range(6):
+        n = int(rng.integers(1, 7))
+        vecs = [rng.integers(-4, 5, size=n).astype(float) for _ in range(K)]
+        if trial == 0 and K >= 2:
+            vecs[1] = np.zeros(n)
+        res, cf, st = oracle.adasum_tree(vecs)
+        eres, ecf, est = exact.adasum_tree(vecs)
+        scale = max(1.0, max(abs(float(v)) for v in eres))
+        for x, e in zip(res, eres):
+            assert abs(x - float(e)) <= 1e-13 * scale
+        for (ca, cb), (ea, eb) in zip(cf, ecf):
+            assert abs(ca - float(ea)) <= 1e-13 * max(1, abs(float(ea)))
+            assert abs(cb - float(eb)) <= 1e-13 * max(1, abs(float(eb)))
+        for i, ((d, A, B), (ed, eA, eB)) in enumerate(zip(st, est)):
+            if i < K // 2:  # level 1 sees the integer inputs: exact
+                assert (d, A, B) == (float(ed), float(eA), float(eB))
+            for x, e in ((d, ed), (A, eA), (B, eB)):
+                assert abs(x - float(e)) <= 1e-13 * max(1.0, abs(float(eA)), abs(float(eB)))
+
+
+@pytest.mark.parametrize("K", [2, 3, 5, 8])
+def test_chain_matches_exact_bruteforce(K):
+    rng = np.random.default_rng(200 + K)
+    vecs = [rng.integers(-3, 4, size=4).astype(float) for _ in range(K)]
+    res, _, _ = oracle.adasum_chain(vecs)
+    eres, _, _ = exact.adasum_chain(vecs)
+    np.testing.assert_allclose(res, [float(e) for e in eres], rtol=1e-13, atol=1e-13)
+
+
+def test_tree_schedule_shape():
+    sched = oracle.tree_schedule(6)
+    # 6 -> 3 nodes; 3 -> 1 node + carry; 2 -> 1 node
+    assert [len(l) for l in sched] == [3, 1, 1]
+    assert sched[0] == [(("leaf", 0), ("leaf", 1)), (("leaf", 2), ("leaf", 3)), (("leaf", 4), ("leaf", 5))]
+    assert sched[1] == [(("node", 0), ("node", 1))]
+    assert sched[2] == [(("node", 3), ("node", 2))]
+    assert sum(len(l) for l in oracle.tree_schedule(37)) == 36
+    assert oracle.tree_schedule(1) == []
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_symmetry_and_scale_invariance():
+    rng = np.random.default_rng(5)
+    a, b = rng.standard_normal(50), rng.standard_normal(50)
+    r1, (ca, cb), _ = oracle.adasum_pair(a, b)
+    r2, (cb2, ca2), _ = oracle.adasum_pair(b, a)
+    np.testing.assert_allclose(r1, r2, rtol=1e-14, atol=1e-14)
+    assert (ca, cb) == pytest.approx((ca2, cb2), rel=1e-14)
+    for s in (1e-6, 3.0, 1e8):
+        _, (sa, sb), _ = oracle.adasum_pair(s * a, s * b)
+        assert (sa, sb) == pytest.approx((ca, cb), rel=1e-12)
+
+
+def test_permutation_equivariance_within_segment():
+    rng = np.random.default_rng(6)
+    vecs = [rng.standard_normal(64) for _ in range(8)]
+    perm = rng.permutation(64)
+    r, _, _ = oracle.adasum_tree(vecs)
+    rp, _, _ = oracle.adasum_tree([v[perm] for v in vecs])
+    np.testing.assert_allclose(rp, r[perm], rtol=1e-12, atol=1e-13)
+
+
+def test_segments_are_independent():
+    rng = np.random.default_rng(7)
+    off = [0, 10, 10, 35, 36, 80]
+    vecs = [rng.standard_normal(80) for _ in range(5)]
+    base = oracle.combine(vecs, off)
+    pert = [v.copy() for v in vecs]
+    pert[2][12:30] += 5.0  # only segment 2 ([10, 35))
+    res = oracle.combine(pert, off)
+    changed = np.abs(res["out"] - base["out"]) > 0
+    assert changed[10:35].any()
+    assert not changed[:10].any() and not changed[35:].any()
+    # per-segment result equals the tree on that slice alone
+    seg, _, _ = oracle.adasum_tree([v[35:36] for v in vecs])
+    assert np.array_equal(base["out"][35:36], seg)
+
+
+def test_emitted_norm_identity():
+    # |c|^2 = ca^2 A + 2 ca cb d + cb^2 B, the statistic the next tree level needs
+    rng = np.random.default_rng(8)
+    a, b = rng.standard_normal(100), rng.standard_normal(100)
+    c, (ca, cb), (d, A, B) = oracle.adasum_pair(a, b)
+    assert c @ c == pytest.approx(ca * ca * A + 2 * ca * cb * d + cb * cb * B, rel=1e-12)
+
+
+def test_combine_layout_and_empty_segments():
+    rng = np.random.default_rng(9)
+    off = [0, 0, 3, 3, 7]
+    vecs = [rng.standard_normal(7).astype(np.float32) for _ in range(4)]
+    res = oracle.combine(vecs, off, out_format="f32")
+    assert res["coeffs"].shape == (3, 4, 2) and res["stats"].shape == (3, 4, 3)
+    # an empty segment has zero-norm operands: coefficient 1, statistics 0
+    assert np.all(res["coeffs"][:, 0] == 1.0) and np.all(res["stats"][:, 2] == 0.0)
+    assert np.array_equal(res["out_rounded"], res["out"].astype(np.float32).astype(np.float64))
+    assert oracle.combine(vecs[:1], off)["coeffs"].shape == (0, 4, 2)
+    np.testing.assert_array_equal(oracle.combine(vecs[:1], off)["out"], vecs[0].astype(np.float64))
+    with pytest.raises(ValueError):
+        oracle.combine(vecs, [0, 5, 3, 7])
+    with pytest.raises(ValueError):
+        oracle.combine(vecs, [0, 3, 6])
+
+
+def test_plain_sum_exact_order():
+    rng = np.random.default_rng(10)
+    vecs = [rng.integers(-1000, 1000, size=20).astype(float) for _ in range(6)]
+    np.testing.assert_array_equal(oracle.plain_sum(vecs)["out"], np.sum(vecs, axis=0))
+
+
+def test_orthogonality_zero_segment_nan():
+    vecs = [np.zeros(4), np.zeros(4)]
+    assert np.isnan(oracle.orthogonality(vecs, [0, 4])[0])
+
+
+# ---------------------------------------------------------------- rounding
+
+def _edge_values():
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * np.exp(rng.uniform(-120, 120, 20000)),
+        rng.standard_normal(20000) * np.exp(rng.uniform(-20, 12, 20000)),
+        [0.0, -0.0, 1.0, -1.0, 65504.0, 65520.0, 65519.99, 6e-8, 3e-8, 2.98e-8,
+         2.0 ** -149, 2.0 ** -150, 1.5 * 2.0 ** -149, 3.4028235e38, 3.4028236e38,
+         np.inf, -np.inf, 1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24, 1e300, -1e-300],
+    ])
+    return vals
+
+
+@pytest.mark.parametrize("fmt,npdt", [("f32", np.float32), ("f16", np.float16)])
+def test_rounding_matches_numpy_casts(fmt, npdt):
+    x = _edge_values()
+    with np.errstate(over="ignore"):
+        ref = x.astype(npdt).astype(np.float64)
+    got = round_to_format(x, fmt)
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_rounding_bf16_ties_and_library():
+    # values exactly representable in fp32: torch's fp32 -> bf16 cast is RNE
+    x = _edge_values().astype(np.float32)
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = round_to_format(x.astype(np.float64), "bf16")
+    assert np.array_equal(got, ref)
+    # ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1.0);
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    assert round_to_format(1 + 2.0 ** -8, "bf16") == 1.0
+    assert round_to_format(1 + 3 * 2.0 ** -8, "bf16") == 1 + 2.0 ** -6
+    # directly from fp64 (no double rounding): just above the tie rounds up
+    assert round_to_format(1 + 2.0 ** -8 + 2.0 ** -40, "bf16") == 1 + 2.0 ** -7
+    assert round_to_format(3.4e38, "bf16") == np.inf  # beyond bf16's largest finite
+    assert round_to_format(2.0 ** -133, "bf16") == 2.0 ** -133  # smallest subnormal
+    assert round_to_format(2.0 ** -134, "bf16") == 0.0  # tie to even (zero)
