@@ -1,0 +1,173 @@
+"""Throughput of the Adasum combine on one MI355X.
+
+One step is one full combine (every tree level of every segment) of the
+K gradient buffers of a synthetic workload that is already resident in HBM.
+Default workload: the BERT-Large-shaped set, K = 16 fp32 gradients of
+335,141,888 parameters in 391 segments.
+
+Prints one JSON line: gradient GB/s (K * N * bytes per element / step time),
+the HBM-roofline figures of the dominant kernel (from HIP events around every
+launch inside the timed region) and of the whole path (minimum traffic of
+reading K gradients once and writing one), and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gradient GB/s combined (K·bytes/time) and % of HBM roofline, 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_NAMES = {1: "small_k2_f32", 2: "resnet50_k8_f32", 3: "bert_large_k16_f32",
+                  4: "bert_base_k64_f16", 5: "stress_20k_k32_bf16"}
+BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "distributed_sgd_gradient_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the fp64 oracle on whole segments copied from the GPU workload,
+    adding segments (largest-first order of the layer list) until the budget
+    is spent; one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    order = list(range(5, wl.nseg)) + list(range(0, 5))  # encoder layers first, embeddings last
+    used, elems, spent = [], 0, 0.0
+    with threadpool_limits(limits=1):
+        for s in order:
+            rows = wl.segment_host(s)
+            t0 = time.perf_counter()
+            oracle.adasum_tree(rows)
+            spent += time.perf_counter() - t0
+            used.append(s)
+            elems += rows[0].size
+            if spent >= budget_s:
+                break
+    gbs = wl.K * elems * BYTES[wl.dtype] / spent / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(used)} of {wl.nseg} segments ({elems} of {wl.N} elements per worker), "
+                      f"{spent:.1f} s of fp64 NumPy with one BLAS thread",
+            "seconds": spent}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the combine has no multi-GPU path", file=sys.stderr, flush=True)
+        sys.exit(1)
+
+    import torch
+
+    import distributed_sgd_gradient_amd as A
+    from distributed_sgd_gradient_amd import _native
+    import workloads as W
+
+    dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", "0")))
+    torch.cuda.set_device(dev)
+    log(f"generating workload {args.config} ({WORKLOAD_NAMES[args.config]}) on {dev}")
+    wl = W.make_workload(args.config, seed=args.seed, device=dev)
+    K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
+    out = torch.empty_like(wl.grads[0])
+    ws = torch.empty(max(A.workspace_bytes(K, wl.seg_offsets, wl.grads[0].dtype), 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        A.combine(wl.grads, wl.seg_offsets, out=out, workspace=ws)
+
+    log(f"K={K} N={N} nseg={wl.nseg}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    _native.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = _native.profile_end()
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+
+    grad_bytes = K * N * esz
+    b_min = grad_bytes + N * esz
+    value = grad_bytes / (ms * 1e-3) / 1e9
+    dom_name = max(kernels, key=lambda k: kernels[k]["milliseconds"])
+    dom = kernels[dom_name]
+    per_launch_ms = dom["milliseconds"] / dom["launches"]
+    per_launch_bytes = dom["bytes"] / dom["launches"]
+    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(WORKLOAD_NAMES[args.config], dom_name),
+                "kernel": dom_name, "launch_ms": per_launch_ms, "algorithmic_bytes_per_launch": per_launch_bytes}
+    path = {"B_min_bytes": b_min, "achieved": b_min / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": b_min / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    for name, k in sorted(kernels.items()):
+        log(f"  {name:12s} launches {k['launches']:5d}  {k['milliseconds'] / args.steps:8.3f} ms/step  "
+            f"{k['bytes'] / (k['milliseconds'] * 1e-3) / 1e9 if k['milliseconds'] > 0 else 0:8.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s)")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg,
+                   "io_dtype": wl.dtype, "seed": wl.seed, "parallelism": "none (one GPU)"},
+        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu,
+        "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
+                        "bytes_per_step": v["bytes"] / args.steps} for k, v in kernels.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

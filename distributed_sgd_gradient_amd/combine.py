@@ -1,0 +1,117 @@
+"""Python front end of the Adasum combiner: torch tensors in, torch tensor out.
+
+Only argument marshalling happens here: the tensors' device pointers, the
+segment offsets and the current HIP stream are handed to the C ABI, and every
+step of the combine runs in the library's gfx950 kernels.  torch provides the
+device memory (output, workspace, statistics) and the stream.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _native
+
+DTYPE_CODES = {torch.float32: _native.F32, torch.float16: _native.F16, torch.bfloat16: _native.BF16}
+
+
+def _offsets(seg_offsets, N=None):
+    off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+    if off.ndim != 1 or off.size < 1:
+        raise ValueError("seg_offsets must be a 1-D sequence of nseg + 1 offsets")
+    if N is not None and int(off[-1]) != N:
+        raise ValueError(f"seg_offsets[-1] = {int(off[-1])} but the gradients hold {N} elements")
+    return off
+
+
+def _grad_list(grads):
+    if isinstance(grads, torch.Tensor):
+        if grads.dim() != 2:
+            raise ValueError("a tensor of gradients must be 2-D [K, N]")
+        grads = list(grads.unbind(0))
+    grads = list(grads)
+    if not grads:
+        raise ValueError("need at least one gradient")
+    g0 = grads[0]
+    for g in grads:
+        if not isinstance(g, torch.Tensor) or g.device != g0.device or g.dtype != g0.dtype:
+            raise ValueError("all gradients must be tensors of one dtype on one device")
+        if g.dim() != 1 or g.numel() != g0.numel() or not g.is_contiguous():
+            raise ValueError("all gradients must be contiguous 1-D tensors of equal length")
+    if g0.device.type != "cuda":
+        raise ValueError("gradients must be on a GPU")
+    if g0.dtype not in DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {g0.dtype}")
+    return grads
+
+
+def workspace_bytes(K, seg_offsets, dtype):
+    off = _offsets(seg_offsets)
+    code = DTYPE_CODES[dtype]
+    L = _native.lib()
+    return _native.check(L.adasum_workspace_bytes(
+        K, off.ctypes.data_as(_native._I64P), off.size - 1, code))
+
+
+def combine(grads, seg_offsets, *, out=None, workspace=None, return_coeffs=False, return_stats=False,
+            stream=None):
+    """Tree Adasum of K gradients, each segment on its own.
+
+    grads: list of K contiguous 1-D GPU tensors (fp32 / fp16 / bf16), or one
+      [K, N] tensor.  seg_offsets: nseg + 1 CSR offsets (host).  Returns the
+      combined gradient (same dtype), plus the fp64 coefficient table
+      [K-1, nseg, 2] and statistics table [K-1, nseg, 3] when requested.
+    """
+    grads = _grad_list(grads)
+    g0 = grads[0]
+    off = _offsets(seg_offsets, g0.numel())
+    K, nseg = len(grads), off.size - 1
+    dev = g0.device
+    if out is None:
+        out = torch.empty_like(g0)
+    elif out.device != dev or out.dtype != g0.dtype or out.numel() != g0.numel() or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like the gradients")
+    need = workspace_bytes(K, off, g0.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    coeffs = torch.empty((max(K - 1, 0), nseg, 2), dtype=torch.float64, device=dev) if return_coeffs else None
+    stats = torch.empty((max(K - 1, 0), nseg, 3), dtype=torch.float64, device=dev) if return_stats else None
+    ptrs = (ctypes.c_void_p * K)(*[g.data_ptr() for g in grads])
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    L = _native.lib()
+    with torch.cuda.device(dev):
+        _native.check(L.adasum_combine_ex(
+            ptrs, K, off.ctypes.data_as(_native._I64P), nseg, DTYPE_CODES[g0.dtype],
+            out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            coeffs.data_ptr() if coeffs is not None else None,
+            stats.data_ptr() if stats is not None else None,
+            ctypes.c_void_p(stream.cuda_stream)))
+    if not (return_coeffs or return_stats):
+        return out
+    res = [out]
+    if return_coeffs:
+        res.append(coeffs)
+    if return_stats:
+        res.append(stats)
+    return tuple(res)
+
+
+def combine_cached(grads, seg_offsets, *, out=None, stream=None):
+    """Like :func:`combine` but through ``adasum_combine``, whose workspace the
+    library allocates and caches per (device, stream)."""
+    grads = _grad_list(grads)
+    g0 = grads[0]
+    off = _offsets(seg_offsets, g0.numel())
+    if out is None:
+        out = torch.empty_like(g0)
+    ptrs = (ctypes.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
+    if stream is None:
+        stream = torch.cuda.current_stream(g0.device)
+    L = _native.lib()
+    with torch.cuda.device(g0.device):
+        _native.check(L.adasum_combine(ptrs, len(grads), off.ctypes.data_as(_native._I64P), off.size - 1,
+                                       DTYPE_CODES[g0.dtype], out.data_ptr(),
+                                       ctypes.c_void_p(stream.cuda_stream)))
+    return out

@@ -1,0 +1,517 @@
+// adasum.hip - C ABI, argument validation, plan cache and level scheduler.
+//
+// One call enqueues, for each tree level:
+//   1. a triple-dot pass for the pairs whose statistics are not known yet
+//      (all pairs of level 1; above level 1 only a pair that meets a carried
+//      vector), writing one fp64 partial per (pair, tile);
+//   2. finalize: per (pair, segment) the tile partials are summed in tile
+//      order and turned into the coefficients (ca, cb);
+//   3. combine: every node of the level is computed over every tile; jobs
+//      that compute two sibling nodes also emit the per-tile statistics of
+//      the pair those siblings form one level up, so no level above the first
+//      needs a separate statistics pass.
+// Each of those steps is one launch covering all pairs and all segments of
+// the level (split only when a level has more jobs than one launch's
+// argument block holds).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <list>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/adasum.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace adasum {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+  g_last_error = buf;
+  return ADASUM_EHIP;
+}
+
+// ---------------------------------------------------------------- plan cache
+
+struct DeviceTables {
+  Tile* tiles = nullptr;
+  int32_t* seg_tile = nullptr;
+};
+
+struct CachedPlan {
+  Plan plan;
+  std::map<int, DeviceTables> per_device;
+};
+
+constexpr size_t kMaxCachedPlans = 64;
+
+std::mutex g_mu;
+std::list<std::shared_ptr<CachedPlan>> g_plans;  // most recently used first
+
+bool same_shape(const Plan& p, int K, const int64_t* off, int nseg, DType dt) {
+  return p.K == K && p.nseg == nseg && p.dtype == dt &&
+         std::memcmp(p.offsets.data(), off, sizeof(int64_t) * (size_t)(nseg + 1)) == 0;
+}
+
+void release_tables(CachedPlan& cp) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return;
+  for (auto& kv : cp.per_device) {
+    if (hipSetDevice(kv.first) != hipSuccess) continue;
+    (void)hipDeviceSynchronize();  // kernels of earlier calls may still read the tables
+    (void)hipFree(kv.second.tiles);
+    (void)hipFree(kv.second.seg_tile);
+  }
+  (void)hipSetDevice(cur);
+}
+
+// Caller holds g_mu.
+std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType dt) {
+  for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
+    if (same_shape((*it)->plan, K, off, nseg, dt)) {
+      auto hit = *it;
+      g_plans.erase(it);
+      g_plans.push_front(hit);
+      return hit;
+    }
+  }
+  auto cp = std::make_shared<CachedPlan>();
+  cp->plan = build_plan(K, off, nseg, dt);
+  g_plans.push_front(cp);
+  if (g_plans.size() > kMaxCachedPlans) {
+    release_tables(*g_plans.back());
+    g_plans.pop_back();
+  }
+  return cp;
+}
+
+// Caller holds g_mu.  Uploads the tile tables to `device` once.
+int device_tables(CachedPlan& cp, int device, DeviceTables* out) {
+  auto it = cp.per_device.find(device);
+  if (it != cp.per_device.end()) {
+    *out = it->second;
+    return ADASUM_OK;
+  }
+  const Plan& p = cp.plan;
+  DeviceTables t;
+  const size_t tile_bytes = sizeof(Tile) * (p.tiles.empty() ? 1 : p.tiles.size());
+  const size_t seg_bytes = sizeof(int32_t) * p.seg_tile.size();
+  hipError_t e = hipMalloc(&t.tiles, tile_bytes);
+  if (e != hipSuccess) return fail(ADASUM_ENOMEM, "hipMalloc of the tile table failed");
+  e = hipMalloc(&t.seg_tile, seg_bytes);
+  if (e != hipSuccess) {
+    (void)hipFree(t.tiles);
+    return fail(ADASUM_ENOMEM, "hipMalloc of the segment table failed");
+  }
+  if (!p.tiles.empty()) e = hipMemcpy(t.tiles, p.tiles.data(), sizeof(Tile) * p.tiles.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(t.seg_tile, p.seg_tile.data(), seg_bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(t.tiles);
+    (void)hipFree(t.seg_tile);
+    return fail_hip(e, "uploading the plan tables");
+  }
+  cp.per_device[device] = t;
+  *out = t;
+  return ADASUM_OK;
+}
+
+// ---------------------------------------------------------------- library workspace
+
+struct OwnedWorkspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::map<std::pair<int, void*>, OwnedWorkspace> g_ws;  // (device, stream) -> buffer; guarded by g_mu
+
+// ---------------------------------------------------------------- launch timing
+
+enum KernelKind { kDot = 0, kFinalize, kCombine, kWiden, kCopy, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"triple_dot", "finalize", "combine", "widen", "copy"};
+
+struct ProfRecord {
+  int kind;
+  double bytes;
+  hipEvent_t start, stop;
+};
+
+bool g_prof_on = false;                                 // guarded by g_mu
+std::vector<ProfRecord> g_prof;                         // guarded by g_mu
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_ev_pool;  // guarded by g_mu
+
+// Records the start event of a launch; returns the record index or -1.
+int prof_start(int kind, double bytes, hipStream_t st) {
+  if (!g_prof_on) return -1;
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  if (!g_ev_pool.empty()) {
+    ev = g_ev_pool.back();
+    g_ev_pool.pop_back();
+  } else if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess) {
+    return -1;
+  }
+  if (hipEventRecord(ev.first, st) != hipSuccess) {
+    g_ev_pool.push_back(ev);
+    return -1;
+  }
+  g_prof.push_back(ProfRecord{kind, bytes, ev.first, ev.second});
+  return (int)g_prof.size() - 1;
+}
+
+void prof_stop(int idx, hipStream_t st) {
+  if (idx >= 0) (void)hipEventRecord(g_prof[idx].stop, st);
+}
+
+// ---------------------------------------------------------------- validation helpers
+
+struct Range {
+  uintptr_t lo, hi;
+  const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks every pointer argument of a combine call against the shape.
+int validate_buffers(const void* const* grads, int K, int64_t N, size_t esz, int nseg, const void* out,
+                     const void* ws, size_t ws_bytes, size_t ws_needed, const double* coeffs,
+                     const double* stats) {
+  char buf[200];
+  if (grads == nullptr) return fail(ADASUM_EINVAL, "grads is NULL");
+  const size_t vec_bytes = (size_t)N * esz;
+  if (N > 0) {
+    if (out == nullptr) return fail(ADASUM_EINVAL, "out is NULL");
+    if (!aligned16(out)) return fail(ADASUM_EINVAL, "out must be 16-byte aligned");
+    for (int k = 0; k < K; ++k) {
+      if (grads[k] == nullptr) {
+        snprintf(buf, sizeof buf, "grads[%d] is NULL", k);
+        return fail(ADASUM_EINVAL, buf);
+      }
+      if (!aligned16(grads[k])) {
+        snprintf(buf, sizeof buf, "grads[%d] must be 16-byte aligned", k);
+        return fail(ADASUM_EINVAL, buf);
+      }
+    }
+  }
+  if (ws_needed > 0) {
+    if (ws == nullptr) return fail(ADASUM_EINVAL, "workspace is NULL but this shape needs one");
+    if (ws_bytes < ws_needed) {
+      snprintf(buf, sizeof buf, "workspace too small: %zu bytes given, %zu needed", ws_bytes, ws_needed);
+      return fail(ADASUM_EINVAL, buf);
+    }
+    if (!aligned16(ws)) return fail(ADASUM_EINVAL, "workspace must be 16-byte aligned");
+  }
+  std::vector<Range> others;  // buffers that may be written must not overlap anything
+  const size_t nodes = K > 1 ? (size_t)(K - 1) : 0;
+  auto rng = [](const void* p, size_t bytes, const char* name) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes, name};
+  };
+  std::vector<Range> written;
+  if (vec_bytes > 0) written.push_back(rng(out, vec_bytes, "out"));
+  if (ws_needed > 0) written.push_back(rng(ws, ws_needed, "workspace"));
+  if (coeffs && nodes * nseg > 0) written.push_back(rng(coeffs, nodes * nseg * 2 * sizeof(double), "coeffs"));
+  if (stats && nodes * nseg > 0) written.push_back(rng(stats, nodes * nseg * 3 * sizeof(double), "stats"));
+  for (size_t i = 0; i < written.size(); ++i) {
+    for (size_t j = i + 1; j < written.size(); ++j) {
+      if (overlaps(written[i], written[j])) {
+        snprintf(buf, sizeof buf, "%s overlaps %s", written[i].name, written[j].name);
+        return fail(ADASUM_EINVAL, buf);
+      }
+    }
+    if (vec_bytes == 0) continue;
+    for (int k = 0; k < K; ++k) {
+      if (overlaps(written[i], rng(grads[k], vec_bytes, "input"))) {
+        snprintf(buf, sizeof buf, "%s overlaps input grads[%d]", written[i].name, k);
+        return fail(ADASUM_EINVAL, buf);
+      }
+    }
+  }
+  return ADASUM_OK;
+}
+
+// ---------------------------------------------------------------- scheduler
+
+struct CallBuffers {
+  const void* const* grads;
+  void* out;
+  char* ws;
+  double* coeffs;
+  double* stats;
+};
+
+const void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
+  switch (r.kind) {
+    case Ref::Input: return b.grads[r.idx];
+    case Ref::Slot: return b.ws + p.ws_slots + (size_t)r.idx * (size_t)p.N * sizeof(float);
+    case Ref::Out: return b.out;
+  }
+  return nullptr;
+}
+
+DType ref_type(const Plan& p, Ref r) { return r.kind == Ref::Slot ? DType::F32 : p.dtype; }
+
+int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStream_t st) {
+  const int ntiles = (int)p.tiles.size();
+  const size_t esz = dtype_size(p.dtype);
+  hipError_t e;
+  if (p.K == 1) {
+    if (p.N > 0) {
+      const int pr = prof_start(kCopy, 2.0 * (double)p.N * esz, st);
+      e = hipMemcpyAsync(b.out, b.grads[0], (size_t)p.N * esz, hipMemcpyDeviceToDevice, st);
+      prof_stop(pr, st);
+      if (e != hipSuccess) return fail_hip(e, "copying the single input");
+    }
+    return ADASUM_OK;
+  }
+  double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
+  int first_node = 0;
+  for (size_t l = 0; l < p.levels.size(); ++l) {
+    const Level& lv = p.levels[l];
+    // 1. statistics of pairs no lower combine emitted
+    if (ntiles > 0 && !lv.dot_pairs.empty()) {
+      for (size_t c = 0; c < lv.dot_pairs.size(); c += kMaxDotPairs) {
+        DotArgs a{};
+        int n = 0;
+        DType op_t = DType::F32;
+        for (size_t i = c; i < lv.dot_pairs.size() && n < kMaxDotPairs; ++i, ++n) {
+          const Pair& pr = lv.pairs[lv.dot_pairs[i]];
+          a.a[n] = ref_ptr(p, b, pr.left);
+          a.b[n] = ref_ptr(p, b, pr.right);
+          a.row[n] = lv.dot_pairs[i];
+          op_t = ref_type(p, pr.left);  // both operands of a level share one type
+        }
+        a.tiles = dt.tiles;
+        a.ntiles = ntiles;
+        a.partials = partials;
+        const int pr = prof_start(kDot, (double)n * (2.0 * (double)p.N * dtype_size(op_t) + 24.0 * ntiles), st);
+        e = launch_triple_dot(op_t, a, n, st);
+        prof_stop(pr, st);
+        if (e != hipSuccess) return fail_hip(e, "launching triple_dot");
+      }
+    }
+    // 2. coefficients of every (pair, segment) of this level
+    if (p.nseg > 0) {
+      FinalizeArgs f{};
+      f.partials = partials;
+      f.seg_tile = dt.seg_tile;
+      f.ntiles = ntiles;
+      f.nseg = p.nseg;
+      f.npairs = (int)lv.pairs.size();
+      f.first_node = first_node;
+      f.coeffs = b.coeffs;
+      f.stats = b.stats;
+      const int pr = prof_start(kFinalize, (double)f.npairs * (24.0 * ntiles + 40.0 * p.nseg), st);
+      e = launch_finalize(f, st);
+      prof_stop(pr, st);
+      if (e != hipSuccess) return fail_hip(e, "launching finalize");
+    }
+    // the input carried past level 1 (odd K) is widened into its fp32 slot
+    if (l == 0 && p.carry_slot >= 0 && ntiles > 0) {
+      WidenArgs w{};
+      w.src = b.grads[p.K - 1];
+      w.dst = reinterpret_cast<float*>(b.ws + p.ws_slots + (size_t)p.carry_slot * (size_t)p.N * sizeof(float));
+      w.tiles = dt.tiles;
+      const int pr = prof_start(kWiden, (double)p.N * (esz + 4.0), st);
+      e = launch_widen(p.dtype, w, ntiles, st);
+      prof_stop(pr, st);
+      if (e != hipSuccess) return fail_hip(e, "launching widen");
+    }
+    // 3. combine, sibling jobs and single-node jobs in separate launches
+    if (ntiles > 0) {
+      for (int sib = 1; sib >= 0; --sib) {
+        std::vector<const Job*> jobs;
+        for (const Job& jb : lv.jobs)
+          if ((jb.pair[1] >= 0) == (sib == 1)) jobs.push_back(&jb);
+        for (size_t c = 0; c < jobs.size(); c += kMaxJobs) {
+          CombineArgs a{};
+          int n = 0;
+          DType in_t = DType::F32, out_t = DType::F32;
+          for (size_t i = c; i < jobs.size() && n < kMaxJobs; ++i, ++n) {
+            const Job& jb = *jobs[i];
+            for (int h = 0; h < (sib ? 2 : 1); ++h) {
+              const Pair& pr = lv.pairs[jb.pair[h]];
+              a.x[n][2 * h] = ref_ptr(p, b, pr.left);
+              a.x[n][2 * h + 1] = ref_ptr(p, b, pr.right);
+              a.y[n][h] = const_cast<void*>(ref_ptr(p, b, pr.dst));
+              a.node[n][h] = pr.node;
+              in_t = ref_type(p, pr.left);
+              out_t = ref_type(p, pr.dst);
+            }
+            a.emit[n] = jb.emit;
+          }
+          a.tiles = dt.tiles;
+          a.ntiles = ntiles;
+          a.nseg = p.nseg;
+          a.coeffs = b.coeffs;
+          a.partials = partials;
+          const double per_job = sib ? 4.0 * p.N * dtype_size(in_t) + 2.0 * p.N * dtype_size(out_t) + 24.0 * ntiles
+                                     : 2.0 * p.N * dtype_size(in_t) + 1.0 * p.N * dtype_size(out_t);
+          const int pr = prof_start(kCombine, n * per_job, st);
+          e = launch_combine(in_t, out_t, sib == 1, a, n, st);
+          prof_stop(pr, st);
+          if (e != hipSuccess) return fail_hip(e, "launching combine");
+        }
+      }
+    }
+    first_node += (int)lv.pairs.size();
+  }
+  return ADASUM_OK;
+}
+
+int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, void* out,
+                 void* workspace, size_t workspace_bytes, double* coeffs, double* stats, void* stream,
+                 bool owned_workspace) {
+  std::string err;
+  if (!validate_shape(K, seg_offsets, nseg, dtype, &err)) return fail(ADASUM_EINVAL, err);
+  const DType dt = static_cast<DType>(dtype);
+  const int64_t N = seg_offsets[nseg];
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  std::shared_ptr<CachedPlan> cp = find_plan(K, seg_offsets, nseg, dt);
+  const Plan& p = cp->plan;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int device = 0;
+
+  if (owned_workspace) {
+    int rc = validate_buffers(grads, K, N, dtype_size(dt), nseg, out, nullptr, 0, 0, nullptr, nullptr);
+    if (rc != ADASUM_OK) return rc;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    OwnedWorkspace& ow = g_ws[{device, stream}];
+    if (ow.bytes < p.ws_total) {
+      if (ow.ptr) {
+        e = hipStreamSynchronize(st);  // earlier calls on this stream may still use the old buffer
+        if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize before growing the workspace");
+        (void)hipFree(ow.ptr);
+        ow.ptr = nullptr;
+        ow.bytes = 0;
+      }
+      e = hipMalloc(&ow.ptr, p.ws_total);
+      if (e != hipSuccess) {
+        ow.ptr = nullptr;
+        return fail(ADASUM_ENOMEM, "hipMalloc of the library workspace failed");
+      }
+      ow.bytes = p.ws_total;
+    }
+    workspace = ow.ptr;
+    workspace_bytes = ow.bytes;
+    // inputs and out were checked above; the library buffer cannot alias them
+  } else {
+    int rc = validate_buffers(grads, K, N, dtype_size(dt), nseg, out, workspace, workspace_bytes, p.ws_total,
+                              coeffs, stats);
+    if (rc != ADASUM_OK) return rc;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  }
+
+  DeviceTables tables;
+  int rc = device_tables(*cp, device, &tables);
+  if (rc != ADASUM_OK) return rc;
+  char* ws = static_cast<char*>(workspace);
+  CallBuffers b;
+  b.grads = grads;
+  b.out = out;
+  b.ws = ws;
+  b.coeffs = coeffs ? coeffs : reinterpret_cast<double*>(ws + p.ws_coeffs);
+  b.stats = stats ? stats : reinterpret_cast<double*>(ws + p.ws_stats);
+  return enqueue(p, tables, b, st);
+}
+
+}  // namespace
+}  // namespace adasum
+
+extern "C" {
+
+int adasum_combine(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, void* out,
+                   void* stream) {
+  return adasum::combine_impl(grads, K, seg_offsets, nseg, dtype, out, nullptr, 0, nullptr, nullptr, stream,
+                              true);
+}
+
+int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int nseg, int dtype) {
+  std::string err;
+  if (!adasum::validate_shape(K, seg_offsets, nseg, dtype, &err)) return adasum::fail(ADASUM_EINVAL, err);
+  std::lock_guard<std::mutex> lock(adasum::g_mu);
+  return (int64_t)adasum::find_plan(K, seg_offsets, nseg, static_cast<adasum::DType>(dtype))->plan.ws_total;
+}
+
+int adasum_combine_ex(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, void* out,
+                      void* workspace, size_t workspace_bytes, double* coeffs, double* stats, void* stream) {
+  return adasum::combine_impl(grads, K, seg_offsets, nseg, dtype, out, workspace, workspace_bytes, coeffs, stats,
+                              stream, false);
+}
+
+int adasum_profile_begin(void) {
+  std::lock_guard<std::mutex> lock(adasum::g_mu);
+  for (auto& r : adasum::g_prof) adasum::g_ev_pool.push_back({r.start, r.stop});
+  adasum::g_prof.clear();
+  adasum::g_prof_on = true;
+  return ADASUM_OK;
+}
+
+int adasum_profile_end(adasum_kernel_time_t* rows, int max_rows) {
+  using namespace adasum;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_prof_on = false;
+  if (max_rows < 0 || (max_rows > 0 && rows == nullptr))
+    return fail(ADASUM_EINVAL, "rows must hold max_rows >= 0 entries");
+  int launches[kNumKinds] = {0};
+  double ms[kNumKinds] = {0}, bytes[kNumKinds] = {0};
+  int rc = ADASUM_OK;
+  for (auto& r : g_prof) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) rc = fail_hip(e, "reading profile events");
+    launches[r.kind] += 1;
+    ms[r.kind] += t;
+    bytes[r.kind] += r.bytes;
+    g_ev_pool.push_back({r.start, r.stop});
+  }
+  g_prof.clear();
+  if (rc != ADASUM_OK) return rc;
+  int n = 0;
+  for (int k = 0; k < kNumKinds; ++k) {
+    if (launches[k] == 0) continue;
+    if (n < max_rows) {
+      std::memset(&rows[n], 0, sizeof(rows[n]));
+      std::strncpy(rows[n].kernel, kKindNames[k], sizeof(rows[n].kernel) - 1);
+      rows[n].launches = launches[k];
+      rows[n].milliseconds = ms[k];
+      rows[n].bytes = bytes[k];
+    }
+    ++n;
+  }
+  return n < max_rows ? n : max_rows;
+}
+
+const char* adasum_strerror(int code) {
+  switch (code) {
+    case ADASUM_OK: return "success";
+    case ADASUM_EINVAL: return "invalid argument";
+    case ADASUM_ENOMEM: return "out of memory";
+    case ADASUM_EHIP: return "HIP runtime error";
+  }
+  return "unknown error code";
+}
+
+const char* adasum_last_error(void) { return adasum::g_last_error.c_str(); }
+
+int adasum_version(void) { return 100; }
+
+}  // extern "C"

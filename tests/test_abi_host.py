@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/adasum.h declares, and rejects invalid arguments before any HIP call
+(so these run without a GPU; no call here reaches a kernel)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from distributed_sgd_gradient_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "adasum.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ADASUM_API\s+[\w\s\*]+?\b(adasum_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(_native.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _native.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (adasum_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_strerror():
+    lib = _native.lib()
+    assert lib.adasum_version() >= 100
+    for code in (0, -1, -2, -3):
+        assert lib.adasum_strerror(code)
+    assert lib.adasum_strerror(-99) == b"unknown error code"
+
+
+def _off(*vals):
+    a = np.asarray(vals, dtype=np.int64)
+    return a, a.ctypes.data_as(_native._I64P)
+
+
+def _call_ex(K=2, off=(0, 8, 16), dtype=0, grads=None, out=FAKE + (1 << 30), ws=FAKE + (2 << 30),
+             ws_bytes=1 << 20, coeffs=None, stats=None):
+    lib = _native.lib()
+    arr, p = _off(*off)
+    if grads is None:
+        grads = [FAKE + (k << 20) for k in range(K)]
+    ptrs = (ctypes.c_void_p * max(len(grads), 1))(*grads)
+    rc = lib.adasum_combine_ex(ptrs, K, p, arr.size - 1, dtype, out, ws, ws_bytes, coeffs, stats, None)
+    return rc, lib.adasum_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,needle", [
+    (dict(K=0), "K must be >= 1"),
+    (dict(dtype=7), "unknown dtype"),
+    (dict(off=(1, 8, 16)), "seg_offsets[0] must be 0"),
+    (dict(off=(0, 9, 8)), "non-decreasing"),
+    (dict(out=None), "out is NULL"),
+    (dict(out=FAKE + (1 << 30) + 4), "out must be 16-byte aligned"),
+    (dict(grads=[FAKE, FAKE + 8]), "grads[1] must be 16-byte aligned"),
+    (dict(grads=[FAKE, 0]), "grads[1] is NULL"),
+    (dict(out=FAKE + 16), "overlaps input"),
+    (dict(ws=None), "workspace is NULL"),
+    (dict(ws_bytes=64), "workspace too small"),
+    (dict(ws=FAKE + 32), "overlaps input"),
+    (dict(coeffs=FAKE + (1 << 30) + 8), "overlaps"),
+])
+def test_invalid_arguments_rejected(kwargs, needle):
+    rc, msg = _call_ex(**kwargs)
+    assert rc == _native.EINVAL
+    assert needle in msg
+
+
+def test_negative_nseg_and_null_offsets():
+    lib = _native.lib()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE + 4096)
+    assert lib.adasum_combine(ptrs, 2, None, 1, 0, FAKE + 8192, None) == _native.EINVAL
+    arr, p = _off(0)
+    assert lib.adasum_combine(ptrs, 2, p, -1, 0, FAKE + 8192, None) == _native.EINVAL
+    assert lib.adasum_workspace_bytes(2, p, -1, 0) == _native.EINVAL
+
+
+def test_workspace_size_properties():
+    lib = _native.lib()
+
+    def ws(K, off, dtype=0):
+        arr, p = _off(*off)
+        return lib.adasum_workspace_bytes(K, p, arr.size - 1, dtype)
+
+    assert ws(1, (0, 1000)) == 0                 # K = 1 is a copy
+    two = ws(2, (0, 1000))
+    assert 0 < two < 4096                        # K = 2: no fp32 slots, only tables
+    # an odd K needs one more fp32 slot for the carried input
+    n = 1 << 20
+    assert ws(4, (0, n)) >= 2 * n * 4 and ws(3, (0, n)) >= 2 * n * 4
+    assert ws(16, (0, 2 * n)) > ws(16, (0, n))
+    assert ws(16, (0, 0)) >= 0 and ws(2, (0,)) >= 0

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Gates (the stated tolerances of the combiner):
+  * output: relative L2 error ||gpu - oracle|| / ||oracle|| <= 1e-5 for fp32
+    inputs and <= 2e-3 for fp16 / bf16 inputs, the oracle rounded once to the
+    output dtype;
+  * coefficients: |c_gpu - c_oracle| <= 1e-6 * max(1, |c_oracle|) for every
+    (node, segment);
+  * statistics (reported for diagnosis, gated loosely): relative 1e-5.
+Inputs come from the seeded generators in ``workloads`` on the GPU; the
+oracle sees the same tensors copied to the host.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+COEFF_TOL = 1e-6
+
+
+def _A():
+    import distributed_sgd_gradient_amd as A
+    return A
+
+
+def say(*args):
+    print("[parity]", *args, flush=True)
+
+
+def rel_l2(x, ref):
+    den = float(np.linalg.norm(ref))
+    num = float(np.linalg.norm(x - ref))
+    return num / den if den > 0 else num
+
+
+def check_coeffs(c_gpu, c_ref, what):
+    err = np.abs(c_gpu - c_ref) / np.maximum(1.0, np.abs(c_ref))
+    assert np.all(np.isfinite(c_gpu)), what
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= COEFF_TOL, f"{what}: coefficient error {worst:.3g}"
+    return worst
+
+
+def check_stats(s_gpu, s_ref, what):
+    if s_ref.size == 0:
+        return
+    d, A, B = s_ref[..., 0], s_ref[..., 1], s_ref[..., 2]
+    scale = np.sqrt(np.maximum(A, 0) * np.maximum(B, 0))
+    assert np.all(np.abs(s_gpu[..., 1] - A) <= 1e-5 * A + 1e-300), what
+    assert np.all(np.abs(s_gpu[..., 2] - B) <= 1e-5 * B + 1e-300), what
+    assert np.all(np.abs(s_gpu[..., 0] - d) <= 1e-5 * scale + 1e-300), what
+
+
+def run_gpu(wl):
+    A = _A()
+    out, coeffs, stats = A.combine(wl.grads, wl.seg_offsets, return_coeffs=True, return_stats=True)
+    torch.cuda.synchronize()
+    return out, coeffs, stats
+
+
+def full_check(wl, label):
+    """Compare every element and every (node, segment) with the oracle."""
+    say(label, f"K={wl.K} dtype={wl.dtype} N={wl.N} nseg={wl.nseg}")
+    out, coeffs, stats = run_gpu(wl)
+    ref = oracle.combine([g.double().cpu().numpy() for g in wl.grads], wl.seg_offsets, out_format=wl.dtype)
+    got = out.double().cpu().numpy()
+    err = rel_l2(got, ref["out_rounded"])
+    assert err <= TOL[wl.dtype], f"{label}: relative L2 {err:.3g}"
+    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], label)
+    check_stats(stats.cpu().numpy(), ref["stats"], label)
+    return got, ref, err
+
+
+def sampled_check(wl, segments, label):
+    """Full-size run; compare the chosen segments one by one with the oracle."""
+    say(label, f"K={wl.K} dtype={wl.dtype} N={wl.N} nseg={wl.nseg} sampled={len(segments)}")
+    out, coeffs, stats = run_gpu(wl)
+    c_all = coeffs.cpu().numpy()
+    s_all = stats.cpu().numpy()
+    worst = 0.0
+    num = den = 0.0
+    for s in segments:
+        lo, hi = int(wl.seg_offsets[s]), int(wl.seg_offsets[s + 1])
+        rows = wl.segment_host(s)
+        res, cf, st = oracle.adasum_tree(rows)
+        ref = oracle.round_to_format(res, wl.dtype)
+        got = out[lo:hi].double().cpu().numpy()
+        num += float(np.sum((got - ref) ** 2))
+        den += float(np.sum(ref ** 2))
+        worst = max(worst, check_coeffs(c_all[:, s], np.asarray(cf).reshape(-1, 2), f"{label} seg {s}"))
+        check_stats(s_all[:, s], np.asarray(st).reshape(-1, 3), f"{label} seg {s}")
+    err = np.sqrt(num / den) if den > 0 else np.sqrt(num)
+    say(label, f"sampled relative L2 {err:.3g}, worst coefficient error {worst:.3g}")
+    assert err <= TOL[wl.dtype]
+    return out
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_config1_full(gpu):
+    wl = W.make_workload(1, device=gpu)
+    _, _, err = full_check(wl, "config1")
+    say("config1 relative L2", err)
+
+
+def test_config2_full(gpu):
+    wl = W.make_workload(2, device=gpu)
+    full_check(wl, "config2")
+
+
+def _spread(nseg, rng, extra=()):
+    pick = set(range(min(3, nseg))) | set(range(max(0, nseg - 3), nseg)) | set(extra)
+    pick |= set(rng.choice(nseg, size=min(8, nseg), replace=False).tolist())
+    return sorted(pick)
+
+
+def test_config3_sampled_full_size(gpu):
+    # the BERT-Large workload at full size, as the benchmark runs it
+    wl = W.make_workload(3, device=gpu)
+    lengths = np.diff(wl.seg_offsets)
+    segs = _spread(wl.nseg, np.random.default_rng(3), extra=[int(np.argmax(lengths)), 10, 11, 15, 16])
+    sampled_check(wl, segs, "config3")
+
+
+def test_config4_sampled_full_size(gpu):
+    wl = W.make_workload(4, device=gpu)
+    segs = _spread(wl.nseg, np.random.default_rng(4), extra=[0, 9, 13])
+    sampled_check(wl, segs, "config4")
+
+
+def test_config5_sampled_full_size(gpu):
+    wl = W.make_workload(5, device=gpu)
+    lengths = np.diff(wl.seg_offsets)
+    zero = wl.notes["params"]["zero"]
+    flagged = np.flatnonzero(zero.any(axis=0))
+    all_zero = np.flatnonzero(zero.all(axis=0))
+    rng = np.random.default_rng(5)
+    extra = list(flagged[:12]) + list(all_zero[:2]) + [int(np.argmin(lengths)), int(np.argmax(lengths))]
+    extra += list(np.flatnonzero(lengths == 1)[:5])
+    segs = _spread(wl.nseg, rng, extra=extra)
+    sampled_check(wl, [int(s) for s in segs], "config5")
+
+
+# ---------------------------------------------------------------- edge cases
+
+RAGGED = [1, 3, 8, 9, 0, 8191, 8192, 8193, 20000, 5, 16, 17]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16])
+def test_small_K_ragged_segments(gpu, K, dtype):
+    wl = W.random_case(K, RAGGED, dtype=dtype, seed=K, kind="shared")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"ragged K={K} {dtype}")
+
+
+def test_fp16_subnormal_scales(gpu):
+    wl = W.random_case(8, [3000] * 16 + [7, 1], dtype="f16", seed=11, kind="scaled")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, "fp16 scaled")
+
+
+def test_zero_workers(gpu):
+    wl = W.random_case(8, [100, 1, 9000, 33], dtype="bf16", seed=12, zero_workers=(0, 3, 4, 5))
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    got, ref, _ = full_check(wl, "zero workers")
+    allzero = W.random_case(4, [50, 7], seed=13, zero_workers=(0, 1, 2, 3))
+    allzero.grads = [g.to(gpu) for g in allzero.grads]
+    out, coeffs, stats = run_gpu(allzero)
+    assert torch.count_nonzero(out) == 0
+    assert torch.all(coeffs == 1.0) and torch.all(stats == 0.0)
+
+
+def test_antiparallel_pair_is_exactly_zero(gpu):
+    A = _A()
+    g = torch.randn(10000, generator=torch.Generator().manual_seed(5)).to(gpu)
+    out, coeffs = A.combine([g, -g], [0, 10000], return_coeffs=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+    assert torch.all(coeffs == 1.5)
+
+
+def test_orthogonal_supports_give_exact_sum(gpu):
+    A = _A()
+    n = 4096
+    gs = []
+    for k in range(4):
+        x = torch.zeros(n)
+        x[k * 1000:(k + 1) * 1000] = torch.randn(1000, generator=torch.Generator().manual_seed(k))
+        gs.append(x.to(gpu))
+    out = A.combine(gs, [0, n])
+    torch.cuda.synchronize()
+    assert torch.equal(out, gs[0] + gs[1] + gs[2] + gs[3])
+
+
+@pytest.mark.parametrize("K", [2, 5, 16])
+def test_identical_inputs_return_input_exactly(gpu, K):
+    A = _A()
+    g = torch.randn(12345, generator=torch.Generator().manual_seed(K)).to(gpu)
+    out = A.combine([g] * K, [0, 100, 12345])
+    torch.cuda.synchronize()
+    assert torch.equal(out, g)
+
+
+def test_no_segments_and_empty_segments(gpu):
+    A = _A()
+    e = torch.empty(0, device=gpu)
+    out = A.combine([e, e, e], [0])
+    assert out.numel() == 0
+    out, coeffs, stats = A.combine([e, e, e], [0, 0, 0], return_coeffs=True, return_stats=True)
+    torch.cuda.synchronize()
+    assert coeffs.shape == (2, 2, 2) and torch.all(coeffs == 1.0) and torch.all(stats == 0.0)
+
+
+def test_deterministic_across_runs_and_streams(gpu):
+    A = _A()
+    wl = W.random_case(16, [70000, 12345, 3, 200000], dtype="f32", seed=21, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    first = A.combine(grads, wl.seg_offsets, return_coeffs=True)
+    second = A.combine(grads, wl.seg_offsets, return_coeffs=True)
+    side = torch.cuda.Stream(device=gpu)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        third = A.combine(grads, wl.seg_offsets, return_coeffs=True)
+    torch.cuda.synchronize()
+    for x, y in ((first, second), (first, third)):
+        assert torch.equal(x[0], y[0]) and torch.equal(x[1], y[1])
+    cached = A.combine_cached(grads, wl.seg_offsets)
+    torch.cuda.synchronize()
+    assert torch.equal(cached, first[0])
+
+
+def test_stacked_tensor_input_and_out_argument(gpu):
+    A = _A()
+    wl = W.random_case(4, [1000, 24], dtype="f32", seed=31)
+    stacked = torch.stack(wl.grads).to(gpu)  # rows of 1024 fp32: 16-byte aligned
+    out = torch.empty(1024, device=gpu)
+    res = A.combine(stacked, wl.seg_offsets, out=out)
+    torch.cuda.synchronize()
+    assert res.data_ptr() == out.data_ptr()
+    ref = A.combine([g.to(gpu) for g in wl.grads], wl.seg_offsets)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
