@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 3 plain fp32 copies of MIB MiB (read MIB, write MIB) "
+                         "so that rocprofv3 counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -108,6 +111,15 @@ def main():
 
     dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", "0")))
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 3}))
+        return
     log(f"generating workload {args.config} ({WORKLOAD_NAMES[args.config]}) on {dev}")
     wl = W.make_workload(args.config, seed=args.seed, device=dev)
     K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
