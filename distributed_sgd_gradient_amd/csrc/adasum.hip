@@ -1,20 +1,21 @@
-// adasum.hip - C ABI, argument validation, plan cache and level scheduler.
+// adasum.hip - C ABI, argument validation, plan cache and stage scheduler.
 //
-// One call enqueues, for each tree level:
-//   1. a triple-dot pass for the pairs whose statistics are not known yet
-//      (all pairs of level 1; above level 1 only a pair that meets a carried
-//      vector), writing one fp64 partial per (pair, tile);
-//   2. finalize: per (pair, segment) the tile partials are summed in tile
-//      order and turned into the coefficients (ca, cb);
-//   3. combine: every node of the level is computed over every tile; jobs
-//      that compute two sibling nodes also emit the per-tile statistics of
-//      the pair those siblings form one level up, so no level above the first
-//      needs a separate statistics pass.
-// Each of those steps is one launch covering all pairs and all segments of
-// the level (split only when a level has more jobs than one launch's
-// argument block holds).
+// The tree is cut into stages of at most four levels; each stage is a set
+// of blocks (subtrees of at most 16 operands).  One call enqueues, stage by
+// stage:
+//   1. widen: inputs carried into a stage above the first become fp32 slots;
+//   2. gram: one launch per block size over every block and every tile: the
+//      fp64 Gram partials of each block's operands;
+//   3. tree: one launch over every (block, segment): tile partials summed in
+//      tile order, every merge of the block evaluated on the Gram matrix
+//      (statistics, coefficients), the final operand weights written;
+//   4. wsum: one launch per (block size, types) over every block and tile:
+//      the block's result, sum_k w_k x_k, into an fp32 slot or into out.
+// So a combine of K <= 16 gradients is three launches and two passes over
+// the inputs, whatever the number of segments.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <list>
@@ -51,6 +52,8 @@ int fail_hip(hipError_t e, const char* what) {
 struct DeviceTables {
   Tile* tiles = nullptr;
   int32_t* seg_tile = nullptr;
+  BlockDesc* descs = nullptr;
+  Merge* merges = nullptr;
 };
 
 struct CachedPlan {
@@ -76,6 +79,8 @@ void release_tables(CachedPlan& cp) {
     (void)hipDeviceSynchronize();  // kernels of earlier calls may still read the tables
     (void)hipFree(kv.second.tiles);
     (void)hipFree(kv.second.seg_tile);
+    (void)hipFree(kv.second.descs);
+    (void)hipFree(kv.second.merges);
   }
   (void)hipSetDevice(cur);
 }
@@ -100,7 +105,7 @@ std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType
   return cp;
 }
 
-// Caller holds g_mu.  Uploads the tile tables to `device` once.
+// Caller holds g_mu.  Uploads the plan tables to `device` once.
 int device_tables(CachedPlan& cp, int device, DeviceTables* out) {
   auto it = cp.per_device.find(device);
   if (it != cp.per_device.end()) {
@@ -109,21 +114,35 @@ int device_tables(CachedPlan& cp, int device, DeviceTables* out) {
   }
   const Plan& p = cp.plan;
   DeviceTables t;
-  const size_t tile_bytes = sizeof(Tile) * (p.tiles.empty() ? 1 : p.tiles.size());
-  const size_t seg_bytes = sizeof(int32_t) * p.seg_tile.size();
-  hipError_t e = hipMalloc(&t.tiles, tile_bytes);
-  if (e != hipSuccess) return fail(ADASUM_ENOMEM, "hipMalloc of the tile table failed");
-  e = hipMalloc(&t.seg_tile, seg_bytes);
-  if (e != hipSuccess) {
-    (void)hipFree(t.tiles);
-    return fail(ADASUM_ENOMEM, "hipMalloc of the segment table failed");
+  struct Upload {
+    void** dst;
+    const void* src;
+    size_t bytes;
+  } ups[] = {
+      {reinterpret_cast<void**>(&t.tiles), p.tiles.data(), sizeof(Tile) * p.tiles.size()},
+      {reinterpret_cast<void**>(&t.seg_tile), p.seg_tile.data(), sizeof(int32_t) * p.seg_tile.size()},
+      {reinterpret_cast<void**>(&t.descs), p.descs.data(), sizeof(BlockDesc) * p.descs.size()},
+      {reinterpret_cast<void**>(&t.merges), p.merges.data(), sizeof(Merge) * p.merges.size()},
+  };
+  int rc = ADASUM_OK;
+  for (Upload& u : ups) {
+    if (hipMalloc(u.dst, u.bytes > 0 ? u.bytes : 16) != hipSuccess) {
+      *u.dst = nullptr;
+      rc = fail(ADASUM_ENOMEM, "hipMalloc of a plan table failed");
+      break;
+    }
+    if (u.bytes > 0) {
+      hipError_t e = hipMemcpy(*u.dst, u.src, u.bytes, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        rc = fail_hip(e, "uploading the plan tables");
+        break;
+      }
+    }
   }
-  if (!p.tiles.empty()) e = hipMemcpy(t.tiles, p.tiles.data(), sizeof(Tile) * p.tiles.size(), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(t.seg_tile, p.seg_tile.data(), seg_bytes, hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(t.tiles);
-    (void)hipFree(t.seg_tile);
-    return fail_hip(e, "uploading the plan tables");
+  if (rc != ADASUM_OK) {
+    for (Upload& u : ups)
+      if (*u.dst) (void)hipFree(*u.dst);
+    return rc;
   }
   cp.per_device[device] = t;
   *out = t;
@@ -140,8 +159,8 @@ std::map<std::pair<int, void*>, OwnedWorkspace> g_ws;  // (device, stream) -> bu
 
 // ---------------------------------------------------------------- launch timing
 
-enum KernelKind { kDot = 0, kFinalize, kCombine, kWiden, kCopy, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"triple_dot", "finalize", "combine", "widen", "copy"};
+enum KernelKind { kGram = 0, kTree, kWsum, kWiden, kCopy, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "widen", "copy"};
 
 struct ProfRecord {
   int kind;
@@ -254,9 +273,9 @@ struct CallBuffers {
   double* stats;
 };
 
-const void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
+void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
   switch (r.kind) {
-    case Ref::Input: return b.grads[r.idx];
+    case Ref::Input: return const_cast<void*>(b.grads[r.idx]);
     case Ref::Slot: return b.ws + p.ws_slots + (size_t)r.idx * (size_t)p.N * sizeof(float);
     case Ref::Out: return b.out;
   }
@@ -279,96 +298,113 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
     return ADASUM_OK;
   }
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
-  int first_node = 0;
-  for (size_t l = 0; l < p.levels.size(); ++l) {
-    const Level& lv = p.levels[l];
-    // 1. statistics of pairs no lower combine emitted
-    if (ntiles > 0 && !lv.dot_pairs.empty()) {
-      for (size_t c = 0; c < lv.dot_pairs.size(); c += kMaxDotPairs) {
-        DotArgs a{};
-        int n = 0;
-        DType op_t = DType::F32;
-        for (size_t i = c; i < lv.dot_pairs.size() && n < kMaxDotPairs; ++i, ++n) {
-          const Pair& pr = lv.pairs[lv.dot_pairs[i]];
-          a.a[n] = ref_ptr(p, b, pr.left);
-          a.b[n] = ref_ptr(p, b, pr.right);
-          a.row[n] = lv.dot_pairs[i];
-          op_t = ref_type(p, pr.left);  // both operands of a level share one type
-        }
-        a.tiles = dt.tiles;
-        a.ntiles = ntiles;
-        a.partials = partials;
-        const int pr = prof_start(kDot, (double)n * (2.0 * (double)p.N * dtype_size(op_t) + 24.0 * ntiles), st);
-        e = launch_triple_dot(op_t, a, n, st);
-        prof_stop(pr, st);
-        if (e != hipSuccess) return fail_hip(e, "launching triple_dot");
-      }
-    }
-    // 2. coefficients of every (pair, segment) of this level
-    if (p.nseg > 0) {
-      FinalizeArgs f{};
-      f.partials = partials;
-      f.seg_tile = dt.seg_tile;
-      f.ntiles = ntiles;
-      f.nseg = p.nseg;
-      f.npairs = (int)lv.pairs.size();
-      f.first_node = first_node;
-      f.coeffs = b.coeffs;
-      f.stats = b.stats;
-      const int pr = prof_start(kFinalize, (double)f.npairs * (24.0 * ntiles + 40.0 * p.nseg), st);
-      e = launch_finalize(f, st);
-      prof_stop(pr, st);
-      if (e != hipSuccess) return fail_hip(e, "launching finalize");
-    }
-    // the input carried past level 1 (odd K) is widened into its fp32 slot
-    if (l == 0 && p.carry_slot >= 0 && ntiles > 0) {
+  double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
+  for (const Stage& sg : p.stages) {
+    // 1. inputs carried into this stage, widened once to fp32
+    for (const auto& wd : sg.widen) {
+      if (ntiles == 0) break;
       WidenArgs w{};
-      w.src = b.grads[p.K - 1];
-      w.dst = reinterpret_cast<float*>(b.ws + p.ws_slots + (size_t)p.carry_slot * (size_t)p.N * sizeof(float));
+      w.src = b.grads[wd.first];
+      w.dst = reinterpret_cast<float*>(b.ws + p.ws_slots + (size_t)wd.second * (size_t)p.N * sizeof(float));
       w.tiles = dt.tiles;
       const int pr = prof_start(kWiden, (double)p.N * (esz + 4.0), st);
       e = launch_widen(p.dtype, w, ntiles, st);
       prof_stop(pr, st);
       if (e != hipSuccess) return fail_hip(e, "launching widen");
     }
-    // 3. combine, sibling jobs and single-node jobs in separate launches
-    if (ntiles > 0) {
-      for (int sib = 1; sib >= 0; --sib) {
-        std::vector<const Job*> jobs;
-        for (const Job& jb : lv.jobs)
-          if ((jb.pair[1] >= 0) == (sib == 1)) jobs.push_back(&jb);
-        for (size_t c = 0; c < jobs.size(); c += kMaxJobs) {
-          CombineArgs a{};
-          int n = 0;
-          DType in_t = DType::F32, out_t = DType::F32;
-          for (size_t i = c; i < jobs.size() && n < kMaxJobs; ++i, ++n) {
-            const Job& jb = *jobs[i];
-            for (int h = 0; h < (sib ? 2 : 1); ++h) {
-              const Pair& pr = lv.pairs[jb.pair[h]];
-              a.x[n][2 * h] = ref_ptr(p, b, pr.left);
-              a.x[n][2 * h + 1] = ref_ptr(p, b, pr.right);
-              a.y[n][h] = const_cast<void*>(ref_ptr(p, b, pr.dst));
-              a.node[n][h] = pr.node;
-              in_t = ref_type(p, pr.left);
-              out_t = ref_type(p, pr.dst);
+    // 2. Gram partials, blocks grouped by (operand type, Gram size)
+    // 4. weighted sums, grouped by (operand type, Gram size, result type)
+    for (int pass = 0; pass < 2; ++pass) {
+      if (ntiles == 0) break;
+      std::vector<char> done(sg.blocks.size(), 0);
+      for (size_t i = 0; i < sg.blocks.size(); ++i) {
+        if (done[i]) continue;
+        const Block& b0 = sg.blocks[i];
+        const DType in_t = ref_type(p, b0.operands[0]);
+        const DType out_t = ref_type(p, b0.dst);
+        const int nbt = p.descs[b0.desc].nbt;
+        std::vector<const Block*> group;
+        for (size_t k = i; k < sg.blocks.size(); ++k) {
+          const Block& bk = sg.blocks[k];
+          if (done[k] || p.descs[bk.desc].nbt != nbt || ref_type(p, bk.operands[0]) != in_t) continue;
+          if (pass == 1 && ref_type(p, bk.dst) != out_t) continue;
+          done[k] = 1;
+          group.push_back(&bk);
+        }
+        for (size_t c = 0; c < group.size(); c += kMaxJobs) {
+          const int n = (int)std::min<size_t>(kMaxJobs, group.size() - c);
+          double in_bytes = 0, out_bytes = 0;
+          if (pass == 0) {
+            GramArgs a{};
+            for (int j = 0; j < n; ++j) {
+              const Block& bk = *group[c + j];
+              for (size_t k = 0; k < bk.operands.size(); ++k) a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+              a.poff[j] = p.descs[bk.desc].poff;
+              in_bytes += (double)bk.operands.size() * p.N * dtype_size(in_t);
+              out_bytes += 8.0 * gram_entries(nbt) * ntiles;
             }
-            a.emit[n] = jb.emit;
+            a.tiles = dt.tiles;
+            a.partials = partials;
+            const int pr = prof_start(kGram, in_bytes + out_bytes, st);
+            e = launch_gram(in_t, nbt, a, ntiles, n, st);
+            prof_stop(pr, st);
+            if (e != hipSuccess) return fail_hip(e, "launching gram");
+          } else {
+            WsumArgs a{};
+            for (int j = 0; j < n; ++j) {
+              const Block& bk = *group[c + j];
+              for (size_t k = 0; k < bk.operands.size(); ++k) a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+              a.y[j] = ref_ptr(p, b, bk.dst);
+              a.wrow[j] = p.descs[bk.desc].wrow;
+              in_bytes += (double)bk.operands.size() * p.N * dtype_size(in_t);
+              out_bytes += (double)p.N * dtype_size(out_t);
+            }
+            a.tiles = dt.tiles;
+            a.nseg = p.nseg;
+            a.weights = weights;
+            const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
+            e = launch_wsum(in_t, nbt, out_t, a, ntiles, n, st);
+            prof_stop(pr, st);
+            if (e != hipSuccess) return fail_hip(e, "launching wsum");
           }
-          a.tiles = dt.tiles;
-          a.ntiles = ntiles;
-          a.nseg = p.nseg;
-          a.coeffs = b.coeffs;
-          a.partials = partials;
-          const double per_job = sib ? 4.0 * p.N * dtype_size(in_t) + 2.0 * p.N * dtype_size(out_t) + 24.0 * ntiles
-                                     : 2.0 * p.N * dtype_size(in_t) + 1.0 * p.N * dtype_size(out_t);
-          const int pr = prof_start(kCombine, n * per_job, st);
-          e = launch_combine(in_t, out_t, sib == 1, a, n, st);
-          prof_stop(pr, st);
-          if (e != hipSuccess) return fail_hip(e, "launching combine");
         }
       }
+      if (pass == 0 && p.nseg > 0) {
+        // 3. per (block, segment): statistics, coefficients, operand weights
+        TreeArgs t{};
+        t.descs = dt.descs;
+        t.merges = dt.merges;
+        t.seg_tile = dt.seg_tile;
+        t.partials = partials;
+        t.desc0 = sg.blocks.front().desc;
+        t.nblocks = (int)sg.blocks.size();
+        t.nseg = p.nseg;
+        t.weights = weights;
+        t.coeffs = b.coeffs;
+        t.stats = b.stats;
+        double bytes = 0;
+        for (const Block& bk : sg.blocks) bytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
+        const int pr = prof_start(kTree, bytes, st);
+        e = launch_tree(t, st);
+        prof_stop(pr, st);
+        if (e != hipSuccess) return fail_hip(e, "launching tree");
+      }
     }
-    first_node += (int)lv.pairs.size();
+    if (ntiles == 0 && p.nseg > 0) {
+      TreeArgs t{};
+      t.descs = dt.descs;
+      t.merges = dt.merges;
+      t.seg_tile = dt.seg_tile;
+      t.partials = partials;
+      t.desc0 = sg.blocks.front().desc;
+      t.nblocks = (int)sg.blocks.size();
+      t.nseg = p.nseg;
+      t.weights = weights;
+      t.coeffs = b.coeffs;
+      t.stats = b.stats;
+      e = launch_tree(t, st);
+      if (e != hipSuccess) return fail_hip(e, "launching tree");
+    }
   }
   return ADASUM_OK;
 }

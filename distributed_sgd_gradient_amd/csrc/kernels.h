@@ -7,42 +7,40 @@
 
 namespace adasum {
 
-// Per-tile partial statistics (a.b, |a|^2, |b|^2) of up to kMaxDotPairs pairs.
-// Partials of pair j, tile t go to partials[(row[j] * ntiles + t) * 3 + {0,1,2}].
-struct DotArgs {
-  const void* a[kMaxDotPairs];
-  const void* b[kMaxDotPairs];
-  int row[kMaxDotPairs];
+// Gram pass: per (block, tile), the packed upper triangle of the fp64 Gram
+// matrix of the block's operands over the tile.  Operands x[j][k] with k at
+// or beyond the block's operand count are NULL and read as zero.
+struct GramArgs {
+  const void* x[kMaxJobs][kMaxOps];
+  int64_t poff[kMaxJobs];  // partials of tile t: partials + poff + t * gram_entries(nbt)
   const Tile* tiles;
-  int ntiles;
   double* partials;
 };
 
-// Per (pair, segment): sum the tile partials in tile order, derive the
-// coefficients, write the coefficient and statistic tables.
-struct FinalizeArgs {
-  const double* partials;   // rows 0..npairs-1, ntiles each
+// Tree walk: per (block, segment), sum the tile Gram partials in tile order,
+// then evaluate the block's merges on the Gram matrix: statistics,
+// coefficients and the final weight of every operand.
+struct TreeArgs {
+  const BlockDesc* descs;
+  const Merge* merges;
   const int32_t* seg_tile;  // nseg + 1
-  int ntiles;
+  const double* partials;
+  int desc0;                // first block of this launch (consecutive descs)
+  int nblocks;
   int nseg;
-  int npairs;
-  int first_node;           // global node id of pair 0 of this level
+  double* weights;          // [nblocks total][nseg][kMaxOps]
   double* coeffs;           // [K-1][nseg][2]
   double* stats;            // [K-1][nseg][3]
 };
 
-// One launch of combine jobs: each job computes one node c = ca*x0 + cb*x1,
-// or two sibling nodes and the per-tile statistics of the pair they form.
-struct CombineArgs {
-  const void* x[kMaxJobs][4];
-  void* y[kMaxJobs][2];
-  int node[kMaxJobs][2];
-  int emit[kMaxJobs];       // partials row for the emitted statistics (sibling jobs)
+// Weighted sum: per (block, tile), y = sum_k w_k x_k, rounded once.
+struct WsumArgs {
+  const void* x[kMaxJobs][kMaxOps];
+  void* y[kMaxJobs];
+  int wrow[kMaxJobs];
   const Tile* tiles;
-  int ntiles;
   int nseg;
-  const double* coeffs;
-  double* partials;
+  const double* weights;
 };
 
 // Widen one input to fp32 over every tile.
@@ -52,12 +50,11 @@ struct WidenArgs {
   const Tile* tiles;
 };
 
-// Operand element type of a launch: the input dtype, or fp32 for slots.
-hipError_t launch_triple_dot(DType operand, const DotArgs& a, int npairs, hipStream_t st);
-hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t st);
-// in_t: type of x operands; out_t: type of y results; siblings: two-node jobs
-hipError_t launch_combine(DType in_t, DType out_t, bool siblings, const CombineArgs& a, int njobs,
-                          hipStream_t st);
+// nbt: Gram size of every block in the launch (2, 4, 8 or 16).
+hipError_t launch_gram(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st);
+hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
+hipError_t launch_wsum(DType in_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
+                       hipStream_t st);
 hipError_t launch_widen(DType src_t, const WidenArgs& a, int ntiles, hipStream_t st);
 
 }  // namespace adasum

@@ -1,25 +1,30 @@
-// kernels.hip - gfx950 kernels of the level-by-level Adasum combine.
+// kernels.hip - gfx950 kernels of the Adasum combine.
 //
-// Every kernel walks tiles of the plan's tile table.  A tile lies inside one
-// segment; its body starts at a multiple of kGroup elements, so each thread
-// moves kGroup elements per step with 16-byte loads and stores (base pointers
-// are 16-byte aligned), and the unaligned head of a segment's first tile and
-// the ragged tail of its last tile are done one element per thread.
+// The pairwise operator of "Scaling Distributed Training with Adaptive
+// Summation" needs the dot product and both norms of its operands before it
+// can combine them (Sec. 4: the operation cannot be streamed).  Every node of
+// the tree is a linear combination of the operands below it, so all the
+// statistics of a subtree are quadratic forms in the Gram matrix of its
+// operands.  A block (a subtree of at most 16 operands, four levels) is
+// therefore combined in three launches:
+//   gram  - one pass over the operands: per tile, the fp64 Gram matrix
+//           (packed upper triangle), accumulated per thread with fma,
+//           reduced across the workgroup in a fixed order;
+//   tree  - per segment: the tile partials summed in tile order, then the
+//           block's merges evaluated on the Gram matrix level by level:
+//           d = wL.G.wR, A = wL.G.wL, B = wR.G.wR, ca = 1 - d/(2A),
+//           cb = 1 - d/(2B) (coefficient 1 for a zero norm), and the
+//           weights of the merged operands scaled by ca and cb;
+//   wsum  - one pass: y = sum_k w_k x_k in fp64, rounded once.
+// Quadratic forms and the weighted sum use separately rounded products and
+// sums (no fused multiply-add), so mirrored terms cancel exactly: an operand
+// pair (a, -a) gives an exactly zero node, as the plain definition does.
 //
-// Arithmetic (the pairwise operator of "Scaling Distributed Training with
-// Adaptive Summation", whose dot product and norms must be complete before
-// the pair is combined, Sec. 4):
-//   * statistics a.b, |a|^2, |b|^2 accumulate in fp64 per thread, then a
-//     fixed xor-butterfly over the wave64 and a fixed-order sum of the four
-//     waves give one partial per tile; the finalize kernel sums the tiles of a
-//     segment in a fixed order, so results are bitwise reproducible without
-//     atomics;
-//   * coefficients ca = 1 - d/(2A), cb = 1 - d/(2B) in fp64 with IEEE
-//     division; a zero-norm operand (A == 0 exactly) gets coefficient 1;
-//   * the combine evaluates fma(ca, a, cb*b) in fp64 and rounds once, to fp32
-//     for an intermediate level or to the output dtype at the root; the
-//     statistics it emits for the next level are taken from the rounded
-//     values it stores.
+// Every kernel walks tiles of the plan's tile table.  A tile lies inside
+// one segment; its body starts at a multiple of kGroup elements, so vector
+// loads and stores are 16-byte aligned (base pointers are 16-byte aligned);
+// the unaligned head and the ragged tail are handled element by element.
+// No atomics anywhere: results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -135,47 +140,7 @@ struct Elem<bf16_t> {
   }
 };
 
-// ----------------------------------------------------------------- reductions
-
-// xor butterfly: partners add the same two values, so every lane ends with
-// the identical, order-fixed sum
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Sum three fp64 values over the block; the result is valid in thread 0.
-__device__ __forceinline__ void block_sum3(double& a, double& b, double& c) {
-  __shared__ double red[kBlock / 64][3];
-  a = wave_sum(a);
-  b = wave_sum(b);
-  c = wave_sum(c);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) {
-    red[w][0] = a;
-    red[w][1] = b;
-    red[w][2] = c;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    a = red[0][0];
-    b = red[0][1];
-    c = red[0][2];
-#pragma unroll
-    for (int i = 1; i < kBlock / 64; ++i) {
-      a += red[i][0];
-      b += red[i][1];
-      c += red[i][2];
-    }
-  }
-}
-
-__device__ __forceinline__ void add_stats(double x, double y, double& d, double& A, double& B) {
-  d = fma(x, y, d);
-  A = fma(x, x, A);
-  B = fma(y, y, B);
-}
+// ----------------------------------------------------------------- tiles
 
 // Bounds of a tile: [lo, body_lo) head, [body_lo, body_hi) aligned body,
 // [body_hi, hi) tail.
@@ -194,145 +159,282 @@ __device__ __forceinline__ TileSpan span_of(const Tile& t) {
   return s;
 }
 
-// ----------------------------------------------------------------- triple dot
+// ----------------------------------------------------------------- Gram pass
 
+constexpr int kSubRows = 1024;  // rows of every operand staged in LDS per step
+
+// Loads 8 consecutive elements starting at `row` (a multiple of kGroup) as
+// floats; elements outside [lo, hi) and every element of a NULL operand
+// read as zero.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void triple_dot_kernel(DotArgs args) {
+__device__ __forceinline__ void load_group(const T* __restrict__ x, int64_t row, int64_t lo, int64_t hi,
+                                           float (&v)[kGroup]) {
+  if (x != nullptr && row >= lo && row + kGroup <= hi) {
+    Elem<T>::load8(x + row, v);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < kGroup; ++e) {
+    const int64_t i = row + e;
+    v[e] = (x != nullptr && i >= lo && i < hi) ? Elem<T>::load1(x + i) : 0.f;
+  }
+}
+
+// Workgroup roles (one per wave64): wave 0 accumulates the Gram block of
+// operands [0, H) with themselves, wave 1 that of [H, 2H), waves 2 and 3
+// the cross block [0, H) x [H, 2H), on alternate 64-row strips.  Per row
+// that is H(H+1)/2, H(H+1)/2, H*H/2, H*H/2 fused multiply-adds, so the four
+// waves carry nearly equal work, and the code inside each wave is uniform.
+template <typename T, int NB>
+__global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
+  constexpr int H = NB / 2;
+  constexpr int NAA = H * (H + 1) / 2;
+  constexpr int NAB = H * H;
+  constexpr int NE = gram_entries(NB);
+  constexpr int S = kSubRows;
+  constexpr int RG = S / kGroup;              // row groups per operand per step
+  constexpr int GPT = NB * RG / kBlock;       // row groups each thread stages
+  static_assert(GPT * kBlock == NB * RG, "staging must divide evenly");
+  static_assert(RG % 64 == 0, "a wave must stage rows of a single operand");
+  static_assert(2 * 64 * NAB * sizeof(double) <= NB * S * sizeof(float), "reduction must fit the stage buffer");
+  __shared__ __align__(16) float stage[NB * S];  // operand-major: stage[k * S + r]
+
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
-  const TileSpan sp = span_of(args.tiles[tile_id]);
-  const T* __restrict__ a = static_cast<const T*>(args.a[j]);
-  const T* __restrict__ b = static_cast<const T*>(args.b[j]);
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int nsteps = (int)((hi - first + S - 1) / S);
   const int tid = threadIdx.x;
-  double d = 0.0, A = 0.0, B = 0.0;
-  if (tid < sp.body_lo - sp.lo) {
-    const int64_t i = sp.lo + tid;
-    add_stats(Elem<T>::load1(a + i), Elem<T>::load1(b + i), d, A, B);
-  }
-  for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
-    float x[kGroup], y[kGroup];
-    Elem<T>::load8(a + g, x);
-    Elem<T>::load8(b + g, y);
+  const int role = tid >> 6;
+  const int lane = tid & 63;
+
+  const T* xs[NB];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) add_stats(x[e], y[e], d, A, B);
+  for (int k = 0; k < NB; ++k) xs[k] = static_cast<const T*>(args.x[j][k]);
+
+  double acc[NAB];
+#pragma unroll
+  for (int e = 0; e < NAB; ++e) acc[e] = 0.0;
+
+  float pre[GPT][kGroup];
+  auto fetch = [&](int step) {
+    const int64_t r0 = first + (int64_t)step * S;
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int q = tid + g * kBlock;
+      // a wave's 64 lanes share one operand (RG is a multiple of 64): make that explicit
+      const int k = __builtin_amdgcn_readfirstlane(q / RG);
+      const int rg = q % RG;
+      load_group<T>(xs[k], r0 + (int64_t)rg * kGroup, lo, hi, pre[g]);
+    }
+  };
+
+  fetch(0);
+  for (int step = 0; step < nsteps; ++step) {
+    if (step > 0) __syncthreads();  // every wave is done reading the previous step
+#pragma unroll
+    for (int g = 0; g < GPT; ++g) {
+      const int q = tid + g * kBlock;
+      float* dst = &stage[(q / RG) * S + (q % RG) * kGroup];
+      *reinterpret_cast<float4*>(dst) = make_float4(pre[g][0], pre[g][1], pre[g][2], pre[g][3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(pre[g][4], pre[g][5], pre[g][6], pre[g][7]);
+    }
+    __syncthreads();
+    if (step + 1 < nsteps) fetch(step + 1);  // in flight while this step is accumulated
+    const int64_t r0 = first + (int64_t)step * S;
+    const int nrows = (int)(hi - r0 < S ? hi - r0 : S);
+    if (role < 2) {
+      const float* base = stage + role * H * S;
+      for (int r = lane; r < nrows; r += 64) {
+        double v[H];
+#pragma unroll
+        for (int i = 0; i < H; ++i) v[i] = (double)base[i * S + r];
+#pragma unroll
+        for (int i = 0; i < H; ++i)
+#pragma unroll
+          for (int k = i; k < H; ++k) acc[gram_index(H, i, k)] = fma(v[i], v[k], acc[gram_index(H, i, k)]);
+      }
+    } else {
+      for (int r = (role - 2) * 64 + lane; r < nrows; r += 128) {
+        double a[H], b[H];
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          a[i] = (double)stage[i * S + r];
+          b[i] = (double)stage[(H + i) * S + r];
+        }
+#pragma unroll
+        for (int i = 0; i < H; ++i)
+#pragma unroll
+          for (int k = 0; k < H; ++k) acc[i * H + k] = fma(a[i], b[k], acc[i * H + k]);
+      }
+    }
   }
-  if (tid < sp.hi - sp.body_hi) {
-    const int64_t i = sp.body_hi + tid;
-    add_stats(Elem<T>::load1(a + i), Elem<T>::load1(b + i), d, A, B);
+  __syncthreads();
+
+  // Reduce every accumulator over its lanes through LDS, in lane order.
+  double* red = reinterpret_cast<double*>(stage);
+  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+  if (role >= 2) {
+#pragma unroll
+    for (int e = 0; e < NAB; ++e) red[((role - 2) * NAB + e) * 64 + lane] = acc[e];
   }
-  block_sum3(d, A, B);
+  __syncthreads();
+  if (tid < NAB) {
+    double sum = 0.0;
+    for (int w = 0; w < 2; ++w)
+      for (int l = 0; l < 64; ++l) sum += red[(w * NAB + tid) * 64 + l];
+    out[gram_index(NB, tid / H, H + tid % H)] = sum;
+  }
+  __syncthreads();
+  if (role < 2) {
+#pragma unroll
+    for (int e = 0; e < NAA; ++e) red[(role * NAA + e) * 64 + lane] = acc[e];
+  }
+  __syncthreads();
+  if ((tid & 63) < NAA && tid < 128) {
+    const int w = tid >> 6, e = tid & 63;
+    double sum = 0.0;
+    for (int l = 0; l < 64; ++l) sum += red[(w * NAA + e) * 64 + l];
+    // packed index e of the H x H triangle -> (i, k)
+    int i = 0, rem = e;
+    while (rem >= H - i) {
+      rem -= H - i;
+      ++i;
+    }
+    out[gram_index(NB, w * H + i, w * H + i + rem)] = sum;
+  }
+}
+
+// ----------------------------------------------------------------- tree walk
+
+// Products and sums rounded separately, never fused, so that terms that
+// mirror each other cancel exactly.
+__device__ __forceinline__ double mul_rn(double a, double b) { return __dmul_rn(a, b); }
+__device__ __forceinline__ double add_rn(double a, double b) { return __dadd_rn(a, b); }
+
+__device__ __forceinline__ double gram_at(const double* G, int n, int i, int k) {
+  return i <= k ? G[gram_index(n, i, k)] : G[gram_index(n, k, i)];
+}
+
+// sum_{i in [a0,a1)} w_i * (sum_{k in [b0,b1)} w_k G(i,k))
+__device__ double quad_form(const double* G, int n, const double* w, int a0, int a1, int b0, int b1) {
+  double total = 0.0;
+  for (int i = a0; i < a1; ++i) {
+    double row = 0.0;
+    for (int k = b0; k < b1; ++k) row = add_rn(row, mul_rn(w[k], gram_at(G, n, i, k)));
+    total = add_rn(total, mul_rn(w[i], row));
+  }
+  return total;
+}
+
+constexpr int kTreeWaves = kBlock / 64;
+
+// One workgroup per (block, segment).  Wave q sums the tile partials of the
+// q-th quarter of the segment's tiles (lanes over Gram entries, tiles in
+// order); the four quarter sums are then added in wave order.  The split
+// depends only on the tile count, so the result is reproducible.
+__global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
+  __shared__ double part[kTreeWaves][gram_entries(kMaxOps)];
+  __shared__ double G[gram_entries(kMaxOps)];
+  __shared__ double w[kMaxOps];
+  const int item = blockIdx.x;
+  const int b = item / a.nseg;
+  const int s = item % a.nseg;
+  const BlockDesc d = a.descs[a.desc0 + b];
+  const int n = d.nbt;
+  const int ne = gram_entries(n);
+  const int tid = threadIdx.x;
+  const int q = tid >> 6, lane = tid & 63;
+  const int t0 = a.seg_tile[s], t1 = a.seg_tile[s + 1];
+  const int chunk = (t1 - t0 + kTreeWaves - 1) / kTreeWaves;
+  const int q0 = min(t1, t0 + q * chunk), q1 = min(t1, q0 + chunk);
+  for (int e = lane; e < ne; e += 64) {
+    const double* p = a.partials + d.poff + e;
+    double sum = 0.0;
+#pragma unroll 8
+    for (int t = q0; t < q1; ++t) sum += p[(int64_t)t * ne];
+    part[q][e] = sum;
+  }
+  __syncthreads();
+  for (int e = tid; e < ne; e += kBlock) {
+    double sum = part[0][e];
+#pragma unroll
+    for (int i = 1; i < kTreeWaves; ++i) sum += part[i][e];
+    G[e] = sum;
+  }
+  if (tid < kMaxOps) w[tid] = 1.0;
+  __syncthreads();
   if (tid == 0) {
-    double* out = args.partials + ((int64_t)args.row[j] * args.ntiles + tile_id) * 3;
-    out[0] = d;
-    out[1] = A;
-    out[2] = B;
+    for (int m = 0; m < d.nmerges; ++m) {
+      const Merge mg = a.merges[d.merge0 + m];
+      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
+      const double A = quad_form(G, n, w, l0, l1, l0, l1);
+      const double B = quad_form(G, n, w, l1, r1, l1, r1);
+      const double dd = quad_form(G, n, w, l0, l1, l1, r1);
+      const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
+      const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
+      for (int i = l0; i < l1; ++i) w[i] = mul_rn(w[i], ca);
+      for (int i = l1; i < r1; ++i) w[i] = mul_rn(w[i], cb);
+      const int64_t at = (int64_t)mg.node * a.nseg + s;
+      a.coeffs[at * 2] = ca;
+      a.coeffs[at * 2 + 1] = cb;
+      a.stats[at * 3] = dd;
+      a.stats[at * 3 + 1] = A;
+      a.stats[at * 3 + 2] = B;
+    }
   }
+  __syncthreads();
+  if (tid < kMaxOps) a.weights[((int64_t)d.wrow * a.nseg + s) * kMaxOps + tid] = w[tid];
 }
 
-// ----------------------------------------------------------------- finalize
+// ----------------------------------------------------------------- weighted sum
 
-constexpr int kFinalizeItemsPerBlock = kBlock / 64;  // one wave per (pair, segment)
-
-__global__ __launch_bounds__(kBlock) void finalize_kernel(FinalizeArgs args) {
-  const int64_t item = (int64_t)blockIdx.x * kFinalizeItemsPerBlock + (threadIdx.x >> 6);
-  if (item >= (int64_t)args.npairs * args.nseg) return;  // uniform per wave; no block barrier below
-  const int p = (int)(item / args.nseg);
-  const int s = (int)(item % args.nseg);
-  const int lane = threadIdx.x & 63;
-  const double* row = args.partials + (int64_t)p * args.ntiles * 3;
-  double d = 0.0, A = 0.0, B = 0.0;
-  for (int t = args.seg_tile[s] + lane; t < args.seg_tile[s + 1]; t += 64) {
-    d += row[(int64_t)t * 3];
-    A += row[(int64_t)t * 3 + 1];
-    B += row[(int64_t)t * 3 + 2];
-  }
-  d = wave_sum(d);
-  A = wave_sum(A);
-  B = wave_sum(B);
-  if (lane == 0) {
-    const double ca = (A == 0.0) ? 1.0 : 1.0 - d / (2.0 * A);
-    const double cb = (B == 0.0) ? 1.0 : 1.0 - d / (2.0 * B);
-    const int64_t at = (int64_t)(args.first_node + p) * args.nseg + s;
-    args.coeffs[at * 2] = ca;
-    args.coeffs[at * 2 + 1] = cb;
-    args.stats[at * 3] = d;
-    args.stats[at * 3 + 1] = A;
-    args.stats[at * 3 + 2] = B;
-  }
-}
-
-// ----------------------------------------------------------------- combine
-
-template <typename TIn, typename TOut, bool SIB>
-__global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs args) {
+template <typename TIn, int NB, typename TOut>
+__global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
   const TileSpan sp = span_of(tile);
-  const int64_t c0 = ((int64_t)args.node[j][0] * args.nseg + tile.seg) * 2;
-  const double ca0 = args.coeffs[c0], cb0 = args.coeffs[c0 + 1];
-  double ca1 = 0.0, cb1 = 0.0;
-  if (SIB) {
-    const int64_t c1 = ((int64_t)args.node[j][1] * args.nseg + tile.seg) * 2;
-    ca1 = args.coeffs[c1];
-    cb1 = args.coeffs[c1 + 1];
+  const double* wrow = args.weights + ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  const TIn* xs[NB];
+  double w[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    xs[k] = static_cast<const TIn*>(args.x[j][k]);
+    w[k] = wrow[k];
   }
-  const TIn* __restrict__ x0 = static_cast<const TIn*>(args.x[j][0]);
-  const TIn* __restrict__ x1 = static_cast<const TIn*>(args.x[j][1]);
-  const TIn* __restrict__ x2 = static_cast<const TIn*>(args.x[j][2]);
-  const TIn* __restrict__ x3 = static_cast<const TIn*>(args.x[j][3]);
-  TOut* __restrict__ y0 = static_cast<TOut*>(args.y[j][0]);
-  TOut* __restrict__ y1 = static_cast<TOut*>(args.y[j][1]);
+  TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
   const int tid = threadIdx.x;
-  double d = 0.0, A = 0.0, B = 0.0;
+  double unused;
 
   auto one = [&](int64_t i) {
-    double p;
-    Elem<TOut>::store1(y0 + i, Elem<TOut>::round(fma(ca0, (double)Elem<TIn>::load1(x0 + i),
-                                                     cb0 * (double)Elem<TIn>::load1(x1 + i)), &p));
-    if (SIB) {
-      double q;
-      Elem<TOut>::store1(y1 + i, Elem<TOut>::round(fma(ca1, (double)Elem<TIn>::load1(x2 + i),
-                                                       cb1 * (double)Elem<TIn>::load1(x3 + i)), &q));
-      add_stats(p, q, d, A, B);
-    }
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (xs[k] != nullptr) acc = add_rn(acc, mul_rn(w[k], (double)Elem<TIn>::load1(xs[k] + i)));
+    Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
   };
 
   if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
   for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
-    float a0[kGroup], a1[kGroup];
-    Elem<TIn>::load8(x0 + g, a0);
-    Elem<TIn>::load8(x1 + g, a1);
-    TOut r0[kGroup];
-    double p[kGroup];
+    double acc[kGroup];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) r0[e] = Elem<TOut>::round(fma(ca0, (double)a0[e], cb0 * (double)a1[e]), &p[e]);
-    Elem<TOut>::store8(y0 + g, r0);
-    if (SIB) {
-      float a2[kGroup], a3[kGroup];
-      Elem<TIn>::load8(x2 + g, a2);
-      Elem<TIn>::load8(x3 + g, a3);
-      TOut r1[kGroup];
+    for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
 #pragma unroll
-      for (int e = 0; e < kGroup; ++e) {
-        double q;
-        r1[e] = Elem<TOut>::round(fma(ca1, (double)a2[e], cb1 * (double)a3[e]), &q);
-        add_stats(p[e], q, d, A, B);
-      }
-      Elem<TOut>::store8(y1 + g, r1);
+    for (int k = 0; k < NB; ++k) {
+      if (xs[k] == nullptr) continue;
+      float v[kGroup];
+      Elem<TIn>::load8(xs[k] + g, v);
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) acc[e] = add_rn(acc[e], mul_rn(w[k], (double)v[e]));
     }
+    TOut r[kGroup];
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) r[e] = Elem<TOut>::round(acc[e], &unused);
+    Elem<TOut>::store8(y + g, r);
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
-
-  if (SIB) {
-    block_sum3(d, A, B);
-    if (tid == 0) {
-      double* out = args.partials + ((int64_t)args.emit[j] * args.ntiles + tile_id) * 3;
-      out[0] = d;
-      out[1] = A;
-      out[2] = B;
-    }
-  }
 }
 
 // ----------------------------------------------------------------- widen
@@ -365,14 +467,6 @@ hipError_t by_type(DType t, Args&&... args) {
 }
 
 template <typename T>
-struct RunDot {
-  static hipError_t run(const DotArgs& a, int npairs, hipStream_t st) {
-    hipLaunchKernelGGL(triple_dot_kernel<T>, dim3(a.ntiles, npairs), dim3(kBlock), 0, st, a);
-    return hipGetLastError();
-  }
-};
-
-template <typename T>
 struct RunWiden {
   static hipError_t run(const WidenArgs& a, int ntiles, hipStream_t st) {
     hipLaunchKernelGGL(widen_kernel<T>, dim3(ntiles), dim3(kBlock), 0, st, a);
@@ -380,23 +474,41 @@ struct RunWiden {
   }
 };
 
+template <typename T>
+struct RunGram {
+  static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+    const dim3 grid(ntiles, njobs);
+    switch (nbt) {
+      case 2: hipLaunchKernelGGL((gram_kernel<T, 2>), grid, dim3(kBlock), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((gram_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((gram_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+};
+
 template <typename TIn, typename TOut>
-hipError_t run_combine(bool siblings, const CombineArgs& a, int njobs, hipStream_t st) {
-  const dim3 grid(a.ntiles, njobs);
-  if (siblings)
-    hipLaunchKernelGGL((combine_kernel<TIn, TOut, true>), grid, dim3(kBlock), 0, st, a);
-  else
-    hipLaunchKernelGGL((combine_kernel<TIn, TOut, false>), grid, dim3(kBlock), 0, st, a);
+hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
+  const dim3 grid(ntiles, njobs);
+  switch (nbt) {
+    case 2: hipLaunchKernelGGL((wsum_kernel<TIn, 2, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((wsum_kernel<TIn, 8, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((wsum_kernel<TIn, 16, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <typename TIn>
-struct RunCombineIn {
-  static hipError_t run(DType out_t, bool siblings, const CombineArgs& a, int njobs, hipStream_t st) {
+struct RunWsum {
+  static hipError_t run(int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
     switch (out_t) {
-      case DType::F32: return run_combine<TIn, float>(siblings, a, njobs, st);
-      case DType::F16: return run_combine<TIn, _Float16>(siblings, a, njobs, st);
-      case DType::BF16: return run_combine<TIn, bf16_t>(siblings, a, njobs, st);
+      case DType::F32: return run_wsum<TIn, float>(nbt, a, ntiles, njobs, st);
+      case DType::F16: return run_wsum<TIn, _Float16>(nbt, a, ntiles, njobs, st);
+      case DType::BF16: return run_wsum<TIn, bf16_t>(nbt, a, ntiles, njobs, st);
     }
     return hipErrorInvalidValue;
   }
@@ -404,20 +516,18 @@ struct RunCombineIn {
 
 }  // namespace
 
-hipError_t launch_triple_dot(DType operand, const DotArgs& a, int npairs, hipStream_t st) {
-  return by_type<RunDot>(operand, a, npairs, st);
+hipError_t launch_gram(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+  return by_type<RunGram>(operand, nbt, a, ntiles, njobs, st);
 }
 
-hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t st) {
-  const int64_t items = (int64_t)a.npairs * a.nseg;
-  const int64_t blocks = (items + kFinalizeItemsPerBlock - 1) / kFinalizeItemsPerBlock;
-  hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, a);
+hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(tree_kernel, dim3((unsigned)((int64_t)a.nblocks * a.nseg)), dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(DType in_t, DType out_t, bool siblings, const CombineArgs& a, int njobs,
-                          hipStream_t st) {
-  return by_type<RunCombineIn>(in_t, out_t, siblings, a, njobs, st);
+hipError_t launch_wsum(DType in_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
+                       hipStream_t st) {
+  return by_type<RunWsum>(in_t, nbt, out_t, a, ntiles, njobs, st);
 }
 
 hipError_t launch_widen(DType src_t, const WidenArgs& a, int ntiles, hipStream_t st) {

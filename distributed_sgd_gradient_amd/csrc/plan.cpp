@@ -1,4 +1,4 @@
-// plan.cpp - tile table, tree schedule and workspace layout (host only).
+// plan.cpp - tile table, staged tree schedule and workspace layout (host only).
 #include "plan.h"
 
 #include <algorithm>
@@ -87,76 +87,88 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
     }
   }
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
+  const size_t ntiles = p.tiles.size();
 
-  // ---- tree schedule
-  std::vector<Ref> cur(K);
-  for (int k = 0; k < K; ++k) cur[k] = Ref{Ref::Input, k};
+  // ---- tree, stage by stage.  The level schedule is the fixed binary
+  // tree: each level pairs (v0,v1), (v2,v3), ... and carries an odd last
+  // vector.  A stage runs up to four levels over its operand list; the
+  // elements left at its top are the roots of its blocks (or operands that
+  // were carried through untouched).
+  struct Elem {
+    int lo, hi;   // operand range of the stage
+    bool merged;  // false: a bare operand carried through the stage
+  };
+  std::vector<Ref> operands(K);
+  for (int k = 0; k < K; ++k) operands[k] = Ref{Ref::Input, k};
   int node = 0;
-  bool first = true;
-  while (cur.size() > 1) {
-    Level lv;
-    const int npairs = (int)cur.size() / 2;
-    const bool odd = cur.size() % 2 == 1;
-    lv.final_level = (cur.size() == 2);
-    for (int j = 0; j < npairs; ++j) {
-      Pair pr;
-      pr.left = cur[2 * j];
-      pr.right = cur[2 * j + 1];
-      pr.node = node++;
-      if (lv.final_level) {
-        pr.dst = Ref{Ref::Out, 0};
-      } else if (first) {
-        pr.dst = Ref{Ref::Slot, j};
-      } else {
-        pr.dst = pr.left;  // in place: each element is read, then written, by one thread
+  std::vector<std::pair<int, int>> pending_widen;  // carried inputs the next stage reads from fp32 slots
+  while (operands.size() > 1) {
+    Stage st;
+    st.widen.swap(pending_widen);
+    std::vector<Elem> cur;
+    for (int i = 0; i < (int)operands.size(); ++i) cur.push_back(Elem{i, i + 1, false});
+    std::vector<Merge> stage_merges;
+    for (int level = 0; level < 4 && cur.size() > 1; ++level) {
+      std::vector<Elem> next;
+      for (size_t j = 0; 2 * j + 1 < cur.size(); ++j) {
+        const Elem& l = cur[2 * j];
+        const Elem& r = cur[2 * j + 1];
+        stage_merges.push_back(Merge{(int8_t)l.lo, (int8_t)l.hi, (int8_t)r.hi, 0, node++});
+        next.push_back(Elem{l.lo, r.hi, true});
       }
-      lv.pairs.push_back(pr);
+      if (cur.size() % 2 == 1) next.push_back(cur.back());
+      cur = next;
     }
-    std::vector<Ref> next;
-    for (const Pair& pr : lv.pairs) next.push_back(pr.dst);
-    if (odd) {
-      Ref carried = cur.back();
-      if (carried.kind == Ref::Input) {
-        // an input carried past level 1 is widened once into an fp32 slot so
-        // that every operand above level 1 is fp32
-        p.carry_slot = npairs;
-        carried = Ref{Ref::Slot, npairs};
+    const bool last = cur.size() == 1;
+    std::vector<Ref> next_operands;
+    for (const Elem& e : cur) {
+      if (!e.merged) {
+        Ref r = operands[e.lo];
+        if (r.kind == Ref::Input) {  // widen a carried input once, so later stages read fp32 only
+          const int slot = p.nslots++;
+          r = Ref{Ref::Slot, slot};
+          pending_widen.push_back({operands[e.lo].idx, slot});
+        }
+        next_operands.push_back(r);
+        continue;
       }
-      next.push_back(carried);
+      Block b;
+      b.operands.assign(operands.begin() + e.lo, operands.begin() + e.hi);
+      b.dst = last ? Ref{Ref::Out, 0} : Ref{Ref::Slot, p.nslots++};
+      BlockDesc d{};
+      d.nb = e.hi - e.lo;
+      d.nbt = d.nb <= 2 ? 2 : d.nb <= 4 ? 4 : d.nb <= 8 ? 8 : 16;
+      d.merge0 = (int)p.merges.size();
+      for (const Merge& m : stage_merges) {
+        if (m.llo >= e.lo && m.rhi <= e.hi) {
+          p.merges.push_back(Merge{(int8_t)(m.llo - e.lo), (int8_t)(m.lhi - e.lo), (int8_t)(m.rhi - e.lo), 0, m.node});
+        }
+      }
+      d.nmerges = (int)p.merges.size() - d.merge0;
+      d.wrow = p.nblocks++;
+      b.desc = (int)p.descs.size();
+      p.descs.push_back(d);
+      st.blocks.push_back(b);
+      next_operands.push_back(b.dst);
     }
-    if (first) {
-      p.nslots = lv.final_level ? 0 : npairs + (odd ? 1 : 0);
-      for (int j = 0; j < npairs; ++j) lv.dot_pairs.push_back(j);
+    // Gram partials of this stage: one region per block, reused by later stages
+    size_t off = 0;
+    for (const Block& b : st.blocks) {
+      p.descs[b.desc].poff = (int64_t)off;
+      off += (size_t)gram_entries(p.descs[b.desc].nbt) * ntiles;
     }
-    // combine jobs: siblings (2m, 2m+1) of this level form pair m of the next
-    // level, so the job computing both emits that pair's statistics
-    if (lv.final_level) {
-      lv.jobs.push_back(Job{{0, -1}, -1});
-    } else {
-      for (int m = 0; 2 * m + 1 < npairs; ++m) lv.jobs.push_back(Job{{2 * m, 2 * m + 1}, m});
-      if (npairs % 2 == 1) lv.jobs.push_back(Job{{npairs - 1, -1}, -1});
-    }
-    p.max_pairs = std::max(p.max_pairs, npairs);
-    p.levels.push_back(lv);
-    cur = next;
-    first = false;
+    p.partial_doubles = std::max(p.partial_doubles, off);
+    p.stages.push_back(st);
+    operands = next_operands;
   }
-  // pairs of level l >= 2 whose statistics no sibling job emitted need a
-  // triple-dot pass over their stored operands
-  for (size_t l = 1; l < p.levels.size(); ++l) {
-    std::vector<char> emitted(p.levels[l].pairs.size(), 0);
-    for (const Job& jb : p.levels[l - 1].jobs)
-      if (jb.emit >= 0) emitted[jb.emit] = 1;
-    for (size_t j = 0; j < emitted.size(); ++j)
-      if (!emitted[j]) p.levels[l].dot_pairs.push_back((int)j);
-  }
-
   // ---- workspace layout
   size_t off = 0;
   p.ws_slots = off;
   off = align256(off + (size_t)p.nslots * (size_t)p.N * sizeof(float));
   p.ws_partials = off;
-  off = align256(off + p.partials_bytes());
+  off = align256(off + p.partial_doubles * sizeof(double));
+  p.ws_weights = off;
+  off = align256(off + (size_t)p.nblocks * nseg * kMaxOps * sizeof(double));
   p.ws_coeffs = off;
   off = align256(off + p.table_bytes(2));
   p.ws_stats = off;

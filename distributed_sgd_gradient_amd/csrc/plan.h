@@ -1,20 +1,22 @@
 // plan.h - host-side execution plan of one Adasum combine shape.
 //
 // A plan depends only on (K, dtype, segment offsets).  It holds
-//   * the tile table: every segment cut into tiles of at most kTile elements,
-//     the first tile starting at the segment start and every later tile at a
-//     multiple of kGroup elements, so that vector loads inside a tile are
-//     16-byte aligned whatever the segment boundaries are;
-//   * the tree schedule: level by level, pairs (v0,v1), (v2,v3), ... of the
-//     current vectors with the odd last one carried (the recursive
-//     application of the pairwise operator), and for every level the combine
-//     jobs, each of which computes one node or two sibling nodes and, for
-//     siblings, emits the statistics of the pair they form one level up;
-//   * the workspace layout: fp32 slots for intermediate levels, the fp64
-//     per-tile partial statistics, and the coefficient / statistic tables.
+//   * the tile table: every segment cut into tiles of at most kTile
+//     elements, the first tile starting at the segment start and every later
+//     tile at a multiple of kGroup elements, so that vector loads inside a
+//     tile are 16-byte aligned whatever the segment boundaries are;
+//   * the tree, cut into stages of at most four levels.  Within a stage,
+//     every maximal subtree is a block of at most 16 operands.  Every
+//     statistic a node of the block needs (a.b, |a|^2, |b|^2 of its two
+//     children) is a quadratic form in the Gram matrix of the block's
+//     operands, because every node is a linear combination of them; so a
+//     block needs one Gram pass over its operands, a small per-segment walk
+//     of its merges, and one weighted-sum pass that writes its result;
+//   * the workspace layout: fp32 slots for block results that feed a later
+//     stage, fp64 per-tile Gram partials, leaf weights, and the coefficient
+//     and statistic tables.
 //
-// Pure C++: it is built into the HIP library and into nothing else, and it
-// makes no HIP call, so it can be exercised on a machine without a GPU.
+// Pure C++: it makes no HIP call, so it can be exercised without a GPU.
 #pragma once
 
 #include <cstddef>
@@ -24,43 +26,61 @@
 
 namespace adasum {
 
-constexpr int kGroup = 8;       // elements per thread per vector step (16 B of 16-bit, 32 B of fp32)
-constexpr int kTile = 8192;     // elements per tile (a multiple of kGroup)
-constexpr int kBlock = 256;     // threads per workgroup (4 wave64)
-constexpr int kMaxJobs = 16;    // combine jobs per launch (kernel-argument budget)
-constexpr int kMaxDotPairs = 32;  // triple-dot pairs per launch
+constexpr int kGroup = 8;        // elements per thread per vector step (16 B of 16-bit, 32 B of fp32)
+constexpr int kTile = 32768;     // elements per tile (a multiple of kGroup)
+constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
+constexpr int kMaxOps = 16;      // operands per block: four tree levels
+constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 
 inline size_t dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
 
+// Number of distinct entries of the symmetric n x n Gram matrix.
+constexpr int gram_entries(int n) { return n * (n + 1) / 2; }
+
+// Position of entry (i, j), i <= j, in the packed upper triangle (row-major).
+constexpr int gram_index(int n, int i, int j) { return i * n - i * (i - 1) / 2 + (j - i); }
+
 struct Tile {      // 16 bytes, read by every kernel from device memory
   int64_t start;   // first element (global index into the N-element buffers)
-  int32_t len;     // number of elements, 1..kTile
+  int32_t len;     // number of elements
   int32_t seg;     // owning segment
 };
 
-// Where an operand or result of a tree node lives.
+// One tree node inside a block: node = Adasum(left, right), where left is
+// the block operands [llo, lhi) and right the operands [lhi, rhi), each
+// already combined into one vector by earlier merges of the block.
+struct Merge {
+  int8_t llo, lhi, rhi, pad;
+  int32_t node;    // global node id, level-major over the whole tree
+};
+
+struct BlockDesc {  // device-visible description of one block
+  int32_t nb;       // operands (2..16)
+  int32_t nbt;      // Gram size the kernels use: 2, 4, 8 or 16 (operands >= nb are zero)
+  int32_t merge0;   // first merge in the merge table
+  int32_t nmerges;  // merges of this block, children before parents
+  int64_t poff;     // Gram partials of tile t start at partials + poff + t * gram_entries(nbt)
+  int32_t wrow;     // row of this block in the leaf-weight table
+  int32_t pad;
+};
+
+// Where an operand or result lives.
 struct Ref {
   enum Kind : int8_t { Input = 0, Slot = 1, Out = 2 } kind;
   int32_t idx;     // worker index for Input, slot index for Slot
 };
 
-struct Pair {      // one tree node: node = Adasum(left, right) -> dst
-  Ref left, right, dst;
-  int node;        // global node id, level-major
+struct Block {
+  std::vector<Ref> operands;  // nb refs; all Input in stage 0, all Slot later
+  Ref dst;                    // Slot, or Out for the root block
+  int desc;                   // index into Plan::descs
 };
 
-struct Job {       // one combine job: one node, or two siblings + emitted stats
-  int pair[2];     // indices into Level::pairs; pair[1] < 0 for a single node
-  int emit;        // index of the next-level pair whose stats this job emits, or -1
-};
-
-struct Level {
-  std::vector<Pair> pairs;
-  std::vector<Job> jobs;
-  std::vector<int> dot_pairs;  // pairs whose stats need a triple-dot pass first
-  bool final_level = false;
+struct Stage {
+  std::vector<Block> blocks;
+  std::vector<std::pair<int, int>> widen;  // (input k, slot): inputs carried into this stage
 };
 
 struct Plan {
@@ -68,17 +88,18 @@ struct Plan {
   DType dtype = DType::F32;
   int nseg = 0;
   int64_t N = 0;
-  std::vector<int64_t> offsets;      // nseg + 1
+  std::vector<int64_t> offsets;   // nseg + 1
   std::vector<Tile> tiles;
-  std::vector<int32_t> seg_tile;     // nseg + 1: tiles of segment s are [seg_tile[s], seg_tile[s+1])
-  std::vector<Level> levels;
-  int nslots = 0;                    // fp32 intermediate vectors of N elements
-  int carry_slot = -1;               // slot receiving the carried input when K is odd (K >= 3)
-  int max_pairs = 0;                 // largest pair count of any level (partials rows)
+  std::vector<int32_t> seg_tile;  // nseg + 1: tiles of segment s are [seg_tile[s], seg_tile[s+1])
+  std::vector<Stage> stages;
+  std::vector<BlockDesc> descs;
+  std::vector<Merge> merges;
+  int nslots = 0;                 // fp32 vectors of N elements
+  int nblocks = 0;                // rows of the leaf-weight table
+  size_t partial_doubles = 0;     // largest per-stage Gram partials footprint
 
   // workspace layout, byte offsets (each 256-aligned)
-  size_t ws_slots = 0, ws_partials = 0, ws_coeffs = 0, ws_stats = 0, ws_total = 0;
-  size_t partials_bytes() const { return (size_t)max_pairs * tiles.size() * 3 * sizeof(double); }
+  size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_coeffs = 0, ws_stats = 0, ws_total = 0;
   size_t table_bytes(int per_node) const { return (size_t)(K > 1 ? K - 1 : 0) * nseg * per_node * sizeof(double); }
 };
 

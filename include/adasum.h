@@ -115,8 +115,10 @@ ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int
  *                right, then level 2, ...), or NULL.
  *   stats        device fp64 array [K-1][nseg][3] receiving (a.b, |a|^2,
  *                |b|^2) of every tree node in the same order, or NULL.
- *                Statistics of level >= 2 are taken from the fp32 values the
- *                lower level stored.
+ *                Within each block of up to 16 operands (four tree levels)
+ *                the statistics are evaluated in fp64 from the Gram matrix of
+ *                the block's operands; above a block, from the fp32 values
+ *                its result was stored in.
  *   Other arguments as for adasum_combine.
  */
 ADASUM_API int adasum_combine_ex(const void* const* grads, int K, const int64_t* seg_offsets, int nseg,
@@ -134,7 +136,7 @@ ADASUM_API int adasum_combine_ex(const void* const* grads, int K, const int64_t*
  * most max_rows; rows may be NULL when max_rows is 0) or a negative code.
  */
 typedef struct {
-  char kernel[32];     /* "triple_dot", "finalize", "combine", "widen", "copy" */
+  char kernel[32];     /* "gram", "tree", "wsum", "widen", "copy" */
   int launches;
   double milliseconds;
   double bytes;

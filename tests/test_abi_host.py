@@ -97,11 +97,14 @@ def test_workspace_size_properties():
         arr, p = _off(*off)
         return lib.adasum_workspace_bytes(K, p, arr.size - 1, dtype)
 
-    assert ws(1, (0, 1000)) == 0                 # K = 1 is a copy
-    two = ws(2, (0, 1000))
-    assert 0 < two < 4096                        # K = 2: no fp32 slots, only tables
-    # an odd K needs one more fp32 slot for the carried input
     n = 1 << 20
-    assert ws(4, (0, n)) >= 2 * n * 4 and ws(3, (0, n)) >= 2 * n * 4
-    assert ws(16, (0, 2 * n)) > ws(16, (0, n))
+    assert ws(1, (0, 1000)) == 0                 # K = 1 is a copy
+    # up to 16 operands form one block: no fp32 intermediates, only
+    # Gram partials and tables
+    for K in (2, 3, 9, 16):
+        assert 0 < ws(K, (0, n)) < n
+    # 17 = a block of 16 plus one carried input widened to fp32: two slots
+    assert 2 * n * 4 <= ws(17, (0, n)) < 3 * n * 4
+    assert 4 * n * 4 <= ws(64, (0, n)) < 5 * n * 4   # four blocks of 16
+    assert ws(16, (0, 64 * n)) > ws(16, (0, n))
     assert ws(16, (0, 0)) >= 0 and ws(2, (0,)) >= 0

@@ -160,6 +160,15 @@ def test_small_K_ragged_segments(gpu, K, dtype):
     full_check(wl, f"ragged K={K} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [17, 20, 33, 64, 70])
+def test_multistage_K(gpu, K, dtype):
+    # more than 16 operands: blocks of 16, fp32 block results, carried inputs
+    wl = W.random_case(K, [1, 300, 9, 40000, 8], dtype=dtype, seed=100 + K, kind="shared")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"multistage K={K} {dtype}")
+
+
 def test_fp16_subnormal_scales(gpu):
     wl = W.random_case(8, [3000] * 16 + [7, 1], dtype="f16", seed=11, kind="scaled")
     wl.grads = [g.to(gpu) for g in wl.grads]
