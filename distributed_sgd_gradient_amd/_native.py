@@ -14,6 +14,7 @@ import torch  # noqa: F401  (must be loaded first, see above)
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libadasum.so")
 
 F32, F16, BF16 = 0, 1, 2
+TREE, CHAIN = 0, 1
 OK, EINVAL, ENOMEM, EHIP = 0, -1, -2, -3
 
 # name -> (restype, argtypes); mirrors include/adasum.h
@@ -21,9 +22,12 @@ _VP = ctypes.c_void_p
 _I64P = ctypes.POINTER(ctypes.c_int64)
 SIGNATURES = {
     "adasum_combine": (ctypes.c_int, [_VP, ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, _VP, _VP]),
-    "adasum_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int]),
-    "adasum_combine_ex": (ctypes.c_int, [_VP, ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, _VP, _VP,
-                                         ctypes.c_size_t, _VP, _VP, _VP]),
+    "adasum_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "adasum_combine_ex": (ctypes.c_int, [_VP, ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         _VP, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP]),
+    "adasum_sum": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int, _VP, _VP, ctypes.c_size_t,
+                                  _VP]),
+    "adasum_sum_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
     "adasum_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "adasum_last_error": (ctypes.c_char_p, []),
     "adasum_version": (ctypes.c_int, []),

@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit fused multiply-add: products and sums that the kernels
+    # write separately stay separately rounded (explicit fma() is kept)
+    "-ffp-contract=off",
     "-fvisibility=hidden",
 ]
 

@@ -14,6 +14,7 @@ import torch
 from . import _native
 
 DTYPE_CODES = {torch.float32: _native.F32, torch.float16: _native.F16, torch.bfloat16: _native.BF16}
+SCHEDULES = {"tree": _native.TREE, "chain": _native.CHAIN}
 
 
 def _offsets(seg_offsets, N=None):
@@ -46,56 +47,81 @@ def _grad_list(grads):
     return grads
 
 
-def workspace_bytes(K, seg_offsets, dtype):
+def workspace_bytes(K, seg_offsets, dtype, schedule="tree"):
     off = _offsets(seg_offsets)
     code = DTYPE_CODES[dtype]
     L = _native.lib()
     return _native.check(L.adasum_workspace_bytes(
-        K, off.ctypes.data_as(_native._I64P), off.size - 1, code))
+        K, off.ctypes.data_as(_native._I64P), off.size - 1, code, SCHEDULES[schedule]))
 
 
-def combine(grads, seg_offsets, *, out=None, workspace=None, return_coeffs=False, return_stats=False,
-            stream=None):
-    """Tree Adasum of K gradients, each segment on its own.
+def _check_out(out, g0):
+    if out is None:
+        return torch.empty_like(g0)
+    if out.device != g0.device or out.dtype != g0.dtype or out.numel() != g0.numel() or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like the gradients")
+    return out
+
+
+def combine(grads, seg_offsets, *, schedule="tree", out=None, workspace=None, return_coeffs=False,
+            return_stats=False, return_ortho=False, stream=None):
+    """Adasum of K gradients, each segment on its own.
 
     grads: list of K contiguous 1-D GPU tensors (fp32 / fp16 / bf16), or one
-      [K, N] tensor.  seg_offsets: nseg + 1 CSR offsets (host).  Returns the
-      combined gradient (same dtype), plus the fp64 coefficient table
-      [K-1, nseg, 2] and statistics table [K-1, nseg, 3] when requested.
+      [K, N] tensor.  seg_offsets: nseg + 1 CSR offsets (host).  schedule:
+      "tree" (pairs level by level) or "chain" (left-to-right recursion).
+      Returns the combined gradient (same dtype), followed, when requested,
+      by the fp64 coefficient table [K-1, nseg, 2], the statistics table
+      [K-1, nseg, 3] and the per-segment orthogonality ratio [nseg].
     """
     grads = _grad_list(grads)
     g0 = grads[0]
     off = _offsets(seg_offsets, g0.numel())
     K, nseg = len(grads), off.size - 1
     dev = g0.device
-    if out is None:
-        out = torch.empty_like(g0)
-    elif out.device != dev or out.dtype != g0.dtype or out.numel() != g0.numel() or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like the gradients")
-    need = workspace_bytes(K, off, g0.dtype)
+    out = _check_out(out, g0)
+    need = workspace_bytes(K, off, g0.dtype, schedule)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     coeffs = torch.empty((max(K - 1, 0), nseg, 2), dtype=torch.float64, device=dev) if return_coeffs else None
     stats = torch.empty((max(K - 1, 0), nseg, 3), dtype=torch.float64, device=dev) if return_stats else None
+    ortho = torch.empty((nseg,), dtype=torch.float64, device=dev) if return_ortho else None
     ptrs = (ctypes.c_void_p * K)(*[g.data_ptr() for g in grads])
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     L = _native.lib()
     with torch.cuda.device(dev):
         _native.check(L.adasum_combine_ex(
-            ptrs, K, off.ctypes.data_as(_native._I64P), nseg, DTYPE_CODES[g0.dtype],
+            ptrs, K, off.ctypes.data_as(_native._I64P), nseg, DTYPE_CODES[g0.dtype], SCHEDULES[schedule],
             out.data_ptr(), workspace.data_ptr(), workspace.numel(),
             coeffs.data_ptr() if coeffs is not None else None,
             stats.data_ptr() if stats is not None else None,
+            ortho.data_ptr() if ortho is not None else None,
             ctypes.c_void_p(stream.cuda_stream)))
-    if not (return_coeffs or return_stats):
-        return out
-    res = [out]
-    if return_coeffs:
-        res.append(coeffs)
-    if return_stats:
-        res.append(stats)
-    return tuple(res)
+    extra = [t for t, want in ((coeffs, return_coeffs), (stats, return_stats), (ortho, return_ortho)) if want]
+    return tuple([out] + extra) if extra else out
+
+
+def plain_sum(grads, *, out=None, workspace=None, stream=None):
+    """Synchronous-SGD combination: the element-wise sum of the K gradients,
+    accumulated in fp64 in worker order and rounded once."""
+    grads = _grad_list(grads)
+    g0 = grads[0]
+    K, N, dev = len(grads), g0.numel(), g0.device
+    out = _check_out(out, g0)
+    L = _native.lib()
+    need = _native.check(L.adasum_sum_workspace_bytes(K, N, DTYPE_CODES[g0.dtype]))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ptrs = (ctypes.c_void_p * K)(*[g.data_ptr() for g in grads])
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        _native.check(L.adasum_sum(ptrs, K, N, DTYPE_CODES[g0.dtype], out.data_ptr(),
+                                   workspace.data_ptr() if workspace is not None else None,
+                                   workspace.numel() if workspace is not None else 0,
+                                   ctypes.c_void_p(stream.cuda_stream)))
+    return out
 
 
 def combine_cached(grads, seg_offsets, *, out=None, stream=None):

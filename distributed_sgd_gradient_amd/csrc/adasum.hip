@@ -66,8 +66,8 @@ constexpr size_t kMaxCachedPlans = 64;
 std::mutex g_mu;
 std::list<std::shared_ptr<CachedPlan>> g_plans;  // most recently used first
 
-bool same_shape(const Plan& p, int K, const int64_t* off, int nseg, DType dt) {
-  return p.K == K && p.nseg == nseg && p.dtype == dt &&
+bool same_shape(const Plan& p, int K, const int64_t* off, int nseg, DType dt, Schedule sc) {
+  return p.K == K && p.nseg == nseg && p.dtype == dt && p.schedule == sc &&
          std::memcmp(p.offsets.data(), off, sizeof(int64_t) * (size_t)(nseg + 1)) == 0;
 }
 
@@ -86,9 +86,9 @@ void release_tables(CachedPlan& cp) {
 }
 
 // Caller holds g_mu.
-std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType dt) {
+std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType dt, Schedule sc) {
   for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
-    if (same_shape((*it)->plan, K, off, nseg, dt)) {
+    if (same_shape((*it)->plan, K, off, nseg, dt, sc)) {
       auto hit = *it;
       g_plans.erase(it);
       g_plans.push_front(hit);
@@ -96,7 +96,7 @@ std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType
     }
   }
   auto cp = std::make_shared<CachedPlan>();
-  cp->plan = build_plan(K, off, nseg, dt);
+  cp->plan = build_plan(K, off, nseg, dt, sc);
   g_plans.push_front(cp);
   if (g_plans.size() > kMaxCachedPlans) {
     release_tables(*g_plans.back());
@@ -159,8 +159,8 @@ std::map<std::pair<int, void*>, OwnedWorkspace> g_ws;  // (device, stream) -> bu
 
 // ---------------------------------------------------------------- launch timing
 
-enum KernelKind { kGram = 0, kTree, kWsum, kWiden, kCopy, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "widen", "copy"};
+enum KernelKind { kGram = 0, kTree, kWsum, kWiden, kSum, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "widen", "sum"};
 
 struct ProfRecord {
   int kind;
@@ -208,7 +208,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Checks every pointer argument of a combine call against the shape.
 int validate_buffers(const void* const* grads, int K, int64_t N, size_t esz, int nseg, const void* out,
                      const void* ws, size_t ws_bytes, size_t ws_needed, const double* coeffs,
-                     const double* stats) {
+                     const double* stats, const double* ortho) {
   char buf[200];
   if (grads == nullptr) return fail(ADASUM_EINVAL, "grads is NULL");
   const size_t vec_bytes = (size_t)N * esz;
@@ -245,6 +245,7 @@ int validate_buffers(const void* const* grads, int K, int64_t N, size_t esz, int
   if (ws_needed > 0) written.push_back(rng(ws, ws_needed, "workspace"));
   if (coeffs && nodes * nseg > 0) written.push_back(rng(coeffs, nodes * nseg * 2 * sizeof(double), "coeffs"));
   if (stats && nodes * nseg > 0) written.push_back(rng(stats, nodes * nseg * 3 * sizeof(double), "stats"));
+  if (ortho && nseg > 0) written.push_back(rng(ortho, (size_t)nseg * sizeof(double), "ortho"));
   for (size_t i = 0; i < written.size(); ++i) {
     for (size_t j = i + 1; j < written.size(); ++j) {
       if (overlaps(written[i], written[j])) {
@@ -271,6 +272,7 @@ struct CallBuffers {
   char* ws;
   double* coeffs;
   double* stats;
+  double* ortho;
 };
 
 void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
@@ -288,15 +290,6 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
   const int ntiles = (int)p.tiles.size();
   const size_t esz = dtype_size(p.dtype);
   hipError_t e;
-  if (p.K == 1) {
-    if (p.N > 0) {
-      const int pr = prof_start(kCopy, 2.0 * (double)p.N * esz, st);
-      e = hipMemcpyAsync(b.out, b.grads[0], (size_t)p.N * esz, hipMemcpyDeviceToDevice, st);
-      prof_stop(pr, st);
-      if (e != hipSuccess) return fail_hip(e, "copying the single input");
-    }
-    return ADASUM_OK;
-  }
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
   double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
   for (const Stage& sg : p.stages) {
@@ -382,6 +375,9 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         t.weights = weights;
         t.coeffs = b.coeffs;
         t.stats = b.stats;
+        t.ortho = b.ortho;
+        t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
+        t.nblocks_total = p.nblocks;
         double bytes = 0;
         for (const Block& bk : sg.blocks) bytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
         const int pr = prof_start(kTree, bytes, st);
@@ -402,6 +398,9 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
       t.weights = weights;
       t.coeffs = b.coeffs;
       t.stats = b.stats;
+      t.ortho = b.ortho;
+      t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
+      t.nblocks_total = p.nblocks;
       e = launch_tree(t, st);
       if (e != hipSuccess) return fail_hip(e, "launching tree");
     }
@@ -409,22 +408,23 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
   return ADASUM_OK;
 }
 
-int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, void* out,
-                 void* workspace, size_t workspace_bytes, double* coeffs, double* stats, void* stream,
-                 bool owned_workspace) {
+int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, int schedule,
+                 void* out, void* workspace, size_t workspace_bytes, double* coeffs, double* stats,
+                 double* ortho, void* stream, bool owned_workspace) {
   std::string err;
-  if (!validate_shape(K, seg_offsets, nseg, dtype, &err)) return fail(ADASUM_EINVAL, err);
+  if (!validate_shape(K, seg_offsets, nseg, dtype, schedule, &err)) return fail(ADASUM_EINVAL, err);
   const DType dt = static_cast<DType>(dtype);
+  const Schedule sc = static_cast<Schedule>(schedule);
   const int64_t N = seg_offsets[nseg];
 
   std::lock_guard<std::mutex> lock(g_mu);
-  std::shared_ptr<CachedPlan> cp = find_plan(K, seg_offsets, nseg, dt);
+  std::shared_ptr<CachedPlan> cp = find_plan(K, seg_offsets, nseg, dt, sc);
   const Plan& p = cp->plan;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int device = 0;
 
   if (owned_workspace) {
-    int rc = validate_buffers(grads, K, N, dtype_size(dt), nseg, out, nullptr, 0, 0, nullptr, nullptr);
+    int rc = validate_buffers(grads, K, N, dtype_size(dt), nseg, out, nullptr, 0, 0, nullptr, nullptr, nullptr);
     if (rc != ADASUM_OK) return rc;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -449,7 +449,7 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
     // inputs and out were checked above; the library buffer cannot alias them
   } else {
     int rc = validate_buffers(grads, K, N, dtype_size(dt), nseg, out, workspace, workspace_bytes, p.ws_total,
-                              coeffs, stats);
+                              coeffs, stats, ortho);
     if (rc != ADASUM_OK) return rc;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -465,6 +465,7 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
   b.ws = ws;
   b.coeffs = coeffs ? coeffs : reinterpret_cast<double*>(ws + p.ws_coeffs);
   b.stats = stats ? stats : reinterpret_cast<double*>(ws + p.ws_stats);
+  b.ortho = ortho;
   return enqueue(p, tables, b, st);
 }
 
@@ -475,21 +476,68 @@ extern "C" {
 
 int adasum_combine(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, void* out,
                    void* stream) {
-  return adasum::combine_impl(grads, K, seg_offsets, nseg, dtype, out, nullptr, 0, nullptr, nullptr, stream,
-                              true);
+  return adasum::combine_impl(grads, K, seg_offsets, nseg, dtype, int(adasum::Schedule::Tree), out, nullptr, 0,
+                              nullptr, nullptr, nullptr, stream, true);
 }
 
-int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int nseg, int dtype) {
+int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int nseg, int dtype, int schedule) {
   std::string err;
-  if (!adasum::validate_shape(K, seg_offsets, nseg, dtype, &err)) return adasum::fail(ADASUM_EINVAL, err);
+  if (!adasum::validate_shape(K, seg_offsets, nseg, dtype, schedule, &err))
+    return adasum::fail(ADASUM_EINVAL, err);
   std::lock_guard<std::mutex> lock(adasum::g_mu);
-  return (int64_t)adasum::find_plan(K, seg_offsets, nseg, static_cast<adasum::DType>(dtype))->plan.ws_total;
+  return (int64_t)adasum::find_plan(K, seg_offsets, nseg, static_cast<adasum::DType>(dtype),
+                                    static_cast<adasum::Schedule>(schedule))
+      ->plan.ws_total;
 }
 
-int adasum_combine_ex(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype, void* out,
-                      void* workspace, size_t workspace_bytes, double* coeffs, double* stats, void* stream) {
-  return adasum::combine_impl(grads, K, seg_offsets, nseg, dtype, out, workspace, workspace_bytes, coeffs, stats,
-                              stream, false);
+int adasum_combine_ex(const void* const* grads, int K, const int64_t* seg_offsets, int nseg, int dtype,
+                      int schedule, void* out, void* workspace, size_t workspace_bytes, double* coeffs,
+                      double* stats, double* ortho, void* stream) {
+  return adasum::combine_impl(grads, K, seg_offsets, nseg, dtype, schedule, out, workspace, workspace_bytes, coeffs,
+                              stats, ortho, stream, false);
+}
+
+int64_t adasum_sum_workspace_bytes(int K, int64_t N, int dtype) {
+  using namespace adasum;
+  if (K < 1 || N < 0 || (dtype != int(DType::F32) && dtype != int(DType::F16) && dtype != int(DType::BF16)))
+    return fail(ADASUM_EINVAL, "adasum_sum_workspace_bytes: K >= 1, N >= 0 and a known dtype are required");
+  // more operands than one launch holds: an fp64 running sum between launches
+  return K <= kSumOps ? 0 : N * (int64_t)sizeof(double);
+}
+
+int adasum_sum(const void* const* grads, int K, int64_t N, int dtype, void* out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  using namespace adasum;
+  const int64_t need = adasum_sum_workspace_bytes(K, N, dtype);
+  if (need < 0) return (int)need;
+  const int64_t off[2] = {0, N};
+  std::string err;
+  if (!validate_shape(K, off, 1, dtype, 0, &err)) return fail(ADASUM_EINVAL, err);
+  const DType dt = static_cast<DType>(dtype);
+  int rc = validate_buffers(grads, K, N, dtype_size(dt), 0, out, workspace, workspace_bytes, (size_t)need,
+                            nullptr, nullptr, nullptr);
+  if (rc != ADASUM_OK) return rc;
+  if (N == 0) return ADASUM_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_mu);
+  double* acc = static_cast<double*>(workspace);
+  for (int k0 = 0; k0 < K; k0 += kSumOps) {
+    SumArgs a{};
+    a.nx = std::min(kSumOps, K - k0);
+    for (int i = 0; i < a.nx; ++i) a.x[i] = grads[k0 + i];
+    a.acc_in = k0 > 0 ? acc : nullptr;
+    const bool final_launch = k0 + kSumOps >= K;
+    a.acc_out = final_launch ? nullptr : acc;
+    a.out = out;
+    a.n = N;
+    const double bytes = (double)N * (a.nx * dtype_size(dt) + (a.acc_in ? 8.0 : 0.0) +
+                                      (final_launch ? dtype_size(dt) : 8.0));
+    const int pr = prof_start(kSum, bytes, st);
+    hipError_t e = launch_sum(dt, a, st);
+    prof_stop(pr, st);
+    if (e != hipSuccess) return fail_hip(e, "launching sum");
+  }
+  return ADASUM_OK;
 }
 
 int adasum_profile_begin(void) {

@@ -27,10 +27,13 @@ struct TreeArgs {
   const double* partials;
   int desc0;                // first block of this launch (consecutive descs)
   int nblocks;
+  int nblocks_total;        // blocks of the whole plan (rows of weights / leafnorm)
   int nseg;
   double* weights;          // [nblocks total][nseg][kMaxOps]
+  double* leafnorm;         // [nblocks total][nseg]: sum of |g_k|^2 over the block's input operands
   double* coeffs;           // [K-1][nseg][2]
   double* stats;            // [K-1][nseg][3]
+  double* ortho;            // [nseg] or NULL: |result|^2 / sum_k |g_k|^2, written by the root block
 };
 
 // Weighted sum: per (block, tile), y = sum_k w_k x_k, rounded once.
@@ -41,6 +44,19 @@ struct WsumArgs {
   const Tile* tiles;
   int nseg;
   const double* weights;
+};
+
+// Plain sum of up to kSumOps operands, element by element in fp64, in
+// operand order: acc = (acc_in ? acc_in : 0) + x0 + x1 + ...; the result goes
+// to acc_out (fp64) or, rounded once, to out.
+constexpr int kSumOps = 64;
+struct SumArgs {
+  const void* x[kSumOps];
+  int nx;
+  const double* acc_in;
+  double* acc_out;
+  void* out;
+  int64_t n;
 };
 
 // Widen one input to fp32 over every tile.
@@ -56,5 +72,6 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
 hipError_t launch_wsum(DType in_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
                        hipStream_t st);
 hipError_t launch_widen(DType src_t, const WidenArgs& a, int ntiles, hipStream_t st);
+hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st);
 
 }  // namespace adasum

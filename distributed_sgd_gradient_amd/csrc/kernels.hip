@@ -27,6 +27,7 @@
 // No atomics anywhere: results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "kernels.h"
@@ -60,15 +61,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Loads through address space 1, so that pointers fetched from argument
+// tables still compile to global (not flat) memory instructions.
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 template <typename T>
 struct Elem;
 
 template <>
 struct Elem<float> {
-  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ float load1(const float* p) { return gload(p); }
   static __device__ __forceinline__ void load8(const float* p, float (&v)[kGroup]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    const v4f a = gload(reinterpret_cast<const v4f*>(p));
+    const v4f b = gload(reinterpret_cast<const v4f*>(p + 4));
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
@@ -87,9 +98,9 @@ struct Elem<float> {
 
 template <>
 struct Elem<_Float16> {
-  static __device__ __forceinline__ float load1(const _Float16* p) { return (float)*p; }
+  static __device__ __forceinline__ float load1(const _Float16* p) { return (float)gload(p); }
   static __device__ __forceinline__ void load8(const _Float16* p, float (&v)[kGroup]) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const v4u raw = gload(reinterpret_cast<const v4u*>(p));
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -116,9 +127,11 @@ struct Elem<_Float16> {
 template <>
 struct Elem<bf16_t> {
   static __device__ __forceinline__ float widen(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-  static __device__ __forceinline__ float load1(const bf16_t* p) { return widen(p->bits); }
+  static __device__ __forceinline__ float load1(const bf16_t* p) {
+    return widen(gload(reinterpret_cast<const uint16_t*>(p)));
+  }
   static __device__ __forceinline__ void load8(const bf16_t* p, float (&v)[kGroup]) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const v4u raw = gload(reinterpret_cast<const v4u*>(p));
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -196,7 +209,6 @@ __global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
   constexpr int GPT = NB * RG / kBlock;       // row groups each thread stages
   static_assert(GPT * kBlock == NB * RG, "staging must divide evenly");
   static_assert(RG % 64 == 0, "a wave must stage rows of a single operand");
-  static_assert(2 * 64 * NAB * sizeof(double) <= NB * S * sizeof(float), "reduction must fit the stage buffer");
   __shared__ __align__(16) float stage[NB * S];  // operand-major: stage[k * S + r]
 
   const int tile_id = blockIdx.x;
@@ -209,24 +221,35 @@ __global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
   const int role = tid >> 6;
   const int lane = tid & 63;
 
-  const T* xs[NB];
-#pragma unroll
-  for (int k = 0; k < NB; ++k) xs[k] = static_cast<const T*>(args.x[j][k]);
-
   double acc[NAB];
 #pragma unroll
   for (int e = 0; e < NAB; ++e) acc[e] = 0.0;
 
+  // Operand k of row group q: a wave's 64 lanes share one operand (RG is a
+  // multiple of 64), so k is wave-uniform and the pointer is read straight
+  // from the argument table.  A step that lies inside [lo, hi) for every
+  // operand loads unconditionally, so all of a thread's loads are in flight
+  // together; edge steps and absent operands take the guarded path.
+  bool any_null = false;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) any_null |= (args.x[j][k] == nullptr);
   float pre[GPT][kGroup];
   auto fetch = [&](int step) {
     const int64_t r0 = first + (int64_t)step * S;
+    if (!any_null && r0 >= lo && r0 + S <= hi) {
 #pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int q = tid + g * kBlock;
-      // a wave's 64 lanes share one operand (RG is a multiple of 64): make that explicit
-      const int k = __builtin_amdgcn_readfirstlane(q / RG);
-      const int rg = q % RG;
-      load_group<T>(xs[k], r0 + (int64_t)rg * kGroup, lo, hi, pre[g]);
+      for (int g = 0; g < GPT; ++g) {
+        const int q = tid + g * kBlock;
+        const int k = __builtin_amdgcn_readfirstlane(q / RG);
+        Elem<T>::load8(static_cast<const T*>(args.x[j][k]) + r0 + (int64_t)(q % RG) * kGroup, pre[g]);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < GPT; ++g) {
+        const int q = tid + g * kBlock;
+        const int k = __builtin_amdgcn_readfirstlane(q / RG);
+        load_group<T>(static_cast<const T*>(args.x[j][k]), r0 + (int64_t)(q % RG) * kGroup, lo, hi, pre[g]);
+      }
     }
   };
 
@@ -273,29 +296,38 @@ __global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
   __syncthreads();
 
   // Reduce every accumulator over its lanes through LDS, in lane order.
+  // Rows of a lane are padded by one entry so that neither the writes (one
+  // row per lane) nor the reads (one column per thread) pile onto one bank.
   double* red = reinterpret_cast<double*>(stage);
   double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
-  if (role >= 2) {
+  constexpr int PAB = NAB + 1, PAA = NAA + 1;
+  static_assert(64 * PAB * sizeof(double) <= NB * S * sizeof(float), "reduction must fit the stage buffer");
+  static_assert(2 * 64 * PAA * sizeof(double) <= NB * S * sizeof(float), "reduction must fit the stage buffer");
+  if (role == 2) {
 #pragma unroll
-    for (int e = 0; e < NAB; ++e) red[((role - 2) * NAB + e) * 64 + lane] = acc[e];
+    for (int e = 0; e < NAB; ++e) red[lane * PAB + e] = acc[e];
+  }
+  __syncthreads();
+  if (role == 3) {  // wave 3 adds its strips after wave 2's, lane by lane
+#pragma unroll
+    for (int e = 0; e < NAB; ++e) red[lane * PAB + e] += acc[e];
   }
   __syncthreads();
   if (tid < NAB) {
     double sum = 0.0;
-    for (int w = 0; w < 2; ++w)
-      for (int l = 0; l < 64; ++l) sum += red[(w * NAB + tid) * 64 + l];
+    for (int l = 0; l < 64; ++l) sum += red[l * PAB + tid];
     out[gram_index(NB, tid / H, H + tid % H)] = sum;
   }
   __syncthreads();
   if (role < 2) {
 #pragma unroll
-    for (int e = 0; e < NAA; ++e) red[(role * NAA + e) * 64 + lane] = acc[e];
+    for (int e = 0; e < NAA; ++e) red[(role * 64 + lane) * PAA + e] = acc[e];
   }
   __syncthreads();
   if ((tid & 63) < NAA && tid < 128) {
     const int w = tid >> 6, e = tid & 63;
     double sum = 0.0;
-    for (int l = 0; l < 64; ++l) sum += red[(w * NAA + e) * 64 + l];
+    for (int l = 0; l < 64; ++l) sum += red[(w * 64 + l) * PAA + e];
     // packed index e of the H x H triangle -> (i, k)
     int i = 0, rem = e;
     while (rem >= H - i) {
@@ -383,6 +415,20 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       a.stats[at * 3 + 1] = A;
       a.stats[at * 3 + 2] = B;
     }
+    // sum of |g_k|^2 over the block's input operands, in operand order
+    double leaf = 0.0;
+    for (int k = 0; k < d.nb; ++k)
+      if ((d.leafmask >> k) & 1) leaf += G[gram_index(n, k, k)];
+    a.leafnorm[(int64_t)d.wrow * a.nseg + s] = leaf;
+    if (d.root && a.ortho != nullptr) {
+      // orthogonality of the segment's gradients: |result|^2 over the sum
+      // of their squared norms (lower blocks finished in earlier launches)
+      double total = 0.0;
+      for (int r = 0; r < a.nblocks_total; ++r)
+        total += (r == d.wrow) ? leaf : a.leafnorm[(int64_t)r * a.nseg + s];
+      const double out2 = quad_form(G, n, w, 0, d.nb, 0, d.nb);
+      a.ortho[s] = (total == 0.0) ? __builtin_nan("") : out2 / total;
+    }
   }
   __syncthreads();
   if (tid < kMaxOps) a.weights[((int64_t)d.wrow * a.nseg + s) * kMaxOps + tid] = w[tid];
@@ -390,6 +436,10 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 
 // ----------------------------------------------------------------- weighted sum
 
+// Operands at or beyond the block's count are NULL in the argument table;
+// they alias operand 0 (cache hits, no extra HBM traffic) and their terms are
+// masked to zero, so the loop has no branches and every load of a step is in
+// flight at once.
 template <typename TIn, int NB, typename TOut>
 __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   const int tile_id = blockIdx.x;
@@ -397,11 +447,14 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   const Tile tile = args.tiles[tile_id];
   const TileSpan sp = span_of(tile);
   const double* wrow = args.weights + ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  const TIn* x0 = static_cast<const TIn*>(args.x[j][0]);
   const TIn* xs[NB];
+  bool live[NB];
   double w[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    xs[k] = static_cast<const TIn*>(args.x[j][k]);
+    live[k] = args.x[j][k] != nullptr;
+    xs[k] = live[k] ? static_cast<const TIn*>(args.x[j][k]) : x0;
     w[k] = wrow[k];
   }
   TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
@@ -411,30 +464,95 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   auto one = [&](int64_t i) {
     double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < NB; ++k)
-      if (xs[k] != nullptr) acc = add_rn(acc, mul_rn(w[k], (double)Elem<TIn>::load1(xs[k] + i)));
+    for (int k = 0; k < NB; ++k) {
+      const double t = mul_rn(w[k], (double)Elem<TIn>::load1(xs[k] + i));
+      acc = add_rn(acc, live[k] ? t : 0.0);
+    }
     Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
   };
 
   if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
   for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
-    double acc[kGroup];
+    float v[NB][kGroup];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if (xs[k] == nullptr) continue;
-      float v[kGroup];
-      Elem<TIn>::load8(xs[k] + g, v);
-#pragma unroll
-      for (int e = 0; e < kGroup; ++e) acc[e] = add_rn(acc[e], mul_rn(w[k], (double)v[e]));
-    }
+    for (int k = 0; k < NB; ++k) Elem<TIn>::load8(xs[k] + g, v[k]);
     TOut r[kGroup];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) r[e] = Elem<TOut>::round(acc[e], &unused);
+    for (int e = 0; e < kGroup; ++e) {
+      double acc = 0.0;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const double t = mul_rn(w[k], (double)v[k][e]);
+        acc = add_rn(acc, live[k] ? t : 0.0);
+      }
+      r[e] = Elem<TOut>::round(acc, &unused);
+    }
     Elem<TOut>::store8(y + g, r);
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
+}
+
+// ----------------------------------------------------------------- plain sum
+
+template <typename T>
+__device__ __forceinline__ void sum_group(const SumArgs& a, int64_t g, int cnt) {
+  double acc[kGroup];
+  int k0 = 0;
+  if (a.acc_in != nullptr) {
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) acc[e] = e < cnt ? a.acc_in[g + e] : 0.0;
+  } else {  // the sum starts from the first operand itself
+    const T* x = static_cast<const T*>(a.x[0]);
+    float v[kGroup];
+    if (cnt == kGroup) {
+      Elem<T>::load8(x + g, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) v[e] = e < cnt ? Elem<T>::load1(x + g + e) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) acc[e] = (double)v[e];
+    k0 = 1;
+  }
+  for (int k = k0; k < a.nx; ++k) {
+    const T* x = static_cast<const T*>(a.x[k]);
+    float v[kGroup];
+    if (cnt == kGroup) {
+      Elem<T>::load8(x + g, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) v[e] = e < cnt ? Elem<T>::load1(x + g + e) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) acc[e] = add_rn(acc[e], (double)v[e]);
+  }
+  if (a.acc_out != nullptr) {
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e)
+      if (e < cnt) a.acc_out[g + e] = acc[e];
+  } else {
+    T* y = static_cast<T*>(a.out);
+    double unused;
+    if (cnt == kGroup) {
+      T r[kGroup];
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) r[e] = Elem<T>::round(acc[e], &unused);
+      Elem<T>::store8(y + g, r);
+    } else {
+      for (int e = 0; e < cnt; ++e) Elem<T>::store1(y + g + e, Elem<T>::round(acc[e], &unused));
+    }
+  }
+}
+
+// Grid-stride over groups of kGroup elements; the last group may be short.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void sum_kernel(SumArgs a) {
+  const int64_t ngroups = (a.n + kGroup - 1) / kGroup;
+  for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < ngroups; q += (int64_t)gridDim.x * kBlock) {
+    const int64_t g = q * kGroup;
+    const int cnt = (int)(a.n - g < kGroup ? a.n - g : kGroup);
+    sum_group<T>(a, g, cnt);
+  }
 }
 
 // ----------------------------------------------------------------- widen
@@ -470,6 +588,16 @@ template <typename T>
 struct RunWiden {
   static hipError_t run(const WidenArgs& a, int ntiles, hipStream_t st) {
     hipLaunchKernelGGL(widen_kernel<T>, dim3(ntiles), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+  }
+};
+
+template <typename T>
+struct RunSum {
+  static hipError_t run(const SumArgs& a, hipStream_t st) {
+    const int64_t groups = (a.n + kGroup - 1) / kGroup;
+    const int64_t blocks = std::min<int64_t>((groups + kBlock - 1) / kBlock, 8192);
+    hipLaunchKernelGGL(sum_kernel<T>, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(kBlock), 0, st, a);
     return hipGetLastError();
   }
 };
@@ -533,5 +661,7 @@ hipError_t launch_wsum(DType in_t, int nbt, DType out_t, const WsumArgs& a, int 
 hipError_t launch_widen(DType src_t, const WidenArgs& a, int ntiles, hipStream_t st) {
   return by_type<RunWiden>(src_t, a, ntiles, st);
 }
+
+hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st) { return by_type<RunSum>(t, a, st); }
 
 }  // namespace adasum

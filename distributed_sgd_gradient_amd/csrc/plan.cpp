@@ -16,8 +16,13 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, std::string* err) {
+bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, int schedule, std::string* err) {
   char buf[160];
+  if (schedule != int(Schedule::Tree) && schedule != int(Schedule::Chain)) {
+    snprintf(buf, sizeof buf, "unknown schedule %d (0 = tree, 1 = chain)", schedule);
+    *err = buf;
+    return false;
+  }
   if (K < 1) {
     snprintf(buf, sizeof buf, "K must be >= 1 (got %d)", K);
     *err = buf;
@@ -64,10 +69,47 @@ bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, std::str
   return true;
 }
 
-Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
+namespace {
+
+struct Elem {
+  int lo, hi;   // operand range of the stage
+  bool merged;  // false: a bare operand carried through the stage
+};
+
+// Merges of one stage of the tree schedule: up to four levels of pairing
+// (v0,v1), (v2,v3), ... over `cur`, the odd last element carried.
+void tree_stage(std::vector<Elem>& cur, std::vector<Merge>& merges, int& node) {
+  for (int level = 0; level < 4 && cur.size() > 1; ++level) {
+    std::vector<Elem> next;
+    for (size_t j = 0; 2 * j + 1 < cur.size(); ++j) {
+      const Elem& l = cur[2 * j];
+      const Elem& r = cur[2 * j + 1];
+      merges.push_back(Merge{(int8_t)l.lo, (int8_t)l.hi, (int8_t)r.hi, 0, node++});
+      next.push_back(Elem{l.lo, r.hi, true});
+    }
+    if (cur.size() % 2 == 1) next.push_back(cur.back());
+    cur = next;
+  }
+}
+
+// One stage of the chain schedule: the accumulated vector (first element)
+// meets the following operands one at a time, all of them in this stage.
+void chain_stage(std::vector<Elem>& cur, std::vector<Merge>& merges, int& node) {
+  Elem acc = cur[0];
+  for (size_t j = 1; j < cur.size(); ++j) {
+    merges.push_back(Merge{(int8_t)acc.lo, (int8_t)acc.hi, (int8_t)cur[j].hi, 0, node++});
+    acc = Elem{acc.lo, cur[j].hi, true};
+  }
+  cur.assign(1, acc);
+}
+
+}  // namespace
+
+Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule schedule) {
   Plan p;
   p.K = K;
   p.dtype = dtype;
+  p.schedule = schedule;
   p.nseg = nseg;
   p.offsets.assign(offsets, offsets + nseg + 1);
   p.N = offsets[nseg];
@@ -89,40 +131,36 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
   const size_t ntiles = p.tiles.size();
 
-  // ---- tree, stage by stage.  The level schedule is the fixed binary
-  // tree: each level pairs (v0,v1), (v2,v3), ... and carries an odd last
-  // vector.  A stage runs up to four levels over its operand list; the
-  // elements left at its top are the roots of its blocks (or operands that
-  // were carried through untouched).
-  struct Elem {
-    int lo, hi;   // operand range of the stage
-    bool merged;  // false: a bare operand carried through the stage
-  };
+  // ---- blocks, stage by stage.  Every operand of a stage above the first
+  // is an fp32 slot: the result of a lower block, or an input gradient
+  // widened once before the stage that first reads it.
   std::vector<Ref> operands(K);
+  std::vector<char> is_leaf(K, 1);   // per operand of the current stage
   for (int k = 0; k < K; ++k) operands[k] = Ref{Ref::Input, k};
   int node = 0;
+  int next_leaf = K;                 // chain: first input not yet in any stage
+  if (schedule == Schedule::Chain) {
+    next_leaf = std::min(K, kMaxOps);
+    operands.resize(next_leaf);
+    is_leaf.resize(next_leaf);
+  }
   std::vector<std::pair<int, int>> pending_widen;  // carried inputs the next stage reads from fp32 slots
-  while (operands.size() > 1) {
+  bool first = true;
+  while (first || operands.size() > 1) {
     Stage st;
     st.widen.swap(pending_widen);
     std::vector<Elem> cur;
     for (int i = 0; i < (int)operands.size(); ++i) cur.push_back(Elem{i, i + 1, false});
     std::vector<Merge> stage_merges;
-    for (int level = 0; level < 4 && cur.size() > 1; ++level) {
-      std::vector<Elem> next;
-      for (size_t j = 0; 2 * j + 1 < cur.size(); ++j) {
-        const Elem& l = cur[2 * j];
-        const Elem& r = cur[2 * j + 1];
-        stage_merges.push_back(Merge{(int8_t)l.lo, (int8_t)l.hi, (int8_t)r.hi, 0, node++});
-        next.push_back(Elem{l.lo, r.hi, true});
-      }
-      if (cur.size() % 2 == 1) next.push_back(cur.back());
-      cur = next;
-    }
-    const bool last = cur.size() == 1;
+    if (schedule == Schedule::Tree)
+      tree_stage(cur, stage_merges, node);
+    else
+      chain_stage(cur, stage_merges, node);
+    const bool last = cur.size() == 1 && next_leaf == K;
     std::vector<Ref> next_operands;
+    std::vector<char> next_is_leaf;
     for (const Elem& e : cur) {
-      if (!e.merged) {
+      if (!e.merged && !(last && operands.size() == 1)) {
         Ref r = operands[e.lo];
         if (r.kind == Ref::Input) {  // widen a carried input once, so later stages read fp32 only
           const int slot = p.nslots++;
@@ -130,8 +168,10 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
           pending_widen.push_back({operands[e.lo].idx, slot});
         }
         next_operands.push_back(r);
+        next_is_leaf.push_back(is_leaf[e.lo]);
         continue;
       }
+      // a block: the operands under e (K = 1: the single input, no merge)
       Block b;
       b.operands.assign(operands.begin() + e.lo, operands.begin() + e.hi);
       b.dst = last ? Ref{Ref::Out, 0} : Ref{Ref::Slot, p.nslots++};
@@ -146,10 +186,25 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
       }
       d.nmerges = (int)p.merges.size() - d.merge0;
       d.wrow = p.nblocks++;
+      for (int k = e.lo; k < e.hi; ++k)
+        if (is_leaf[k]) d.leafmask |= (uint16_t)(1u << (k - e.lo));
+      d.root = last ? 1 : 0;
       b.desc = (int)p.descs.size();
       p.descs.push_back(d);
       st.blocks.push_back(b);
       next_operands.push_back(b.dst);
+      next_is_leaf.push_back(0);
+    }
+    // chain: the next stage is the accumulated vector plus up to 15 more inputs
+    if (schedule == Schedule::Chain && !last) {
+      const int take = std::min(K - next_leaf, kMaxOps - 1);
+      for (int k = next_leaf; k < next_leaf + take; ++k) {
+        const int slot = p.nslots++;
+        pending_widen.push_back({k, slot});
+        next_operands.push_back(Ref{Ref::Slot, slot});
+        next_is_leaf.push_back(1);
+      }
+      next_leaf += take;
     }
     // Gram partials of this stage: one region per block, reused by later stages
     size_t off = 0;
@@ -160,7 +215,11 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
     p.partial_doubles = std::max(p.partial_doubles, off);
     p.stages.push_back(st);
     operands = next_operands;
+    is_leaf = next_is_leaf;
+    first = false;
+    if (last) break;
   }
+
   // ---- workspace layout
   size_t off = 0;
   p.ws_slots = off;
@@ -169,6 +228,8 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype) {
   off = align256(off + p.partial_doubles * sizeof(double));
   p.ws_weights = off;
   off = align256(off + (size_t)p.nblocks * nseg * kMaxOps * sizeof(double));
+  p.ws_leafnorm = off;
+  off = align256(off + (size_t)p.nblocks * nseg * sizeof(double));
   p.ws_coeffs = off;
   off = align256(off + p.table_bytes(2));
   p.ws_stats = off;

@@ -34,6 +34,11 @@ constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 
+// Order in which the pairwise operator is applied to the K gradients.
+//   Tree:  level by level, pairs (v0,v1), (v2,v3), ..., odd last carried;
+//   Chain: left to right, acc = Adasum(acc, g_{i+1}).
+enum class Schedule : int { Tree = 0, Chain = 1 };
+
 inline size_t dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
 
 // Number of distinct entries of the symmetric n x n Gram matrix.
@@ -57,13 +62,14 @@ struct Merge {
 };
 
 struct BlockDesc {  // device-visible description of one block
-  int32_t nb;       // operands (2..16)
+  int32_t nb;       // operands (1..16; 1 only for K = 1)
   int32_t nbt;      // Gram size the kernels use: 2, 4, 8 or 16 (operands >= nb are zero)
   int32_t merge0;   // first merge in the merge table
   int32_t nmerges;  // merges of this block, children before parents
   int64_t poff;     // Gram partials of tile t start at partials + poff + t * gram_entries(nbt)
   int32_t wrow;     // row of this block in the leaf-weight table
-  int32_t pad;
+  uint16_t leafmask;  // bit k: operand k is one of the K input gradients
+  uint16_t root;      // 1 for the block whose result is the output
 };
 
 // Where an operand or result lives.
@@ -86,6 +92,7 @@ struct Stage {
 struct Plan {
   int K = 0;
   DType dtype = DType::F32;
+  Schedule schedule = Schedule::Tree;
   int nseg = 0;
   int64_t N = 0;
   std::vector<int64_t> offsets;   // nseg + 1
@@ -99,14 +106,15 @@ struct Plan {
   size_t partial_doubles = 0;     // largest per-stage Gram partials footprint
 
   // workspace layout, byte offsets (each 256-aligned)
-  size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_coeffs = 0, ws_stats = 0, ws_total = 0;
+  size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_leafnorm = 0, ws_coeffs = 0, ws_stats = 0,
+         ws_total = 0;
   size_t table_bytes(int per_node) const { return (size_t)(K > 1 ? K - 1 : 0) * nseg * per_node * sizeof(double); }
 };
 
-// Validate (K, offsets, nseg, dtype); on failure return false with a message.
-bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, std::string* err);
+// Validate (K, offsets, nseg, dtype, schedule); on failure return false with a message.
+bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, int schedule, std::string* err);
 
 // Build the plan of a validated shape.
-Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype);
+Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule schedule);
 
 }  // namespace adasum

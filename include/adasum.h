@@ -63,6 +63,12 @@ typedef enum {
   ADASUM_BF16 = 2
 } adasum_dtype_t;
 
+/* Order in which the pairwise operator is applied to the K gradients. */
+typedef enum {
+  ADASUM_TREE = 0, /* level by level: (g0,g1), (g2,g3), ...; the odd last vector is carried */
+  ADASUM_CHAIN = 1 /* left to right: acc = Adasum(acc, g_{i+1}), the linear recursion */
+} adasum_schedule_t;
+
 #define ADASUM_OK 0
 #define ADASUM_EINVAL (-1) /* bad argument: see adasum_last_error()          */
 #define ADASUM_ENOMEM (-2) /* a device or host allocation failed             */
@@ -94,36 +100,60 @@ ADASUM_API int adasum_combine(const void* const* grads, int K, const int64_t* se
 
 /*
  * adasum_workspace_bytes - device workspace adasum_combine_ex needs for this
- * shape, in bytes (0 when none is needed).  Returns a negative ADASUM_E*
- * code for invalid arguments (same checks as adasum_combine on K, offsets,
- * nseg and dtype).
+ * shape and schedule, in bytes.  Returns a negative ADASUM_E* code for
+ * invalid arguments (same checks as adasum_combine_ex on K, offsets, nseg,
+ * dtype and schedule).
  */
-ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int nseg, int dtype);
+ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int nseg, int dtype,
+                                          int schedule);
 
 /*
- * adasum_combine_ex - adasum_combine with caller-provided memory and the
- * per-node statistics exposed.
+ * adasum_combine_ex - adasum_combine with a choice of schedule, caller-
+ * provided memory and the per-node statistics exposed.
  *
+ *   schedule     ADASUM_TREE (the combine above) or ADASUM_CHAIN (the linear
+ *                recursion the text introduces first: the running result
+ *                meets g_1, g_2, ... in turn).
  *   workspace, workspace_bytes
  *                device buffer of at least adasum_workspace_bytes(...)
- *                bytes, 16-byte aligned, not overlapping any other argument;
- *                may be NULL when that size is 0.  Its contents on entry do
- *                not matter; calls sharing one workspace must be ordered on
- *                one stream.
+ *                bytes, 16-byte aligned, not overlapping any other argument.
+ *                Its contents on entry do not matter; calls sharing one
+ *                workspace must be ordered on one stream.
  *   coeffs       device fp64 array [K-1][nseg][2] receiving (ca, cb) of every
- *                tree node, nodes in level-major order (level 1 left to
- *                right, then level 2, ...), or NULL.
+ *                node, or NULL.  Tree nodes are in level-major order (level 1
+ *                left to right, then level 2, ...); chain nodes in step order.
  *   stats        device fp64 array [K-1][nseg][3] receiving (a.b, |a|^2,
- *                |b|^2) of every tree node in the same order, or NULL.
+ *                |b|^2) of every node in the same order, or NULL.
  *                Within each block of up to 16 operands (four tree levels)
  *                the statistics are evaluated in fp64 from the Gram matrix of
  *                the block's operands; above a block, from the fp32 values
  *                its result was stored in.
+ *   ortho        device fp64 array [nseg] receiving, per segment, the
+ *                orthogonality ratio |result|^2 / sum_k |g_k|^2 of Figure 1
+ *                (1 for mutually orthogonal gradients, 1/K for K equal ones;
+ *                NaN when every gradient of the segment is zero or the
+ *                segment is empty), or NULL.
  *   Other arguments as for adasum_combine.
  */
 ADASUM_API int adasum_combine_ex(const void* const* grads, int K, const int64_t* seg_offsets, int nseg,
-                      int dtype, void* out, void* workspace, size_t workspace_bytes,
-                      double* coeffs, double* stats, void* stream);
+                                 int dtype, int schedule, void* out, void* workspace,
+                                 size_t workspace_bytes, double* coeffs, double* stats, double* ortho,
+                                 void* stream);
+
+/*
+ * adasum_sum - the synchronous-SGD combination the text compares against:
+ * out = g_0 + g_1 + ... + g_{K-1}, element by element, accumulated in fp64 in
+ * worker order and rounded once to dtype (Sec. 2 of the text: the allreduce
+ * that sums the local gradients).  Segments play no role.
+ *
+ *   grads, K, dtype, out, stream   as for adasum_combine; N elements each.
+ *   workspace    device buffer of adasum_sum_workspace_bytes(K, N, dtype)
+ *                bytes (0 for K <= 64, then NULL is allowed), 16-byte
+ *                aligned.
+ */
+ADASUM_API int adasum_sum(const void* const* grads, int K, int64_t N, int dtype, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+ADASUM_API int64_t adasum_sum_workspace_bytes(int K, int64_t N, int dtype);
 
 /*
  * Kernel timing, for benchmarks.  Between adasum_profile_begin() and
@@ -136,7 +166,7 @@ ADASUM_API int adasum_combine_ex(const void* const* grads, int K, const int64_t*
  * most max_rows; rows may be NULL when max_rows is 0) or a negative code.
  */
 typedef struct {
-  char kernel[32];     /* "gram", "tree", "wsum", "widen", "copy" */
+  char kernel[32];     /* "gram", "tree", "wsum", "widen", "sum" */
   int launches;
   double milliseconds;
   double bytes;

@@ -50,13 +50,14 @@ def _off(*vals):
 
 
 def _call_ex(K=2, off=(0, 8, 16), dtype=0, grads=None, out=FAKE + (1 << 30), ws=FAKE + (2 << 30),
-             ws_bytes=1 << 20, coeffs=None, stats=None):
+             ws_bytes=1 << 20, coeffs=None, stats=None, ortho=None, schedule=0):
     lib = _native.lib()
     arr, p = _off(*off)
     if grads is None:
         grads = [FAKE + (k << 20) for k in range(K)]
     ptrs = (ctypes.c_void_p * max(len(grads), 1))(*grads)
-    rc = lib.adasum_combine_ex(ptrs, K, p, arr.size - 1, dtype, out, ws, ws_bytes, coeffs, stats, None)
+    rc = lib.adasum_combine_ex(ptrs, K, p, arr.size - 1, dtype, schedule, out, ws, ws_bytes, coeffs, stats,
+                               ortho, None)
     return rc, lib.adasum_last_error().decode()
 
 
@@ -74,6 +75,8 @@ def _call_ex(K=2, off=(0, 8, 16), dtype=0, grads=None, out=FAKE + (1 << 30), ws=
     (dict(ws_bytes=64), "workspace too small"),
     (dict(ws=FAKE + 32), "overlaps input"),
     (dict(coeffs=FAKE + (1 << 30) + 8), "overlaps"),
+    (dict(ortho=FAKE + 32), "overlaps input"),
+    (dict(schedule=5), "unknown schedule"),
 ])
 def test_invalid_arguments_rejected(kwargs, needle):
     rc, msg = _call_ex(**kwargs)
@@ -87,18 +90,19 @@ def test_negative_nseg_and_null_offsets():
     assert lib.adasum_combine(ptrs, 2, None, 1, 0, FAKE + 8192, None) == _native.EINVAL
     arr, p = _off(0)
     assert lib.adasum_combine(ptrs, 2, p, -1, 0, FAKE + 8192, None) == _native.EINVAL
-    assert lib.adasum_workspace_bytes(2, p, -1, 0) == _native.EINVAL
+    assert lib.adasum_workspace_bytes(2, p, -1, 0, 0) == _native.EINVAL
+    assert lib.adasum_workspace_bytes(2, p, 0, 0, 9) == _native.EINVAL
 
 
 def test_workspace_size_properties():
     lib = _native.lib()
 
-    def ws(K, off, dtype=0):
+    def ws(K, off, dtype=0, schedule=0):
         arr, p = _off(*off)
-        return lib.adasum_workspace_bytes(K, p, arr.size - 1, dtype)
+        return lib.adasum_workspace_bytes(K, p, arr.size - 1, dtype, schedule)
 
     n = 1 << 20
-    assert ws(1, (0, 1000)) == 0                 # K = 1 is a copy
+    assert 0 < ws(1, (0, 1000)) < 4096           # K = 1: one single-operand block
     # up to 16 operands form one block: no fp32 intermediates, only
     # Gram partials and tables
     for K in (2, 3, 9, 16):
@@ -108,3 +112,17 @@ def test_workspace_size_properties():
     assert 4 * n * 4 <= ws(64, (0, n)) < 5 * n * 4   # four blocks of 16
     assert ws(16, (0, 64 * n)) > ws(16, (0, n))
     assert ws(16, (0, 0)) >= 0 and ws(2, (0,)) >= 0
+    # chain: 16 inputs, then the running result plus 15 widened inputs per stage
+    assert ws(16, (0, n), 0, 1) < n
+    assert ws(17, (0, n), 0, 1) >= 2 * n * 4
+
+
+def test_sum_entry_point_validation():
+    lib = _native.lib()
+    assert lib.adasum_sum_workspace_bytes(64, 1000, 0) == 0
+    assert lib.adasum_sum_workspace_bytes(65, 1000, 0) == 8000   # fp64 running sum
+    assert lib.adasum_sum_workspace_bytes(0, 1000, 0) == _native.EINVAL
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE + (1 << 20))
+    assert lib.adasum_sum(ptrs, 2, 1000, 0, FAKE + 16, None, 0, None) == _native.EINVAL  # out overlaps grads[0]
+    assert "overlaps" in lib.adasum_last_error().decode()
+    assert lib.adasum_sum(ptrs, 2, 1000, 7, FAKE + (2 << 20), None, 0, None) == _native.EINVAL

@@ -256,3 +256,90 @@ def test_stacked_tensor_input_and_out_argument(gpu):
     ref = A.combine([g.to(gpu) for g in wl.grads], wl.seg_offsets)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+# ---------------------------------------------------------------- chain, orthogonality, plain sum
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [2, 3, 5, 16, 17, 33])
+def test_chain_schedule(gpu, K, dtype):
+    A = _A()
+    wl = W.random_case(K, [1, 300, 9, 20000, 8], dtype=dtype, seed=300 + K, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    say(f"chain K={K} {dtype}")
+    out, coeffs, stats = A.combine(grads, wl.seg_offsets, schedule="chain", return_coeffs=True,
+                                   return_stats=True)
+    torch.cuda.synchronize()
+    ref = oracle.combine_chain([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format=dtype)
+    err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
+    assert err <= TOL[dtype], f"chain K={K}: relative L2 {err:.3g}"
+    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], f"chain K={K}")
+    check_stats(stats.cpu().numpy(), ref["stats"], f"chain K={K}")
+
+
+def test_chain_worked_example(gpu):
+    # hand-derived linear-chain value (tests/golden/worked_examples.json)
+    A = _A()
+    g = [torch.tensor(v, dtype=torch.float32, device=gpu) for v in ([1, 0], [1, 1], [0, 2], [-1, 1])]
+    out = A.combine(g, [0, 2], schedule="chain")
+    torch.cuda.synchronize()
+    expect = np.array([94141 / 3023008, 7606071 / 3023008])
+    np.testing.assert_allclose(out.double().cpu().numpy(), expect, rtol=1e-6)
+
+
+@pytest.mark.parametrize("K", [1, 2, 5, 16, 33, 64])
+def test_orthogonality_ratio(gpu, K):
+    A = _A()
+    wl = W.random_case(K, [1, 500, 0, 9000, 7], dtype="f32", seed=400 + K, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    say(f"orthogonality K={K}")
+    out, ortho = A.combine(grads, wl.seg_offsets, return_ortho=True)
+    torch.cuda.synchronize()
+    ref = oracle.orthogonality([g.double().numpy() for g in wl.grads], wl.seg_offsets)
+    got = ortho.cpu().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))  # the empty segment is NaN
+    ok = ~np.isnan(ref)
+    np.testing.assert_allclose(got[ok], ref[ok], rtol=1e-5)
+
+
+def test_orthogonality_closed_forms(gpu):
+    A = _A()
+    n = 4096
+    g = torch.randn(n, generator=torch.Generator().manual_seed(1)).to(gpu)
+    _, ortho = A.combine([g] * 64, [0, n], return_ortho=True)   # 64 equal gradients: 1/64
+    gs = []
+    for k in range(8):                                            # disjoint supports: 1
+        x = torch.zeros(n)
+        x[k * 512:(k + 1) * 512] = torch.randn(512, generator=torch.Generator().manual_seed(k))
+        gs.append(x.to(gpu))
+    _, ortho2 = A.combine(gs, [0, n], return_ortho=True)
+    z = torch.zeros(n, device=gpu)
+    _, ortho3 = A.combine([z, z, z], [0, n], return_ortho=True)  # all zero: undefined
+    torch.cuda.synchronize()
+    assert abs(float(ortho[0]) - 1 / 64) <= 1e-12
+    assert abs(float(ortho2[0]) - 1.0) <= 1e-12
+    assert np.isnan(float(ortho3[0]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 7, 64, 65, 130])
+def test_plain_sum_bit_exact(gpu, K, dtype):
+    A = _A()
+    wl = W.random_case(K, [5, 20001], dtype=dtype, seed=500 + K, kind="scaled")
+    grads = [g.to(gpu) for g in wl.grads]
+    say(f"plain sum K={K} {dtype}")
+    out = A.plain_sum(grads)
+    torch.cuda.synchronize()
+    ref = oracle.plain_sum([g.double().numpy() for g in wl.grads], out_format=dtype)["out_rounded"]
+    got = out.double().cpu().numpy()
+    assert np.array_equal(got, ref), f"max |diff| {np.max(np.abs(got - ref))}"
+
+
+def test_single_worker_is_exact_copy(gpu):
+    A = _A()
+    for dtype in ("f32", "f16", "bf16"):
+        wl = W.random_case(1, RAGGED, dtype=dtype, seed=7)
+        g = wl.grads[0].to(gpu)
+        out = A.combine([g], wl.seg_offsets)
+        torch.cuda.synchronize()
+        assert torch.equal(out, g)
