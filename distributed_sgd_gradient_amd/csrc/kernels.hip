@@ -397,17 +397,33 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   }
   if (tid < kMaxOps) w[tid] = 1.0;
   __syncthreads();
-  if (tid == 0) {
-    for (int m = 0; m < d.nmerges; ++m) {
-      const Merge mg = a.merges[d.merge0 + m];
-      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
-      const double A = quad_form(G, n, w, l0, l1, l0, l1);
-      const double B = quad_form(G, n, w, l1, r1, l1, r1);
-      const double dd = quad_form(G, n, w, l0, l1, l1, r1);
+  // Merges in order.  For merge (L, R) thread i < nb forms its row sums
+  // rowL_i = sum_{k in L} w_k G(i,k) and rowR_i = sum_{k in R} w_k G(i,k) in
+  // k order; thread 0 then forms A = sum_{i in L} w_i rowL_i,
+  // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order.
+  // That is the same arithmetic, term for term, as a serial evaluation.
+  __shared__ double rowL[kMaxOps], rowR[kMaxOps];
+  __shared__ double cab[2];
+  for (int m = 0; m < d.nmerges; ++m) {
+    const Merge mg = a.merges[d.merge0 + m];
+    const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
+    if (tid >= l0 && tid < r1) {
+      double sl = 0.0, sr = 0.0;
+      for (int k = l0; k < l1; ++k) sl = add_rn(sl, mul_rn(w[k], gram_at(G, n, tid, k)));
+      for (int k = l1; k < r1; ++k) sr = add_rn(sr, mul_rn(w[k], gram_at(G, n, tid, k)));
+      rowL[tid] = sl;
+      rowR[tid] = sr;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double A = 0.0, B = 0.0, dd = 0.0;
+      for (int i = l0; i < l1; ++i) A = add_rn(A, mul_rn(w[i], rowL[i]));
+      for (int i = l1; i < r1; ++i) B = add_rn(B, mul_rn(w[i], rowR[i]));
+      for (int i = l0; i < l1; ++i) dd = add_rn(dd, mul_rn(w[i], rowR[i]));
       const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
-      for (int i = l0; i < l1; ++i) w[i] = mul_rn(w[i], ca);
-      for (int i = l1; i < r1; ++i) w[i] = mul_rn(w[i], cb);
+      cab[0] = ca;
+      cab[1] = cb;
       const int64_t at = (int64_t)mg.node * a.nseg + s;
       a.coeffs[at * 2] = ca;
       a.coeffs[at * 2 + 1] = cb;
@@ -415,6 +431,11 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       a.stats[at * 3 + 1] = A;
       a.stats[at * 3 + 2] = B;
     }
+    __syncthreads();
+    if (tid >= l0 && tid < r1) w[tid] = mul_rn(w[tid], tid < l1 ? cab[0] : cab[1]);
+    __syncthreads();
+  }
+  if (tid == 0) {
     // sum of |g_k|^2 over the block's input operands, in operand order
     double leaf = 0.0;
     for (int k = 0; k < d.nb; ++k)
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 // masked to zero, so the loop has no branches and every load of a step is in
 // flight at once.
 template <typename TIn, int NB, typename TOut>
-__global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
+__global__ __launch_bounds__(kBlock, 3) void wsum_kernel(WsumArgs args) {
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];

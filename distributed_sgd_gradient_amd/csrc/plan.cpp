@@ -62,7 +62,7 @@ bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, int sche
     return false;
   }
   // tile count must fit int32 (every kernel indexes tiles with 32-bit ints)
-  if (offsets[nseg] / kTile + nseg + 1 > int64_t(INT32_MAX)) {
+  if (offsets[nseg] / kMinTile + nseg + 1 > int64_t(INT32_MAX)) {
     *err = "too many tiles for this shape";
     return false;
   }
@@ -114,7 +114,9 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   p.offsets.assign(offsets, offsets + nseg + 1);
   p.N = offsets[nseg];
 
-  // ---- tiles
+  // ---- tiles: a workload too small to fill the GPU with kTile tiles is cut
+  // finer, so that every launch has thousands of workgroups
+  p.tile_rows = std::min<int64_t>(kTile, std::max<int64_t>(kMinTile, align_up(p.N / kTargetTiles, 1024)));
   p.seg_tile.resize(nseg + 1);
   for (int s = 0; s < nseg; ++s) {
     p.seg_tile[s] = (int32_t)p.tiles.size();
@@ -123,7 +125,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     while (a < hi) {
       // the first tile absorbs the unaligned head; later tiles start aligned
       const int64_t body_start = align_up(a, kGroup);
-      const int64_t end = std::min(hi, body_start + kTile);
+      const int64_t end = std::min(hi, body_start + p.tile_rows);
       p.tiles.push_back(Tile{a, (int32_t)(end - a), (int32_t)s});
       a = end;
     }

@@ -27,7 +27,9 @@
 namespace adasum {
 
 constexpr int kGroup = 8;        // elements per thread per vector step (16 B of 16-bit, 32 B of fp32)
-constexpr int kTile = 32768;     // elements per tile (a multiple of kGroup)
+constexpr int kTile = 32768;     // largest tile, elements (a multiple of kGroup)
+constexpr int kMinTile = 2048;   // smallest tile a large segment is cut into
+constexpr int kTargetTiles = 4096;  // tiles a workload is cut into when it is small
 constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
 constexpr int kMaxOps = 16;      // operands per block: four tree levels
 constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
@@ -95,6 +97,7 @@ struct Plan {
   Schedule schedule = Schedule::Tree;
   int nseg = 0;
   int64_t N = 0;
+  int64_t tile_rows = kTile;      // tile length: about N / kTargetTiles, in [kMinTile, kTile]
   std::vector<int64_t> offsets;   // nseg + 1
   std::vector<Tile> tiles;
   std::vector<int32_t> seg_tile;  // nseg + 1: tiles of segment s are [seg_tile[s], seg_tile[s+1])
