@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 // masked to zero, so the loop has no branches and every load of a step is in
 // flight at once.
 template <typename TIn, int NB, typename TOut>
-__global__ __launch_bounds__(kBlock, 3) void wsum_kernel(WsumArgs args) {
+__global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
