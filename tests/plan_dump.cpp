@@ -1,0 +1,45 @@
+// Prints the execution plan of K = 1..70 operands, both schedules, as JSON
+// lines, for tests/test_plan_host.py.  Built with g++ on the host together
+// with the library's plan.cpp (pure C++, no HIP).
+#include <cstdio>
+
+#include "plan.h"
+
+using namespace adasum;
+
+int main() {
+  const int64_t off[3] = {0, 13, 40};
+  for (int sched = 0; sched < 2; ++sched) {
+    for (int K = 1; K <= 70; ++K) {
+      const Plan p = build_plan(K, off, 2, DType::F32, static_cast<Schedule>(sched));
+      printf("{\"schedule\": %d, \"K\": %d, \"nslots\": %d, \"stages\": [", sched, K, p.nslots);
+      for (size_t s = 0; s < p.stages.size(); ++s) {
+        const Stage& st = p.stages[s];
+        printf("%s{\"widen\": [", s ? "," : "");
+        for (size_t i = 0; i < st.widen.size(); ++i)
+          printf("%s[%d,%d]", i ? "," : "", st.widen[i].first, st.widen[i].second);
+        printf("], \"blocks\": [");
+        for (size_t b = 0; b < st.blocks.size(); ++b) {
+          const Block& bk = st.blocks[b];
+          const BlockDesc& d = p.descs[bk.desc];
+          printf("%s{\"ops\": [", b ? "," : "");
+          for (size_t k = 0; k < bk.operands.size(); ++k)
+            printf("%s[%d,%d]", k ? "," : "", (int)bk.operands[k].kind, bk.operands[k].idx);
+          printf("], \"dst\": [%d,%d], \"nb\": %d, \"nbt\": %d, \"leafmask\": %d, \"root\": %d, \"merges\": [",
+                 (int)bk.dst.kind, bk.dst.idx, d.nb, d.nbt, (int)d.leafmask, (int)d.root);
+          for (int m = 0; m < d.nmerges; ++m) {
+            const Merge& mg = p.merges[d.merge0 + m];
+            printf("%s[%d,%d,%d,%d]", m ? "," : "", mg.llo, mg.lhi, mg.rhi, mg.node);
+          }
+          printf("]}");
+        }
+        printf("]}");
+      }
+      printf("], \"tiles\": [");
+      for (size_t t = 0; t < p.tiles.size(); ++t)
+        printf("%s[%lld,%d,%d]", t ? "," : "", (long long)p.tiles[t].start, p.tiles[t].len, p.tiles[t].seg);
+      printf("], \"ws_total\": %zu}\n", p.ws_total);
+    }
+  }
+  return 0;
+}

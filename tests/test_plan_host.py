@@ -1,0 +1,108 @@
+"""The host planner's tree, checked against the oracle's schedule on the CPU.
+
+tests/plan_dump.cpp is compiled with g++ (AddressSanitizer and UBSan on)
+together with the library's plan.cpp and prints every plan for K = 1..70 in
+both schedules.  Every merge the GPU path will evaluate must be exactly the
+node the oracle defines: same two children (as leaf ranges), same position
+in the node order, every input used once, stage operands fp32 above stage 1.
+"""
+
+import json
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "distributed_sgd_gradient_amd", "csrc")
+
+
+@pytest.fixture(scope="module")
+def plans(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("plan") / "plan_dump")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", CSRC, os.path.join(ROOT, "tests", "plan_dump.cpp"), os.path.join(CSRC, "plan.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True,
+                         env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1")).stdout
+    return [json.loads(line) for line in out.splitlines()]
+
+
+def oracle_nodes(K, schedule):
+    """node id -> (lo, mid, hi): the node merges leaves [lo, mid) with [mid, hi)."""
+    if schedule == 1:
+        return {i: (0, i + 1, i + 2) for i in range(K - 1)}
+    ranges = {}
+    nodes = {}
+    nid = 0
+    for level in oracle.tree_schedule(K):
+        made = []
+        for left, right in level:
+            lr = [(r[1], r[1] + 1) if r[0] == "leaf" else ranges[r[1]] for r in (left, right)]
+            assert lr[0][1] == lr[1][0]
+            nodes[nid] = (lr[0][0], lr[0][1], lr[1][1])
+            made.append((nid, (lr[0][0], lr[1][1])))
+            nid += 1
+        ranges.update(made)
+    return nodes
+
+
+def plan_nodes(P):
+    """Reconstruct the leaf range of every merge the plan evaluates."""
+    slot_range = {}
+    got = {}
+    for si, st in enumerate(P["stages"]):
+        for k, slot in st["widen"]:
+            slot_range[slot] = (k, k + 1)
+        for b in st["blocks"]:
+            if si > 0:
+                assert all(kind == 1 for kind, _ in b["ops"]), "stage operands above the first must be fp32 slots"
+            rng = [(i, i + 1) if kind == 0 else slot_range[i] for kind, i in b["ops"]]
+            assert len(rng) == b["nb"] <= 16 and b["nbt"] >= b["nb"]
+            for i in range(len(rng) - 1):
+                assert rng[i][1] == rng[i + 1][0], "block operands must be adjacent leaf ranges"
+            for llo, lhi, rhi, node in b["merges"]:
+                assert 0 <= llo < lhi < rhi <= len(rng)
+                got[node] = (rng[llo][0], rng[lhi][0], rng[rhi - 1][1])
+            lo, hi = rng[0][0], rng[-1][1]
+            if b["dst"][0] == 1:
+                slot_range[b["dst"][1]] = (lo, hi)
+            else:
+                assert b["root"] == 1 and (lo, hi) == (0, P["K"])
+            # leaf operands are exactly the inputs and the widened inputs
+            leafmask = sum(1 << i for i, (kind, idx) in enumerate(b["ops"])
+                           if kind == 0 or (kind == 1 and rng[i][1] - rng[i][0] == 1
+                                            and idx in {s for _, s in
+                                                        [w for stg in P["stages"] for w in stg["widen"]]}))
+            assert leafmask == b["leafmask"]
+    return got
+
+
+@pytest.mark.parametrize("schedule", [0, 1])
+def test_plan_nodes_match_oracle(plans, schedule):
+    checked = 0
+    for P in plans:
+        if P["schedule"] != schedule:
+            continue
+        K = P["K"]
+        assert plan_nodes(P) == oracle_nodes(K, schedule), f"K={K}"
+        assert sum(1 for st in P["stages"] for b in st["blocks"] if b["root"]) == 1
+        checked += 1
+    assert checked == 70
+
+
+def test_tiles_cover_segments_exactly(plans):
+    off = [0, 13, 40]
+    for P in plans:
+        tiles = np.array(P["tiles"])
+        assert tiles[0][0] == 0 and tiles[:, 1].sum() == 40
+        assert np.all(tiles[1:, 0] == tiles[:-1, 0] + tiles[:-1, 1])   # contiguous
+        for start, length, seg in tiles:
+            assert off[seg] <= start and start + length <= off[seg + 1]   # inside one segment
