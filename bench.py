@@ -163,6 +163,22 @@ def main():
         log(f"  {name:12s} launches {k['launches']:5d}  {k['milliseconds'] / args.steps:8.3f} ms/step  "
             f"{k['bytes'] / (k['milliseconds'] * 1e-3) / 1e9 if k['milliseconds'] > 0 else 0:8.1f} GB/s")
 
+    # the synchronous-SGD plain sum on the same buffers: one pass, reads K
+    # gradients once and writes one result (B_min of traffic)
+    out_sum = torch.empty_like(out)
+    for _ in range(args.warmup):
+        A.plain_sum(wl.grads, out=out_sum)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        A.plain_sum(wl.grads, out=out_sum)
+    torch.cuda.synchronize()
+    sum_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    plain_sum = {"ms_per_step": sum_ms, "gradient_GBps": grad_bytes / (sum_ms * 1e-3) / 1e9,
+                 "path_frac": b_min / (sum_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "adasum_over_sum_time": ms / sum_ms}
+    log(f"plain sum on the same buffers: {sum_ms:.3f} ms/step; Adasum takes {ms / sum_ms:.2f}x as long")
+    del out_sum
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s)")
@@ -174,7 +190,7 @@ def main():
         "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg,
                    "io_dtype": wl.dtype, "seed": wl.seed, "parallelism": "none (one GPU)"},
-        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu,
+        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "plain_sum": plain_sum,
         "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
                         "bytes_per_step": v["bytes"] / args.steps} for k, v in kernels.items()},
     }

@@ -343,3 +343,35 @@ def test_single_worker_is_exact_copy(gpu):
         out = A.combine([g], wl.seg_offsets)
         torch.cuda.synchronize()
         assert torch.equal(out, g)
+
+
+def test_nan_stays_in_its_segment(gpu):
+    A = _A()
+    wl = W.random_case(4, [100, 200, 300], seed=61)
+    grads = [g.clone().to(gpu) for g in wl.grads]
+    grads[2][150] = float("nan")  # inside segment 1
+    out = A.combine(grads, wl.seg_offsets)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert torch.isnan(got[100:300]).all()
+    assert not torch.isnan(got[:100]).any() and not torch.isnan(got[300:]).any()
+    ref = oracle.combine([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format="f32")
+    for lo, hi in ((0, 100), (300, 600)):
+        np.testing.assert_allclose(got[lo:hi].double().numpy(), ref["out_rounded"][lo:hi], rtol=1e-6, atol=1e-7)
+
+
+def test_fp16_subnormal_results_exact(gpu):
+    # disjoint supports: the combine is the exact sum, so subnormal fp16
+    # inputs must come back bit for bit (no flush to zero on load or store)
+    A = _A()
+    n = 2048
+    tiny = torch.tensor([2.0 ** -24, 3 * 2.0 ** -24, -(2.0 ** -20), 1023 * 2.0 ** -24], dtype=torch.float16)
+    gs = []
+    for k in range(2):
+        x = torch.zeros(n, dtype=torch.float16)
+        x[k * 1024:(k + 1) * 1024] = tiny.repeat(256)
+        gs.append(x.to(gpu))
+    out = A.combine(gs, [0, n])
+    torch.cuda.synchronize()
+    assert torch.equal(out, gs[0] + gs[1])
+    assert int((out.abs() < 2.0 ** -14).sum()) == n  # every value below the smallest normal: none flushed

@@ -80,3 +80,14 @@ def test_random_case_zero_workers():
     wl = W.random_case(3, [7, 0, 9], seed=1, zero_workers=(1,))
     assert wl.N == 16 and wl.nseg == 3
     assert bool((wl.grads[1] == 0).all()) and not bool((wl.grads[0] == 0).all())
+
+
+def test_resnet_shared_component_cosine():
+    # g_k = s + n_k with s, n_k ~ N(0,1): pairwise cosine 1/2 (checked on a few large layers)
+    off = W.config_offsets(2)
+    lengths = np.diff(off)
+    segs = np.argsort(lengths)[-3:]
+    wl = W.make_workload(2, segments=segs)
+    a, b = wl.grads[0].double(), wl.grads[5].double()
+    c = float(a @ b / (a.norm() * b.norm()))
+    assert abs(c - 0.5) < 0.01
