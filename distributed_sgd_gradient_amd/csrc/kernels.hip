@@ -338,6 +338,197 @@ __global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
   }
 }
 
+// ----------------------------------------------------------------- Gram pass, 16-bit operands
+
+// For 16-bit operands the Gram matrix of a block is a dense contraction
+// G = X^T X (X: rows x operands), done on the matrix cores: one
+// v_mfma_f32_16x16x32 with the same register as both A and B gives the
+// 16 x 16 Gram matrix of 32 rows.  Lane l holds operand l % 16 at rows
+// 8 * (l / 16) .. +7 (one 16-byte load); output register r of lane l is
+// G[4 * (l / 16) + r][l % 16].  Every instruction starts from zero and its
+// four results go straight into fp64 accumulators, so the fp32 part of the
+// sum is one instruction's 32 products.
+//
+// Those products are exact, and gfx950's matrix cores keep fp16 subnormal
+// inputs and fp32 subnormal results: fp16 values are multiples of 2^-24
+// below 2^16, so products are multiples of 2^-48 below 2^32; bf16 values
+// with magnitudes in [2^-56, 2^61) are multiples of 2^-63, so their products
+// are multiples of 2^-126 below 2^122, and 32 of them stay below 2^127.
+// The hardware rounds the sum of the 32 products once (measured: the sum
+// 1 + 31 * 2^-24 comes out as the nearest fp32 value wherever the 1 sits),
+// so each entry is off by at most 2^-24 of the sum of |a_i b_i| over each
+// 32-row chunk.  A bf16 chunk holding any nonzero value outside that range
+// (inf and NaN included) is instead summed in fp64 by the lanes from LDS.
+constexpr int kMfmaUnroll = 8;    // 32-row chunks per wave per iteration
+constexpr int kGramWaves = kBlock / 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<_Float16> {
+  static constexpr bool kGuard = false;  // every fp16 product is exact
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x4 gram(v4u x) {
+    const v8 h = __builtin_bit_cast(v8, x);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(h, h, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+  static __device__ __forceinline__ double widen(uint16_t bits) { return (double)__builtin_bit_cast(_Float16, bits); }
+};
+
+template <>
+struct Mfma<bf16_t> {
+  static constexpr bool kGuard = true;
+  // magnitude bits of 2^-56 and 2^61: biased exponents 71 and 188
+  static constexpr unsigned kLoBits = 71u << 7, kHiBits = 188u << 7;
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x4 gram(v4u x) {
+    const v8 h = __builtin_bit_cast(v8, x);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, h, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+  static __device__ __forceinline__ double widen(uint16_t bits) { return (double)__uint_as_float((uint32_t)bits << 16); }
+};
+
+// Running range of the magnitude bits of packed 16-bit pairs: the largest,
+// and the smallest nonzero one less one (zero wraps to 0xffff).
+struct RangeU16 {
+  u16x2 mx = {0, 0};
+  u16x2 mn1 = {0xffff, 0xffff};
+  __device__ __forceinline__ void add(uint32_t w) {
+    const u16x2 m = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+    mx = __builtin_elementwise_max(mx, m);
+    mn1 = __builtin_elementwise_min(mn1, m - (u16x2){1, 1});
+  }
+  __device__ __forceinline__ bool outside(unsigned lo_bits, unsigned hi_bits) const {
+    const unsigned hi = mx.x > mx.y ? mx.x : mx.y;
+    const unsigned lo1 = mn1.x < mn1.y ? mn1.x : mn1.y;
+    return hi >= hi_bits || lo1 < lo_bits - 1;
+  }
+};
+
+// Eight raw 16-bit values at rows [row, row + 8) of x, zero outside [lo, hi).
+__device__ __forceinline__ v4u load_raw_group(const uint16_t* __restrict__ x, int64_t row, int64_t lo, int64_t hi) {
+  if (row >= lo && row + kGroup <= hi) return gload(reinterpret_cast<const v4u*>(x + row));
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    uint32_t pair = 0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int64_t i = row + 2 * h + e;
+      if (i >= lo && i < hi) pair |= (uint32_t)gload(x + i) << (16 * e);
+    }
+    w[h] = pair;
+  }
+  return v4u{w[0], w[1], w[2], w[3]};
+}
+
+template <typename T, int NB>
+__global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
+  constexpr int U = kMfmaUnroll;
+  constexpr int R = 32 * U;  // rows per wave per iteration
+  constexpr int NE = gram_entries(NB);
+  __shared__ double red[kGramWaves][64 * 4];
+  __shared__ __align__(16) uint16_t spill[kGramWaves][16 * 32];  // fp64 fallback: [operand][row]
+
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = lane & 15, grp = lane >> 4;
+
+  // Lanes of absent operands (op >= NB, or a NULL slot) read operand 0 and
+  // are masked to zero, so every load of an iteration is unconditional.
+  const void* const* table = args.x[j];
+  const void* mine = op < NB ? table[op] : nullptr;
+  const bool live = mine != nullptr;
+  const uint16_t* xp = static_cast<const uint16_t*>(live ? mine : table[0]);
+
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  const int64_t niter = (hi - first + R - 1) / R;
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+    const int64_t r0 = first + it * R;
+    v4u v[U];
+    if (r0 >= lo && r0 + R <= hi) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4u*>(xp + r0 + 32 * u + 8 * grp));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = load_raw_group(xp, r0 + 32 * u + 8 * grp, lo, hi);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (!live) v[u] = v4u{0u, 0u, 0u, 0u};
+
+    bool exact = true;
+    if constexpr (Mfma<T>::kGuard) {
+      RangeU16 range;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        range.add(v[u].x);
+        range.add(v[u].y);
+        range.add(v[u].z);
+        range.add(v[u].w);
+      }
+      exact = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) == 0;
+    }
+    if (exact) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const f32x4 d = Mfma<T>::gram(v[u]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
+      }
+    } else {
+      // Chunk by chunk through this wave's LDS rows; lane l sums the same
+      // four entries it owns in the matrix-core layout, in fp64.
+      uint16_t* sp = spill[wave];
+      const int i0 = 4 * grp;
+#pragma unroll 1
+      for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_wave_barrier();
+        *reinterpret_cast<uint4*>(&sp[op * 32 + 8 * grp]) = make_uint4(v[u].x, v[u].y, v[u].z, v[u].w);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        double part[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int k = 0; k < 32; ++k) {
+          const double xj = Mfma<T>::widen(sp[op * 32 + k]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[r] = fma(Mfma<T>::widen(sp[(i0 + r) * 32 + k]), xj, part[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += part[r];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+    }
+  }
+
+  // Sum the four waves' matrices in wave order; write the packed triangle.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
+  __syncthreads();
+  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+  for (int e = threadIdx.x; e < NE; e += kBlock) {
+    int i = 0, rem = e;
+    while (rem >= NB - i) {
+      rem -= NB - i;
+      ++i;
+    }
+    const int k = i + rem;  // entry (i, k), i <= k
+    const int src = (k + 16 * (i >> 2)) * 4 + (i & 3);
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGramWaves; ++w) sum += red[w][src];
+    out[e] = sum;
+  }
+}
+
 // ----------------------------------------------------------------- tree walk
 
 // Products and sums rounded separately, never fused, so that terms that
@@ -638,6 +829,21 @@ struct RunGram {
   }
 };
 
+template <typename T>
+struct RunGramMfma {
+  static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+    const dim3 grid(ntiles, njobs);
+    switch (nbt) {
+      case 2: hipLaunchKernelGGL((gram_mfma_kernel<T, 2>), grid, dim3(kBlock), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((gram_mfma_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+};
+
 template <typename TIn, typename TOut>
 hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
   const dim3 grid(ntiles, njobs);
@@ -666,7 +872,12 @@ struct RunWsum {
 }  // namespace
 
 hipError_t launch_gram(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
-  return by_type<RunGram>(operand, nbt, a, ntiles, njobs, st);
+  switch (operand) {
+    case DType::F32: return RunGram<float>::run(nbt, a, ntiles, njobs, st);
+    case DType::F16: return RunGramMfma<_Float16>::run(nbt, a, ntiles, njobs, st);
+    case DType::BF16: return RunGramMfma<bf16_t>::run(nbt, a, ntiles, njobs, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {

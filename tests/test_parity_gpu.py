@@ -175,6 +175,34 @@ def test_fp16_subnormal_scales(gpu):
     full_check(wl, "fp16 scaled")
 
 
+def test_bf16_exponent_extremes(gpu):
+    """bf16 segments at magnitudes near and past the limits of fp32 products.
+
+    Per-segment scales 2^-120 (bf16 subnormals), 2^-57 and 2^61 (values on
+    both sides of the range whose pairwise products are exact in fp32),
+    2^-40, 1 and 2^100, plus one segment that mixes 2^-100 and 2^90 values.
+    """
+    K = 8
+    lengths = [5000, 5000, 5000, 5000, 5000, 5000, 3001]
+    scales = [2.0 ** -120, 2.0 ** -57, 2.0 ** -40, 1.0, 2.0 ** 61, 2.0 ** 100]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    grads = []
+    for k in range(K):
+        g = torch.Generator().manual_seed(900 + k)
+        parts = [torch.randn(n, generator=g, dtype=torch.float64) * sc for n, sc in zip(lengths, scales)]
+        mixed = torch.randn(lengths[-1], generator=g, dtype=torch.float64)
+        mixed[::2] *= 2.0 ** -100
+        mixed[1::2] *= 2.0 ** 90
+        parts.append(mixed)
+        grads.append(torch.cat(parts).to(torch.bfloat16))
+    wl = W.Workload(K=K, dtype="bf16", seg_offsets=off, grads=[x.to(gpu) for x in grads], seed=900)
+    got, ref, _ = full_check(wl, "bf16 exponent extremes")
+    for s in range(len(lengths)):
+        lo, hi = off[s], off[s + 1]
+        err = rel_l2(got[lo:hi], ref["out_rounded"][lo:hi])
+        assert err <= TOL["bf16"], f"segment {s}: relative L2 {err:.3g}"
+
+
 def test_zero_workers(gpu):
     wl = W.random_case(8, [100, 1, 9000, 33], dtype="bf16", seed=12, zero_workers=(0, 3, 4, 5))
     wl.grads = [g.to(gpu) for g in wl.grads]
