@@ -76,6 +76,16 @@ struct Elem;
 
 template <>
 struct Elem<float> {
+  struct Raw8 {
+    v4f a, b;
+  };
+  static __device__ __forceinline__ Raw8 load_raw8(const float* p) {
+    return Raw8{gload(reinterpret_cast<const v4f*>(p)), gload(reinterpret_cast<const v4f*>(p + 4))};
+  }
+  static __device__ __forceinline__ void unpack8(const Raw8& r, float (&v)[kGroup]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  }
   static __device__ __forceinline__ float load1(const float* p) { return gload(p); }
   static __device__ __forceinline__ void load8(const float* p, float (&v)[kGroup]) {
     const v4f a = gload(reinterpret_cast<const v4f*>(p));
@@ -98,6 +108,16 @@ struct Elem<float> {
 
 template <>
 struct Elem<_Float16> {
+  typedef v4u Raw8;
+  static __device__ __forceinline__ Raw8 load_raw8(const _Float16* p) { return gload(reinterpret_cast<const v4u*>(p)); }
+  static __device__ __forceinline__ void unpack8(const Raw8& raw, float (&v)[kGroup]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+      v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+  }
   static __device__ __forceinline__ float load1(const _Float16* p) { return (float)gload(p); }
   static __device__ __forceinline__ void load8(const _Float16* p, float (&v)[kGroup]) {
     const v4u raw = gload(reinterpret_cast<const v4u*>(p));
@@ -127,6 +147,16 @@ struct Elem<_Float16> {
 template <>
 struct Elem<bf16_t> {
   static __device__ __forceinline__ float widen(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+  typedef v4u Raw8;
+  static __device__ __forceinline__ Raw8 load_raw8(const bf16_t* p) { return gload(reinterpret_cast<const v4u*>(p)); }
+  static __device__ __forceinline__ void unpack8(const Raw8& raw, float (&v)[kGroup]) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   static __device__ __forceinline__ float load1(const bf16_t* p) {
     return widen(gload(reinterpret_cast<const uint16_t*>(p)));
   }
@@ -684,21 +714,29 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   };
 
   if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
+  // Operand-outer: the raw loads of all operands are in flight together,
+  // but only one operand is widened at a time; every element still sums
+  // its terms in operand order, starting from zero.
   for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
-    float v[NB][kGroup];
+    typename Elem<TIn>::Raw8 raw[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) Elem<TIn>::load8(xs[k] + g, v[k]);
+    for (int k = 0; k < NB; ++k) raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
+    double acc[kGroup];
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      float v[kGroup];
+      Elem<TIn>::unpack8(raw[k], v);
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) {
+        const double t = mul_rn(w[k], (double)v[e]);
+        acc[e] = add_rn(acc[e], live[k] ? t : 0.0);
+      }
+    }
     TOut r[kGroup];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e) {
-      double acc = 0.0;
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const double t = mul_rn(w[k], (double)v[k][e]);
-        acc = add_rn(acc, live[k] ? t : 0.0);
-      }
-      r[e] = Elem<TOut>::round(acc, &unused);
-    }
+    for (int e = 0; e < kGroup; ++e) r[e] = Elem<TOut>::round(acc[e], &unused);
     Elem<TOut>::store8(y + g, r);
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
