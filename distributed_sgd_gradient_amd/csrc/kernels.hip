@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -402,9 +403,9 @@ template <>
 struct Mfma<_Float16> {
   static constexpr bool kGuard = false;  // every fp16 product is exact
   typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ f32x4 gram(v4u x) {
-    const v8 h = __builtin_bit_cast(v8, x);
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(h, h, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  static __device__ __forceinline__ f32x4 gram(v4u a, v4u b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
+                                                  f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
   static __device__ __forceinline__ double widen(uint16_t bits) { return (double)__builtin_bit_cast(_Float16, bits); }
 };
@@ -415,9 +416,9 @@ struct Mfma<bf16_t> {
   // magnitude bits of 2^-56 and 2^61: biased exponents 71 and 188
   static constexpr unsigned kLoBits = 71u << 7, kHiBits = 188u << 7;
   typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-  static __device__ __forceinline__ f32x4 gram(v4u x) {
-    const v8 h = __builtin_bit_cast(v8, x);
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(h, h, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  static __device__ __forceinline__ f32x4 gram(v4u a, v4u b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
+                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
   static __device__ __forceinline__ double widen(uint16_t bits) { return (double)__uint_as_float((uint32_t)bits << 16); }
 };
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
     if (exact) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const f32x4 d = Mfma<T>::gram(v[u]);
+        const f32x4 d = Mfma<T>::gram(v[u], v[u]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
       }
@@ -555,6 +556,160 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
     double sum = 0.0;
 #pragma unroll
     for (int w = 0; w < kGramWaves; ++w) sum += red[w][src];
+    out[e] = sum;
+  }
+}
+
+// 32-operand blocks (at most 32 16-bit inputs, one stage): two 16-operand
+// halves, and per 32-row chunk three instructions, the two diagonal 16 x 16
+// blocks and the cross block (A from the first half, B from the second).
+// Lane l, output register r of sub-block q = (h1, h2) holds
+// G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].
+template <typename T>
+__global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
+  constexpr int NB = 32;
+  constexpr int NH = 2;                  // 16-operand halves
+  constexpr int NP = 3;                  // sub-blocks (0,0), (0,1), (1,1)
+  constexpr int U = kMfmaUnroll / 2;     // two loads per chunk
+  constexpr int R = 32 * U;              // rows per wave per iteration
+  constexpr int NE = gram_entries(NB);
+  // LDS: the fp64 fallback's rows (bf16 only; [operand][row] per wave)
+  // during the loop, the cross-wave reduction after it
+  constexpr int kSpillBytes = Mfma<T>::kGuard ? kGramWaves * 16 * NH * R * 2 : 0;
+  constexpr int kRedBytes = kGramWaves * NP * 64 * 4 * 8;
+  __shared__ __align__(16) unsigned char lds[kSpillBytes > kRedBytes ? kSpillBytes : kRedBytes];
+
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = lane & 15, grp = lane >> 4;
+
+  // NULL operands (beyond the block's count) read operand 0, masked to zero
+  const void* const* table = args.x[j];
+  const uint16_t* xp[NH];
+  bool live[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const void* mine = table[16 * h + op];
+    live[h] = mine != nullptr;
+    xp[h] = static_cast<const uint16_t*>(live[h] ? mine : table[0]);
+  }
+
+  double acc[NP][4];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[q][r] = 0.0;
+
+  const int64_t niter = (hi - first + R - 1) / R;
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+    const int64_t r0 = first + it * R;
+    v4u v[NH][U];
+    if (r0 >= lo && r0 + R <= hi) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) v[h][u] = gload(reinterpret_cast<const v4u*>(xp[h] + r0 + 32 * u + 8 * grp));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) v[h][u] = load_raw_group(xp[h], r0 + 32 * u + 8 * grp, lo, hi);
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (!live[h]) v[h][u] = v4u{0u, 0u, 0u, 0u};
+
+    bool exact = true;
+    if constexpr (Mfma<T>::kGuard) {
+      RangeU16 range;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          range.add(v[h][u].x);
+          range.add(v[h][u].y);
+          range.add(v[h][u].z);
+          range.add(v[h][u].w);
+        }
+      exact = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) == 0;
+    }
+    if (exact) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int q = 0;
+#pragma unroll
+        for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+          for (int h2 = h1; h2 < NH; ++h2, ++q) {
+            const f32x4 d = Mfma<T>::gram(v[h1][u], v[h2][u]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[q][r] += (double)d[r];
+          }
+      }
+    } else if constexpr (Mfma<T>::kGuard) {
+      // The iteration's rows go to this wave's LDS area (the loaded
+      // registers are free from here on), and each lane sums, in fp64, the
+      // same entries it owns in the matrix-core layout.
+      uint16_t* sp = reinterpret_cast<uint16_t*>(lds) + wave * 16 * NH * R;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          *reinterpret_cast<uint4*>(&sp[(16 * h + op) * R + 32 * u + 8 * grp]) =
+              make_uint4(v[h][u].x, v[h][u].y, v[h][u].z, v[h][u].w);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const int i0 = 4 * grp;
+      int q = 0;
+#pragma unroll
+      for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+        for (int h2 = h1; h2 < NH; ++h2, ++q) {
+          double part[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+          for (int k = 0; k < R; ++k) {
+            const double xj = Mfma<T>::widen(sp[(16 * h2 + op) * R + k]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[r] = fma(Mfma<T>::widen(sp[(16 * h1 + i0 + r) * R + k]), xj, part[r]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[q][r] += part[r];
+        }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // Sum the four waves' matrices in wave order; write the packed triangle.
+  // (The reduction reuses the fallback's LDS: every wave leaves its loop first.)
+  double(*red)[NP][64 * 4] = reinterpret_cast<double(*)[NP][64 * 4]>(lds);
+  if constexpr (kSpillBytes > 0) __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][q][lane * 4 + r] = acc[q][r];
+  __syncthreads();
+  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+  for (int e = threadIdx.x; e < NE; e += kBlock) {
+    int i = 0, rem = e;
+    while (rem >= NB - i) {
+      rem -= NB - i;
+      ++i;
+    }
+    const int k = i + rem;  // entry (i, k), i <= k
+    const int q = (i >> 4) == 0 ? (k >> 4) : 2;
+    const int src = ((k & 15) + 16 * ((i & 15) >> 2)) * 4 + (i & 3);
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGramWaves; ++w) sum += red[w][q][src];
     out[e] = sum;
   }
 }
@@ -876,6 +1031,7 @@ struct RunGramMfma {
       case 4: hipLaunchKernelGGL((gram_mfma_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
       case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
       case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
+      case 32: hipLaunchKernelGGL((gram_mfma32_kernel<T>), grid, dim3(kBlock), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -890,6 +1046,13 @@ hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream
     case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut>), grid, dim3(kBlock), 0, st, a); break;
     case 8: hipLaunchKernelGGL((wsum_kernel<TIn, 8, TOut>), grid, dim3(kBlock), 0, st, a); break;
     case 16: hipLaunchKernelGGL((wsum_kernel<TIn, 16, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 32:
+      // 32-operand blocks exist only over 16-bit inputs, with an fp32 or same-type result
+      if constexpr (sizeof(TIn) == 2 && (sizeof(TOut) == 4 || std::is_same<TIn, TOut>::value)) {
+        hipLaunchKernelGGL((wsum_kernel<TIn, 32, TOut>), grid, dim3(kBlock), 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -76,15 +76,21 @@ struct Elem {
   bool merged;  // false: a bare operand carried through the stage
 };
 
-// Merges of one stage of the tree schedule: up to four levels of pairing
-// (v0,v1), (v2,v3), ... over `cur`, the odd last element carried.
-void tree_stage(std::vector<Elem>& cur, std::vector<Merge>& merges, int& node) {
-  for (int level = 0; level < 4 && cur.size() > 1; ++level) {
+// A merge in stage-wide operand positions (a stage can hold any number of
+// operands; only block-relative positions fit the 8-bit fields of Merge).
+struct StageMerge {
+  int llo, lhi, rhi, node;
+};
+
+// Merges of one stage of the tree schedule: up to `levels` levels of
+// pairing (v0,v1), (v2,v3), ... over `cur`, the odd last element carried.
+void tree_stage(std::vector<Elem>& cur, std::vector<StageMerge>& merges, int& node, int levels) {
+  for (int level = 0; level < levels && cur.size() > 1; ++level) {
     std::vector<Elem> next;
     for (size_t j = 0; 2 * j + 1 < cur.size(); ++j) {
       const Elem& l = cur[2 * j];
       const Elem& r = cur[2 * j + 1];
-      merges.push_back(Merge{(int8_t)l.lo, (int8_t)l.hi, (int8_t)r.hi, 0, node++});
+      merges.push_back(StageMerge{l.lo, l.hi, r.hi, node++});
       next.push_back(Elem{l.lo, r.hi, true});
     }
     if (cur.size() % 2 == 1) next.push_back(cur.back());
@@ -94,10 +100,10 @@ void tree_stage(std::vector<Elem>& cur, std::vector<Merge>& merges, int& node) {
 
 // One stage of the chain schedule: the accumulated vector (first element)
 // meets the following operands one at a time, all of them in this stage.
-void chain_stage(std::vector<Elem>& cur, std::vector<Merge>& merges, int& node) {
+void chain_stage(std::vector<Elem>& cur, std::vector<StageMerge>& merges, int& node) {
   Elem acc = cur[0];
   for (size_t j = 1; j < cur.size(); ++j) {
-    merges.push_back(Merge{(int8_t)acc.lo, (int8_t)acc.hi, (int8_t)cur[j].hi, 0, node++});
+    merges.push_back(StageMerge{acc.lo, acc.hi, cur[j].hi, node++});
     acc = Elem{acc.lo, cur[j].hi, true};
   }
   cur.assign(1, acc);
@@ -142,7 +148,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   int node = 0;
   int next_leaf = K;                 // chain: first input not yet in any stage
   if (schedule == Schedule::Chain) {
-    next_leaf = std::min(K, kMaxOps);
+    next_leaf = std::min(K, first_stage_ops(dtype, K));
     operands.resize(next_leaf);
     is_leaf.resize(next_leaf);
   }
@@ -153,9 +159,11 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     st.widen.swap(pending_widen);
     std::vector<Elem> cur;
     for (int i = 0; i < (int)operands.size(); ++i) cur.push_back(Elem{i, i + 1, false});
-    std::vector<Merge> stage_merges;
+    std::vector<StageMerge> stage_merges;
+    // the first stage reads the inputs; every later one reads fp32 slots
+    const int ops = first ? first_stage_ops(dtype, K) : kMaxOps32;
     if (schedule == Schedule::Tree)
-      tree_stage(cur, stage_merges, node);
+      tree_stage(cur, stage_merges, node, ops == 32 ? 5 : 4);
     else
       chain_stage(cur, stage_merges, node);
     const bool last = cur.size() == 1 && next_leaf == K;
@@ -179,9 +187,9 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
       b.dst = last ? Ref{Ref::Out, 0} : Ref{Ref::Slot, p.nslots++};
       BlockDesc d{};
       d.nb = e.hi - e.lo;
-      d.nbt = d.nb <= 2 ? 2 : d.nb <= 4 ? 4 : d.nb <= 8 ? 8 : 16;
+      d.nbt = d.nb <= 2 ? 2 : d.nb <= 4 ? 4 : d.nb <= 8 ? 8 : d.nb <= 16 ? 16 : 32;
       d.merge0 = (int)p.merges.size();
-      for (const Merge& m : stage_merges) {
+      for (const StageMerge& m : stage_merges) {
         if (m.llo >= e.lo && m.rhi <= e.hi) {
           p.merges.push_back(Merge{(int8_t)(m.llo - e.lo), (int8_t)(m.lhi - e.lo), (int8_t)(m.rhi - e.lo), 0, m.node});
         }
@@ -189,7 +197,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
       d.nmerges = (int)p.merges.size() - d.merge0;
       d.wrow = p.nblocks++;
       for (int k = e.lo; k < e.hi; ++k)
-        if (is_leaf[k]) d.leafmask |= (uint16_t)(1u << (k - e.lo));
+        if (is_leaf[k]) d.leafmask |= 1u << (k - e.lo);
       d.root = last ? 1 : 0;
       b.desc = (int)p.descs.size();
       p.descs.push_back(d);
@@ -199,7 +207,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     }
     // chain: the next stage is the accumulated vector plus up to 15 more inputs
     if (schedule == Schedule::Chain && !last) {
-      const int take = std::min(K - next_leaf, kMaxOps - 1);
+      const int take = std::min(K - next_leaf, kMaxOps32 - 1);
       for (int k = next_leaf; k < next_leaf + take; ++k) {
         const int slot = p.nslots++;
         pending_widen.push_back({k, slot});

@@ -5,8 +5,10 @@
 //     elements, the first tile starting at the segment start and every later
 //     tile at a multiple of kGroup elements, so that vector loads inside a
 //     tile are 16-byte aligned whatever the segment boundaries are;
-//   * the tree, cut into stages of at most four levels.  Within a stage,
-//     every maximal subtree is a block of at most 16 operands.  Every
+//   * the tree, cut into stages.  Within a stage, every maximal subtree is a
+//     block of up to four levels (16 operands); with at most 32 16-bit
+//     inputs, whose Gram pass runs on the matrix cores, the single stage
+//     takes five levels (32 operands).  Every
 //     statistic a node of the block needs (a.b, |a|^2, |b|^2 of its two
 //     children) is a quadratic form in the Gram matrix of the block's
 //     operands, because every node is a linear combination of them; so a
@@ -31,7 +33,8 @@ constexpr int kTile = 32768;     // largest tile, elements (a multiple of kGroup
 constexpr int kMinTile = 2048;   // smallest tile a large segment is cut into
 constexpr int kTargetTiles = 4096;  // tiles a workload is cut into when it is small
 constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
-constexpr int kMaxOps = 16;      // operands per block: four tree levels
+constexpr int kMaxOps = 32;      // operands per block over 16-bit inputs: five tree levels
+constexpr int kMaxOps32 = 16;    // operands per block over fp32 operands: four tree levels
 constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
@@ -42,6 +45,12 @@ enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 enum class Schedule : int { Tree = 0, Chain = 1 };
 
 inline size_t dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// Largest block of the first stage.  32-operand blocks (16-bit inputs only)
+// pay off only where they finish the whole combine in one stage: above 32
+// inputs the tree needs a second stage anyway, and 16-operand blocks stream
+// faster (half the concurrent streams per pass).
+inline int first_stage_ops(DType t, int K) { return (t != DType::F32 && K <= kMaxOps) ? kMaxOps : kMaxOps32; }
 
 // Number of distinct entries of the symmetric n x n Gram matrix.
 constexpr int gram_entries(int n) { return n * (n + 1) / 2; }
@@ -64,14 +73,15 @@ struct Merge {
 };
 
 struct BlockDesc {  // device-visible description of one block
-  int32_t nb;       // operands (1..16; 1 only for K = 1)
-  int32_t nbt;      // Gram size the kernels use: 2, 4, 8 or 16 (operands >= nb are zero)
+  int32_t nb;       // operands (1..32; 1 only for K = 1)
+  int32_t nbt;      // Gram size the kernels use: 2, 4, 8, 16 or 32 (operands >= nb are zero)
   int32_t merge0;   // first merge in the merge table
   int32_t nmerges;  // merges of this block, children before parents
   int64_t poff;     // Gram partials of tile t start at partials + poff + t * gram_entries(nbt)
   int32_t wrow;     // row of this block in the leaf-weight table
-  uint16_t leafmask;  // bit k: operand k is one of the K input gradients
-  uint16_t root;      // 1 for the block whose result is the output
+  uint32_t leafmask;  // bit k: operand k is one of the K input gradients
+  int32_t root;       // 1 for the block whose result is the output
+  int32_t pad;
 };
 
 // Where an operand or result lives.

@@ -160,10 +160,11 @@ def test_small_K_ragged_segments(gpu, K, dtype):
     full_check(wl, f"ragged K={K} {dtype}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("K", [17, 20, 33, 64, 70])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 64, 70, 130])
 def test_multistage_K(gpu, K, dtype):
-    # more than 16 operands: blocks of 16, fp32 block results, carried inputs
+    # more than 16 operands: blocks of 16 (fp32) or 32 (16-bit inputs), fp32
+    # block results, carried inputs; K = 130 has stage positions beyond 127
     wl = W.random_case(K, [1, 300, 9, 40000, 8], dtype=dtype, seed=100 + K, kind="shared")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"multistage K={K} {dtype}")
@@ -288,8 +289,8 @@ def test_stacked_tensor_input_and_out_argument(gpu):
 
 # ---------------------------------------------------------------- chain, orthogonality, plain sum
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("K", [2, 3, 5, 16, 17, 33])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("K", [2, 3, 5, 16, 17, 32, 33, 40])
 def test_chain_schedule(gpu, K, dtype):
     A = _A()
     wl = W.random_case(K, [1, 300, 9, 20000, 8], dtype=dtype, seed=300 + K, kind="shared")

@@ -1,10 +1,13 @@
 """The host planner's tree, checked against the oracle's schedule on the CPU.
 
 tests/plan_dump.cpp is compiled with g++ (AddressSanitizer and UBSan on)
-together with the library's plan.cpp and prints every plan for K = 1..70 in
-both schedules.  Every merge the GPU path will evaluate must be exactly the
-node the oracle defines: same two children (as leaf ranges), same position
-in the node order, every input used once, stage operands fp32 above stage 1.
+together with the library's plan.cpp and prints every plan for K = 1..70 and
+some larger K (up to 300), in both schedules, for fp32 and for 16-bit
+inputs.  Every merge the GPU path will evaluate must be exactly the node the
+oracle defines: same two children (as leaf ranges), same position in the
+node order, every input used once, stage operands fp32 above stage 1; blocks
+hold at most 16 operands, or 32 when at most 32 16-bit inputs make the
+whole combine one stage.
 """
 
 import json
@@ -65,7 +68,8 @@ def plan_nodes(P):
             if si > 0:
                 assert all(kind == 1 for kind, _ in b["ops"]), "stage operands above the first must be fp32 slots"
             rng = [(i, i + 1) if kind == 0 else slot_range[i] for kind, i in b["ops"]]
-            assert len(rng) == b["nb"] <= 16 and b["nbt"] >= b["nb"]
+            limit = 32 if (si == 0 and P["dtype"] == 1 and P["K"] <= 32) else 16
+            assert len(rng) == b["nb"] <= limit and b["nbt"] >= b["nb"]
             for i in range(len(rng) - 1):
                 assert rng[i][1] == rng[i + 1][0], "block operands must be adjacent leaf ranges"
             for llo, lhi, rhi, node in b["merges"]:
@@ -85,17 +89,29 @@ def plan_nodes(P):
     return got
 
 
+@pytest.mark.parametrize("dtype", [0, 1])
 @pytest.mark.parametrize("schedule", [0, 1])
-def test_plan_nodes_match_oracle(plans, schedule):
+def test_plan_nodes_match_oracle(plans, schedule, dtype):
     checked = 0
     for P in plans:
-        if P["schedule"] != schedule:
+        if P["schedule"] != schedule or P["dtype"] != dtype:
             continue
         K = P["K"]
         assert plan_nodes(P) == oracle_nodes(K, schedule), f"K={K}"
         assert sum(1 for st in P["stages"] for b in st["blocks"] if b["root"]) == 1
         checked += 1
-    assert checked == 70
+    assert checked == 79
+
+
+def test_16bit_blocks_are_larger(plans):
+    """With 16-bit inputs up to 32 gradients finish in one stage; more use 16-operand blocks."""
+    for P in plans:
+        if P["schedule"] == 0 and P["K"] in (17, 32, 33, 64):
+            nstages = len(P["stages"])
+            one = P["dtype"] == 1 and P["K"] <= 32
+            assert nstages == (1 if one else 2), (P["K"], P["dtype"], nstages)
+            if P["K"] == 64:
+                assert all(b["nb"] == 16 for b in P["stages"][0]["blocks"])
 
 
 def test_tiles_cover_segments_exactly(plans):
