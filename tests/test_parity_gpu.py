@@ -170,20 +170,22 @@ def test_multistage_K(gpu, K, dtype):
     full_check(wl, f"multistage K={K} {dtype}")
 
 
-def test_fp16_subnormal_scales(gpu):
-    wl = W.random_case(8, [3000] * 16 + [7, 1], dtype="f16", seed=11, kind="scaled")
+@pytest.mark.parametrize("K", [8, 29])
+def test_fp16_subnormal_scales(gpu, K):
+    wl = W.random_case(K, [3000] * 16 + [7, 1], dtype="f16", seed=11, kind="scaled")
     wl.grads = [g.to(gpu) for g in wl.grads]
-    full_check(wl, "fp16 scaled")
+    full_check(wl, f"fp16 scaled K={K}")
 
 
-def test_bf16_exponent_extremes(gpu):
+@pytest.mark.parametrize("K", [8, 24])
+def test_bf16_exponent_extremes(gpu, K):
     """bf16 segments at magnitudes near and past the limits of fp32 products.
 
     Per-segment scales 2^-120 (bf16 subnormals), 2^-57 and 2^61 (values on
     both sides of the range whose pairwise products are exact in fp32),
     2^-40, 1 and 2^100, plus one segment that mixes 2^-100 and 2^90 values.
+    K = 24 runs the 32-operand Gram pass.
     """
-    K = 8
     lengths = [5000, 5000, 5000, 5000, 5000, 5000, 3001]
     scales = [2.0 ** -120, 2.0 ** -57, 2.0 ** -40, 1.0, 2.0 ** 61, 2.0 ** 100]
     off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
@@ -197,7 +199,7 @@ def test_bf16_exponent_extremes(gpu):
         parts.append(mixed)
         grads.append(torch.cat(parts).to(torch.bfloat16))
     wl = W.Workload(K=K, dtype="bf16", seg_offsets=off, grads=[x.to(gpu) for x in grads], seed=900)
-    got, ref, _ = full_check(wl, "bf16 exponent extremes")
+    got, ref, _ = full_check(wl, f"bf16 exponent extremes K={K}")
     for s in range(len(lengths)):
         lo, hi = off[s], off[s + 1]
         err = rel_l2(got[lo:hi], ref["out_rounded"][lo:hi])
