@@ -388,8 +388,7 @@ __global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
 // The hardware rounds the sum of the 32 products once (measured: the sum
 // 1 + 31 * 2^-24 comes out as the nearest fp32 value wherever the 1 sits),
 // so each entry is off by at most 2^-24 of the sum of |a_i b_i| over each
-// 32-row chunk.  A bf16 chunk holding any nonzero value outside that range
-// (inf and NaN included) is instead summed in fp64 by the lanes from LDS.
+// 32-row chunk.
 constexpr int kMfmaUnroll = 8;    // 32-row chunks per wave per iteration
 constexpr int kGramWaves = kBlock / 64;
 
@@ -457,127 +456,42 @@ __device__ __forceinline__ v4u load_raw_group(const uint16_t* __restrict__ x, in
   return v4u{w[0], w[1], w[2], w[3]};
 }
 
-template <typename T, int NB>
-__global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
-  constexpr int U = kMfmaUnroll;
-  constexpr int R = 32 * U;  // rows per wave per iteration
-  constexpr int NE = gram_entries(NB);
-  __shared__ double red[kGramWaves][64 * 4];
-  __shared__ __align__(16) uint16_t spill[kGramWaves][16 * 32];  // fp64 fallback: [operand][row]
+// A bf16 iteration holding a value outside [2^-56, 2^61) takes the scaled
+// path: every operand is multiplied, per iteration, by the power of two that
+// brings its largest magnitude just below 2^61 (exact, a change of exponent),
+// the matrix cores run on the scaled values, and each result is scaled back
+// exactly in fp64 by 2^-(s_row + s_col).  A product lost to the fp32 range
+// then lies at least 2^-190 below the largest value of its operands, and an
+// operand whose values are all tiny keeps its own full precision (its norm
+// decides its Adasum coefficient).  Inf and NaN stay what they are and spoil
+// only the entries of their own operand.
+constexpr int kScaleTop = 127 + 60;  // biased exponent of the scaled maximum
 
-  const int tile_id = blockIdx.x;
-  const int j = blockIdx.y;
-  const Tile tile = args.tiles[tile_id];
-  const int64_t lo = tile.start, hi = tile.start + tile.len;
-  const int64_t first = lo & ~int64_t(kGroup - 1);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int op = lane & 15, grp = lane >> 4;
-
-  // Lanes of absent operands (op >= NB, or a NULL slot) read operand 0 and
-  // are masked to zero, so every load of an iteration is unconditional.
-  const void* const* table = args.x[j];
-  const void* mine = op < NB ? table[op] : nullptr;
-  const bool live = mine != nullptr;
-  const uint16_t* xp = static_cast<const uint16_t*>(live ? mine : table[0]);
-
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  const int64_t niter = (hi - first + R - 1) / R;
-  for (int64_t it = wave; it < niter; it += kGramWaves) {
-    const int64_t r0 = first + it * R;
-    v4u v[U];
-    if (r0 >= lo && r0 + R <= hi) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4u*>(xp + r0 + 32 * u + 8 * grp));
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = load_raw_group(xp, r0 + 32 * u + 8 * grp, lo, hi);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (!live) v[u] = v4u{0u, 0u, 0u, 0u};
-
-    bool exact = true;
-    if constexpr (Mfma<T>::kGuard) {
-      RangeU16 range;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        range.add(v[u].x);
-        range.add(v[u].y);
-        range.add(v[u].z);
-        range.add(v[u].w);
-      }
-      exact = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) == 0;
-    }
-    if (exact) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const f32x4 d = Mfma<T>::gram(v[u], v[u]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
-      }
-    } else {
-      // Chunk by chunk through this wave's LDS rows; lane l sums the same
-      // four entries it owns in the matrix-core layout, in fp64.
-      uint16_t* sp = spill[wave];
-      const int i0 = 4 * grp;
-#pragma unroll 1
-      for (int u = 0; u < U; ++u) {
-        __builtin_amdgcn_wave_barrier();
-        *reinterpret_cast<uint4*>(&sp[op * 32 + 8 * grp]) = make_uint4(v[u].x, v[u].y, v[u].z, v[u].w);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        double part[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int k = 0; k < 32; ++k) {
-          const double xj = Mfma<T>::widen(sp[op * 32 + k]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) part[r] = fma(Mfma<T>::widen(sp[(i0 + r) * 32 + k]), xj, part[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += part[r];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      }
-    }
-  }
-
-  // Sum the four waves' matrices in wave order; write the packed triangle.
-#pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
-  __syncthreads();
-  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
-  for (int e = threadIdx.x; e < NE; e += kBlock) {
-    int i = 0, rem = e;
-    while (rem >= NB - i) {
-      rem -= NB - i;
-      ++i;
-    }
-    const int k = i + rem;  // entry (i, k), i <= k
-    const int src = (k + 16 * (i >> 2)) * 4 + (i & 3);
-    double sum = 0.0;
-#pragma unroll
-    for (int w = 0; w < kGramWaves; ++w) sum += red[w][src];
-    out[e] = sum;
-  }
+// x * 2^s for a 16-bit bf16 value, rounded back to bf16 (exact unless the
+// result leaves the normal range)
+__device__ __forceinline__ uint32_t bf16_scale(uint32_t bits, int s) {
+  const float f = (float)__builtin_amdgcn_ldexp((double)__uint_as_float(bits << 16), s);
+  return __float_as_uint(f) >> 16;
 }
 
-// 32-operand blocks (at most 32 16-bit inputs, one stage): two 16-operand
-// halves, and per 32-row chunk three instructions, the two diagonal 16 x 16
-// blocks and the cross block (A from the first half, B from the second).
-// Lane l, output register r of sub-block q = (h1, h2) holds
-// G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].
-template <typename T>
-__global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
-  constexpr int NB = 32;
-  constexpr int NH = 2;                  // 16-operand halves
-  constexpr int NP = 3;                  // sub-blocks (0,0), (0,1), (1,1)
-  constexpr int U = kMfmaUnroll / 2;     // two loads per chunk
-  constexpr int R = 32 * U;              // rows per wave per iteration
+__device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, int s) {
+  return bf16_scale(w & 0xffffu, s) | (bf16_scale(w >> 16, s) << 16);
+}
+
+// Blocks of up to 16 operands use one 16-operand half; the 32-operand block
+// (at most 32 16-bit inputs, one stage) uses two, with three instructions
+// per 32-row chunk: the two diagonal 16 x 16 blocks and the cross block
+// (A from the first half, B from the second).  Lane l, output register r of
+// sub-block q = (h1, h2) holds G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].
+template <typename T, int NB>
+__global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
+  constexpr int NH = NB > 16 ? 2 : 1;  // 16-operand halves
+  constexpr int NP = NH * (NH + 1) / 2;  // sub-blocks (h1 <= h2)
+  constexpr int U = kMfmaUnroll / NH;  // 32-row chunks per wave per iteration
+  constexpr int R = 32 * U;            // rows per wave per iteration
   constexpr int NE = gram_entries(NB);
-  // LDS: the fp64 fallback's rows (bf16 only; [operand][row] per wave)
-  // during the loop, the cross-wave reduction after it
-  constexpr int kSpillBytes = Mfma<T>::kGuard ? kGramWaves * 16 * NH * R * 2 : 0;
-  constexpr int kRedBytes = kGramWaves * NP * 64 * 4 * 8;
-  __shared__ __align__(16) unsigned char lds[kSpillBytes > kRedBytes ? kSpillBytes : kRedBytes];
+  static_assert(NB <= 32, "at most two halves");
+  __shared__ double red[kGramWaves][NP][64 * 4];
 
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
@@ -588,13 +502,15 @@ __global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
   const int wave = threadIdx.x >> 6;
   const int op = lane & 15, grp = lane >> 4;
 
-  // NULL operands (beyond the block's count) read operand 0, masked to zero
+  // Lanes of absent operands (index >= NB, or a NULL slot) read operand 0
+  // and are masked to zero, so every load of an iteration is unconditional.
   const void* const* table = args.x[j];
   const uint16_t* xp[NH];
   bool live[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    const void* mine = table[16 * h + op];
+    const int k = 16 * h + op;
+    const void* mine = k < NB ? table[k] : nullptr;
     live[h] = mine != nullptr;
     xp[h] = static_cast<const uint16_t*>(live[h] ? mine : table[0]);
   }
@@ -626,7 +542,8 @@ __global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
       for (int u = 0; u < U; ++u)
         if (!live[h]) v[h][u] = v4u{0u, 0u, 0u, 0u};
 
-    bool exact = true;
+    bool scaled = false;
+    int sc[NH] = {};  // per-operand power of two of the scaled path
     if constexpr (Mfma<T>::kGuard) {
       RangeU16 range;
 #pragma unroll
@@ -638,9 +555,29 @@ __global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
           range.add(v[h][u].z);
           range.add(v[h][u].w);
         }
-      exact = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) == 0;
+      scaled = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) != 0;
+      if (scaled) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          uint32_t m = 0;  // largest biased exponent among the lane's values
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const uint32_t w[4] = {v[h][u].x, v[h][u].y, v[h][u].z, v[h][u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = max(m, max((w[e] >> 7) & 0xffu, (w[e] >> 23) & 0xffu));
+          }
+          // the four lanes holding this operand's rows
+          m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+          m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+          sc[h] = kScaleTop - (int)(m == 0 ? 1 : m);  // all-zero or subnormal operand: exponent 1
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            v[h][u] = v4u{bf16x2_scale(v[h][u].x, sc[h]), bf16x2_scale(v[h][u].y, sc[h]),
+                          bf16x2_scale(v[h][u].z, sc[h]), bf16x2_scale(v[h][u].w, sc[h])};
+        }
+      }
     }
-    if (exact) {
+    if (!scaled) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         int q = 0;
@@ -653,45 +590,29 @@ __global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
             for (int r = 0; r < 4; ++r) acc[q][r] += (double)d[r];
           }
       }
-    } else if constexpr (Mfma<T>::kGuard) {
-      // The iteration's rows go to this wave's LDS area (the loaded
-      // registers are free from here on), and each lane sums, in fp64, the
-      // same entries it owns in the matrix-core layout.
-      uint16_t* sp = reinterpret_cast<uint16_t*>(lds) + wave * 16 * NH * R;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          *reinterpret_cast<uint4*>(&sp[(16 * h + op) * R + 32 * u + 8 * grp]) =
-              make_uint4(v[h][u].x, v[h][u].y, v[h][u].z, v[h][u].w);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      const int i0 = 4 * grp;
+    } else {
+      // entry (row, col) of sub-block (h1, h2): row operand 4 grp + r of
+      // half h1 (its scale from the lane that holds it), column operand op
+      // of half h2 (this lane's own)
       int q = 0;
 #pragma unroll
       for (int h1 = 0; h1 < NH; ++h1)
 #pragma unroll
         for (int h2 = h1; h2 < NH; ++h2, ++q) {
-          double part[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-          for (int k = 0; k < R; ++k) {
-            const double xj = Mfma<T>::widen(sp[(16 * h2 + op) * R + k]);
+          int back[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[r] = fma(Mfma<T>::widen(sp[(16 * h1 + i0 + r) * R + k]), xj, part[r]);
+          for (int r = 0; r < 4; ++r) back[r] = -(__shfl(sc[h1], 4 * grp + r) + sc[h2]);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const f32x4 d = Mfma<T>::gram(v[h1][u], v[h2][u]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[q][r] += __builtin_amdgcn_ldexp((double)d[r], back[r]);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[q][r] += part[r];
         }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
     }
   }
 
   // Sum the four waves' matrices in wave order; write the packed triangle.
-  // (The reduction reuses the fallback's LDS: every wave leaves its loop first.)
-  double(*red)[NP][64 * 4] = reinterpret_cast<double(*)[NP][64 * 4]>(lds);
-  if constexpr (kSpillBytes > 0) __syncthreads();
 #pragma unroll
   for (int q = 0; q < NP; ++q)
 #pragma unroll
@@ -705,7 +626,7 @@ __global__ __launch_bounds__(kBlock) void gram_mfma32_kernel(GramArgs args) {
       ++i;
     }
     const int k = i + rem;  // entry (i, k), i <= k
-    const int q = (i >> 4) == 0 ? (k >> 4) : 2;
+    const int q = (i >> 4) == 0 ? (k >> 4) : 2;  // (0,0) -> 0, (0,1) -> 1, (1,1) -> 2
     const int src = ((k & 15) + 16 * ((i & 15) >> 2)) * 4 + (i & 3);
     double sum = 0.0;
 #pragma unroll
@@ -1031,7 +952,7 @@ struct RunGramMfma {
       case 4: hipLaunchKernelGGL((gram_mfma_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
       case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
       case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
-      case 32: hipLaunchKernelGGL((gram_mfma32_kernel<T>), grid, dim3(kBlock), 0, st, a); break;
+      case 32: hipLaunchKernelGGL((gram_mfma_kernel<T, 32>), grid, dim3(kBlock), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
