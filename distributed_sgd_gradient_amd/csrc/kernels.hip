@@ -406,7 +406,6 @@ struct Mfma<_Float16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
-  static __device__ __forceinline__ double widen(uint16_t bits) { return (double)__builtin_bit_cast(_Float16, bits); }
 };
 
 template <>
@@ -419,7 +418,6 @@ struct Mfma<bf16_t> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
                                                    f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
-  static __device__ __forceinline__ double widen(uint16_t bits) { return (double)__uint_as_float((uint32_t)bits << 16); }
 };
 
 // Running range of the magnitude bits of packed 16-bit pairs: the largest,
