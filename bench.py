@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each step alone after writing a 1 GiB scratch buffer (caches cold); "
+                         "reported under 'cold', the headline value stays the back-to-back rate")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 3 plain fp32 copies of MIB MiB (read MIB, write MIB) "
                          "so that rocprofv3 counters can be scaled against a kernel of known traffic")
@@ -163,6 +166,28 @@ def main():
         log(f"  {name:12s} launches {k['launches']:5d}  {k['milliseconds'] / args.steps:8.3f} ms/step  "
             f"{k['bytes'] / (k['milliseconds'] * 1e-3) / 1e9 if k['milliseconds'] > 0 else 0:8.1f} GB/s")
 
+    cold = None
+    if args.cold:
+        # each step alone, after a 1 GiB write has pushed the inputs out of
+        # the L2 and Infinity caches; events on the stream the combine uses
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        times = []
+        for _ in range(args.steps):
+            scratch.fill_(1.0)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            step()
+            ev1.record()
+            ev1.synchronize()
+            times.append(ev0.elapsed_time(ev1))
+        del scratch
+        cold_ms = float(sorted(times)[len(times) // 2])
+        cold = {"ms_per_step_median": cold_ms, "ms_per_step_min": float(min(times)),
+                "gradient_GBps": grad_bytes / (cold_ms * 1e-3) / 1e9,
+                "path_frac": b_min / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "note": "one step at a time after a 1 GiB scratch write"}
+        log(f"cold (caches flushed before every step): median {cold_ms:.3f} ms/step")
+
     # the synchronous-SGD plain sum on the same buffers: one pass, reads K
     # gradients once and writes one result (B_min of traffic)
     out_sum = torch.empty_like(out)
@@ -191,6 +216,7 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg,
                    "io_dtype": wl.dtype, "seed": wl.seed, "parallelism": "none (one GPU)"},
         "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "plain_sum": plain_sum,
+        **({"cold": cold} if cold is not None else {}),
         "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
                         "bytes_per_step": v["bytes"] / args.steps} for k, v in kernels.items()},
     }

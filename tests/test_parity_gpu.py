@@ -376,6 +376,41 @@ def test_single_worker_is_exact_copy(gpu):
         assert torch.equal(out, g)
 
 
+def test_offsets_beyond_2_pow_31(gpu):
+    """K = 2 bf16 with 2^31 + 3500 elements: tiles past 2^31 (64-bit offsets).
+
+    The middle segment (2^31 - 500 elements) holds the same gradient in
+    both workers, so Adasum returns it exactly with coefficients 1/2; the
+    small segments on either side are checked against the oracle.
+    """
+    A = _A()
+    n0, n1, n2 = 1000, 2 ** 31 - 500, 3000
+    off = np.array([0, n0, n0 + n1, n0 + n1 + n2], dtype=np.int64)
+    say("offsets beyond 2^31", f"N={int(off[-1])}")
+    g = torch.Generator(device=gpu).manual_seed(31)
+    a = torch.empty(int(off[-1]), dtype=torch.bfloat16, device=gpu)
+    b = torch.empty_like(a)
+    a[n0:n0 + n1].normal_(generator=g)
+    b[n0:n0 + n1].copy_(a[n0:n0 + n1])
+    for t in (a, b):
+        t[:n0].normal_(generator=g)
+        t[n0 + n1:].normal_(generator=g)
+    out, coeffs = A.combine([a, b], off, return_coeffs=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[n0:n0 + n1], a[n0:n0 + n1])
+    c = coeffs.cpu().numpy()
+    assert c[0, 1, 0] == 0.5 and c[0, 1, 1] == 0.5
+    for s, (lo, hi) in ((0, (0, n0)), (2, (n0 + n1, int(off[-1])))):
+        rows = [a[lo:hi].double().cpu().numpy(), b[lo:hi].double().cpu().numpy()]
+        res, cf, _ = oracle.adasum_tree(rows)
+        ref = oracle.round_to_format(res, "bf16")
+        got = out[lo:hi].double().cpu().numpy()
+        assert rel_l2(got, ref) <= TOL["bf16"], f"segment {s}"
+        check_coeffs(c[:, s], np.asarray(cf).reshape(-1, 2), f"segment {s}")
+    del a, b, out
+    torch.cuda.empty_cache()
+
+
 def test_nan_stays_in_its_segment(gpu):
     A = _A()
     wl = W.random_case(4, [100, 200, 300], seed=61)
