@@ -1,18 +1,19 @@
 // adasum.hip - C ABI, argument validation, plan cache and stage scheduler.
 //
-// The tree is cut into stages of at most four levels; each stage is a set
-// of blocks (subtrees of at most 16 operands).  One call enqueues, stage by
-// stage:
+// The tree is cut into stages of at most four levels (five when at most 32
+// 16-bit inputs make it one stage); each stage is a set of blocks (subtrees
+// of at most 16 operands, or that one 32-operand block).  One call enqueues,
+// stage by stage:
 //   1. widen: inputs carried into a stage above the first become fp32 slots;
 //   2. gram: one launch per block size over every block and every tile: the
-//      fp64 Gram partials of each block's operands;
+//      Gram partials of each block's operands, accumulated in fp64;
 //   3. tree: one launch over every (block, segment): tile partials summed in
 //      tile order, every merge of the block evaluated on the Gram matrix
 //      (statistics, coefficients), the final operand weights written;
 //   4. wsum: one launch per (block size, types) over every block and tile:
 //      the block's result, sum_k w_k x_k, into an fp32 slot or into out.
-// So a combine of K <= 16 gradients is three launches and two passes over
-// the inputs, whatever the number of segments.
+// So a combine of K <= 16 gradients (K <= 32 for 16-bit ones) is three
+// launches and two passes over the inputs, whatever the number of segments.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -204,6 +205,7 @@ struct Range {
 bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 // Checks every pointer argument of a combine call against the shape.
 int validate_buffers(const void* const* grads, int K, int64_t N, size_t esz, int nseg, const void* out,
@@ -234,7 +236,8 @@ int validate_buffers(const void* const* grads, int K, int64_t N, size_t esz, int
     }
     if (!aligned16(ws)) return fail(ADASUM_EINVAL, "workspace must be 16-byte aligned");
   }
-  std::vector<Range> others;  // buffers that may be written must not overlap anything
+  if (!aligned8(coeffs) || !aligned8(stats) || !aligned8(ortho))
+    return fail(ADASUM_EINVAL, "coeffs, stats and ortho must be 8-byte aligned");
   const size_t nodes = K > 1 ? (size_t)(K - 1) : 0;
   auto rng = [](const void* p, size_t bytes, const char* name) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);

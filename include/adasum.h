@@ -124,10 +124,13 @@ ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int
  *                left to right, then level 2, ...); chain nodes in step order.
  *   stats        device fp64 array [K-1][nseg][3] receiving (a.b, |a|^2,
  *                |b|^2) of every node in the same order, or NULL.
- *                Within each block of up to 16 operands (four tree levels)
- *                the statistics are evaluated in fp64 from the Gram matrix of
- *                the block's operands; above a block, from the fp32 values
- *                its result was stored in.
+ *                Within each block of up to 16 operands (four tree levels;
+ *                32 operands and five levels when at most 32 16-bit inputs
+ *                make the whole tree one block) the statistics are evaluated
+ *                from the Gram matrix of the block's operands, accumulated
+ *                in fp64; above a block, from the fp32 values its result was
+ *                stored in.  coeffs, stats and ortho must be 8-byte aligned
+ *                and overlap no other argument.
  *   ortho        device fp64 array [nseg] receiving, per segment, the
  *                orthogonality ratio |result|^2 / sum_k |g_k|^2 of Figure 1
  *                (1 for mutually orthogonal gradients, 1/K for K equal ones;

@@ -77,6 +77,8 @@ def _call_ex(K=2, off=(0, 8, 16), dtype=0, grads=None, out=FAKE + (1 << 30), ws=
     (dict(coeffs=FAKE + (1 << 30) + 8), "overlaps"),
     (dict(ortho=FAKE + 32), "overlaps input"),
     (dict(schedule=5), "unknown schedule"),
+    (dict(stats=FAKE + (3 << 30) + 4), "8-byte aligned"),
+    (dict(ortho=FAKE + (3 << 30) + 2), "8-byte aligned"),
 ])
 def test_invalid_arguments_rejected(kwargs, needle):
     rc, msg = _call_ex(**kwargs)
