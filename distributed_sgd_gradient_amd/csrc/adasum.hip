@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <list>
 #include <map>
@@ -39,6 +40,22 @@ thread_local std::string g_last_error;
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
   return code;
+}
+
+// ADASUM_LOG=1 in the environment: one line on stderr per new plan and per
+// launch (kind, grid, algorithmic bytes), for tracing a call's schedule.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("ADASUM_LOG");
+    return v != nullptr && v[0] != '\0' && v[0] != '0';
+  }();
+  return on;
+}
+
+void log_launch(const char* kind, int stage, int ntiles, int njobs, int nbt, double bytes) {
+  if (!log_enabled()) return;
+  std::fprintf(stderr, "[adasum] stage %d %-5s grid %d x %d  Gram size %d  %.0f bytes\n", stage, kind, ntiles, njobs,
+               nbt, bytes);
 }
 
 int fail_hip(hipError_t e, const char* what) {
@@ -98,6 +115,13 @@ std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType
   }
   auto cp = std::make_shared<CachedPlan>();
   cp->plan = build_plan(K, off, nseg, dt, sc);
+  if (log_enabled()) {
+    const Plan& p = cp->plan;
+    std::fprintf(stderr, "[adasum] plan K=%d nseg=%d N=%lld dtype=%d schedule=%s: %zu tiles of <= %lld, %zu stages, "
+                 "%d blocks, %d fp32 slots, workspace %zu bytes\n", K, nseg, (long long)p.N, (int)dt,
+                 sc == Schedule::Tree ? "tree" : "chain", p.tiles.size(), (long long)p.tile_rows, p.stages.size(),
+                 p.nblocks, p.nslots, p.ws_total);
+  }
   g_plans.push_front(cp);
   if (g_plans.size() > kMaxCachedPlans) {
     release_tables(*g_plans.back());
@@ -295,7 +319,9 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
   hipError_t e;
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
   double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
+  int stage_no = 0;
   for (const Stage& sg : p.stages) {
+    ++stage_no;
     // 1. inputs carried into this stage, widened once to fp32
     for (const auto& wd : sg.widen) {
       if (ntiles == 0) break;
@@ -303,6 +329,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
       w.src = b.grads[wd.first];
       w.dst = reinterpret_cast<float*>(b.ws + p.ws_slots + (size_t)wd.second * (size_t)p.N * sizeof(float));
       w.tiles = dt.tiles;
+      log_launch("widen", stage_no, ntiles, 1, 0, (double)p.N * (esz + 4.0));
       const int pr = prof_start(kWiden, (double)p.N * (esz + 4.0), st);
       e = launch_widen(p.dtype, w, ntiles, st);
       prof_stop(pr, st);
@@ -341,6 +368,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             }
             a.tiles = dt.tiles;
             a.partials = partials;
+            log_launch("gram", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kGram, in_bytes + out_bytes, st);
             e = launch_gram(in_t, nbt, a, ntiles, n, st);
             prof_stop(pr, st);
@@ -358,6 +386,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             a.tiles = dt.tiles;
             a.nseg = p.nseg;
             a.weights = weights;
+            log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
             e = launch_wsum(in_t, nbt, out_t, a, ntiles, n, st);
             prof_stop(pr, st);
@@ -383,6 +412,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         t.nblocks_total = p.nblocks;
         double bytes = 0;
         for (const Block& bk : sg.blocks) bytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
+        log_launch("tree", stage_no, t.nblocks * p.nseg, 1, 0, bytes);
         const int pr = prof_start(kTree, bytes, st);
         e = launch_tree(t, st);
         prof_stop(pr, st);

@@ -128,3 +128,19 @@ def test_sum_entry_point_validation():
     assert lib.adasum_sum(ptrs, 2, 1000, 0, FAKE + 16, None, 0, None) == _native.EINVAL  # out overlaps grads[0]
     assert "overlaps" in lib.adasum_last_error().decode()
     assert lib.adasum_sum(ptrs, 2, 1000, 7, FAKE + (2 << 20), None, 0, None) == _native.EINVAL
+
+
+def test_adasum_log_reports_the_plan():
+    """ADASUM_LOG=1 prints one line per new plan (and per launch on a GPU)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, numpy as np\n"
+            "from distributed_sgd_gradient_amd import _native\n"
+            "off = np.array([0, 1000, 70000], dtype=np.int64)\n"
+            "p = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))\n"
+            "print(_native.lib().adasum_workspace_bytes(40, p, 2, 2, 0))\n")
+    env = dict(os.environ, ADASUM_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "[adasum] plan K=40 nseg=2 N=70000" in r.stderr
+    assert "2 stages" in r.stderr and int(r.stdout.strip()) > 0
