@@ -692,17 +692,28 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   }
   if (tid < kMaxOps) w[tid] = 1.0;
   __syncthreads();
-  // Merges in order.  For merge (L, R) thread i < nb forms its row sums
+  // Merges run level by level: merges of a block are stored children
+  // before parents, and the merges of one level cover disjoint operand
+  // ranges (a batch ends where a merge starts left of the previous one).
+  // For merge (L, R), thread i in L u R forms its row sums
   // rowL_i = sum_{k in L} w_k G(i,k) and rowR_i = sum_{k in R} w_k G(i,k) in
-  // k order; thread 0 then forms A = sum_{i in L} w_i rowL_i,
+  // k order; one thread per merge then forms A = sum_{i in L} w_i rowL_i,
   // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order.
   // That is the same arithmetic, term for term, as a serial evaluation.
   __shared__ double rowL[kMaxOps], rowR[kMaxOps];
-  __shared__ double cab[2];
-  for (int m = 0; m < d.nmerges; ++m) {
-    const Merge mg = a.merges[d.merge0 + m];
-    const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
-    if (tid >= l0 && tid < r1) {
+  __shared__ double cab[kMaxOps][2];
+  __shared__ Merge ms[kMaxOps];
+  if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
+  __syncthreads();
+  for (int m0 = 0; m0 < d.nmerges;) {
+    int m1 = m0 + 1;
+    while (m1 < d.nmerges && ms[m1].llo >= ms[m1 - 1].rhi) ++m1;
+    // the merge of this batch that holds operand tid, if any
+    int mine = -1;
+    for (int m = m0; m < m1; ++m)
+      if (tid >= ms[m].llo && tid < ms[m].rhi) mine = m;
+    if (mine >= 0) {
+      const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
       double sl = 0.0, sr = 0.0;
       for (int k = l0; k < l1; ++k) sl = add_rn(sl, mul_rn(w[k], gram_at(G, n, tid, k)));
       for (int k = l1; k < r1; ++k) sr = add_rn(sr, mul_rn(w[k], gram_at(G, n, tid, k)));
@@ -710,15 +721,17 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       rowR[tid] = sr;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < m1 - m0) {
+      const Merge mg = ms[m0 + tid];
+      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
       double A = 0.0, B = 0.0, dd = 0.0;
       for (int i = l0; i < l1; ++i) A = add_rn(A, mul_rn(w[i], rowL[i]));
       for (int i = l1; i < r1; ++i) B = add_rn(B, mul_rn(w[i], rowR[i]));
       for (int i = l0; i < l1; ++i) dd = add_rn(dd, mul_rn(w[i], rowR[i]));
       const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
-      cab[0] = ca;
-      cab[1] = cb;
+      cab[m0 + tid][0] = ca;
+      cab[m0 + tid][1] = cb;
       const int64_t at = (int64_t)mg.node * a.nseg + s;
       a.coeffs[at * 2] = ca;
       a.coeffs[at * 2 + 1] = cb;
@@ -727,8 +740,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       a.stats[at * 3 + 2] = B;
     }
     __syncthreads();
-    if (tid >= l0 && tid < r1) w[tid] = mul_rn(w[tid], tid < l1 ? cab[0] : cab[1]);
+    if (mine >= 0) w[tid] = mul_rn(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
     __syncthreads();
+    m0 = m1;
   }
   if (tid == 0) {
     // sum of |g_k|^2 over the block's input operands, in operand order
