@@ -61,8 +61,9 @@ bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, int sche
     *err = buf;
     return false;
   }
-  // tile count must fit int32 (every kernel indexes tiles with 32-bit ints)
-  if (offsets[nseg] / kMinTile + nseg + 1 > int64_t(INT32_MAX)) {
+  // tile count (times the weighted sum's parts per tile) must fit a launch
+  // grid and the kernels' 32-bit tile indices
+  if ((offsets[nseg] / kMinTile + nseg + 1) * kWsumSplit > int64_t(INT32_MAX)) {
     *err = "too many tiles for this shape";
     return false;
   }
