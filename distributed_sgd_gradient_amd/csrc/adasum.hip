@@ -291,6 +291,64 @@ int validate_buffers(const void* const* grads, int K, int64_t N, size_t esz, int
   return ADASUM_OK;
 }
 
+// Checks that p is device memory of `device` and, where the runtime can
+// tell the allocation's extent, that [p, p + bytes) lies inside it (a host
+// pointer, or a buffer on another GPU, would otherwise fault inside a
+// kernel).  Failed queries are cleared so that they cannot surface later as
+// the error of a launch.
+int check_device_range(const void* p, size_t bytes, const char* name, int device) {
+  char buf[200];
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    snprintf(buf, sizeof buf, "%s is not device memory known to the HIP runtime", name);
+    return fail(ADASUM_EINVAL, buf);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) {
+    snprintf(buf, sizeof buf, "%s is not device memory (memory type %d)", name, (int)attr.type);
+    return fail(ADASUM_EINVAL, buf);
+  }
+  if (attr.type == hipMemoryTypeDevice && attr.device != device) {
+    snprintf(buf, sizeof buf, "%s is on device %d but the call runs on device %d", name, attr.device, device);
+    return fail(ADASUM_EINVAL, buf);
+  }
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();  // extent unknown (e.g. virtually mapped memory): nothing more to check
+    return ADASUM_OK;
+  }
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(base), end = lo + size;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (a < lo || a + bytes > end) {
+    snprintf(buf, sizeof buf, "%s: %zu bytes from this address run past the end of its allocation", name, bytes);
+    return fail(ADASUM_EINVAL, buf);
+  }
+  return ADASUM_OK;
+}
+
+// Every caller buffer of a combine or sum call, on the current device.
+int check_devices(const void* const* grads, int K, size_t vec_bytes, const void* out, const void* ws,
+                  size_t ws_needed, const double* coeffs, const double* stats, const double* ortho, size_t nodes,
+                  int nseg, int device) {
+  char name[32];
+  int rc = ADASUM_OK;
+  if (vec_bytes > 0) {
+    for (int k = 0; k < K && rc == ADASUM_OK; ++k) {
+      snprintf(name, sizeof name, "grads[%d]", k);
+      rc = check_device_range(grads[k], vec_bytes, name, device);
+    }
+    if (rc == ADASUM_OK) rc = check_device_range(out, vec_bytes, "out", device);
+  }
+  if (rc == ADASUM_OK && ws != nullptr && ws_needed > 0) rc = check_device_range(ws, ws_needed, "workspace", device);
+  if (rc == ADASUM_OK && coeffs && nodes * nseg > 0)
+    rc = check_device_range(coeffs, nodes * nseg * 2 * sizeof(double), "coeffs", device);
+  if (rc == ADASUM_OK && stats && nodes * nseg > 0)
+    rc = check_device_range(stats, nodes * nseg * 3 * sizeof(double), "stats", device);
+  if (rc == ADASUM_OK && ortho && nseg > 0) rc = check_device_range(ortho, (size_t)nseg * sizeof(double), "ortho", device);
+  return rc;
+}
+
 // ---------------------------------------------------------------- scheduler
 
 struct CallBuffers {
@@ -461,6 +519,9 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
     if (rc != ADASUM_OK) return rc;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    rc = check_devices(grads, K, (size_t)N * dtype_size(dt), out, nullptr, 0, nullptr, nullptr, nullptr, 0, nseg,
+                       device);
+    if (rc != ADASUM_OK) return rc;
     OwnedWorkspace& ow = g_ws[{device, stream}];
     if (ow.bytes < p.ws_total) {
       if (ow.ptr) {
@@ -486,6 +547,9 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
     if (rc != ADASUM_OK) return rc;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    rc = check_devices(grads, K, (size_t)N * dtype_size(dt), out, workspace, p.ws_total, coeffs, stats, ortho,
+                       K > 1 ? (size_t)(K - 1) : 0, nseg, device);
+    if (rc != ADASUM_OK) return rc;
   }
 
   DeviceTables tables;
@@ -551,6 +615,12 @@ int adasum_sum(const void* const* grads, int K, int64_t N, int dtype, void* out,
                             nullptr, nullptr, nullptr);
   if (rc != ADASUM_OK) return rc;
   if (N == 0) return ADASUM_OK;
+  int device = 0;
+  hipError_t de = hipGetDevice(&device);
+  if (de != hipSuccess) return fail_hip(de, "hipGetDevice");
+  rc = check_devices(grads, K, (size_t)N * dtype_size(dt), out, workspace, (size_t)need, nullptr, nullptr, nullptr, 0,
+                     0, device);
+  if (rc != ADASUM_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   std::lock_guard<std::mutex> lock(g_mu);
   double* acc = static_cast<double*>(workspace);
