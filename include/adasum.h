@@ -24,8 +24,12 @@
  * Conventions shared by all entry points
  *   - Return 0 (ADASUM_OK) on success or a negative ADASUM_E* code.  The text
  *     of the last failure on the calling thread is adasum_last_error().
- *   - Arguments are validated on the host before any HIP call, so invalid
- *     arguments never reach the GPU and never leave work enqueued.
+ *   - Arguments are validated before any work is enqueued, so invalid
+ *     arguments never reach the GPU: first on the host alone (shapes,
+ *     NULLs, alignment, overlaps), then with the HIP runtime's pointer
+ *     queries (ADASUM_EINVAL for host memory, memory of another device, or
+ *     a buffer shorter than the call needs where the runtime knows its
+ *     allocation's extent).
  *   - Pointers named "device" must be device memory of the current HIP device
  *     (hipSetDevice); pointers named "host" are ordinary host memory read
  *     during the call only.
