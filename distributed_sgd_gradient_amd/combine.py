@@ -83,6 +83,8 @@ def combine(grads, seg_offsets, *, schedule="tree", out=None, workspace=None, re
     need = workspace_bytes(K, off, g0.dtype, schedule)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the gradients' device")
     coeffs = torch.empty((max(K - 1, 0), nseg, 2), dtype=torch.float64, device=dev) if return_coeffs else None
     stats = torch.empty((max(K - 1, 0), nseg, 3), dtype=torch.float64, device=dev) if return_stats else None
     ortho = torch.empty((nseg,), dtype=torch.float64, device=dev) if return_ortho else None
@@ -93,7 +95,7 @@ def combine(grads, seg_offsets, *, schedule="tree", out=None, workspace=None, re
     with torch.cuda.device(dev):
         _native.check(L.adasum_combine_ex(
             ptrs, K, off.ctypes.data_as(_native._I64P), nseg, DTYPE_CODES[g0.dtype], SCHEDULES[schedule],
-            out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             coeffs.data_ptr() if coeffs is not None else None,
             stats.data_ptr() if stats is not None else None,
             ortho.data_ptr() if ortho is not None else None,
@@ -113,13 +115,15 @@ def plain_sum(grads, *, out=None, workspace=None, stream=None):
     need = _native.check(L.adasum_sum_workspace_bytes(K, N, DTYPE_CODES[g0.dtype]))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the gradients' device")
     ptrs = (ctypes.c_void_p * K)(*[g.data_ptr() for g in grads])
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     with torch.cuda.device(dev):
         _native.check(L.adasum_sum(ptrs, K, N, DTYPE_CODES[g0.dtype], out.data_ptr(),
                                    workspace.data_ptr() if workspace is not None else None,
-                                   workspace.numel() if workspace is not None else 0,
+                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                    ctypes.c_void_p(stream.cuda_stream)))
     return out
 
@@ -130,8 +134,7 @@ def combine_cached(grads, seg_offsets, *, out=None, stream=None):
     grads = _grad_list(grads)
     g0 = grads[0]
     off = _offsets(seg_offsets, g0.numel())
-    if out is None:
-        out = torch.empty_like(g0)
+    out = _check_out(out, g0)
     ptrs = (ctypes.c_void_p * len(grads))(*[g.data_ptr() for g in grads])
     if stream is None:
         stream = torch.cuda.current_stream(g0.device)
