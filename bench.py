@@ -127,11 +127,8 @@ def main():
     wl = W.make_workload(args.config, seed=args.seed, device=dev)
     K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
     out = torch.empty_like(wl.grads[0])
-    ws = torch.empty(max(A.workspace_bytes(K, wl.seg_offsets, wl.grads[0].dtype), 1), dtype=torch.uint8, device=dev)
+    step = A.Combiner(wl.grads, wl.seg_offsets, out=out)  # arguments marshalled once; one combine per call
     torch.cuda.synchronize()
-
-    def step():
-        A.combine(wl.grads, wl.seg_offsets, out=out, workspace=ws)
 
     log(f"K={K} N={N} nseg={wl.nseg}; warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -6,6 +6,6 @@ loads the library and fails loudly when the library has not been built.
 """
 
 from ._native import AdasumError, lib as _lib  # noqa: F401
-from .combine import combine, combine_cached, plain_sum, workspace_bytes  # noqa: F401
+from .combine import Combiner, combine, combine_cached, plain_sum, workspace_bytes  # noqa: F401
 
 _lib()  # fail at import time when the HIP library is missing

@@ -144,3 +144,46 @@ def combine_cached(grads, seg_offsets, *, out=None, stream=None):
                                        DTYPE_CODES[g0.dtype], out.data_ptr(),
                                        ctypes.c_void_p(stream.cuda_stream)))
     return out
+
+
+class Combiner:
+    """A combine whose arguments are marshalled once: for calling Adasum on
+    the same gradient buffers every step (their contents may change between
+    calls, their storage may not).  Each call enqueues one combine on the
+    given (else the current) stream and returns ``out``; the coefficient,
+    statistic and orthogonality tables, when requested, are the attributes
+    ``coeffs``, ``stats`` and ``ortho``, overwritten by every call.
+    """
+
+    def __init__(self, grads, seg_offsets, *, schedule="tree", out=None, return_coeffs=False, return_stats=False,
+                 return_ortho=False):
+        self.grads = _grad_list(grads)  # kept alive for the pointers below
+        g0 = self.grads[0]
+        self._off = _offsets(seg_offsets, g0.numel())
+        K, nseg = len(self.grads), self._off.size - 1
+        self.device = dev = g0.device
+        self.out = _check_out(out, g0)
+        need = workspace_bytes(K, self._off, g0.dtype, schedule)
+        self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.coeffs = torch.empty((max(K - 1, 0), nseg, 2), dtype=torch.float64, device=dev) if return_coeffs else None
+        self.stats = torch.empty((max(K - 1, 0), nseg, 3), dtype=torch.float64, device=dev) if return_stats else None
+        self.ortho = torch.empty((nseg,), dtype=torch.float64, device=dev) if return_ortho else None
+        self._ptrs = (ctypes.c_void_p * K)(*[g.data_ptr() for g in self.grads])
+        self._args = (self._ptrs, K, self._off.ctypes.data_as(_native._I64P), nseg, DTYPE_CODES[g0.dtype],
+                      SCHEDULES[schedule], self.out.data_ptr(), self._ws.data_ptr(), self._ws.numel(),
+                      self.coeffs.data_ptr() if self.coeffs is not None else None,
+                      self.stats.data_ptr() if self.stats is not None else None,
+                      self.ortho.data_ptr() if self.ortho is not None else None)
+        self._fn = _native.lib().adasum_combine_ex
+        self._index = dev.index if dev.index is not None else torch.cuda.current_device()
+
+    def __call__(self, stream=None):
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        st = ctypes.c_void_p(stream.cuda_stream)
+        if torch.cuda.current_device() == self._index:
+            _native.check(self._fn(*self._args, st))
+        else:
+            with torch.cuda.device(self.device):
+                _native.check(self._fn(*self._args, st))
+        return self.out

@@ -470,3 +470,21 @@ def test_host_pointers_rejected_before_any_launch(gpu):
     torch.cuda.synchronize()
     ref = oracle.combine([a.double().cpu().numpy(), b.double().cpu().numpy()], off, out_format="f32")["out_rounded"]
     assert rel_l2(out.double().cpu().numpy(), ref) <= TOL["f32"]
+
+
+def test_prepared_combiner_matches_combine(gpu):
+    """Combiner marshals once; every call reads the buffers' current contents."""
+    A = _A()
+    wl = W.random_case(5, RAGGED, dtype="f32", seed=77, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    comb = A.Combiner(grads, wl.seg_offsets, return_coeffs=True, return_ortho=True)
+    for rep in range(3):
+        if rep:
+            for g in grads:
+                g.mul_(0.5).add_(torch.randn_like(g))
+        out = comb()
+        ref, coeffs, ortho = A.combine(grads, wl.seg_offsets, return_coeffs=True, return_ortho=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert torch.equal(comb.coeffs, coeffs)
+        assert torch.equal(torch.nan_to_num(comb.ortho, nan=-1.0), torch.nan_to_num(ortho, nan=-1.0))
