@@ -5,11 +5,14 @@
 // can combine them (Sec. 4: the operation cannot be streamed).  Every node of
 // the tree is a linear combination of the operands below it, so all the
 // statistics of a subtree are quadratic forms in the Gram matrix of its
-// operands.  A block (a subtree of at most 16 operands, four levels) is
+// operands.  A block (a subtree of at most 16 operands, four levels; 32
+// operands and five levels for 16-bit inputs that fit one block) is
 // therefore combined in three launches:
-//   gram  - one pass over the operands: per tile, the fp64 Gram matrix
-//           (packed upper triangle), accumulated per thread with fma,
-//           reduced across the workgroup in a fixed order;
+//   gram  - one pass over the operands: per tile, the Gram matrix (packed
+//           upper triangle), fp64 products and sums on the VALU for fp32
+//           operands, 32-row sums of exact products on the matrix cores
+//           added in fp64 for 16-bit operands; reduced across the
+//           workgroup in a fixed order;
 //   tree  - per segment: the tile partials summed in tile order, then the
 //           block's merges evaluated on the Gram matrix level by level:
 //           d = wL.G.wR, A = wL.G.wL, B = wR.G.wR, ca = 1 - d/(2A),
