@@ -206,169 +206,100 @@ __device__ __forceinline__ TileSpan span_of(const Tile& t) {
   return s;
 }
 
-// ----------------------------------------------------------------- Gram pass
+// ----------------------------------------------------------------- Gram pass, fp32 operands on the matrix cores
 
-constexpr int kSubRows = 1024;  // rows of every operand staged in LDS per step
+// An fp32 value widened to fp64 multiplies exactly (24 x 24 significant bits
+// fit fp64's 53), and v_mfma_f64_16x16x4_f64 accumulates in fp64, so the
+// matrix cores give the Gram block the accuracy of fp64 fused multiply-adds
+// on exact products, with a handful of accumulator registers and no LDS
+// staging: every lane loads 16 bytes (4 rows of one operand) per 16-row
+// chunk, so many loads stay in flight.  Lane l, output register r holds
+// D[l % 16][4 r + l / 16] (measured on gfx950).  Blocks of NB < 16 operands
+// pack 16 / NB row sets into the 16 operand lanes: lane l carries operand
+// (l % 16) % NB of row set (l % 16) / NB, and the Gram matrix is the sum of
+// the diagonal NB x NB blocks of D.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kF64Unroll = 8;  // 16-row chunks per wave per iteration
+constexpr int kGramWaves = kBlock / 64;
 
-// Loads 8 consecutive elements starting at `row` (a multiple of kGroup) as
-// floats; elements outside [lo, hi) and every element of a NULL operand
-// read as zero.
-template <typename T>
-__device__ __forceinline__ void load_group(const T* __restrict__ x, int64_t row, int64_t lo, int64_t hi,
-                                           float (&v)[kGroup]) {
-  if (x != nullptr && row >= lo && row + kGroup <= hi) {
-    Elem<T>::load8(x + row, v);
-    return;
-  }
+// Four consecutive fp32 values at rows [row, row + 4) of x, zero outside [lo, hi).
+__device__ __forceinline__ v4f load_f32x4(const float* __restrict__ x, int64_t row, int64_t lo, int64_t hi) {
+  if (row >= lo && row + 4 <= hi) return gload(reinterpret_cast<const v4f*>(x + row));
+  float w[4];
 #pragma unroll
-  for (int e = 0; e < kGroup; ++e) {
-    const int64_t i = row + e;
-    v[e] = (x != nullptr && i >= lo && i < hi) ? Elem<T>::load1(x + i) : 0.f;
-  }
+  for (int e = 0; e < 4; ++e) w[e] = (row + e >= lo && row + e < hi) ? gload(x + row + e) : 0.f;
+  return v4f{w[0], w[1], w[2], w[3]};
 }
 
-// Workgroup roles (one per wave64): wave 0 accumulates the Gram block of
-// operands [0, H) with themselves, wave 1 that of [H, 2H), waves 2 and 3
-// the cross block [0, H) x [H, 2H), on alternate 64-row strips.  Per row
-// that is H(H+1)/2, H(H+1)/2, H*H/2, H*H/2 fused multiply-adds, so the four
-// waves carry nearly equal work, and the code inside each wave is uniform.
-template <typename T, int NB>
-__global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
-  constexpr int H = NB / 2;
-  constexpr int NAA = H * (H + 1) / 2;
-  constexpr int NAB = H * H;
+template <int NB>
+__global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
+  constexpr int SETS = 16 / NB;          // row sets packed into the 16 operand lanes
+  constexpr int U = kF64Unroll;
+  constexpr int RC = 16 * SETS;          // rows per chunk
+  constexpr int R = RC * U;              // rows per wave per iteration
   constexpr int NE = gram_entries(NB);
-  constexpr int S = kSubRows;
-  constexpr int RG = S / kGroup;              // row groups per operand per step
-  constexpr int GPT = NB * RG / kBlock;       // row groups each thread stages
-  static_assert(GPT * kBlock == NB * RG, "staging must divide evenly");
-  static_assert(RG % 64 == 0, "a wave must stage rows of a single operand");
-  __shared__ __align__(16) float stage[NB * S];  // operand-major: stage[k * S + r]
+  static_assert(NB * SETS == 16, "NB divides 16");
+  __shared__ double red[kGramWaves][64 * 4];
 
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
   const int64_t lo = tile.start, hi = tile.start + tile.len;
   const int64_t first = lo & ~int64_t(kGroup - 1);
-  const int nsteps = (int)((hi - first + S - 1) / S);
-  const int tid = threadIdx.x;
-  const int role = tid >> 6;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = (lane & 15) % NB, set = (lane & 15) / NB, grp = lane >> 4;
 
-  double acc[NAB];
-#pragma unroll
-  for (int e = 0; e < NAB; ++e) acc[e] = 0.0;
+  // a NULL operand (beyond the block's count) reads operand 0, masked to zero
+  const void* mine = args.x[j][op];
+  const bool live = mine != nullptr;
+  const float* xp = static_cast<const float*>(live ? mine : args.x[j][0]);
+  const int64_t lane_row = (int64_t)set * 16 + 4 * grp;  // first row of this lane in a chunk
 
-  // Operand k of row group q: a wave's 64 lanes share one operand (RG is a
-  // multiple of 64), so k is wave-uniform and the pointer is read straight
-  // from the argument table.  A step that lies inside [lo, hi) for every
-  // operand loads unconditionally, so all of a thread's loads are in flight
-  // together; edge steps and absent operands take the guarded path.
-  bool any_null = false;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  const int64_t niter = (hi - first + R - 1) / R;
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+    const int64_t r0 = first + it * R;
+    v4f v[U];
+    if (r0 >= lo && r0 + R <= hi) {
 #pragma unroll
-  for (int k = 0; k < NB; ++k) any_null |= (args.x[j][k] == nullptr);
-  float pre[GPT][kGroup];
-  auto fetch = [&](int step) {
-    const int64_t r0 = first + (int64_t)step * S;
-    if (!any_null && r0 >= lo && r0 + S <= hi) {
-#pragma unroll
-      for (int g = 0; g < GPT; ++g) {
-        const int q = tid + g * kBlock;
-        const int k = __builtin_amdgcn_readfirstlane(q / RG);
-        Elem<T>::load8(static_cast<const T*>(args.x[j][k]) + r0 + (int64_t)(q % RG) * kGroup, pre[g]);
-      }
+      for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4f*>(xp + r0 + u * RC + lane_row));
     } else {
 #pragma unroll
-      for (int g = 0; g < GPT; ++g) {
-        const int q = tid + g * kBlock;
-        const int k = __builtin_amdgcn_readfirstlane(q / RG);
-        load_group<T>(static_cast<const T*>(args.x[j][k]), r0 + (int64_t)(q % RG) * kGroup, lo, hi, pre[g]);
-      }
+      for (int u = 0; u < U; ++u) v[u] = load_f32x4(xp, r0 + u * RC + lane_row, lo, hi);
     }
-  };
-
-  fetch(0);
-  for (int step = 0; step < nsteps; ++step) {
-    if (step > 0) __syncthreads();  // every wave is done reading the previous step
 #pragma unroll
-    for (int g = 0; g < GPT; ++g) {
-      const int q = tid + g * kBlock;
-      float* dst = &stage[(q / RG) * S + (q % RG) * kGroup];
-      *reinterpret_cast<float4*>(dst) = make_float4(pre[g][0], pre[g][1], pre[g][2], pre[g][3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(pre[g][4], pre[g][5], pre[g][6], pre[g][7]);
-    }
-    __syncthreads();
-    if (step + 1 < nsteps) fetch(step + 1);  // in flight while this step is accumulated
-    const int64_t r0 = first + (int64_t)step * S;
-    const int nrows = (int)(hi - r0 < S ? hi - r0 : S);
-    if (role < 2) {
-      const float* base = stage + role * H * S;
-      for (int r = lane; r < nrows; r += 64) {
-        double v[H];
-#pragma unroll
-        for (int i = 0; i < H; ++i) v[i] = (double)base[i * S + r];
-#pragma unroll
-        for (int i = 0; i < H; ++i)
-#pragma unroll
-          for (int k = i; k < H; ++k) acc[gram_index(H, i, k)] = fma(v[i], v[k], acc[gram_index(H, i, k)]);
-      }
-    } else {
-      for (int r = (role - 2) * 64 + lane; r < nrows; r += 128) {
-        double a[H], b[H];
-#pragma unroll
-        for (int i = 0; i < H; ++i) {
-          a[i] = (double)stage[i * S + r];
-          b[i] = (double)stage[(H + i) * S + r];
-        }
-#pragma unroll
-        for (int i = 0; i < H; ++i)
-#pragma unroll
-          for (int k = 0; k < H; ++k) acc[i * H + k] = fma(a[i], b[k], acc[i * H + k]);
-      }
+    for (int u = 0; u < U; ++u) {
+      if (!live) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].x, (double)v[u].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].y, (double)v[u].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].z, (double)v[u].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].w, (double)v[u].w, acc, 0, 0, 0);
     }
   }
-  __syncthreads();
 
-  // Reduce every accumulator over its lanes through LDS, in lane order.
-  // Rows of a lane are padded by one entry so that neither the writes (one
-  // row per lane) nor the reads (one column per thread) pile onto one bank.
-  double* red = reinterpret_cast<double*>(stage);
+  // Sum the four waves' matrices (and the row sets' diagonal blocks) in a
+  // fixed order; write the packed triangle.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
+  __syncthreads();
   double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
-  constexpr int PAB = NAB + 1, PAA = NAA + 1;
-  static_assert(64 * PAB * sizeof(double) <= NB * S * sizeof(float), "reduction must fit the stage buffer");
-  static_assert(2 * 64 * PAA * sizeof(double) <= NB * S * sizeof(float), "reduction must fit the stage buffer");
-  if (role == 2) {
-#pragma unroll
-    for (int e = 0; e < NAB; ++e) red[lane * PAB + e] = acc[e];
-  }
-  __syncthreads();
-  if (role == 3) {  // wave 3 adds its strips after wave 2's, lane by lane
-#pragma unroll
-    for (int e = 0; e < NAB; ++e) red[lane * PAB + e] += acc[e];
-  }
-  __syncthreads();
-  if (tid < NAB) {
-    double sum = 0.0;
-    for (int l = 0; l < 64; ++l) sum += red[l * PAB + tid];
-    out[gram_index(NB, tid / H, H + tid % H)] = sum;
-  }
-  __syncthreads();
-  if (role < 2) {
-#pragma unroll
-    for (int e = 0; e < NAA; ++e) red[(role * 64 + lane) * PAA + e] = acc[e];
-  }
-  __syncthreads();
-  if ((tid & 63) < NAA && tid < 128) {
-    const int w = tid >> 6, e = tid & 63;
-    double sum = 0.0;
-    for (int l = 0; l < 64; ++l) sum += red[(w * 64 + l) * PAA + e];
-    // packed index e of the H x H triangle -> (i, k)
+  for (int e = threadIdx.x; e < NE; e += kBlock) {
     int i = 0, rem = e;
-    while (rem >= H - i) {
-      rem -= H - i;
+    while (rem >= NB - i) {
+      rem -= NB - i;
       ++i;
     }
-    out[gram_index(NB, w * H + i, w * H + i + rem)] = sum;
+    const int k = i + rem;  // entry (i, k), i <= k
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGramWaves; ++w)
+#pragma unroll
+      for (int q = 0; q < SETS; ++q) {
+        const int m = q * NB + i, n = q * NB + k;  // D[m][n]: lane m + 16 (n % 4), register n / 4
+        sum += red[w][(m + 16 * (n & 3)) * 4 + (n >> 2)];
+      }
+    out[e] = sum;
   }
 }
 
@@ -393,7 +324,6 @@ __global__ __launch_bounds__(kBlock, 2) void gram_kernel(GramArgs args) {
 // so each entry is off by at most 2^-24 of the sum of |a_i b_i| over each
 // 32-row chunk.
 constexpr int kMfmaUnroll = 8;    // 32-row chunks per wave per iteration
-constexpr int kGramWaves = kBlock / 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -956,15 +886,14 @@ struct RunSum {
   }
 };
 
-template <typename T>
-struct RunGram {
+struct RunGramF64 {
   static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
     const dim3 grid(ntiles, njobs);
     switch (nbt) {
-      case 2: hipLaunchKernelGGL((gram_kernel<T, 2>), grid, dim3(kBlock), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((gram_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((gram_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((gram_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((gram_f64mfma_kernel<2>), grid, dim3(kBlock), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((gram_f64mfma_kernel<4>), grid, dim3(kBlock), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16>), grid, dim3(kBlock), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1023,7 +952,7 @@ struct RunWsum {
 
 hipError_t launch_gram(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
   switch (operand) {
-    case DType::F32: return RunGram<float>::run(nbt, a, ntiles, njobs, st);
+    case DType::F32: return RunGramF64::run(nbt, a, ntiles, njobs, st);
     case DType::F16: return RunGramMfma<_Float16>::run(nbt, a, ntiles, njobs, st);
     case DType::BF16: return RunGramMfma<bf16_t>::run(nbt, a, ntiles, njobs, st);
   }
