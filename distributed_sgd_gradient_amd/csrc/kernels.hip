@@ -219,7 +219,7 @@ __device__ __forceinline__ TileSpan span_of(const Tile& t) {
 // (l % 16) % NB of row set (l % 16) / NB, and the Gram matrix is the sum of
 // the diagonal NB x NB blocks of D.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-constexpr int kF64Unroll = 8;  // 16-row chunks per wave per iteration
+constexpr int kF64Unroll = 16; // 16-row chunks per wave per iteration
 constexpr int kGramWaves = kBlock / 64;
 
 // Four consecutive fp32 values at rows [row, row + 4) of x, zero outside [lo, hi).
