@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
 // 1 + 31 * 2^-24 comes out as the nearest fp32 value wherever the 1 sits),
 // so each entry is off by at most 2^-24 of the sum of |a_i b_i| over each
 // 32-row chunk.
-constexpr int kMfmaUnroll = 8;    // 32-row chunks per wave per iteration
+constexpr int kMfmaUnroll = 16;   // 32-row chunks per wave per iteration
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
