@@ -25,7 +25,7 @@ CSRC = os.path.join(ROOT, "distributed_sgd_gradient_amd", "csrc")
 
 
 @pytest.fixture(scope="module")
-def plans(tmp_path_factory):
+def plan_exe(tmp_path_factory):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("g++ not available")
@@ -33,7 +33,12 @@ def plans(tmp_path_factory):
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", CSRC, os.path.join(ROOT, "tests", "plan_dump.cpp"), os.path.join(CSRC, "plan.cpp"), "-o", exe]
     subprocess.run(cmd, check=True, capture_output=True)
-    out = subprocess.run([exe], check=True, capture_output=True, text=True,
+    return exe
+
+
+@pytest.fixture(scope="module")
+def plans(plan_exe):
+    out = subprocess.run([plan_exe], check=True, capture_output=True, text=True,
                          env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1")).stdout
     return [json.loads(line) for line in out.splitlines()]
 
@@ -122,3 +127,74 @@ def test_tiles_cover_segments_exactly(plans):
         assert np.all(tiles[1:, 0] == tiles[:-1, 0] + tiles[:-1, 1])   # contiguous
         for start, length, seg in tiles:
             assert off[seg] <= start and start + length <= off[seg + 1]   # inside one segment
+
+
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(n):
+        K = int(rng.choice([rng.integers(1, 40), rng.integers(40, 301)]))
+        nseg = int(rng.integers(0, 30))
+        kind = rng.integers(0, 3)
+        if kind == 0:      # small and empty segments
+            lengths = rng.integers(0, 50, size=nseg)
+        elif kind == 1:    # ragged, spanning several tiles
+            lengths = rng.integers(0, 200000, size=nseg)
+        else:              # log-uniform, some empty
+            lengths = np.floor(np.exp(rng.uniform(0, np.log(3e5), size=nseg))).astype(np.int64)
+            lengths[rng.random(nseg) < 0.1] = 0
+        shapes.append((K, int(rng.integers(0, 2)), int(rng.integers(0, 2)), np.concatenate([[0], np.cumsum(lengths)])))
+    return shapes
+
+
+def test_random_shapes_tiles_tree_and_workspace(plan_exe):
+    """Seeded random shapes (K up to 300, empty and ragged segments, both
+    dtypes and schedules): tiles partition every segment with aligned bodies,
+    the tree is the oracle's, blocks respect their size limits, and the
+    workspace regions are disjoint, ordered and 256-byte aligned."""
+    shapes = _random_shapes(400, 2024)
+    text = "\n".join(f"{K} {dt} {sc} {len(off) - 1} " + " ".join(str(int(x)) for x in off[1:])
+                     for K, dt, sc, off in shapes) + "\n"
+    out = subprocess.run([plan_exe, "--stdin"], input=text, check=True, capture_output=True, text=True,
+                         env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1")).stdout.splitlines()
+    assert len(out) == len(shapes)
+    for (K, dt, sc, off), line in zip(shapes, out):
+        P = json.loads(line)
+        assert "error" not in P, (K, P)
+        N, nseg, T = int(off[-1]), len(off) - 1, P["tile_rows"]
+        tiles = P["tiles"]
+        # tiles: in order, contiguous, inside their segment, bodies 8-aligned, bounded length
+        pos = 0
+        for t, (start, length, seg) in enumerate(tiles):
+            assert start == pos and length >= 1 and off[seg] <= start and start + length <= off[seg + 1]
+            first_of_seg = start == off[seg]
+            assert first_of_seg or start % 8 == 0
+            body = -(-start // 8) * 8 if first_of_seg else start
+            assert start + length <= body + T
+            pos += length
+        assert pos == N
+        st = P["seg_tile"]
+        assert len(st) == nseg + 1 and st[0] == 0 and st[-1] == len(tiles)
+        for s in range(nseg):
+            assert all(tiles[t][2] == s for t in range(st[s], st[s + 1]))
+            assert (st[s + 1] > st[s]) == (off[s + 1] > off[s])
+        # the tree (or chain) is the oracle's, with the block size limits
+        assert plan_nodes(P) == oracle_nodes(K, sc), (K, dt, sc)
+        for si, stg in enumerate(P["stages"]):
+            regions = []
+            for b in stg["blocks"]:
+                big = si == 0 and dt == 1 and K <= 32
+                assert b["nb"] <= (32 if big else 16) and b["nbt"] in (2, 4, 8, 16, 32) and b["nbt"] >= b["nb"]
+                entries = b["nbt"] * (b["nbt"] + 1) // 2
+                assert 0 <= b["poff"] and b["poff"] + entries * len(tiles) <= P["partial_doubles"]
+                regions.append((b["poff"], b["poff"] + entries * len(tiles)))
+            regions.sort()
+            assert all(regions[i][1] <= regions[i + 1][0] for i in range(len(regions) - 1))  # a stage's partials disjoint
+        # workspace regions: ordered, 256-aligned, each large enough
+        ws = P["ws"]
+        assert all(x % 256 == 0 for x in ws) and ws == sorted(ws)
+        nodes = max(K - 1, 0)
+        sizes = [P["nslots"] * N * 4, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
+                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8]
+        for r, size in enumerate(sizes):
+            assert ws[r] + size <= ws[r + 1], (K, r)
