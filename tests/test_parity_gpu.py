@@ -488,3 +488,29 @@ def test_prepared_combiner_matches_combine(gpu):
         assert torch.equal(out, ref)
         assert torch.equal(comb.coeffs, coeffs)
         assert torch.equal(torch.nan_to_num(comb.ortho, nan=-1.0), torch.nan_to_num(ortho, nan=-1.0))
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_shapes(gpu, case):
+    """Seeded random shapes: K, dtype, schedule and ragged segment lengths
+    (empty and length-1 segments included) against the oracle."""
+    A = _A()
+    rng = np.random.default_rng(4000 + case)
+    K = int(rng.integers(1, 49))
+    dtype = ["f32", "f16", "bf16"][case % 3]
+    schedule = "chain" if case % 4 == 3 else "tree"
+    nseg = int(rng.integers(1, 12))
+    lengths = [int(x) for x in np.floor(np.exp(rng.uniform(0, np.log(60000), size=nseg)))]
+    lengths[int(rng.integers(0, nseg))] = 0
+    wl = W.random_case(K, lengths, dtype=dtype, seed=4000 + case, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    say(f"random case {case}: K={K} {dtype} {schedule} lengths={lengths}")
+    out, coeffs, stats = A.combine(grads, wl.seg_offsets, schedule=schedule, return_coeffs=True, return_stats=True)
+    torch.cuda.synchronize()
+    host = [g.double().numpy() for g in wl.grads]
+    run = oracle.combine if schedule == "tree" else oracle.combine_chain
+    ref = run(host, wl.seg_offsets, out_format=dtype)
+    err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
+    assert err <= TOL[dtype], f"random case {case}: relative L2 {err:.3g}"
+    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], f"random case {case}")
+    check_stats(stats.cpu().numpy(), ref["stats"], f"random case {case}")
