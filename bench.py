@@ -64,7 +64,8 @@ def cpu_baseline(wl, budget_s):
 
     import oracle
 
-    order = list(range(5, wl.nseg)) + list(range(0, 5))  # encoder layers first, embeddings last
+    first = min(5, wl.nseg)  # encoder layers first, the (large) embedding segments last
+    order = list(range(first, wl.nseg)) + list(range(0, first))
     used, elems, spent = [], 0, 0.0
     with threadpool_limits(limits=1):
         for s in order:
