@@ -9,10 +9,10 @@
 // operands and five levels for 16-bit inputs that fit one block) is
 // therefore combined in three launches:
 //   gram  - one pass over the operands: per tile, the Gram matrix (packed
-//           upper triangle), fp64 products and sums on the VALU for fp32
-//           operands, 32-row sums of exact products on the matrix cores
-//           added in fp64 for 16-bit operands; reduced across the
-//           workgroup in a fixed order;
+//           upper triangle) on the matrix cores: fp64 instructions on the
+//           widened values (exact products, fp64 sums) for fp32 operands,
+//           32-row sums of exact products added in fp64 for 16-bit
+//           operands; reduced across the workgroup in a fixed order;
 //   tree  - per segment: the tile partials summed in tile order, then the
 //           block's merges evaluated on the Gram matrix level by level:
 //           d = wL.G.wR, A = wL.G.wL, B = wR.G.wR, ca = 1 - d/(2A),
@@ -828,14 +828,66 @@ __device__ __forceinline__ void sum_group(const SumArgs& a, int64_t g, int cnt) 
   }
 }
 
+// A whole group of kGroup elements.  The operands go in batches of
+// kSumBatch whose loads are all in flight together; an operand index past the
+// count loads the batch's first operand again (a cache hit) and its term is
+// dropped by a select, not added as zero, so the sum, its operand order and
+// the sign of a zero result are those of the serial loop above.
+constexpr int kSumBatch = 16;
+
+template <typename T>
+__device__ __forceinline__ void sum_full_group(const SumArgs& a, int64_t g) {
+  const bool from_acc = a.acc_in != nullptr;
+  double acc[kGroup];
+#pragma unroll
+  for (int e = 0; e < kGroup; ++e) acc[e] = from_acc ? a.acc_in[g + e] : 0.0;
+  for (int kb = 0; kb < a.nx; kb += kSumBatch) {
+    typename Elem<T>::Raw8 raw[kSumBatch];
+#pragma unroll
+    for (int i = 0; i < kSumBatch; ++i) {
+      const int k = kb + i < a.nx ? kb + i : kb;
+      raw[i] = Elem<T>::load_raw8(static_cast<const T*>(a.x[k]) + g);
+    }
+    // keep the whole batch's loads ahead of its first add (the operand
+    // pointers come from runtime-indexed argument loads, and the scheduler
+    // would otherwise interleave them with the adds, two operands deep)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kSumBatch; ++i) {
+      float v[kGroup];
+      Elem<T>::unpack8(raw[i], v);
+      const bool live = kb + i < a.nx;
+      const bool first = !from_acc && kb + i == 0;  // the sum starts from the first operand itself
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) {
+        const double s = first ? (double)v[e] : add_rn(acc[e], (double)v[e]);
+        acc[e] = live ? s : acc[e];
+      }
+    }
+  }
+  if (a.acc_out != nullptr) {
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) a.acc_out[g + e] = acc[e];
+  } else {
+    T r[kGroup];
+    double unused;
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) r[e] = Elem<T>::round(acc[e], &unused);
+    Elem<T>::store8(static_cast<T*>(a.out) + g, r);
+  }
+}
+
 // Grid-stride over groups of kGroup elements; the last group may be short.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void sum_kernel(SumArgs a) {
+  const int64_t full = a.n / kGroup;
   const int64_t ngroups = (a.n + kGroup - 1) / kGroup;
   for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < ngroups; q += (int64_t)gridDim.x * kBlock) {
     const int64_t g = q * kGroup;
-    const int cnt = (int)(a.n - g < kGroup ? a.n - g : kGroup);
-    sum_group<T>(a, g, cnt);
+    if (q < full)
+      sum_full_group<T>(a, g);
+    else
+      sum_group<T>(a, g, (int)(a.n - g));
   }
 }
 

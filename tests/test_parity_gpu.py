@@ -366,6 +366,30 @@ def test_plain_sum_bit_exact(gpu, K, dtype):
     assert np.array_equal(got, ref), f"max |diff| {np.max(np.abs(got - ref))}"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [1, 2, 17, 64, 65])
+def test_plain_sum_signed_zeros(gpu, K, dtype):
+    # a sum of -0 terms is -0 and a mix of -0 and +0 is +0 (IEEE round to
+    # nearest), for every operand count: one launch, one batch and a partial
+    # one, a full launch, and a second launch continuing from fp64 partials
+    A = _A()
+    rng = np.random.default_rng(90 + K)
+    base = rng.standard_normal((K, 4099)).astype(np.float32)
+    base[:, :1000] = -0.0
+    base[:, 1000:2000] = 0.0
+    base[0, 1000:2000] = -0.0
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    grads = [torch.from_numpy(base[k].copy()).to(tdt) for k in range(K)]
+    say(f"plain sum signed zeros K={K} {dtype}")
+    out = A.plain_sum([g.to(gpu) for g in grads])
+    torch.cuda.synchronize()
+    ref = oracle.plain_sum([g.double().numpy() for g in grads], out_format=dtype)["out_rounded"]
+    got = out.double().cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    assert np.all(np.signbit(got[:1000])) and (K == 1 or not np.any(np.signbit(got[1000:2000])))
+
+
 def test_single_worker_is_exact_copy(gpu):
     A = _A()
     for dtype in ("f32", "f16", "bf16"):
