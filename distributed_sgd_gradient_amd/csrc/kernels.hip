@@ -705,8 +705,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 // flight at once.
 template <typename TIn, int NB, typename TOut>
 __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
-  const int tile_id = blockIdx.x / kWsumSplit;
-  const int part = blockIdx.x % kWsumSplit;
+  constexpr int kSplit = wsum_split(sizeof(TIn));
+  const int tile_id = blockIdx.x / kSplit;
+  const int part = blockIdx.x % kSplit;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
   TileSpan sp = span_of(tile);
@@ -714,11 +715,11 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
     // part p takes the p-th share of the aligned body; the unaligned head
     // goes with part 0 and the tail with the last part
     const int64_t groups = (sp.body_hi - sp.body_lo) / kGroup;
-    const int64_t per = (groups + kWsumSplit - 1) / kWsumSplit * kGroup;
+    const int64_t per = (groups + kSplit - 1) / kSplit * kGroup;
     const int64_t b0 = min(sp.body_lo + part * per, sp.body_hi);
     const int64_t b1 = min(b0 + per, sp.body_hi);
     if (part > 0) sp.lo = b0;
-    if (part < kWsumSplit - 1) sp.hi = b1;
+    if (part < kSplit - 1) sp.hi = b1;
     sp.body_lo = b0;
     sp.body_hi = b1;
   }
@@ -970,7 +971,7 @@ struct RunGramMfma {
 
 template <typename TIn, typename TOut>
 hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
-  const dim3 grid((unsigned)ntiles * kWsumSplit, njobs);
+  const dim3 grid((unsigned)ntiles * wsum_split(sizeof(TIn)), njobs);
   switch (nbt) {
     case 2: hipLaunchKernelGGL((wsum_kernel<TIn, 2, TOut>), grid, dim3(kBlock), 0, st, a); break;
     case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut>), grid, dim3(kBlock), 0, st, a); break;

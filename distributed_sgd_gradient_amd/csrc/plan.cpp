@@ -63,7 +63,7 @@ bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, int sche
   }
   // tile count (times the weighted sum's parts per tile) must fit a launch
   // grid and the kernels' 32-bit tile indices
-  if ((offsets[nseg] / kMinTile + nseg + 1) * kWsumSplit > int64_t(INT32_MAX)) {
+  if ((offsets[nseg] / kMinTile + nseg + 1) * kWsumSplitMax > int64_t(INT32_MAX)) {
     *err = "too many tiles for this shape";
     return false;
   }

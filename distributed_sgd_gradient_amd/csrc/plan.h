@@ -36,10 +36,13 @@ constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
 constexpr int kMaxOps = 32;      // operands per block over 16-bit inputs: five tree levels
 constexpr int kMaxOps32 = 16;    // operands per block over fp32 operands: four tree levels
 constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
-// The weighted sum cuts every tile into kWsumSplit aligned parts, one
-// workgroup each: it streams best with shorter per-workgroup ranges than
-// the Gram pass, whose per-tile reduction favours long tiles.
-constexpr int kWsumSplit = 4;
+// The weighted sum cuts every tile into aligned parts, one workgroup each,
+// so that a workgroup's range holds 16 KB of every operand of a full tile:
+// 8 parts for fp32 inputs, 4 for 16-bit ones.  It streams best with shorter
+// per-workgroup ranges than the Gram pass, whose per-tile reduction favours
+// long tiles.
+constexpr int wsum_split(int elem_bytes) { return elem_bytes == 4 ? 8 : 4; }
+constexpr int kWsumSplitMax = 8;
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 
