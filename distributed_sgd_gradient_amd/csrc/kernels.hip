@@ -501,10 +501,43 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
           m = max(m, (uint32_t)__shfl_xor((int)m, 16));
           m = max(m, (uint32_t)__shfl_xor((int)m, 32));
           sc[h] = kScaleTop - (int)(m == 0 ? 1 : m);  // all-zero or subnormal operand: exponent 1
+        }
+        // entry (row, col) of sub-block (h1, h2): row operand 4 grp + r of
+        // half h1 (its scale from the lane that holds it), column operand op
+        // of half h2 (this lane's own)
+        int back[NP][4];
+        {
+          int q = 0;
 #pragma unroll
-          for (int u = 0; u < U; ++u)
-            v[h][u] = v4u{bf16x2_scale(v[h][u].x, sc[h]), bf16x2_scale(v[h][u].y, sc[h]),
-                          bf16x2_scale(v[h][u].z, sc[h]), bf16x2_scale(v[h][u].w, sc[h])};
+          for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+            for (int h2 = h1; h2 < NH; ++h2, ++q)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) back[q][r] = -(__shfl(sc[h1], 4 * grp + r) + sc[h2]);
+        }
+        // one chunk at a time, read again (it was just read, so from cache):
+        // scale, multiply, accumulate scaled back.  The registers of the
+        // first read are free by now, which keeps this rare path from
+        // raising the kernel's register count.
+#pragma unroll 1
+        for (int u = 0; u < U; ++u) {
+          v4u c[NH];
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            const int64_t row = r0 + 32 * u + 8 * grp;
+            c[h] = live[h] ? load_raw_group(xp[h], row, lo, hi) : v4u{0u, 0u, 0u, 0u};
+            c[h] = v4u{bf16x2_scale(c[h].x, sc[h]), bf16x2_scale(c[h].y, sc[h]), bf16x2_scale(c[h].z, sc[h]),
+                       bf16x2_scale(c[h].w, sc[h])};
+          }
+          int q = 0;
+#pragma unroll
+          for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+            for (int h2 = h1; h2 < NH; ++h2, ++q) {
+              const f32x4 d = Mfma<T>::gram(c[h1], c[h2]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[q][r] += __builtin_amdgcn_ldexp((double)d[r], back[q][r]);
+            }
         }
       }
     }
@@ -521,25 +554,6 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
             for (int r = 0; r < 4; ++r) acc[q][r] += (double)d[r];
           }
       }
-    } else {
-      // entry (row, col) of sub-block (h1, h2): row operand 4 grp + r of
-      // half h1 (its scale from the lane that holds it), column operand op
-      // of half h2 (this lane's own)
-      int q = 0;
-#pragma unroll
-      for (int h1 = 0; h1 < NH; ++h1)
-#pragma unroll
-        for (int h2 = h1; h2 < NH; ++h2, ++q) {
-          int back[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) back[r] = -(__shfl(sc[h1], 4 * grp + r) + sc[h2]);
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const f32x4 d = Mfma<T>::gram(v[h1][u], v[h2][u]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[q][r] += __builtin_amdgcn_ldexp((double)d[r], back[r]);
-          }
-        }
     }
   }
 
