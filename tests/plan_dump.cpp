@@ -1,5 +1,5 @@
 // Prints execution plans as JSON lines for tests/test_plan_host.py: with no
-// argument, K = 1..70 and a few larger K, both schedules, fp32 and fp16
+// argument, K = 1..70 and a few larger K, both schedules, fp32, fp16 and bf16
 // inputs, over two fixed segments; with --stdin, one plan per input line
 // "K dtype schedule nseg off_1 .. off_nseg".  Built with g++ on the host together
 // with the library's plan.cpp (pure C++, no HIP).
@@ -26,8 +26,8 @@ static void dump(const Plan& p, int dt, int sched, int K) {
       printf("%s{\"ops\": [", b ? "," : "");
       for (size_t k = 0; k < bk.operands.size(); ++k)
         printf("%s[%d,%d]", k ? "," : "", (int)bk.operands[k].kind, bk.operands[k].idx);
-      printf("], \"dst\": [%d,%d], \"nb\": %d, \"nbt\": %d, \"leafmask\": %u, \"root\": %d, \"poff\": %lld, "
-             "\"merges\": [", (int)bk.dst.kind, bk.dst.idx, d.nb, d.nbt, d.leafmask, (int)d.root, (long long)d.poff);
+      printf("], \"dst\": [%d,%d], \"nb\": %d, \"nbt\": %d, \"leafmask\": %llu, \"root\": %d, \"poff\": %lld, "
+             "\"merges\": [", (int)bk.dst.kind, bk.dst.idx, d.nb, d.nbt, (unsigned long long)d.leafmask, (int)d.root, (long long)d.poff);
       for (int m = 0; m < d.nmerges; ++m) {
         const Merge& mg = p.merges[d.merge0 + m];
         printf("%s[%d,%d,%d,%d]", m ? "," : "", mg.llo, mg.lhi, mg.rhi, mg.node);
@@ -66,9 +66,9 @@ int main(int argc, char** argv) {
   std::vector<int> Ks;
   for (int K = 1; K <= 70; ++K) Ks.push_back(K);
   for (int K : {96, 127, 128, 129, 200, 255, 256, 257, 300}) Ks.push_back(K);
-  for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 3; ++dt)
     for (int sched = 0; sched < 2; ++sched)
       for (int K : Ks)
-        dump(build_plan(K, off, 2, dt ? DType::F16 : DType::F32, static_cast<Schedule>(sched)), dt, sched, K);
+        dump(build_plan(K, off, 2, static_cast<DType>(dt), static_cast<Schedule>(sched)), dt, sched, K);
   return 0;
 }

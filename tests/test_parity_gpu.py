@@ -161,10 +161,11 @@ def test_small_K_ragged_segments(gpu, K, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 64, 70, 130])
+@pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 48, 63, 64, 65, 70, 130])
 def test_multistage_K(gpu, K, dtype):
-    # more than 16 operands: blocks of 16 (fp32) or 32 (16-bit inputs), fp32
-    # block results, carried inputs; K = 130 has stage positions beyond 127
+    # more than 16 operands: one block of 32 (at most 32 16-bit inputs), else
+    # blocks of 16 with fp32 block results and carried inputs; K = 130 has
+    # stage positions beyond 127
     wl = W.random_case(K, [1, 300, 9, 40000, 8], dtype=dtype, seed=100 + K, kind="shared")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"multistage K={K} {dtype}")

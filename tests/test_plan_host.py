@@ -62,6 +62,12 @@ def oracle_nodes(K, schedule):
     return nodes
 
 
+def block_limit(stage, dtype, K):
+    """Largest block the planner may form: 16 operands, except the single
+    stage over at most 32 16-bit inputs (32)."""
+    return 32 if (stage == 0 and dtype != 0 and K <= 32) else 16
+
+
 def plan_nodes(P):
     """Reconstruct the leaf range of every merge the plan evaluates."""
     slot_range = {}
@@ -73,7 +79,7 @@ def plan_nodes(P):
             if si > 0:
                 assert all(kind == 1 for kind, _ in b["ops"]), "stage operands above the first must be fp32 slots"
             rng = [(i, i + 1) if kind == 0 else slot_range[i] for kind, i in b["ops"]]
-            limit = 32 if (si == 0 and P["dtype"] == 1 and P["K"] <= 32) else 16
+            limit = block_limit(si, P["dtype"], P["K"])
             assert len(rng) == b["nb"] <= limit and b["nbt"] >= b["nb"]
             for i in range(len(rng) - 1):
                 assert rng[i][1] == rng[i + 1][0], "block operands must be adjacent leaf ranges"
@@ -94,7 +100,7 @@ def plan_nodes(P):
     return got
 
 
-@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("dtype", [0, 1, 2])
 @pytest.mark.parametrize("schedule", [0, 1])
 def test_plan_nodes_match_oracle(plans, schedule, dtype):
     checked = 0
@@ -109,14 +115,22 @@ def test_plan_nodes_match_oracle(plans, schedule, dtype):
 
 
 def test_16bit_blocks_are_larger(plans):
-    """With 16-bit inputs up to 32 gradients finish in one stage; more use 16-operand blocks."""
+    """Up to 32 16-bit inputs (fp16 or bf16) finish in one stage of one
+    32-operand block; beyond that the first stage uses 16-operand blocks."""
+    seen = set()
     for P in plans:
-        if P["schedule"] == 0 and P["K"] in (17, 32, 33, 64):
+        if P["schedule"] == 0 and P["K"] in (17, 32, 33, 64, 65):
+            K, dt = P["K"], P["dtype"]
+            one = dt != 0 and K <= 32
             nstages = len(P["stages"])
-            one = P["dtype"] == 1 and P["K"] <= 32
-            assert nstages == (1 if one else 2), (P["K"], P["dtype"], nstages)
-            if P["K"] == 64:
-                assert all(b["nb"] == 16 for b in P["stages"][0]["blocks"])
+            assert nstages == (1 if one else 2), (K, dt, nstages)
+            blocks = P["stages"][0]["blocks"]
+            if one:
+                assert len(blocks) == 1 and blocks[0]["nb"] == K and blocks[0]["nbt"] == 32
+            else:
+                assert all(b["nb"] <= 16 for b in blocks)
+            seen.add((K, dt))
+    assert len(seen) == 15
 
 
 def test_tiles_cover_segments_exactly(plans):
@@ -143,13 +157,13 @@ def _random_shapes(n, seed):
         else:              # log-uniform, some empty
             lengths = np.floor(np.exp(rng.uniform(0, np.log(3e5), size=nseg))).astype(np.int64)
             lengths[rng.random(nseg) < 0.1] = 0
-        shapes.append((K, int(rng.integers(0, 2)), int(rng.integers(0, 2)), np.concatenate([[0], np.cumsum(lengths)])))
+        shapes.append((K, int(rng.integers(0, 3)), int(rng.integers(0, 2)), np.concatenate([[0], np.cumsum(lengths)])))
     return shapes
 
 
 def test_random_shapes_tiles_tree_and_workspace(plan_exe):
-    """Seeded random shapes (K up to 300, empty and ragged segments, both
-    dtypes and schedules): tiles partition every segment with aligned bodies,
+    """Seeded random shapes (K up to 300, empty and ragged segments, all
+    three dtypes, both schedules): tiles partition every segment with aligned bodies,
     the tree is the oracle's, blocks respect their size limits, and the
     workspace regions are disjoint, ordered and 256-byte aligned."""
     shapes = _random_shapes(400, 2024)
@@ -183,8 +197,7 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         for si, stg in enumerate(P["stages"]):
             regions = []
             for b in stg["blocks"]:
-                big = si == 0 and dt == 1 and K <= 32
-                assert b["nb"] <= (32 if big else 16) and b["nbt"] in (2, 4, 8, 16, 32) and b["nbt"] >= b["nb"]
+                assert b["nb"] <= block_limit(si, dt, K) and b["nbt"] in (2, 4, 8, 16, 32) and b["nbt"] >= b["nb"]
                 entries = b["nbt"] * (b["nbt"] + 1) // 2
                 assert 0 <= b["poff"] and b["poff"] + entries * len(tiles) <= P["partial_doubles"]
                 regions.append((b["poff"], b["poff"] + entries * len(tiles)))
