@@ -144,3 +144,28 @@ def test_adasum_log_reports_the_plan():
     assert r.returncode == 0, r.stderr
     assert "[adasum] plan K=40 nseg=2 N=70000" in r.stderr
     assert "2 stages" in r.stderr and int(r.stdout.strip()) > 0
+
+
+def test_last_error_is_per_thread():
+    """The message of a failure belongs to the thread that made the call."""
+    import threading
+
+    lib = _native.lib()
+    arr, p = _off(0, 10, 5)
+    assert lib.adasum_workspace_bytes(2, p, 2, 0, 0) == _native.EINVAL
+    mine = lib.adasum_last_error().decode()
+    assert "non-decreasing" in mine
+    seen = {}
+
+    def other():
+        seen["fresh"] = lib.adasum_last_error().decode()
+        a2, p2 = _off(0, 8)
+        seen["rc"] = lib.adasum_workspace_bytes(0, p2, 1, 0, 0)
+        seen["own"] = lib.adasum_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["fresh"] == ""
+    assert seen["rc"] == _native.EINVAL and "K must be >= 1" in seen["own"]
+    assert lib.adasum_last_error().decode() == mine

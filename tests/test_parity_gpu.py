@@ -497,6 +497,49 @@ def test_host_pointers_rejected_before_any_launch(gpu):
     assert rel_l2(out.double().cpu().numpy(), ref) <= TOL["f32"]
 
 
+def test_concurrent_calls_from_threads(gpu):
+    """Four host threads, each on its own stream with its own shape and
+    dtype, call the library at the same time through both entry points (the
+    caller's workspace and the library's cached one); every result equals the
+    single-threaded result bit for bit."""
+    import threading
+
+    A = _A()
+    cases = [(5, "f32", [1000, 0, 70001]), (16, "f16", [4099, 12, 30000]), (24, "bf16", [77, 50000]),
+             (3, "f32", [8193, 8193, 8193])]
+    data = []
+    for i, (K, dt, lengths) in enumerate(cases):
+        wl = W.random_case(K, lengths, dtype=dt, seed=700 + i, kind="shared")
+        grads = [g.to(gpu) for g in wl.grads]
+        ref = A.combine(grads, wl.seg_offsets)
+        data.append((grads, wl.seg_offsets, ref))
+    torch.cuda.synchronize()
+    say("concurrent: 4 threads x 20 calls")
+    errors = []
+
+    def worker(i):
+        try:
+            grads, off, ref = data[i]
+            s = torch.cuda.Stream(device=gpu)
+            with torch.cuda.stream(s):
+                for r in range(20):
+                    out = A.combine(grads, off) if r % 2 == 0 else A.combine_cached(grads, off)
+                    s.synchronize()
+                    if not torch.equal(out, ref):
+                        errors.append((i, r, "differs"))
+                        return
+        except Exception as e:  # reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=90)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+
+
 def test_prepared_combiner_matches_combine(gpu):
     """Combiner marshals once; every call reads the buffers' current contents."""
     A = _A()
