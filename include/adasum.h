@@ -42,6 +42,15 @@
  *     dtype give the same bits on every call and on every stream.
  *   - Device base pointers (inputs, out, workspace) must be 16-byte aligned;
  *     segment boundaries inside the buffers may fall anywhere.
+ *   - Graph capture: the first call for a shape (K, offsets, dtype,
+ *     schedule) on a device uploads that shape's tables; adasum_combine's
+ *     first call on a stream, or for a larger shape, also allocates its
+ *     workspace.  A later call of that shape enqueues kernels only (no
+ *     allocation, copy, memset or synchronisation), so it may be captured
+ *     into a HIP graph, as long as the library still caches the shape (the
+ *     64 most recently used shapes; making room for a new shape waits for
+ *     the device).  Profiling (adasum_profile_begin) must be off while
+ *     capturing.
  */
 #ifndef ADASUM_H
 #define ADASUM_H

@@ -540,6 +540,37 @@ def test_concurrent_calls_from_threads(gpu):
     assert not errors, errors
 
 
+def test_graph_capture_and_replay(gpu):
+    """A prepared combine (plan and workspace made by an earlier call) is
+    captured in a graph; each of five replays, with the inputs changed in
+    place and eager work and synchronisations in between, equals the eager
+    combine of the same inputs bit for bit."""
+    A = _A()
+    wl = W.random_case(7, [1000, 0, 65537, 300], dtype="f32", seed=808, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    out = torch.empty_like(grads[0])
+    step = A.Combiner(grads, wl.seg_offsets, out=out)
+    side = torch.cuda.Stream(device=gpu)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(5):
+        for x in grads:
+            x.mul_(1.5 if r % 2 == 0 else -0.75)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = A.combine(grads, wl.seg_offsets)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
+
+
 def test_prepared_combiner_matches_combine(gpu):
     """Combiner marshals once; every call reads the buffers' current contents."""
     A = _A()
