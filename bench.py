@@ -55,10 +55,10 @@ def measured_traffic(workload, kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s):
-    """Time the fp64 oracle on whole segments copied from the GPU workload,
-    adding segments (largest-first order of the layer list) until the budget
-    is spent; one thread."""
+def cpu_baseline(wl, budget_s, schedule="tree"):
+    """Time the fp64 oracle (the same schedule as the GPU run) on whole
+    segments copied from the GPU workload, adding segments (largest-first
+    order of the layer list) until the budget is spent; one thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -71,7 +71,7 @@ def cpu_baseline(wl, budget_s):
         for s in order:
             rows = wl.segment_host(s)
             t0 = time.perf_counter()
-            oracle.adasum_tree(rows)
+            (oracle.adasum_chain if schedule == "chain" else oracle.adasum_tree)(rows)
             spent += time.perf_counter() - t0
             used.append(s)
             elems += rows[0].size
@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--schedule", choices=["tree", "chain"], default="tree",
+                    help="order of the pairwise combines: the tree (default) or the left-to-right chain")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
@@ -128,7 +130,7 @@ def main():
     wl = W.make_workload(args.config, seed=args.seed, device=dev)
     K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
     out = torch.empty_like(wl.grads[0])
-    step = A.Combiner(wl.grads, wl.seg_offsets, out=out)  # arguments marshalled once; one combine per call
+    step = A.Combiner(wl.grads, wl.seg_offsets, schedule=args.schedule, out=out)  # marshalled once
     torch.cuda.synchronize()
 
     log(f"K={K} N={N} nseg={wl.nseg}; warmup {args.warmup}")
@@ -205,14 +207,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s)")
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu = cpu_baseline(wl, args.cpu_budget, args.schedule)
 
     line = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg,
-                   "io_dtype": wl.dtype, "seed": wl.seed, "parallelism": "none (one GPU)"},
+                   "io_dtype": wl.dtype, "seed": wl.seed, "schedule": args.schedule,
+                   "parallelism": "none (one GPU)"},
         "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "plain_sum": plain_sum,
         **({"cold": cold} if cold is not None else {}),
         "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
