@@ -2,15 +2,15 @@
 //
 // The tree is cut into stages of at most four levels (five when at most 32
 // 16-bit inputs make it one stage); each stage is a set of blocks (subtrees
-// of at most 16 operands, or that one 32-operand block).  One call enqueues,
-// stage by stage:
-//   1. widen: inputs carried into a stage above the first become fp32 slots;
-//   2. gram: one launch per block size over every block and every tile: the
-//      Gram partials of each block's operands, accumulated in fp64;
-//   3. tree: one launch over every (block, segment): tile partials summed in
+// of at most 16 operands, or that one 32-operand block).  A block above the
+// first stage reads fp32 slots and, where an input is carried up, that input
+// in its own dtype.  One call enqueues, stage by stage:
+//   1. gram: one launch per (block size, operand types) over every block and
+//      every tile: the Gram partials of each block's operands, in fp64;
+//   2. tree: one launch over every (block, segment): tile partials summed in
 //      tile order, every merge of the block evaluated on the Gram matrix
 //      (statistics, coefficients), the final operand weights written;
-//   4. wsum: one launch per (block size, types) over every block and tile:
+//   3. wsum: one launch per (block size, types) over every block and tile:
 //      the block's result, sum_k w_k x_k, into an fp32 slot or into out.
 // So a combine of K <= 16 gradients (K <= 32 for 16-bit ones) is three
 // launches and two passes over the inputs, whatever the number of segments.
@@ -184,8 +184,8 @@ std::map<std::pair<int, void*>, OwnedWorkspace> g_ws;  // (device, stream) -> bu
 
 // ---------------------------------------------------------------- launch timing
 
-enum KernelKind { kGram = 0, kTree, kWsum, kWiden, kSum, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "widen", "sum"};
+enum KernelKind { kGram = 0, kTree, kWsum, kSum, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "sum"};
 
 struct ProfRecord {
   int kind;
@@ -371,43 +371,53 @@ void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
 
 DType ref_type(const Plan& p, Ref r) { return r.kind == Ref::Slot ? DType::F32 : p.dtype; }
 
+// The kernels a block needs: its operands' type, and, for an fp32 block that
+// also reads 16-bit inputs (carried up from below), the inputs' type and
+// which operands they are.
+struct BlockKind {
+  DType in_t;        // operand type of the launch
+  DType narrow_t;    // 16-bit type of the marked operands, or F32 for none
+  uint32_t narrow;   // bit k: operand k is read in narrow_t
+};
+
+BlockKind block_kind(const Plan& p, const Block& b) {
+  bool any_slot = false;
+  for (const Ref& r : b.operands) any_slot |= r.kind == Ref::Slot;
+  if (!any_slot) return {p.dtype, DType::F32, 0u};  // inputs only, in their own type
+  BlockKind k{DType::F32, DType::F32, 0u};
+  if (p.dtype != DType::F32) {
+    for (size_t i = 0; i < b.operands.size(); ++i)
+      if (b.operands[i].kind == Ref::Input) k.narrow |= 1u << i;
+    if (k.narrow) k.narrow_t = p.dtype;
+  }
+  return k;
+}
+
 int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStream_t st) {
   const int ntiles = (int)p.tiles.size();
-  const size_t esz = dtype_size(p.dtype);
   hipError_t e;
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
   double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
   int stage_no = 0;
   for (const Stage& sg : p.stages) {
     ++stage_no;
-    // 1. inputs carried into this stage, widened once to fp32
-    for (const auto& wd : sg.widen) {
-      if (ntiles == 0) break;
-      WidenArgs w{};
-      w.src = b.grads[wd.first];
-      w.dst = reinterpret_cast<float*>(b.ws + p.ws_slots + (size_t)wd.second * (size_t)p.N * sizeof(float));
-      w.tiles = dt.tiles;
-      log_launch("widen", stage_no, ntiles, 1, 0, (double)p.N * (esz + 4.0));
-      const int pr = prof_start(kWiden, (double)p.N * (esz + 4.0), st);
-      e = launch_widen(p.dtype, w, ntiles, st);
-      prof_stop(pr, st);
-      if (e != hipSuccess) return fail_hip(e, "launching widen");
-    }
-    // 2. Gram partials, blocks grouped by (operand type, Gram size)
-    // 4. weighted sums, grouped by (operand type, Gram size, result type)
+    // 1. Gram partials, blocks grouped by (operand types, Gram size)
+    // 3. weighted sums, grouped by (operand types, Gram size, result type)
     for (int pass = 0; pass < 2; ++pass) {
       if (ntiles == 0) break;
       std::vector<char> done(sg.blocks.size(), 0);
       for (size_t i = 0; i < sg.blocks.size(); ++i) {
         if (done[i]) continue;
         const Block& b0 = sg.blocks[i];
-        const DType in_t = ref_type(p, b0.operands[0]);
+        const BlockKind kind0 = block_kind(p, b0);
+        const DType in_t = kind0.in_t;
         const DType out_t = ref_type(p, b0.dst);
         const int nbt = p.descs[b0.desc].nbt;
         std::vector<const Block*> group;
         for (size_t k = i; k < sg.blocks.size(); ++k) {
           const Block& bk = sg.blocks[k];
-          if (done[k] || p.descs[bk.desc].nbt != nbt || ref_type(p, bk.operands[0]) != in_t) continue;
+          const BlockKind kk = block_kind(p, bk);
+          if (done[k] || p.descs[bk.desc].nbt != nbt || kk.in_t != in_t || kk.narrow_t != kind0.narrow_t) continue;
           if (pass == 1 && ref_type(p, bk.dst) != out_t) continue;
           done[k] = 1;
           group.push_back(&bk);
@@ -419,26 +429,32 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             GramArgs a{};
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
-              for (size_t k = 0; k < bk.operands.size(); ++k) a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+              for (size_t k = 0; k < bk.operands.size(); ++k) {
+                a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+                in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
+              }
+              a.narrow[j] = block_kind(p, bk).narrow;
               a.poff[j] = p.descs[bk.desc].poff;
-              in_bytes += (double)bk.operands.size() * p.N * dtype_size(in_t);
               out_bytes += 8.0 * gram_entries(nbt) * ntiles;
             }
             a.tiles = dt.tiles;
             a.partials = partials;
             log_launch("gram", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kGram, in_bytes + out_bytes, st);
-            e = launch_gram(in_t, nbt, a, ntiles, n, st);
+            e = launch_gram(in_t, kind0.narrow_t, nbt, a, ntiles, n, st);
             prof_stop(pr, st);
             if (e != hipSuccess) return fail_hip(e, "launching gram");
           } else {
             WsumArgs a{};
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
-              for (size_t k = 0; k < bk.operands.size(); ++k) a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+              for (size_t k = 0; k < bk.operands.size(); ++k) {
+                a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+                in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
+              }
+              a.narrow[j] = block_kind(p, bk).narrow;
               a.y[j] = ref_ptr(p, b, bk.dst);
               a.wrow[j] = p.descs[bk.desc].wrow;
-              in_bytes += (double)bk.operands.size() * p.N * dtype_size(in_t);
               out_bytes += (double)p.N * dtype_size(out_t);
             }
             a.tiles = dt.tiles;
@@ -446,7 +462,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             a.weights = weights;
             log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
-            e = launch_wsum(in_t, nbt, out_t, a, ntiles, n, st);
+            e = launch_wsum(in_t, kind0.narrow_t, nbt, out_t, a, ntiles, n, st);
             prof_stop(pr, st);
             if (e != hipSuccess) return fail_hip(e, "launching wsum");
           }

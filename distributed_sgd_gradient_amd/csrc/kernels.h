@@ -9,9 +9,12 @@ namespace adasum {
 
 // Gram pass: per (block, tile), the packed upper triangle of the fp64 Gram
 // matrix of the block's operands over the tile.  Operands x[j][k] with k at
-// or beyond the block's operand count are NULL and read as zero.
+// or beyond the block's operand count are NULL and read as zero.  In an fp32
+// launch, bit k of narrow[j] marks operand k of job j as an input gradient
+// stored in the launch's 16-bit type (read and widened exactly on load).
 struct GramArgs {
   const void* x[kMaxJobs][kMaxOps];
+  uint32_t narrow[kMaxJobs];
   int64_t poff[kMaxJobs];  // partials of tile t: partials + poff + t * gram_entries(nbt)
   const Tile* tiles;
   double* partials;
@@ -36,9 +39,11 @@ struct TreeArgs {
   double* ortho;            // [nseg] or NULL: |result|^2 / sum_k |g_k|^2, written by the root block
 };
 
-// Weighted sum: per (block, tile), y = sum_k w_k x_k, rounded once.
+// Weighted sum: per (block, tile), y = sum_k w_k x_k, rounded once; narrow
+// as for the Gram pass.
 struct WsumArgs {
   const void* x[kMaxJobs][kMaxOps];
+  uint32_t narrow[kMaxJobs];
   void* y[kMaxJobs];
   int wrow[kMaxJobs];
   const Tile* tiles;
@@ -59,19 +64,14 @@ struct SumArgs {
   int64_t n;
 };
 
-// Widen one input to fp32 over every tile.
-struct WidenArgs {
-  const void* src;
-  float* dst;
-  const Tile* tiles;
-};
-
-// nbt: Gram size of every block in the launch (2, 4, 8 or 16).
-hipError_t launch_gram(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st);
-hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
-hipError_t launch_wsum(DType in_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
+// nbt: Gram size of every block in the launch (2 .. 32).  operand: the
+// operands' dtype; with operand F32, narrow_t is the 16-bit dtype of the
+// operands the narrow masks mark (F32 when there are none).
+hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
                        hipStream_t st);
-hipError_t launch_widen(DType src_t, const WidenArgs& a, int ntiles, hipStream_t st);
+hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
+hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
+                       hipStream_t st);
 hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st);
 
 }  // namespace adasum

@@ -74,6 +74,7 @@ __device__ __forceinline__ T gload(const T* p) {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Elem;
@@ -187,6 +188,19 @@ struct Elem<bf16_t> {
   }
 };
 
+// A 16-bit input gradient read by an fp32 launch (an input carried into a
+// later stage), widened exactly to fp32.
+template <typename TN>
+__device__ __forceinline__ float narrow_to_f32(uint32_t bits16);
+template <>
+__device__ __forceinline__ float narrow_to_f32<_Float16>(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+template <>
+__device__ __forceinline__ float narrow_to_f32<bf16_t>(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
 // ----------------------------------------------------------------- tiles
 
 // Bounds of a tile: [lo, body_lo) head, [body_lo, body_hi) aligned body,
@@ -231,8 +245,46 @@ __device__ __forceinline__ v4f load_f32x4(const float* __restrict__ x, int64_t r
   return v4f{w[0], w[1], w[2], w[3]};
 }
 
-template <int NB>
+// The same for an operand stored in the 16-bit type TN, widened.
+template <typename TN>
+__device__ __forceinline__ v4f load_n16x4(const uint16_t* __restrict__ x, int64_t row, int64_t lo, int64_t hi) {
+  if (row >= lo && row + 4 <= hi) {
+    const v2u w = gload(reinterpret_cast<const v2u*>(x + row));
+    return v4f{narrow_to_f32<TN>(w.x & 0xffffu), narrow_to_f32<TN>(w.x >> 16), narrow_to_f32<TN>(w.y & 0xffffu),
+               narrow_to_f32<TN>(w.y >> 16)};
+  }
+  float w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = (row + e >= lo && row + e < hi) ? narrow_to_f32<TN>(gload(x + row + e)) : 0.f;
+  return v4f{w[0], w[1], w[2], w[3]};
+}
+
+// Eight consecutive values at rows [row, row + 8) of a 16-bit operand, widened, zero outside [lo, hi).
+template <typename TN>
+__device__ __forceinline__ void load_n16x8(const uint16_t* __restrict__ x, int64_t row, int64_t lo, int64_t hi,
+                                           v4f& a, v4f& b) {
+  if (row >= lo && row + 8 <= hi) {
+    const v4u w = gload(reinterpret_cast<const v4u*>(x + row));
+    a = v4f{narrow_to_f32<TN>(w.x & 0xffffu), narrow_to_f32<TN>(w.x >> 16), narrow_to_f32<TN>(w.y & 0xffffu),
+            narrow_to_f32<TN>(w.y >> 16)};
+    b = v4f{narrow_to_f32<TN>(w.z & 0xffffu), narrow_to_f32<TN>(w.z >> 16), narrow_to_f32<TN>(w.w & 0xffffu),
+            narrow_to_f32<TN>(w.w >> 16)};
+    return;
+  }
+  a = load_n16x4<TN>(x, row, lo, hi);
+  b = load_n16x4<TN>(x, row + 4, lo, hi);
+}
+
+// TN = float: every operand is fp32.  Otherwise the lanes of operands that
+// the job's narrow mask marks read them in TN (16-bit inputs carried into a
+// later stage) and widen them exactly; the products stay exact.  Such a
+// launch takes 32-row chunks with eight consecutive rows per lane, so that a
+// 16-bit lane reads 16 bytes at once (an fp32 lane two times 16); any
+// assignment of rows to the instruction steps gives the same Gram matrix, as
+// long as every operand lane uses the same row at each step.
+template <int NB, typename TN>
 __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
+  constexpr bool kMixed = !std::is_same<TN, float>::value;
   constexpr int SETS = 16 / NB;          // row sets packed into the 16 operand lanes
   constexpr int U = kF64Unroll;
   constexpr int RC = 16 * SETS;          // rows per chunk
@@ -254,27 +306,85 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
   const void* mine = args.x[j][op];
   const bool live = mine != nullptr;
   const float* xp = static_cast<const float*>(live ? mine : args.x[j][0]);
-  const int64_t lane_row = (int64_t)set * 16 + 4 * grp;  // first row of this lane in a chunk
+  // a masked operand reads operand 0, in operand 0's type
+  const bool narrow = kMixed && ((args.narrow[j] >> (live ? op : 0)) & 1u);
+  const uint16_t* xn = reinterpret_cast<const uint16_t*>(xp);
 
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
   const int64_t niter = (hi - first + R - 1) / R;
-  for (int64_t it = wave; it < niter; it += kGramWaves) {
-    const int64_t r0 = first + it * R;
-    v4f v[U];
-    if (r0 >= lo && r0 + R <= hi) {
+  if constexpr (!kMixed) {
+    const int64_t lane_row = (int64_t)set * 16 + 4 * grp;  // first row of this lane in a chunk
+    for (int64_t it = wave; it < niter; it += kGramWaves) {
+      const int64_t r0 = first + it * R;
+      v4f v[U];
+      if (r0 >= lo && r0 + R <= hi) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4f*>(xp + r0 + u * RC + lane_row));
-    } else {
+        for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4f*>(xp + r0 + u * RC + lane_row));
+      } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = load_f32x4(xp, r0 + u * RC + lane_row, lo, hi);
+        for (int u = 0; u < U; ++u) v[u] = load_f32x4(xp, r0 + u * RC + lane_row, lo, hi);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!live) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].x, (double)v[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].y, (double)v[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].z, (double)v[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].w, (double)v[u].w, acc, 0, 0, 0);
+      }
     }
+  } else {
+    constexpr int RC2 = 32 * SETS;  // rows per chunk: eight per lane
+    constexpr int U2 = U / 2;       // chunks per iteration (the same R rows)
+    static_assert(RC2 * U2 == R, "same rows per iteration");
+    const int64_t lane_row = (int64_t)set * 32 + 8 * grp;
+    for (int64_t it = wave; it < niter; it += kGramWaves) {
+      const int64_t r0 = first + it * R;
+      v4f va[U2], vb[U2];
+      if (r0 >= lo && r0 + R <= hi) {  // the whole iteration inside the tile: no per-row checks
+        if (narrow) {
+          v4u w[U2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!live) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].x, (double)v[u].x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].y, (double)v[u].y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].z, (double)v[u].z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].w, (double)v[u].w, acc, 0, 0, 0);
+          for (int u = 0; u < U2; ++u) w[u] = gload(reinterpret_cast<const v4u*>(xn + r0 + u * RC2 + lane_row));
+#pragma unroll
+          for (int u = 0; u < U2; ++u) {
+            va[u] = v4f{narrow_to_f32<TN>(w[u].x & 0xffffu), narrow_to_f32<TN>(w[u].x >> 16),
+                        narrow_to_f32<TN>(w[u].y & 0xffffu), narrow_to_f32<TN>(w[u].y >> 16)};
+            vb[u] = v4f{narrow_to_f32<TN>(w[u].z & 0xffffu), narrow_to_f32<TN>(w[u].z >> 16),
+                        narrow_to_f32<TN>(w[u].w & 0xffffu), narrow_to_f32<TN>(w[u].w >> 16)};
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < U2; ++u) {
+            const float* p = xp + r0 + u * RC2 + lane_row;
+            va[u] = gload(reinterpret_cast<const v4f*>(p));
+            vb[u] = gload(reinterpret_cast<const v4f*>(p + 4));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U2; ++u) {
+          const int64_t row = r0 + u * RC2 + lane_row;
+          if (narrow) {
+            load_n16x8<TN>(xn, row, lo, hi, va[u], vb[u]);
+          } else {
+            va[u] = load_f32x4(xp, row, lo, hi);
+            vb[u] = load_f32x4(xp, row + 4, lo, hi);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U2; ++u) {
+        if (!live) va[u] = vb[u] = v4f{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].x, (double)va[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].y, (double)va[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].z, (double)va[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].w, (double)va[u].w, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].x, (double)vb[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].y, (double)vb[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].z, (double)vb[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].w, (double)vb[u].w, acc, 0, 0, 0);
+      }
     }
   }
 
@@ -717,8 +827,14 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 // they alias operand 0 (cache hits, no extra HBM traffic) and their terms are
 // masked to zero, so the loop has no branches and every load of a step is in
 // flight at once.
-template <typename TIn, int NB, typename TOut>
+//
+// TN = TIn: every operand is TIn.  Otherwise (TIn = float) the operands that
+// the job's narrow mask marks are 16-bit inputs in TN, read as such (16 bytes
+// per 8 elements) and widened exactly.
+template <typename TIn, int NB, typename TOut, typename TN = TIn>
 __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
+  constexpr bool kMixed = !std::is_same<TN, TIn>::value;
+  static_assert(!kMixed || std::is_same<TIn, float>::value, "narrow operands only in fp32 launches");
   constexpr int kSplit = wsum_split(sizeof(TIn));
   const int tile_id = blockIdx.x / kSplit;
   const int part = blockIdx.x % kSplit;
@@ -741,22 +857,30 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   const TIn* x0 = static_cast<const TIn*>(args.x[j][0]);
   const TIn* xs[NB];
   bool live[NB];
+  bool nk[NB];  // read in TN (a masked operand reads operand 0, in operand 0's type)
   double w[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     live[k] = args.x[j][k] != nullptr;
     xs[k] = live[k] ? static_cast<const TIn*>(args.x[j][k]) : x0;
+    nk[k] = kMixed && ((args.narrow[j] >> (live[k] ? k : 0)) & 1u);
     w[k] = wrow[k];
   }
   TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
   const int tid = threadIdx.x;
   double unused;
 
+  auto load1 = [&](int k, int64_t i) -> float {
+    if constexpr (kMixed) {
+      if (nk[k]) return narrow_to_f32<TN>(gload(reinterpret_cast<const uint16_t*>(xs[k]) + i));
+    }
+    return Elem<TIn>::load1(xs[k] + i);
+  };
   auto one = [&](int64_t i) {
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const double t = mul_rn(w[k], (double)Elem<TIn>::load1(xs[k] + i));
+      const double t = mul_rn(w[k], (double)load1(k, i));
       acc = add_rn(acc, live[k] ? t : 0.0);
     }
     Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
@@ -769,14 +893,30 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
     typename Elem<TIn>::Raw8 raw[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
+    for (int k = 0; k < NB; ++k) {
+      if constexpr (kMixed) {
+        if (nk[k]) {  // eight 16-bit values, in the first half of the slot
+          raw[k].a = __builtin_bit_cast(v4f, gload(reinterpret_cast<const v4u*>(
+                                                 reinterpret_cast<const uint16_t*>(xs[k]) + g)));
+          continue;
+        }
+      }
+      raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
+    }
     double acc[kGroup];
 #pragma unroll
     for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       float v[kGroup];
-      Elem<TIn>::unpack8(raw[k], v);
+      bool unpacked = false;
+      if constexpr (kMixed) {
+        if (nk[k]) {
+          Elem<TN>::unpack8(__builtin_bit_cast(v4u, raw[k].a), v);
+          unpacked = true;
+        }
+      }
+      if (!unpacked) Elem<TIn>::unpack8(raw[k], v);
 #pragma unroll
       for (int e = 0; e < kGroup; ++e) {
         const double t = mul_rn(w[k], (double)v[e]);
@@ -906,23 +1046,6 @@ __global__ __launch_bounds__(kBlock) void sum_kernel(SumArgs a) {
   }
 }
 
-// ----------------------------------------------------------------- widen
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void widen_kernel(WidenArgs args) {
-  const TileSpan sp = span_of(args.tiles[blockIdx.x]);
-  const T* __restrict__ src = static_cast<const T*>(args.src);
-  float* __restrict__ dst = args.dst;
-  const int tid = threadIdx.x;
-  if (tid < sp.body_lo - sp.lo) dst[sp.lo + tid] = Elem<T>::load1(src + sp.lo + tid);
-  for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
-    float v[kGroup];
-    Elem<T>::load8(src + g, v);
-    Elem<float>::store8(dst + g, v);
-  }
-  if (tid < sp.hi - sp.body_hi) dst[sp.body_hi + tid] = Elem<T>::load1(src + sp.body_hi + tid);
-}
-
 // ----------------------------------------------------------------- dispatch helpers
 
 template <template <typename> class F, typename... Args>
@@ -935,13 +1058,6 @@ hipError_t by_type(DType t, Args&&... args) {
   return hipErrorInvalidValue;
 }
 
-template <typename T>
-struct RunWiden {
-  static hipError_t run(const WidenArgs& a, int ntiles, hipStream_t st) {
-    hipLaunchKernelGGL(widen_kernel<T>, dim3(ntiles), dim3(kBlock), 0, st, a);
-    return hipGetLastError();
-  }
-};
 
 template <typename T>
 struct RunSum {
@@ -953,14 +1069,15 @@ struct RunSum {
   }
 };
 
+template <typename TN>
 struct RunGramF64 {
   static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
     const dim3 grid(ntiles, njobs);
     switch (nbt) {
-      case 2: hipLaunchKernelGGL((gram_f64mfma_kernel<2>), grid, dim3(kBlock), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((gram_f64mfma_kernel<4>), grid, dim3(kBlock), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8>), grid, dim3(kBlock), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16>), grid, dim3(kBlock), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((gram_f64mfma_kernel<2, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((gram_f64mfma_kernel<4, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16, TN>), grid, dim3(kBlock), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -983,14 +1100,14 @@ struct RunGramMfma {
   }
 };
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, typename TN = TIn>
 hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
   const dim3 grid((unsigned)ntiles * wsum_split(sizeof(TIn)), njobs);
   switch (nbt) {
-    case 2: hipLaunchKernelGGL((wsum_kernel<TIn, 2, TOut>), grid, dim3(kBlock), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut>), grid, dim3(kBlock), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((wsum_kernel<TIn, 8, TOut>), grid, dim3(kBlock), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((wsum_kernel<TIn, 16, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((wsum_kernel<TIn, 2, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((wsum_kernel<TIn, 8, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((wsum_kernel<TIn, 16, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
     case 32:
       // 32-operand blocks exist only over 16-bit inputs, with an fp32 or same-type result
       if constexpr (sizeof(TIn) == 2 && (sizeof(TOut) == 4 || std::is_same<TIn, TOut>::value)) {
@@ -1015,11 +1132,30 @@ struct RunWsum {
   }
 };
 
+// fp32 launches with 16-bit inputs among the operands: the result is an fp32
+// slot or, at the root, the inputs' own type.
+template <typename TN>
+struct RunWsumNarrow {
+  static hipError_t run(int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
+    if (out_t == DType::F32) return run_wsum<float, float, TN>(nbt, a, ntiles, njobs, st);
+    if (sizeof(TN) == 2 && out_t == (std::is_same<TN, _Float16>::value ? DType::F16 : DType::BF16))
+      return run_wsum<float, TN, TN>(nbt, a, ntiles, njobs, st);
+    return hipErrorInvalidValue;
+  }
+};
+
 }  // namespace
 
-hipError_t launch_gram(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
+                       hipStream_t st) {
   switch (operand) {
-    case DType::F32: return RunGramF64::run(nbt, a, ntiles, njobs, st);
+    case DType::F32:
+      switch (narrow_t) {
+        case DType::F32: return RunGramF64<float>::run(nbt, a, ntiles, njobs, st);
+        case DType::F16: return RunGramF64<_Float16>::run(nbt, a, ntiles, njobs, st);
+        case DType::BF16: return RunGramF64<bf16_t>::run(nbt, a, ntiles, njobs, st);
+      }
+      return hipErrorInvalidValue;
     case DType::F16: return RunGramMfma<_Float16>::run(nbt, a, ntiles, njobs, st);
     case DType::BF16: return RunGramMfma<bf16_t>::run(nbt, a, ntiles, njobs, st);
   }
@@ -1031,13 +1167,13 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_wsum(DType in_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
+hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
                        hipStream_t st) {
+  if (in_t == DType::F32 && narrow_t == DType::F16)
+    return RunWsumNarrow<_Float16>::run(nbt, out_t, a, ntiles, njobs, st);
+  if (in_t == DType::F32 && narrow_t == DType::BF16)
+    return RunWsumNarrow<bf16_t>::run(nbt, out_t, a, ntiles, njobs, st);
   return by_type<RunWsum>(in_t, nbt, out_t, a, ntiles, njobs, st);
-}
-
-hipError_t launch_widen(DType src_t, const WidenArgs& a, int ntiles, hipStream_t st) {
-  return by_type<RunWiden>(src_t, a, ntiles, st);
 }
 
 hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st) { return by_type<RunSum>(t, a, st); }

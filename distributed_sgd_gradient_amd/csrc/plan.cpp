@@ -140,9 +140,9 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
   const size_t ntiles = p.tiles.size();
 
-  // ---- blocks, stage by stage.  Every operand of a stage above the first
-  // is an fp32 slot: the result of a lower block, or an input gradient
-  // widened once before the stage that first reads it.
+  // ---- blocks, stage by stage.  An operand of a stage above the first is
+  // an fp32 slot (the result of a lower block) or an input gradient that the
+  // stage reads where it is, in its own dtype.
   std::vector<Ref> operands(K);
   std::vector<char> is_leaf(K, 1);   // per operand of the current stage
   for (int k = 0; k < K; ++k) operands[k] = Ref{Ref::Input, k};
@@ -153,15 +153,13 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     operands.resize(next_leaf);
     is_leaf.resize(next_leaf);
   }
-  std::vector<std::pair<int, int>> pending_widen;  // carried inputs the next stage reads from fp32 slots
   bool first = true;
   while (first || operands.size() > 1) {
     Stage st;
-    st.widen.swap(pending_widen);
     std::vector<Elem> cur;
     for (int i = 0; i < (int)operands.size(); ++i) cur.push_back(Elem{i, i + 1, false});
     std::vector<StageMerge> stage_merges;
-    // the first stage reads the inputs; every later one reads fp32 slots
+    // the first stage reads only inputs; later ones read fp32 slots (and inputs carried up)
     const int ops = first ? first_stage_ops(dtype, K) : kMaxOps32;
     if (schedule == Schedule::Tree)
       tree_stage(cur, stage_merges, node, ops == 32 ? 5 : 4);
@@ -172,13 +170,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     std::vector<char> next_is_leaf;
     for (const Elem& e : cur) {
       if (!e.merged && !(last && operands.size() == 1)) {
-        Ref r = operands[e.lo];
-        if (r.kind == Ref::Input) {  // widen a carried input once, so later stages read fp32 only
-          const int slot = p.nslots++;
-          r = Ref{Ref::Slot, slot};
-          pending_widen.push_back({operands[e.lo].idx, slot});
-        }
-        next_operands.push_back(r);
+        next_operands.push_back(operands[e.lo]);  // carried up unchanged
         next_is_leaf.push_back(is_leaf[e.lo]);
         continue;
       }
@@ -210,9 +202,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     if (schedule == Schedule::Chain && !last) {
       const int take = std::min(K - next_leaf, kMaxOps32 - 1);
       for (int k = next_leaf; k < next_leaf + take; ++k) {
-        const int slot = p.nslots++;
-        pending_widen.push_back({k, slot});
-        next_operands.push_back(Ref{Ref::Slot, slot});
+        next_operands.push_back(Ref{Ref::Input, k});
         next_is_leaf.push_back(1);
       }
       next_leaf += take;

@@ -16,7 +16,9 @@
 //     of its merges, and one weighted-sum pass that writes its result;
 //   * the workspace layout: fp32 slots for block results that feed a later
 //     stage, fp64 per-tile Gram partials, leaf weights, and the coefficient
-//     and statistic tables.
+//     and statistic tables.  An input that a later stage reads (an odd vector
+//     carried up the tree, or the chain's next inputs) is read where it is,
+//     in its own dtype, next to the fp32 slots.
 //
 // Pure C++: it makes no HIP call, so it can be exercised without a GPU.
 #pragma once
@@ -98,14 +100,13 @@ struct Ref {
 };
 
 struct Block {
-  std::vector<Ref> operands;  // nb refs; all Input in stage 0, all Slot later
+  std::vector<Ref> operands;  // nb refs; all Input in stage 0; Slot, or Input carried up, later
   Ref dst;                    // Slot, or Out for the root block
   int desc;                   // index into Plan::descs
 };
 
 struct Stage {
   std::vector<Block> blocks;
-  std::vector<std::pair<int, int>> widen;  // (input k, slot): inputs carried into this stage
 };
 
 struct Plan {

@@ -17,9 +17,7 @@ static void dump(const Plan& p, int dt, int sched, int K) {
          sched, K, p.nslots, (long long)p.tile_rows);
   for (size_t s = 0; s < p.stages.size(); ++s) {
     const Stage& st = p.stages[s];
-    printf("%s{\"widen\": [", s ? "," : "");
-    for (size_t i = 0; i < st.widen.size(); ++i) printf("%s[%d,%d]", i ? "," : "", st.widen[i].first, st.widen[i].second);
-    printf("], \"blocks\": [");
+    printf("%s{\"blocks\": [", s ? "," : "");
     for (size_t b = 0; b < st.blocks.size(); ++b) {
       const Block& bk = st.blocks[b];
       const BlockDesc& d = p.descs[bk.desc];

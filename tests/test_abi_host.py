@@ -109,14 +109,17 @@ def test_workspace_size_properties():
     # Gram partials and tables
     for K in (2, 3, 9, 16):
         assert 0 < ws(K, (0, n)) < n
-    # 17 = a block of 16 plus one carried input widened to fp32: two slots
-    assert 2 * n * 4 <= ws(17, (0, n)) < 3 * n * 4
+    # 17 = a block of 16 (its result in one fp32 slot) and the carried input,
+    # which the second stage reads where it is
+    assert n * 4 <= ws(17, (0, n)) < 2 * n * 4
     assert 4 * n * 4 <= ws(64, (0, n)) < 5 * n * 4   # four blocks of 16
     assert ws(16, (0, 64 * n)) > ws(16, (0, n))
     assert ws(16, (0, 0)) >= 0 and ws(2, (0,)) >= 0
-    # chain: 16 inputs, then the running result plus 15 widened inputs per stage
+    # chain: 16 inputs, then the running result (an fp32 slot) and up to 15
+    # more inputs, read where they are, per stage
     assert ws(16, (0, n), 0, 1) < n
-    assert ws(17, (0, n), 0, 1) >= 2 * n * 4
+    assert n * 4 <= ws(17, (0, n), 0, 1) < 2 * n * 4
+    assert 4 * n * 4 <= ws(64, (0, n), 0, 1) < 5 * n * 4   # four stages below the root
 
 
 def test_sum_entry_point_validation():

@@ -73,11 +73,12 @@ def plan_nodes(P):
     slot_range = {}
     got = {}
     for si, st in enumerate(P["stages"]):
-        for k, slot in st["widen"]:
-            slot_range[slot] = (k, k + 1)
         for b in st["blocks"]:
-            if si > 0:
-                assert all(kind == 1 for kind, _ in b["ops"]), "stage operands above the first must be fp32 slots"
+            if si == 0:
+                assert all(kind == 0 for kind, _ in b["ops"]), "the first stage reads only inputs"
+            else:
+                assert all(kind in (0, 1) for kind, _ in b["ops"])
+                assert any(kind == 1 for kind, _ in b["ops"]), "a later block holds a lower block's result"
             rng = [(i, i + 1) if kind == 0 else slot_range[i] for kind, i in b["ops"]]
             limit = block_limit(si, P["dtype"], P["K"])
             assert len(rng) == b["nb"] <= limit and b["nbt"] >= b["nb"]
@@ -91,11 +92,8 @@ def plan_nodes(P):
                 slot_range[b["dst"][1]] = (lo, hi)
             else:
                 assert b["root"] == 1 and (lo, hi) == (0, P["K"])
-            # leaf operands are exactly the inputs and the widened inputs
-            leafmask = sum(1 << i for i, (kind, idx) in enumerate(b["ops"])
-                           if kind == 0 or (kind == 1 and rng[i][1] - rng[i][0] == 1
-                                            and idx in {s for _, s in
-                                                        [w for stg in P["stages"] for w in stg["widen"]]}))
+            # leaf operands are exactly the inputs (read where they are, in any stage)
+            leafmask = sum(1 << i for i, (kind, idx) in enumerate(b["ops"]) if kind == 0)
             assert leafmask == b["leafmask"]
     return got
 
