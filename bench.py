@@ -219,7 +219,10 @@ def main():
         "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "plain_sum": plain_sum,
         **({"cold": cold} if cold is not None else {}),
         "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
-                        "bytes_per_step": v["bytes"] / args.steps} for k, v in kernels.items()},
+                        "bytes_per_step": v["bytes"] / args.steps,
+                        "achieved_GBps": v["bytes"] / (v["milliseconds"] * 1e-3) / 1e9 if v["milliseconds"] > 0 else 0.0,
+                        "frac": (v["bytes"] / (v["milliseconds"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+                                 if v["milliseconds"] > 0 else 0.0)} for k, v in kernels.items()},
     }
     print(json.dumps(line), flush=True)
 
