@@ -172,3 +172,20 @@ def test_last_error_is_per_thread():
     assert seen["fresh"] == ""
     assert seen["rc"] == _native.EINVAL and "K must be >= 1" in seen["own"]
     assert lib.adasum_last_error().decode() == mine
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    """No fallback: the package's Python files without libadasum.so refuse to import."""
+    import shutil
+    import sys
+
+    pkg = os.path.join(ROOT, "distributed_sgd_gradient_amd")
+    dst = tmp_path / "distributed_sgd_gradient_amd"
+    dst.mkdir()
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            shutil.copy(os.path.join(pkg, name), dst / name)
+    res = subprocess.run([sys.executable, "-c", "import distributed_sgd_gradient_amd"], cwd=tmp_path,
+                         capture_output=True, text=True, env=dict(os.environ, PYTHONPATH=str(tmp_path)))
+    assert res.returncode != 0
+    assert "libadasum.so is missing" in res.stderr
