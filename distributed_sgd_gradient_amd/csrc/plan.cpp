@@ -67,6 +67,13 @@ bool validate_shape(int K, const int64_t* offsets, int nseg, int dtype, int sche
     *err = "too many tiles for this shape";
     return false;
   }
+  // the tree walk launches one workgroup per (block, segment) of a stage,
+  // and a stage has fewer blocks than K
+  if ((int64_t)K * nseg > int64_t(INT32_MAX)) {
+    snprintf(buf, sizeof buf, "K * nseg = %lld exceeds 2^31 - 1", (long long)K * nseg);
+    *err = buf;
+    return false;
+  }
   return true;
 }
 

@@ -105,8 +105,8 @@ typedef enum {
  * Uses a workspace that the library allocates and caches per (device,
  * stream); the first call for a given shape may therefore allocate.
  * Errors: ADASUM_EINVAL (null pointers with N > 0, K < 1, nseg < 0, bad
- * offsets, unknown dtype, misaligned pointer, out overlapping an input),
- * ADASUM_ENOMEM, ADASUM_EHIP.
+ * offsets, unknown dtype, misaligned pointer, out overlapping an input,
+ * N > 2^40, K * nseg > 2^31 - 1), ADASUM_ENOMEM, ADASUM_EHIP.
  */
 ADASUM_API int adasum_combine(const void* const* grads, int K, const int64_t* seg_offsets, int nseg,
                    int dtype, void* out, void* stream);

@@ -189,3 +189,14 @@ def test_package_fails_loudly_without_the_library(tmp_path):
                          capture_output=True, text=True, env=dict(os.environ, PYTHONPATH=str(tmp_path)))
     assert res.returncode != 0
     assert "libadasum.so is missing" in res.stderr
+
+
+def test_k_times_nseg_bound():
+    """One tree-walk workgroup per (block, segment): K * nseg must fit a launch grid."""
+    lib = _native.lib()
+    nseg = (1 << 31) // 1000 + 1
+    arr = np.zeros(nseg + 1, dtype=np.int64)  # all segments empty
+    p = arr.ctypes.data_as(_native._I64P)
+    assert lib.adasum_workspace_bytes(1000, p, nseg, 0, 0) == _native.EINVAL
+    assert "exceeds 2^31 - 1" in lib.adasum_last_error().decode()
+    assert lib.adasum_workspace_bytes(999, p, nseg - 10, 0, 0) > 0
