@@ -61,7 +61,8 @@ def test_bench_json_line(gpu):
     cpu = rec["cpu_baseline"]
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cpu, key
-    assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0
+    assert cpu["kind"] == "oracle" and 1 <= cpu["cores"] <= 16 and cpu["value"] > 0
+    assert cpu["one_core"]["value"] > 0 and cpu["one_core"]["unit"] == cpu["unit"]
 
     # one combine is three launches: gram, tree, weighted sum
     assert set(rec["kernels"]) == {"gram", "tree", "wsum"}
