@@ -9,7 +9,8 @@ Prints one JSON line: gradient GB/s (K * N * bytes per element / step time),
 the HBM-roofline figures of the dominant kernel (from HIP events around every
 launch inside the timed region) and of the whole path (minimum traffic of
 reading K gradients once and writing one), and the fp64 CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload, against which the GPU result of that
+sample is checked ("parity").
 """
 
 import argparse
@@ -72,7 +73,16 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30):
+TOL_REL_L2 = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+TOL_COEFF = 1e-6
+# an operand whose squared norm is at most this fraction of the (nonzero)
+# summed squared norms of the input gradients under it sits at the operator's
+# discontinuity (coefficient 1 at exactly zero, another limit next to it); its
+# coefficient and those of the nodes above it are not gated
+NEAR_ZERO = 1e-8
+
+
+def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, gpu_out=None, gpu_coeffs=None):
     """Time the fp64 oracle (the same schedule as the GPU run, the oracle's
     own code unchanged) on whole segments copied from the GPU workload.
 
@@ -81,9 +91,14 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30):
     `threads` threads, one segment per task, largest first, fetched in
     batches of at most `batch_bytes` of fp64 data (fetches are not timed).
     NumPy releases the GIL in the oracle's dot products and array
-    arithmetic; every BLAS call runs on one thread."""
+    arithmetic; every BLAS call runs on one thread.
+
+    Outside the timed calls, pass 1 also compares the GPU result `gpu_out`
+    and coefficients `gpu_coeffs` ([K-1][nseg][2]) with the oracle's on every
+    sampled segment.  Returns (baseline record, parity record or None)."""
     import concurrent.futures
 
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -92,15 +107,33 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30):
     first = min(5, wl.nseg)  # encoder layers first, the (large) embedding segments last
     order = list(range(first, wl.nseg)) + list(range(0, first))
     used, elems, spent = [], 0, 0.0
+    err2 = ref2 = 0.0
+    cerr = 0.0
+    exempt = 0
+    coeffs_host = gpu_coeffs.cpu().numpy() if gpu_coeffs is not None else None
     with threadpool_limits(limits=1):
         for s in order:
             rows = wl.segment_host(s)
             t0 = time.perf_counter()
-            fn(rows)
+            res, coeffs, stats = fn(rows)
             spent += time.perf_counter() - t0
             used.append(s)
             elems += rows[0].size
-            del rows
+            if gpu_out is not None:
+                lo, hi = int(wl.seg_offsets[s]), int(wl.seg_offsets[s + 1])
+                ref = oracle.round_to_format(res, wl.dtype)
+                got = gpu_out[lo:hi].double().cpu().numpy()
+                err2 += float(np.sum((got - ref) ** 2))
+                ref2 += float(np.sum(ref ** 2))
+            if coeffs_host is not None and len(coeffs):
+                c = np.asarray(coeffs, dtype=np.float64)
+                st = np.asarray(stats, dtype=np.float64)
+                zero = oracle.discontinuity_mask(st, oracle.operand_input_norms(rows, schedule), schedule,
+                                                 NEAR_ZERO)
+                exempt += int(np.count_nonzero(zero))
+                err = np.where(zero, 0.0, np.abs(coeffs_host[:, s, :] - c) / np.maximum(1.0, np.abs(c)))
+                cerr = max(cerr, float(np.max(err)))
+            del rows, res
             if spent >= budget_s:
                 break
         pooled = spent
@@ -120,11 +153,21 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30):
                     pooled += time.perf_counter() - t0
                     del batch
     nbytes = wl.K * elems * BYTES[wl.dtype]
-    return {"value": nbytes / pooled / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    base = {"value": nbytes / pooled / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(used)} of {wl.nseg} segments ({elems} of {wl.N} elements per worker); "
                       f"{threads} threads of fp64 NumPy, one segment per task, one BLAS thread each",
             "seconds": pooled, "cpu_model": cpu_model(),
             "one_core": {"value": nbytes / spent / 1e9, "unit": "GB/s", "seconds": spent}}
+    parity = None
+    if gpu_out is not None:
+        rel = (err2 ** 0.5) / (ref2 ** 0.5) if ref2 > 0 else (0.0 if err2 == 0 else float("inf"))
+        tol = TOL_REL_L2[wl.dtype]
+        parity = {"against": "fp64 oracle, rounded to the output dtype", "segments": len(used),
+                  "elements_per_worker": elems, "rel_l2": rel, "tol_rel_l2": tol,
+                  "max_coeff_err": cerr if coeffs_host is not None else None, "tol_coeff": TOL_COEFF,
+                  "coeffs_at_or_above_zero_discontinuity": exempt if coeffs_host is not None else None,
+                  "pass": bool(rel <= tol and (coeffs_host is None or cerr <= TOL_COEFF))}
+    return base, parity
 
 
 def main():
@@ -174,7 +217,8 @@ def main():
     wl = W.make_workload(args.config, seed=args.seed, device=dev)
     K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
     out = torch.empty_like(wl.grads[0])
-    step = A.Combiner(wl.grads, wl.seg_offsets, schedule=args.schedule, out=out)  # marshalled once
+    # marshalled once; the coefficient table is written by every combine anyway
+    step = A.Combiner(wl.grads, wl.seg_offsets, schedule=args.schedule, out=out, return_coeffs=True)
     torch.cuda.synchronize()
 
     log(f"K={K} N={N} nseg={wl.nseg}; warmup {args.warmup}")
@@ -248,11 +292,15 @@ def main():
     log(f"plain sum on the same buffers: {sum_ms:.3f} ms/step; Adasum takes {ms / sum_ms:.2f}x as long")
     del out_sum
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         threads = host_threads()
-        log(f"timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s on one thread, then on {threads})")
-        cpu = cpu_baseline(wl, args.cpu_budget, args.schedule, threads)
+        log(f"timing the CPU oracle on a sample (~{args.cpu_budget:.0f} s on one thread, then on {threads}); "
+            f"the last timed step's result is checked against it")
+        cpu, parity = cpu_baseline(wl, args.cpu_budget, args.schedule, threads, gpu_out=out,
+                                   gpu_coeffs=step.coeffs)
+        log(f"parity on {parity['segments']} segments: relative L2 {parity['rel_l2']:.3g}, "
+            f"coefficient error {parity['max_coeff_err']}")
 
     line = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -261,7 +309,7 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg,
                    "io_dtype": wl.dtype, "seed": wl.seed, "schedule": args.schedule,
                    "parallelism": "none (one GPU)"},
-        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "plain_sum": plain_sum,
+        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "parity": parity, "plain_sum": plain_sum,
         **({"cold": cold} if cold is not None else {}),
         "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
                         "bytes_per_step": v["bytes"] / args.steps,

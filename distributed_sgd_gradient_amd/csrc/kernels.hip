@@ -19,9 +19,11 @@
 //           cb = 1 - d/(2B) (coefficient 1 for a zero norm), and the
 //           weights of the merged operands scaled by ca and cb;
 //   wsum  - one pass: y = sum_k w_k x_k in fp64, rounded once.
-// Quadratic forms and the weighted sum use separately rounded products and
-// sums (no fused multiply-add), so mirrored terms cancel exactly: an operand
-// pair (a, -a) gives an exactly zero node, as the plain definition does.
+// The merge walk's quadratic forms are summed in double-double from exact
+// products, and the weighted sum uses separately rounded products and sums
+// (no fused multiply-add); either way mirrored terms cancel exactly: an
+// operand pair (a, -a) gives an exactly zero node, as the plain definition
+// does.
 //
 // Every kernel walks tiles of the plan's tile table.  A tile lies inside
 // one segment; its body starts at a multiple of kGroup elements, so vector
@@ -519,6 +521,54 @@ __device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, int s) {
   return bf16_scale(w & 0xffffu, s) | (bf16_scale(w >> 16, s) << 16);
 }
 
+// Tiles of at most kExactRows rows skip the matrix cores: the tile is staged
+// in LDS and every Gram entry is summed in fp64, row by row.  A product of
+// two fp16 or two bf16 values is exact in fp64, so such an entry is the
+// row-order sum of exact products, like an entry of the fp32 pass.  Short
+// segments are where operands can nearly cancel by chance (a segment of a
+// few elements is a short random vector); there the fp32 rounding of a
+// 32-row matrix-core sum, amplified by the cancellation, would reach the
+// coefficients.
+constexpr int kExactRows = 256;
+
+template <typename T>
+__device__ __forceinline__ double widen16(uint16_t bits);
+template <>
+__device__ __forceinline__ double widen16<_Float16>(uint16_t bits) {
+  return (double)__builtin_bit_cast(_Float16, bits);
+}
+template <>
+__device__ __forceinline__ double widen16<bf16_t>(uint16_t bits) {
+  return (double)__uint_as_float((uint32_t)bits << 16);
+}
+
+// The packed Gram triangle of rows [lo, lo + len), len <= kExactRows, of the
+// operands in `table` (NULL: zero) into out; sh holds NB * kExactRows
+// 16-bit values.  Called by every thread of the workgroup.
+template <typename T, int NB>
+__device__ void gram_exact_tile(const void* const* table, int64_t lo, int len, double* __restrict__ out,
+                                uint16_t* sh) {
+  for (int idx = threadIdx.x; idx < NB * len; idx += kBlock) {
+    const int k = idx / len, r = idx - k * len;
+    const uint16_t* x = static_cast<const uint16_t*>(table[k]);
+    sh[k * kExactRows + r] = x != nullptr ? gload(x + lo + r) : (uint16_t)0;
+  }
+  __syncthreads();
+  constexpr int NE = gram_entries(NB);
+  for (int e = threadIdx.x; e < NE; e += kBlock) {
+    int i = 0, rem = e;
+    while (rem >= NB - i) {
+      rem -= NB - i;
+      ++i;
+    }
+    const uint16_t* a = sh + i * kExactRows;
+    const uint16_t* b = sh + (i + rem) * kExactRows;
+    double sum = 0.0;
+    for (int r = 0; r < len; ++r) sum += widen16<T>(a[r]) * widen16<T>(b[r]);  // exact product, one rounding
+    out[e] = sum;
+  }
+}
+
 // Blocks of up to 16 operands use one 16-operand half; the 32-operand block
 // (at most 32 16-bit inputs, one stage) uses two, with three instructions
 // per 32-row chunk: the two diagonal 16 x 16 blocks and the cross block
@@ -538,6 +588,12 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
   const int64_t lo = tile.start, hi = tile.start + tile.len;
+  if (tile.len <= kExactRows) {  // workgroup-uniform: a short tile, summed exactly
+    static_assert(sizeof(red) >= sizeof(uint16_t) * NB * kExactRows, "staging fits the reduction buffer");
+    gram_exact_tile<T, NB>(args.x[j], lo, tile.len, args.partials + args.poff[j] + (int64_t)tile_id * NE,
+                           reinterpret_cast<uint16_t*>(&red[0][0][0]));
+    return;
+  }
   const int64_t first = lo & ~int64_t(kGroup - 1);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -701,6 +757,38 @@ __device__ __forceinline__ double gram_at(const double* G, int n, int i, int k) 
   return i <= k ? G[gram_index(n, i, k)] : G[gram_index(n, k, i)];
 }
 
+// Double-double values (hi + lo, |lo| <= ulp(hi) / 2) for the merge walk's
+// sums.  A node far smaller than the operands under it (a near-cancellation)
+// makes its quadratic form cancel: summed in fp64, the rounding of the terms
+// would be amplified by the ratio of their size to the result's.  With exact
+// products (a fused multiply-add gives the product's rounding error) and
+// compensated sums, the form is accurate to about 2^-104 of the terms.
+// Terms that mirror each other still cancel exactly.
+struct DD {
+  double hi, lo;
+};
+
+__device__ __forceinline__ DD dd_prod(double a, double b) {
+  const double p = a * b;
+  return DD{p, fma(a, b, -p)};
+}
+
+__device__ __forceinline__ DD dd_add(DD x, DD y) {
+  const double s = x.hi + y.hi;
+  const double bb = s - x.hi;
+  double e = (x.hi - (s - bb)) + (y.hi - bb);
+  e += x.lo + y.lo;
+  const double hi = s + e;
+  return DD{hi, e - (hi - s)};
+}
+
+__device__ __forceinline__ DD dd_scale(DD x, double b) {
+  DD p = dd_prod(x.hi, b);
+  p.lo += x.lo * b;
+  const double hi = p.hi + p.lo;
+  return DD{hi, p.lo - (hi - p.hi)};
+}
+
 // sum_{i in [a0,a1)} w_i * (sum_{k in [b0,b1)} w_k G(i,k))
 __device__ double quad_form(const double* G, int n, const double* w, int a0, int a1, int b0, int b1) {
   double total = 0.0;
@@ -755,9 +843,10 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // For merge (L, R), thread i in L u R forms its row sums
   // rowL_i = sum_{k in L} w_k G(i,k) and rowR_i = sum_{k in R} w_k G(i,k) in
   // k order; one thread per merge then forms A = sum_{i in L} w_i rowL_i,
-  // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order.
-  // That is the same arithmetic, term for term, as a serial evaluation.
-  __shared__ double rowL[kMaxOps], rowR[kMaxOps];
+  // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order,
+  // all in double-double, and rounds them to fp64.  That is the same
+  // arithmetic, term for term, as a serial evaluation.
+  __shared__ DD rowL[kMaxOps], rowR[kMaxOps];
   __shared__ double cab[kMaxOps][2];
   __shared__ Merge ms[kMaxOps];
   if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
@@ -771,9 +860,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       if (tid >= ms[m].llo && tid < ms[m].rhi) mine = m;
     if (mine >= 0) {
       const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
-      double sl = 0.0, sr = 0.0;
-      for (int k = l0; k < l1; ++k) sl = add_rn(sl, mul_rn(w[k], gram_at(G, n, tid, k)));
-      for (int k = l1; k < r1; ++k) sr = add_rn(sr, mul_rn(w[k], gram_at(G, n, tid, k)));
+      DD sl{0.0, 0.0}, sr{0.0, 0.0};
+      for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_prod(w[k], gram_at(G, n, tid, k)));
+      for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_prod(w[k], gram_at(G, n, tid, k)));
       rowL[tid] = sl;
       rowR[tid] = sr;
     }
@@ -781,10 +870,11 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     if (tid < m1 - m0) {
       const Merge mg = ms[m0 + tid];
       const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
-      double A = 0.0, B = 0.0, dd = 0.0;
-      for (int i = l0; i < l1; ++i) A = add_rn(A, mul_rn(w[i], rowL[i]));
-      for (int i = l1; i < r1; ++i) B = add_rn(B, mul_rn(w[i], rowR[i]));
-      for (int i = l0; i < l1; ++i) dd = add_rn(dd, mul_rn(w[i], rowR[i]));
+      DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
+      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_scale(rowL[i], w[i]));
+      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_scale(rowR[i], w[i]));
+      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_scale(rowR[i], w[i]));
+      const double A = a2.hi, B = b2.hi, dd = ab.hi;  // normalised: hi is the rounded sum
       const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
       cab[m0 + tid][0] = ca;

@@ -17,7 +17,10 @@ emulated sequential orders, it is applied per layer, it is not elementwise).
 
 Modules
   adasum    fp64 NumPy oracle: pairwise operator, binary tree, per-segment
-            combine, orthogonality ratio, plain sum, linear chain.
+            combine, orthogonality ratio, plain sum, linear chain, and the
+            input norms under each node's operands with the mask of the
+            coefficients at (or above) the operator's discontinuity at a
+            zero operand.
   exact     the same definitions in exact rational arithmetic (fractions),
             for brute force on tiny inputs.
   rounding  IEEE round-to-nearest-even from fp64 to fp32 / fp16 / bf16.
@@ -35,6 +38,8 @@ from .adasum import (  # noqa: F401
     combine_chain,
     plain_sum,
     orthogonality,
+    operand_input_norms,
+    discontinuity_mask,
     tree_schedule,
 )
 from .rounding import round_to_format  # noqa: F401

@@ -213,3 +213,70 @@ def orthogonality(inputs, seg_offsets):
         num = float(np.dot(res[lo:hi], res[lo:hi]))
         ratios[s] = np.nan if den == 0.0 else num / den
     return ratios
+
+
+def operand_input_norms(vectors, schedule="tree"):
+    """Per node, in node order: the summed squared norms of the input vectors
+    under its left operand and under its right operand, (S_L, S_R).
+
+    The operator is discontinuous at a zero operand (coefficient 1 there, see
+    ``adasum_pair``), so a node whose operand norm |a|^2 is tiny against S_L
+    is a near-cancellation at which the coefficient is not a stable quantity.
+    ``schedule`` is "tree" (``tree_schedule``) or "chain" (the running result
+    meets g_1, g_2, ... in turn).  Returns an array [K-1, 2].
+    """
+    norms = [float(np.dot(v, v)) for v in (np.asarray(x, dtype=np.float64) for x in vectors)]
+    K = len(norms)
+    out = []
+    if schedule == "chain":
+        acc = norms[0] if K else 0.0
+        for k in range(1, K):
+            out.append((acc, norms[k]))
+            acc += norms[k]
+    else:
+        under = {("leaf", k): norms[k] for k in range(K)}
+        node = 0
+        for level in tree_schedule(K):
+            for left, right in level:
+                out.append((under[left], under[right]))
+                under[("node", node)] = under[left] + under[right]
+                node += 1
+    return np.asarray(out, dtype=np.float64).reshape(-1, 2)
+
+
+def discontinuity_mask(stats, opnorms, schedule="tree", rel=1e-8):
+    """[K-1, 2] mask of the coefficients that are not stable quantities.
+
+    The operator takes coefficient 1 at an exactly zero operand, but
+    Adasum(eps*u, c) tends to c - (u.c) u / 2 as eps -> 0: a zero operand that
+    carries rounding noise gets an arbitrary coefficient, and the node's value
+    moves by O(|c|).  Marked: the coefficient of every operand whose squared
+    norm (``stats`` [K-1, 3], (a.b, |a|^2, |b|^2)) is at most ``rel`` times
+    the summed squared norms of the input gradients under it (``opnorms``
+    [K-1, 2], nonzero), and both coefficients of every node that consumes
+    such a merge's result, directly or through later nodes.
+    """
+    stats = np.asarray(stats, dtype=np.float64).reshape(-1, 3)
+    opnorms = np.asarray(opnorms, dtype=np.float64).reshape(-1, 2)
+    n = stats.shape[0]
+    mask = (stats[:, 1:3] <= rel * opnorms) & (opnorms > 0)
+    parent = [-1] * n
+    if schedule == "chain":
+        for i in range(n - 1):
+            parent[i] = i + 1
+    else:
+        node = 0
+        for level in tree_schedule(n + 1):
+            for left, right in level:
+                for kind, i in (left, right):
+                    if kind == "node":
+                        parent[i] = node
+                node += 1
+    for i in range(n):
+        if mask[i].any():
+            j = parent[i]
+            while j >= 0:
+                mask[j] = True
+                j = parent[j]
+    return mask
+

@@ -64,6 +64,11 @@ def test_bench_json_line(gpu):
     assert cpu["kind"] == "oracle" and 1 <= cpu["cores"] <= 16 and cpu["value"] > 0
     assert cpu["one_core"]["value"] > 0 and cpu["one_core"]["unit"] == cpu["unit"]
 
+    # the last timed step's result against the oracle on the sampled segments
+    par = rec["parity"]
+    assert par["segments"] >= 1 and par["tol_rel_l2"] == 1e-5 and par["tol_coeff"] == 1e-6
+    assert par["rel_l2"] <= par["tol_rel_l2"] and par["max_coeff_err"] <= par["tol_coeff"] and par["pass"] is True
+
     # one combine is three launches: gram, tree, weighted sum
     assert set(rec["kernels"]) == {"gram", "tree", "wsum"}
     assert all(k["launches"] == 3 for k in rec["kernels"].values())

@@ -170,6 +170,50 @@ def test_tree_schedule_shape():
 
 # ---------------------------------------------------------------- invariants
 
+def test_operand_input_norms_hand_derived():
+    """Inputs with squared norms 1, 4, 9, 16, 25 (g_k = (k + 1) e_0, k = 0..4).
+    Tree: (g0, g1) -> n0, (g2, g3) -> n1, g4 carried; (n0, n1) -> n2, g4
+    carried; (n2, g4) -> n3.  So the operand sums are n0 (1, 4), n1 (9, 16),
+    n2 (1 + 4, 9 + 16), n3 (1 + 4 + 9 + 16, 25).  Chain over the first four:
+    (g0, g1), (g0..g1, g2), (g0..g2, g3) -> (1, 4), (5, 9), (14, 16)."""
+    vecs = [np.array([k + 1.0, 0.0]) for k in range(5)]
+    tree = oracle.operand_input_norms(vecs, "tree")
+    assert tree.tolist() == [[1.0, 4.0], [9.0, 16.0], [5.0, 25.0], [30.0, 25.0]]
+    chain = oracle.operand_input_norms(vecs[:4], "chain")
+    assert chain.tolist() == [[1.0, 4.0], [5.0, 9.0], [14.0, 16.0]]
+    assert oracle.operand_input_norms(vecs[:1], "tree").shape == (0, 2)
+    # the root's two sums cover every input once, whatever K
+    rng = np.random.default_rng(11)
+    for K in range(2, 12):
+        v = [rng.standard_normal(7) for _ in range(K)]
+        total = sum(float(x @ x) for x in v)
+        for sched in ("tree", "chain"):
+            root = oracle.operand_input_norms(v, sched)[-1]
+            assert abs(root.sum() - total) <= 1e-12 * total
+
+
+def test_discontinuity_mask_hand_derived():
+    """Scalars 1, -1 make the exactly zero node n0 = Adasum(1, -1) = 3/2 - 3/2.
+    Tree of (1, -1, 2, 3): n2 = (n0, n1), so only n2's left coefficient is
+    marked.  Tree of (1, -1, 2, 3, 4, 5, 6, 7): n4 = (n0, n1) is marked on
+    the left, and n6 = (n4, n5), which consumes n4, on both sides.  Chain of
+    (1, -1, 2, 3): n1 = (n0, 2) on the left, then n2 = (n1, 3) on both.
+    Inputs with no cancellation mark nothing; all-zero inputs mark nothing
+    (their coefficients are exactly 1)."""
+    def mask(vals, sched):
+        rows = [np.array([float(v)]) for v in vals]
+        fn = oracle.adasum_chain if sched == "chain" else oracle.adasum_tree
+        _, _, st = fn(rows)
+        return oracle.discontinuity_mask(st, oracle.operand_input_norms(rows, sched), sched).tolist()
+
+    assert mask([1, -1, 2, 3], "tree") == [[False, False], [False, False], [True, False]]
+    m8 = mask([1, -1, 2, 3, 4, 5, 6, 7], "tree")
+    assert m8 == [[False, False]] * 4 + [[True, False], [False, False], [True, True]]
+    assert mask([1, -1, 2, 3], "chain") == [[False, False], [True, False], [True, True]]
+    assert not np.any(mask([1, 2, 3, 4, 5], "tree"))
+    assert not np.any(mask([0, 0, 0, 0], "tree"))
+
+
 def test_symmetry_and_scale_invariance():
     rng = np.random.default_rng(5)
     a, b = rng.standard_normal(50), rng.standard_normal(50)
