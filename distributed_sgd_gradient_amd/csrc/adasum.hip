@@ -9,14 +9,20 @@
 //      every tile: the Gram partials of each block's operands, in fp64;
 //   2. tree: one launch over every (block, segment): tile partials summed in
 //      tile order, every merge of the block evaluated on the Gram matrix
-//      (statistics, coefficients), the final operand weights written;
+//      (statistics, coefficients), the final operand weights written.  In a
+//      stage over 16-bit inputs the walk also flags the pairs whose
+//      coefficients the matrix cores' fp32 rounding could move beyond
+//      tolerance; one launch per Gram launch recomputes their tiles exactly
+//      (the others return at once) and a second walk redoes only them;
 //   3. wsum: one launch per (block size, types) over every block and tile:
 //      the block's result, sum_k w_k x_k, into an fp32 slot or into out.
 // So a combine of K <= 16 gradients (K <= 32 for 16-bit ones) is three
-// launches and two passes over the inputs, whatever the number of segments.
+// launches (five for 16-bit inputs) and two passes over the inputs, whatever
+// the number of segments.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -184,8 +190,8 @@ std::map<std::pair<int, void*>, OwnedWorkspace> g_ws;  // (device, stream) -> bu
 
 // ---------------------------------------------------------------- launch timing
 
-enum KernelKind { kGram = 0, kTree, kWsum, kSum, kNumKinds };
-const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "sum"};
+enum KernelKind { kGram = 0, kTree, kWsum, kSum, kExact, kNumKinds };
+const char* const kKindNames[kNumKinds] = {"gram", "tree", "wsum", "sum", "exact"};
 
 struct ProfRecord {
   int kind;
@@ -398,9 +404,18 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
   hipError_t e;
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
   double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(b.ws + p.ws_flags);
   int stage_no = 0;
   for (const Stage& sg : p.stages) {
     ++stage_no;
+    // 16-bit Gram launches of this stage (the only inexact ones), for the
+    // exact recomputation of flagged (block, segment) pairs
+    struct Narrow {
+      GramArgs args;
+      DType t;
+      int nbt, njobs;
+    };
+    std::vector<Narrow> narrow_grams;
     // 1. Gram partials, blocks grouped by (operand types, Gram size)
     // 3. weighted sums, grouped by (operand types, Gram size, result type)
     for (int pass = 0; pass < 2; ++pass) {
@@ -444,6 +459,13 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             e = launch_gram(in_t, kind0.narrow_t, nbt, a, ntiles, n, st);
             prof_stop(pr, st);
             if (e != hipSuccess) return fail_hip(e, "launching gram");
+            if (in_t != DType::F32) {
+              Narrow nw{a, in_t, nbt, n};
+              for (int j = 0; j < n; ++j) nw.args.wrow[j] = p.descs[group[c + j]->desc].wrow;
+              nw.args.flags = flags;
+              nw.args.nseg = p.nseg;
+              narrow_grams.push_back(nw);
+            }
           } else {
             WsumArgs a{};
             for (int j = 0; j < n; ++j) {
@@ -484,6 +506,11 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         t.ortho = b.ortho;
         t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
         t.nblocks_total = p.nblocks;
+        // the matrix cores round each 32-row sum of exact 16-bit products to
+        // fp32 once (relative error 2^-24), with a margin for the fp64
+        // accumulation of the partials
+        t.gram_err = narrow_grams.empty() ? 0.0 : std::ldexp(1.0, -24) * (1.0 + std::ldexp(1.0, -10));
+        t.flags = flags;
         double bytes = 0;
         for (const Block& bk : sg.blocks) bytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
         log_launch("tree", stage_no, t.nblocks * p.nseg, 1, 0, bytes);
@@ -491,6 +518,29 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         e = launch_tree(t, st);
         prof_stop(pr, st);
         if (e != hipSuccess) return fail_hip(e, "launching tree");
+        if (!narrow_grams.empty()) {
+          // pairs whose coefficients the fp32 rounding could move by more
+          // than kRefineTol: their tiles recomputed exactly, then walked again
+          for (const Narrow& nw : narrow_grams) {
+            // algorithmic bytes: the flag of every tile (flagged tiles, none in
+            // the usual case, also re-read their operands)
+            const double fbytes = 4.0 * ntiles * nw.njobs;
+            log_launch("exact", stage_no, ntiles, nw.njobs, nw.nbt, fbytes);
+            const int pe = prof_start(kExact, fbytes, st);
+            e = launch_gram_exact(nw.t, nw.nbt, nw.args, ntiles, nw.njobs, st);
+            prof_stop(pe, st);
+            if (e != hipSuccess) return fail_hip(e, "launching exact gram");
+          }
+          TreeArgs r = t;
+          r.gram_err = 0.0;
+          r.refine = 1;
+          const double rbytes = 4.0 * t.nblocks * p.nseg;  // the flags
+          log_launch("tree", stage_no, t.nblocks * p.nseg, 1, 0, rbytes);
+          const int pt = prof_start(kTree, rbytes, st);
+          e = launch_tree(r, st);
+          prof_stop(pt, st);
+          if (e != hipSuccess) return fail_hip(e, "launching tree");
+        }
       }
     }
     if (ntiles == 0 && p.nseg > 0) {

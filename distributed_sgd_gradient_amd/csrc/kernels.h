@@ -18,6 +18,11 @@ struct GramArgs {
   int64_t poff[kMaxJobs];  // partials of tile t: partials + poff + t * gram_entries(nbt)
   const Tile* tiles;
   double* partials;
+  // exact recomputation only: the tiles of (block, segment) pairs whose
+  // flags[wrow[j]][segment] is set
+  const uint32_t* flags;
+  int32_t wrow[kMaxJobs];
+  int nseg;
 };
 
 // Tree walk: per (block, segment), sum the tile Gram partials in tile order,
@@ -37,7 +42,19 @@ struct TreeArgs {
   double* coeffs;           // [K-1][nseg][2]
   double* stats;            // [K-1][nseg][3]
   double* ortho;            // [nseg] or NULL: |result|^2 / sum_k |g_k|^2, written by the root block
+  // Every chunk sum behind a Gram entry carries a relative rounding error of
+  // at most gram_err (0: the entries are exact up to fp64 rounding).  With
+  // gram_err > 0 the walk sets flags[wrow][segment] to 1 where those errors
+  // could move a coefficient by more than kRefineTol of it, else to 0.
+  // refine = 1: only flagged pairs are walked (again).
+  double gram_err;
+  uint32_t* flags;          // [nblocks total][nseg]
+  int refine;
 };
+
+// Relative coefficient error bound above which a pair's Gram matrix is
+// recomputed exactly (the coefficient gate is 1e-6).
+constexpr double kRefineTol = 2.5e-7;
 
 // Weighted sum: per (block, tile), y = sum_k w_k x_k, rounded once; narrow
 // as for the Gram pass.
@@ -70,6 +87,9 @@ struct SumArgs {
 hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
                        hipStream_t st);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
+// 16-bit operands: the Gram partials of every tile of a flagged (block,
+// segment) pair, recomputed exactly (fp64 sums of exact products, row order).
+hipError_t launch_gram_exact(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st);
 hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
                        hipStream_t st);
 hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st);

@@ -542,31 +542,67 @@ __device__ __forceinline__ double widen16<bf16_t>(uint16_t bits) {
   return (double)__uint_as_float((uint32_t)bits << 16);
 }
 
-// The packed Gram triangle of rows [lo, lo + len), len <= kExactRows, of the
-// operands in `table` (NULL: zero) into out; sh holds NB * kExactRows
-// 16-bit values.  Called by every thread of the workgroup.
+// The packed Gram triangle of rows [lo, lo + len) of the operands in
+// `table` (NULL: zero) into out, every entry the fp64 row-order sum of exact
+// products.  The rows pass through sh (NB * kExactRows 16-bit values)
+// kExactRows at a time.  Called by every thread of the workgroup.
 template <typename T, int NB>
-__device__ void gram_exact_tile(const void* const* table, int64_t lo, int len, double* __restrict__ out,
+__device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t len, double* __restrict__ out,
                                 uint16_t* sh) {
-  for (int idx = threadIdx.x; idx < NB * len; idx += kBlock) {
-    const int k = idx / len, r = idx - k * len;
-    const uint16_t* x = static_cast<const uint16_t*>(table[k]);
-    sh[k * kExactRows + r] = x != nullptr ? gload(x + lo + r) : (uint16_t)0;
-  }
-  __syncthreads();
   constexpr int NE = gram_entries(NB);
-  for (int e = threadIdx.x; e < NE; e += kBlock) {
-    int i = 0, rem = e;
+  constexpr int EPT = (NE + kBlock - 1) / kBlock;  // entries per thread
+  int ei[EPT], ek[EPT];
+  double acc[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = threadIdx.x + q * kBlock;
+    int i = 0, rem = e < NE ? e : 0;
     while (rem >= NB - i) {
       rem -= NB - i;
       ++i;
     }
-    const uint16_t* a = sh + i * kExactRows;
-    const uint16_t* b = sh + (i + rem) * kExactRows;
-    double sum = 0.0;
-    for (int r = 0; r < len; ++r) sum += widen16<T>(a[r]) * widen16<T>(b[r]);  // exact product, one rounding
-    out[e] = sum;
+    ei[q] = i;
+    ek[q] = i + rem;
+    acc[q] = 0.0;
   }
+  for (int64_t c0 = 0; c0 < len; c0 += kExactRows) {
+    const int n = (int)min<int64_t>(kExactRows, len - c0);
+    if (c0 > 0) __syncthreads();  // the previous chunk is consumed
+    for (int idx = threadIdx.x; idx < NB * n; idx += kBlock) {
+      const int k = idx / n, r = idx - k * n;
+      const uint16_t* x = static_cast<const uint16_t*>(table[k]);
+      sh[k * kExactRows + r] = x != nullptr ? gload(x + lo + c0 + r) : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      if (threadIdx.x + q * kBlock >= NE) continue;
+      const uint16_t* x = sh + ei[q] * kExactRows;
+      const uint16_t* y = sh + ek[q] * kExactRows;
+      double sum = acc[q];
+      for (int r = 0; r < n; ++r) sum += widen16<T>(x[r]) * widen16<T>(y[r]);  // exact product, one rounding
+      acc[q] = sum;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < EPT; ++q)
+    if (threadIdx.x + q * kBlock < NE) out[threadIdx.x + q * kBlock] = acc[q];
+}
+
+// Exact recomputation of the Gram partials of every tile of a (block,
+// segment) pair that the tree walk flagged (see TreeArgs): the matrix-core
+// pass rounds each 32-row sum to fp32, which an ill-conditioned merge (a node
+// far smaller than the operands under it) could amplify beyond the
+// coefficient tolerance.  Tiles of other pairs return at once.
+template <typename T, int NB>
+__global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
+  __shared__ uint16_t sh[NB * kExactRows];
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] == 0) return;
+  gram_exact_rows<T, NB>(args.x[j], tile.start, tile.len,
+                         args.partials + args.poff[j] + (int64_t)tile_id * gram_entries(NB), sh);
 }
 
 // Blocks of up to 16 operands use one 16-operand half; the 32-operand block
@@ -590,7 +626,7 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
   const int64_t lo = tile.start, hi = tile.start + tile.len;
   if (tile.len <= kExactRows) {  // workgroup-uniform: a short tile, summed exactly
     static_assert(sizeof(red) >= sizeof(uint16_t) * NB * kExactRows, "staging fits the reduction buffer");
-    gram_exact_tile<T, NB>(args.x[j], lo, tile.len, args.partials + args.poff[j] + (int64_t)tile_id * NE,
+    gram_exact_rows<T, NB>(args.x[j], lo, tile.len, args.partials + args.poff[j] + (int64_t)tile_id * NE,
                            reinterpret_cast<uint16_t*>(&red[0][0][0]));
     return;
   }
@@ -814,6 +850,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   const int b = item / a.nseg;
   const int s = item % a.nseg;
   const BlockDesc d = a.descs[a.desc0 + b];
+  if (a.refine && a.flags[(int64_t)d.wrow * a.nseg + s] == 0) return;  // workgroup-uniform
   const int n = d.nbt;
   const int ne = gram_entries(n);
   const int tid = threadIdx.x;
@@ -849,7 +886,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   __shared__ DD rowL[kMaxOps], rowR[kMaxOps];
   __shared__ double cab[kMaxOps][2];
   __shared__ Merge ms[kMaxOps];
+  __shared__ int unsure;  // some coefficient may be off by more than kRefineTol (gram_err > 0)
   if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
+  if (tid == 0) unsure = 0;
   __syncthreads();
   for (int m0 = 0; m0 < d.nmerges;) {
     int m1 = m0 + 1;
@@ -879,6 +918,26 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
       cab[m0 + tid][0] = ca;
       cab[m0 + tid][1] = cb;
+      if (a.gram_err > 0.0) {
+        // The rounding errors of separate chunk sums are independent, so a
+        // quadratic form over an operand with weights w errs by about
+        // gram_err S, S = sum w_i^2 G_ii (the norm the operand would have if
+        // its parts were orthogonal): S <= A for parallel parts, S ~ A for
+        // orthogonal ones, S >> A only under cancellation.  (The worst case,
+        // with every error aligned, replaces S by (sum |w_i| sqrt(G_ii))^2,
+        // which exceeds A for any orthogonal parts and would flag ordinary
+        // data.)  c = 1 - d / (2A) then moves by about
+        // (|d err| + |d| |A err| / A) / (2A).  An operand whose norm the
+        // estimate cannot tell from zero is flagged too.
+        double sl = 0.0, sr = 0.0;
+        for (int i = l0; i < l1; ++i) sl += w[i] * w[i] * G[gram_index(n, i, i)];
+        for (int i = l1; i < r1; ++i) sr += w[i] * w[i] * G[gram_index(n, i, i)];
+        const double eA = a.gram_err * sl, eB = a.gram_err * sr, ed = a.gram_err * sqrt(fmax(sl * sr, 0.0));
+        bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
+        if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
+        if (B > eB) bad = bad || (ed + fabs(dd) * eB / B) / (2.0 * B) > kRefineTol * fmax(1.0, fabs(cb));
+        if (bad) unsure = 1;
+      }
       const int64_t at = (int64_t)mg.node * a.nseg + s;
       a.coeffs[at * 2] = ca;
       a.coeffs[at * 2 + 1] = cb;
@@ -909,6 +968,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   }
   __syncthreads();
   if (tid < kMaxOps) a.weights[((int64_t)d.wrow * a.nseg + s) * kMaxOps + tid] = w[tid];
+  if (tid == 0 && a.flags != nullptr && !a.refine) a.flags[(int64_t)d.wrow * a.nseg + s] = unsure;
 }
 
 // ----------------------------------------------------------------- weighted sum
@@ -1262,6 +1322,29 @@ hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(tree_kernel, dim3((unsigned)((int64_t)a.nblocks * a.nseg)), dim3(kBlock), 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_gram_exact(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+  const dim3 grid(ntiles, njobs);
+  switch (nbt) {
+    case 2: hipLaunchKernelGGL((gram_exact_kernel<T, 2>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gram_exact_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gram_exact_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((gram_exact_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((gram_exact_kernel<T, 32>), grid, dim3(kBlock), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_exact(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+  switch (operand) {
+    case DType::F16: return run_gram_exact<_Float16>(nbt, a, ntiles, njobs, st);
+    case DType::BF16: return run_gram_exact<bf16_t>(nbt, a, ntiles, njobs, st);
+    case DType::F32: break;  // the fp32 pass is exact already
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,

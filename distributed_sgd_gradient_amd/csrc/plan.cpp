@@ -242,6 +242,8 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   off = align256(off + p.table_bytes(2));
   p.ws_stats = off;
   off = align256(off + p.table_bytes(3));
+  p.ws_flags = off;
+  off = align256(off + (size_t)p.nblocks * nseg * sizeof(uint32_t));
   p.ws_total = off;
   return p;
 }

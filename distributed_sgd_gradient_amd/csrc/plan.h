@@ -15,10 +15,11 @@
 //     block needs one Gram pass over its operands, a small per-segment walk
 //     of its merges, and one weighted-sum pass that writes its result;
 //   * the workspace layout: fp32 slots for block results that feed a later
-//     stage, fp64 per-tile Gram partials, leaf weights, and the coefficient
-//     and statistic tables.  An input that a later stage reads (an odd vector
-//     carried up the tree, or the chain's next inputs) is read where it is,
-//     in its own dtype, next to the fp32 slots.
+//     stage, fp64 per-tile Gram partials, leaf weights, the coefficient and
+//     statistic tables, and per-(block, segment) flags of pairs whose Gram
+//     matrix is recomputed exactly.  An input that a later stage reads (an
+//     odd vector carried up the tree, or the chain's next inputs) is read
+//     where it is, in its own dtype, next to the fp32 slots.
 //
 // Pure C++: it makes no HIP call, so it can be exercised without a GPU.
 #pragma once
@@ -128,7 +129,7 @@ struct Plan {
 
   // workspace layout, byte offsets (each 256-aligned)
   size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_leafnorm = 0, ws_coeffs = 0, ws_stats = 0,
-         ws_total = 0;
+         ws_flags = 0, ws_total = 0;
   size_t table_bytes(int per_node) const { return (size_t)(K > 1 ? K - 1 : 0) * nseg * per_node * sizeof(double); }
 };
 

@@ -182,7 +182,7 @@ ADASUM_API int64_t adasum_sum_workspace_bytes(int K, int64_t N, int dtype);
  * most max_rows; rows may be NULL when max_rows is 0) or a negative code.
  */
 typedef struct {
-  char kernel[32];     /* "gram", "tree", "wsum", "widen", "sum" */
+  char kernel[32];     /* "gram", "tree", "exact", "wsum", "sum" */
   int launches;
   double milliseconds;
   double bytes;

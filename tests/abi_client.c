@@ -452,7 +452,9 @@ static void check_errors(hipStream_t stream) {
   case_free(&c);
 }
 
-/* The kernel timing interface reports the three launches of a combine. */
+/* The kernel timing interface reports the launches of a combine: over fp16
+   inputs the Gram pass, the tree walk, the exact recomputation of flagged
+   pairs, the second walk over them and the weighted sum. */
 static void check_profile(hipStream_t stream) {
   Case c;
   case_alloc(&c, 8, ADASUM_F16, ADASUM_TREE);
@@ -464,13 +466,15 @@ static void check_profile(hipStream_t stream) {
   const int nrows = adasum_profile_end(rows, 8);
   int seen = 0;
   for (int r = 0; r < nrows; ++r) {
-    const int known = !strcmp(rows[r].kernel, "gram") || !strcmp(rows[r].kernel, "tree") ||
-                      !strcmp(rows[r].kernel, "wsum");
-    if (known && rows[r].launches == 1 && rows[r].milliseconds > 0 && rows[r].bytes > 0) ++seen;
+    const int want = !strcmp(rows[r].kernel, "tree") ? 2
+                     : (!strcmp(rows[r].kernel, "gram") || !strcmp(rows[r].kernel, "wsum") ||
+                        !strcmp(rows[r].kernel, "exact")) ? 1 : 0;
+    if (want && rows[r].launches == want && rows[r].milliseconds > 0 && rows[r].bytes > 0) ++seen;
   }
-  char detail[64];
-  snprintf(detail, sizeof detail, "%d rows, %d of gram/tree/wsum as expected", nrows, seen);
-  report(ok && nrows == 3 && seen == 3, "adasum_profile reports gram, tree, wsum", ok && seen == 3 ? "" : detail);
+  char detail[80];
+  snprintf(detail, sizeof detail, "%d rows, %d of gram/tree/exact/wsum as expected", nrows, seen);
+  report(ok && nrows == 4 && seen == 4, "adasum_profile reports gram, tree (twice), exact, wsum",
+         ok && seen == 4 ? "" : detail);
   case_free(&c);
 }
 

@@ -216,6 +216,27 @@ def test_short_random_segments(gpu, K, dtype):
     full_check(wl, f"short K={K} {dtype}")
 
 
+@pytest.mark.parametrize("K,dtype", [(4, "bf16"), (4, "f16"), (32, "bf16"), (32, "f16")])
+def test_long_near_cancelling_pairs_16bit(gpu, K, dtype):
+    """Long segments (tens of thousands of elements, many matrix-core tiles)
+    where every odd worker nearly cancels its even neighbour:
+    g_{2m+1} = -g_{2m} + 0.01 n.  Each level-1 node is then about 1/100 of
+    its operands, and the level-2 merge sees a 1e-4 cancellation: the fp32
+    rounding of the matrix cores' 32-row sums alone would move its
+    coefficients by about 1e-3.  The walk must flag those pairs, have their
+    Gram matrices recomputed exactly, and meet the coefficient gate."""
+    lengths = [70000, 33000, 300, 5]
+    base = W.random_case(K, lengths, dtype="f32", seed=90 + K, kind="normal")
+    grads = []
+    for k in range(K):
+        g = base.grads[k].double()
+        if k % 2 == 1:
+            g = -base.grads[k - 1].double() + 0.01 * g
+        grads.append(g.float().to({"bf16": torch.bfloat16, "f16": torch.float16}[dtype]).to(gpu))
+    wl = W.Workload(K=K, dtype=dtype, seg_offsets=base.seg_offsets, grads=grads, seed=base.seed)
+    full_check(wl, f"near-cancelling K={K} {dtype}")
+
+
 # ---------------------------------------------------------------- edge cases
 
 RAGGED = [1, 3, 8, 9, 0, 8191, 8192, 8193, 20000, 5, 16, 17]

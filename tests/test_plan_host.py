@@ -206,6 +206,6 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         assert all(x % 256 == 0 for x in ws) and ws == sorted(ws)
         nodes = max(K - 1, 0)
         sizes = [P["nslots"] * N * 4, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
-                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8]
+                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4]
         for r, size in enumerate(sizes):
             assert ws[r] + size <= ws[r + 1], (K, r)
