@@ -12,13 +12,18 @@
 //           upper triangle) on the matrix cores: fp64 instructions on the
 //           widened values (exact products, fp64 sums) for fp32 operands,
 //           32-row sums of exact products added in fp64 for 16-bit
-//           operands; reduced across the workgroup in a fixed order;
+//           operands (tiles of at most 256 rows: exact products summed in
+//           fp64); reduced across the workgroup in a fixed order;
 //   tree  - per segment: the tile partials summed in tile order, then the
 //           block's merges evaluated on the Gram matrix level by level:
 //           d = wL.G.wR, A = wL.G.wL, B = wR.G.wR, ca = 1 - d/(2A),
 //           cb = 1 - d/(2B) (coefficient 1 for a zero norm), and the
 //           weights of the merged operands scaled by ca and cb;
 //   wsum  - one pass: y = sum_k w_k x_k in fp64, rounded once.
+// Over 16-bit operands the walk also flags the (block, segment) pairs whose
+// coefficients the fp32 rounding of the matrix-core sums could move beyond
+// tolerance (a merge under cancellation); gram_exact recomputes their Gram
+// partials exactly and the walk is repeated for them alone.
 // The merge walk's quadratic forms are summed in double-double from exact
 // products, and the weighted sum uses separately rounded products and sums
 // (no fused multiply-add); either way mirrored terms cancel exactly: an
