@@ -830,6 +830,13 @@ __device__ __forceinline__ DD dd_scale(DD x, double b) {
   return DD{hi, p.lo - (hi - p.hi)};
 }
 
+__device__ __forceinline__ DD dd_mul(DD x, DD y) {
+  DD p = dd_prod(x.hi, y.hi);
+  p.lo += x.hi * y.lo + x.lo * y.hi;
+  const double hi = p.hi + p.lo;
+  return DD{hi, p.lo - (hi - p.hi)};
+}
+
 // sum_{i in [a0,a1)} w_i * (sum_{k in [b0,b1)} w_k G(i,k))
 __device__ double quad_form(const double* G, int n, const double* w, int a0, int a1, int b0, int b1) {
   double total = 0.0;
@@ -850,7 +857,11 @@ constexpr int kTreeWaves = kBlock / 64;
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   __shared__ double part[kTreeWaves][gram_entries(kMaxOps)];
   __shared__ double G[gram_entries(kMaxOps)];
-  __shared__ double w[kMaxOps];
+  // operand weights: products of the coefficients of the merges above each
+  // operand, in double-double (a chain multiplies up to K - 1 of them, and a
+  // node that nearly cancels would amplify their fp64 rounding)
+  __shared__ DD w[kMaxOps];
+  __shared__ double wf[kMaxOps];  // the weights rounded to fp64
   const int item = blockIdx.x;
   const int b = item / a.nseg;
   const int s = item % a.nseg;
@@ -877,7 +888,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     for (int i = 1; i < kTreeWaves; ++i) sum += part[i][e];
     G[e] = sum;
   }
-  if (tid < kMaxOps) w[tid] = 1.0;
+  if (tid < kMaxOps) w[tid] = DD{1.0, 0.0};
   __syncthreads();
   // Merges run level by level: merges of a block are stored children
   // before parents, and the merges of one level cover disjoint operand
@@ -905,8 +916,8 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     if (mine >= 0) {
       const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
       DD sl{0.0, 0.0}, sr{0.0, 0.0};
-      for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_prod(w[k], gram_at(G, n, tid, k)));
-      for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_prod(w[k], gram_at(G, n, tid, k)));
+      for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_scale(w[k], gram_at(G, n, tid, k)));
+      for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_scale(w[k], gram_at(G, n, tid, k)));
       rowL[tid] = sl;
       rowR[tid] = sr;
     }
@@ -915,9 +926,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       const Merge mg = ms[m0 + tid];
       const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
       DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
-      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_scale(rowL[i], w[i]));
-      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_scale(rowR[i], w[i]));
-      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_scale(rowR[i], w[i]));
+      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_mul(rowL[i], w[i]));
+      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_mul(rowR[i], w[i]));
+      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_mul(rowR[i], w[i]));
       const double A = a2.hi, B = b2.hi, dd = ab.hi;  // normalised: hi is the rounded sum
       const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
@@ -935,8 +946,8 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
         // (|d err| + |d| |A err| / A) / (2A).  An operand whose norm the
         // estimate cannot tell from zero is flagged too.
         double sl = 0.0, sr = 0.0;
-        for (int i = l0; i < l1; ++i) sl += w[i] * w[i] * G[gram_index(n, i, i)];
-        for (int i = l1; i < r1; ++i) sr += w[i] * w[i] * G[gram_index(n, i, i)];
+        for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
+        for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
         const double eA = a.gram_err * sl, eB = a.gram_err * sr, ed = a.gram_err * sqrt(fmax(sl * sr, 0.0));
         bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
         if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
@@ -951,10 +962,12 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       a.stats[at * 3 + 2] = B;
     }
     __syncthreads();
-    if (mine >= 0) w[tid] = mul_rn(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
+    if (mine >= 0) w[tid] = dd_scale(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
     __syncthreads();
     m0 = m1;
   }
+  if (tid < kMaxOps) wf[tid] = w[tid].hi;  // normalised: hi is the rounded value
+  __syncthreads();
   if (tid == 0) {
     // sum of |g_k|^2 over the block's input operands, in operand order
     double leaf = 0.0;
@@ -967,12 +980,12 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       double total = 0.0;
       for (int r = 0; r < a.nblocks_total; ++r)
         total += (r == d.wrow) ? leaf : a.leafnorm[(int64_t)r * a.nseg + s];
-      const double out2 = quad_form(G, n, w, 0, d.nb, 0, d.nb);
+      const double out2 = quad_form(G, n, wf, 0, d.nb, 0, d.nb);
       a.ortho[s] = (total == 0.0) ? __builtin_nan("") : out2 / total;
     }
   }
   __syncthreads();
-  if (tid < kMaxOps) a.weights[((int64_t)d.wrow * a.nseg + s) * kMaxOps + tid] = w[tid];
+  if (tid < kMaxOps) a.weights[((int64_t)d.wrow * a.nseg + s) * kMaxOps + tid] = wf[tid];
   if (tid == 0 && a.flags != nullptr && !a.refine) a.flags[(int64_t)d.wrow * a.nseg + s] = unsure;
 }
 
