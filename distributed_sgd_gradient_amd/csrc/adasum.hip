@@ -78,6 +78,7 @@ struct DeviceTables {
   int32_t* seg_tile = nullptr;
   BlockDesc* descs = nullptr;
   Merge* merges = nullptr;
+  int64_t* short_off = nullptr;
 };
 
 struct CachedPlan {
@@ -105,6 +106,7 @@ void release_tables(CachedPlan& cp) {
     (void)hipFree(kv.second.seg_tile);
     (void)hipFree(kv.second.descs);
     (void)hipFree(kv.second.merges);
+    (void)hipFree(kv.second.short_off);
   }
   (void)hipSetDevice(cur);
 }
@@ -154,6 +156,7 @@ int device_tables(CachedPlan& cp, int device, DeviceTables* out) {
       {reinterpret_cast<void**>(&t.seg_tile), p.seg_tile.data(), sizeof(int32_t) * p.seg_tile.size()},
       {reinterpret_cast<void**>(&t.descs), p.descs.data(), sizeof(BlockDesc) * p.descs.size()},
       {reinterpret_cast<void**>(&t.merges), p.merges.data(), sizeof(Merge) * p.merges.size()},
+      {reinterpret_cast<void**>(&t.short_off), p.short_off.data(), sizeof(int64_t) * p.short_off.size()},
   };
   int rc = ADASUM_OK;
   for (Upload& u : ups) {
@@ -442,11 +445,13 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
           double in_bytes = 0, out_bytes = 0;
           if (pass == 0) {
             GramArgs a{};
+            std::memset(a.side_slot, -1, sizeof a.side_slot);
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
               for (size_t k = 0; k < bk.operands.size(); ++k) {
                 a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
                 in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
+                if (bk.operands[k].kind == Ref::Slot) a.side_slot[j][k] = bk.operands[k].idx;
               }
               a.narrow[j] = block_kind(p, bk).narrow;
               a.poff[j] = p.descs[bk.desc].poff;
@@ -454,6 +459,11 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             }
             a.tiles = dt.tiles;
             a.partials = partials;
+            if (p.short_rows > 0 && in_t == DType::F32) {
+              a.side = reinterpret_cast<const double*>(b.ws + p.ws_side);
+              a.short_off = dt.short_off;
+              a.short_rows = p.short_rows;
+            }
             log_launch("gram", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kGram, in_bytes + out_bytes, st);
             e = launch_gram(in_t, kind0.narrow_t, nbt, a, ntiles, n, st);
@@ -478,10 +488,13 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
               a.y[j] = ref_ptr(p, b, bk.dst);
               a.wrow[j] = p.descs[bk.desc].wrow;
               out_bytes += (double)p.N * dtype_size(out_t);
+              if (bk.dst.kind == Ref::Slot && p.short_rows > 0)
+                a.side[j] = reinterpret_cast<double*>(b.ws + p.ws_side) + (size_t)bk.dst.idx * (size_t)p.short_rows;
             }
             a.tiles = dt.tiles;
             a.nseg = p.nseg;
             a.weights = weights;
+            a.short_off = dt.short_off;
             log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
             e = launch_wsum(in_t, kind0.narrow_t, nbt, out_t, a, ntiles, n, st);

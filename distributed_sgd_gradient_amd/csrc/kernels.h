@@ -23,7 +23,17 @@ struct GramArgs {
   const uint32_t* flags;
   int32_t wrow[kMaxJobs];
   int nseg;
+  // fp32 operands only: operand k of job j is the fp32 slot side_slot[j][k]
+  // (-1: not a slot); a short tile (short_off[t] >= 0) whose job reads a slot
+  // takes that slot's rows from its fp64 side buffer, side + slot *
+  // short_rows + short_off[t], and sums its Gram matrix exactly.  short_off
+  // NULL: no side buffers.
+  const double* side;
+  const int64_t* short_off;
+  int64_t short_rows;
+  int32_t side_slot[kMaxJobs][kMaxOps];
 };
+static_assert(sizeof(GramArgs) <= 4096, "kernel arguments fit 4 KB");
 
 // Tree walk: per (block, segment), sum the tile Gram partials in tile order,
 // then evaluate the block's merges on the Gram matrix: statistics,
@@ -66,7 +76,13 @@ struct WsumArgs {
   const Tile* tiles;
   int nseg;
   const double* weights;
+  // a job whose result is an fp32 slot also writes the fp64 sums of short
+  // tiles to its side buffer, side[j][short_off[t] + row - tile start]
+  // (side[j] NULL: not a slot, or no short tiles)
+  double* side[kMaxJobs];
+  const int64_t* short_off;
 };
+static_assert(sizeof(WsumArgs) <= 4096, "kernel arguments fit 4 KB");
 
 // Plain sum of up to kSumOps operands, element by element in fp64, in
 // operand order: acc = (acc_in ? acc_in : 0) + x0 + x1 + ...; the result goes

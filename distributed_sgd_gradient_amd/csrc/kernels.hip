@@ -289,6 +289,21 @@ __device__ __forceinline__ void load_n16x8(const uint16_t* __restrict__ x, int64
 // 16-bit lane reads 16 bytes at once (an fp32 lane two times 16); any
 // assignment of rows to the instruction steps gives the same Gram matrix, as
 // long as every operand lane uses the same row at each step.
+// Operand op of job j at a row of a short tile, in fp64: from the slot's
+// side buffer (srow: the row's position there) when it is a slot, else the
+// operand itself (fp32, or a 16-bit input marked narrow), widened exactly.
+template <typename TN>
+__device__ __forceinline__ double operand_f64(const GramArgs& a, int j, int op, int64_t row, int64_t srow) {
+  const int slot = a.side_slot[j][op];
+  if (slot >= 0) return a.side[(int64_t)slot * a.short_rows + srow];
+  const void* p = a.x[j][op];
+  if (p == nullptr) return 0.0;
+  if constexpr (!std::is_same<TN, float>::value) {
+    if ((a.narrow[j] >> op) & 1u) return (double)narrow_to_f32<TN>(gload(static_cast<const uint16_t*>(p) + row));
+  }
+  return (double)gload(static_cast<const float*>(p) + row);
+}
+
 template <int NB, typename TN>
 __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
   constexpr bool kMixed = !std::is_same<TN, float>::value;
@@ -304,6 +319,31 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
   const int64_t lo = tile.start, hi = tile.start + tile.len;
+  if (args.short_off != nullptr && tile.len <= kExactRows) {  // workgroup-uniform
+    bool slots = false;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) slots = slots || args.side_slot[j][k] >= 0;
+    if (slots) {
+      // a short tile of a stage above the first: slot operands from their
+      // fp64 side buffers (not the fp32-rounded slots), every entry summed
+      // in fp64 row by row
+      const int64_t so = args.short_off[tile_id];
+      double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+      for (int e = threadIdx.x; e < NE; e += kBlock) {
+        int i = 0, rem = e;
+        while (rem >= NB - i) {
+          rem -= NB - i;
+          ++i;
+        }
+        const int k = i + rem;
+        double sum = 0.0;
+        for (int r = 0; r < tile.len; ++r)
+          sum += operand_f64<TN>(args, j, i, lo + r, so + r) * operand_f64<TN>(args, j, k, lo + r, so + r);
+        out[e] = sum;
+      }
+      return;
+    }
+  }
   const int64_t first = lo & ~int64_t(kGroup - 1);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -533,8 +573,7 @@ __device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, int s) {
 // segments are where operands can nearly cancel by chance (a segment of a
 // few elements is a short random vector); there the fp32 rounding of a
 // 32-row matrix-core sum, amplified by the cancellation, would reach the
-// coefficients.
-constexpr int kExactRows = 256;
+// coefficients.  (kExactRows: the plan's short-tile limit.)
 
 template <typename T>
 __device__ __forceinline__ double widen16(uint16_t bits);
@@ -1038,6 +1077,7 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   const int tid = threadIdx.x;
   double unused;
 
+
   auto load1 = [&](int k, int64_t i) -> float {
     if constexpr (kMixed) {
       if (nk[k]) return narrow_to_f32<TN>(gload(reinterpret_cast<const uint16_t*>(xs[k]) + i));
@@ -1053,6 +1093,25 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
     }
     Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
   };
+
+  if (args.side[j] != nullptr && tile.len <= kExactRows) {
+    // a short tile of a result that feeds a later stage: element by element,
+    // each fp64 sum also kept in the side buffer (row i at side[i + shift])
+    // for that stage's exact Gram sum
+    double* __restrict__ side = args.side[j];
+    const int64_t shift = args.short_off[tile_id] - tile.start;
+    for (int64_t i = sp.lo + tid; i < sp.hi; i += kBlock) {
+      double acc = 0.0;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const double t = mul_rn(w[k], (double)load1(k, i));
+        acc = add_rn(acc, live[k] ? t : 0.0);
+      }
+      Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
+      side[i + shift] = acc;
+    }
+    return;
+  }
 
   if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
   // Operand-outer: the raw loads of all operands are in flight together,

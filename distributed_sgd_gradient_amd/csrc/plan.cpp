@@ -146,6 +146,13 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   }
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
   const size_t ntiles = p.tiles.size();
+  p.short_off.assign(ntiles, -1);
+  for (size_t t = 0; t < ntiles; ++t) {
+    if (p.tiles[t].len <= kExactRows) {
+      p.short_off[t] = p.short_rows;
+      p.short_rows += p.tiles[t].len;
+    }
+  }
 
   // ---- blocks, stage by stage.  An operand of a stage above the first is
   // an fp32 slot (the result of a lower block) or an input gradient that the
@@ -244,6 +251,8 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   off = align256(off + p.table_bytes(3));
   p.ws_flags = off;
   off = align256(off + (size_t)p.nblocks * nseg * sizeof(uint32_t));
+  p.ws_side = off;
+  off = align256(off + (size_t)p.nslots * (size_t)p.short_rows * sizeof(double));
   p.ws_total = off;
   return p;
 }

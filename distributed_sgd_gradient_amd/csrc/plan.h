@@ -16,8 +16,9 @@
 //     of its merges, and one weighted-sum pass that writes its result;
 //   * the workspace layout: fp32 slots for block results that feed a later
 //     stage, fp64 per-tile Gram partials, leaf weights, the coefficient and
-//     statistic tables, and per-(block, segment) flags of pairs whose Gram
-//     matrix is recomputed exactly.  An input that a later stage reads (an
+//     statistic tables, per-(block, segment) flags of pairs whose Gram
+//     matrix is recomputed exactly, and the fp64 side buffers of the fp32
+//     slots (their rows in short tiles).  An input that a later stage reads (an
 //     odd vector carried up the tree, or the chain's next inputs) is read
 //     where it is, in its own dtype, next to the fp32 slots.
 //
@@ -39,6 +40,11 @@ constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
 constexpr int kMaxOps = 32;      // operands per block over 16-bit inputs: five tree levels
 constexpr int kMaxOps32 = 16;    // operands per block over fp32 operands: four tree levels
 constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
+// Tiles of at most kExactRows rows are short: their Gram matrices are summed
+// exactly, and a block result that feeds a later stage also keeps their rows
+// in fp64 (the side buffer), since short segments are where merges nearly
+// cancel by chance.
+constexpr int kExactRows = 256;
 // The weighted sum cuts every tile into aligned parts, one workgroup each,
 // so that a workgroup's range holds 16 KB of every operand of a full tile:
 // 8 parts for fp32 inputs, 4 for 16-bit ones.  It streams best with shorter
@@ -120,6 +126,8 @@ struct Plan {
   std::vector<int64_t> offsets;   // nseg + 1
   std::vector<Tile> tiles;
   std::vector<int32_t> seg_tile;  // nseg + 1: tiles of segment s are [seg_tile[s], seg_tile[s+1])
+  std::vector<int64_t> short_off; // per tile: first row of a short tile in the side buffers, else -1
+  int64_t short_rows = 0;         // rows of all short tiles
   std::vector<Stage> stages;
   std::vector<BlockDesc> descs;
   std::vector<Merge> merges;
@@ -129,7 +137,7 @@ struct Plan {
 
   // workspace layout, byte offsets (each 256-aligned)
   size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_leafnorm = 0, ws_coeffs = 0, ws_stats = 0,
-         ws_flags = 0, ws_total = 0;
+         ws_flags = 0, ws_side = 0, ws_total = 0;
   size_t table_bytes(int per_node) const { return (size_t)(K > 1 ? K - 1 : 0) * nseg * per_node * sizeof(double); }
 };
 

@@ -39,9 +39,12 @@ static void dump(const Plan& p, int dt, int sched, int K) {
     printf("%s[%lld,%d,%d]", t ? "," : "", (long long)p.tiles[t].start, p.tiles[t].len, p.tiles[t].seg);
   printf("], \"seg_tile\": [");
   for (size_t s = 0; s < p.seg_tile.size(); ++s) printf("%s%d", s ? "," : "", p.seg_tile[s]);
-  printf("], \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
+  printf("], \"short_off\": [");
+  for (size_t t = 0; t < p.short_off.size(); ++t) printf("%s%lld", t ? "," : "", (long long)p.short_off[t]);
+  printf("], \"short_rows\": %lld", (long long)p.short_rows);
+  printf(", \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
          p.partial_doubles, p.ws_slots, p.ws_partials, p.ws_weights, p.ws_leafnorm, p.ws_coeffs, p.ws_stats,
-         p.ws_flags, p.ws_total, p.nblocks);
+         p.ws_flags, p.ws_side, p.ws_total, p.nblocks);
 }
 
 int main(int argc, char** argv) {

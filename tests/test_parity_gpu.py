@@ -256,18 +256,9 @@ def test_small_K_ragged_segments(gpu, K, dtype):
     full_check(wl, f"ragged K={K} {dtype}")
 
 
-FP32_STAGE_LIMIT = pytest.mark.xfail(
-    reason="block results that cross a stage boundary are stored in fp32; in this case's one-element "
-           "segment a later merge cancels its operand to 4e-5 of its parts, which turns the 2^-24 storage "
-           "rounding into a 1.8e-6 coefficient error (the oracle keeps fp64); the pairs the walk could flag "
-           "there have no exact recomputation yet", strict=False)
-
-
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 48, 63, 64, 65, 70, 130])
-def test_multistage_K(gpu, K, dtype, request):
-    if (K, dtype) == (130, "f32"):
-        request.applymarker(FP32_STAGE_LIMIT)
+def test_multistage_K(gpu, K, dtype):
     # more than 16 operands: one block of 32 (at most 32 16-bit inputs), else
     # blocks of 16 with fp32 block results and carried inputs; K = 130 has
     # stage positions beyond 127

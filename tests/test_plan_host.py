@@ -206,6 +206,16 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         assert all(x % 256 == 0 for x in ws) and ws == sorted(ws)
         nodes = max(K - 1, 0)
         sizes = [P["nslots"] * N * 4, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
-                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4]
+                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4,
+                 P["nslots"] * P["short_rows"] * 8]
+        # short tiles (at most 256 rows) numbered consecutively in the side buffers
+        pos = 0
+        for (start, length, seg), so in zip(tiles, P["short_off"]):
+            if length <= 256:
+                assert so == pos
+                pos += length
+            else:
+                assert so == -1
+        assert pos == P["short_rows"]
         for r, size in enumerate(sizes):
             assert ws[r] + size <= ws[r + 1], (K, r)
