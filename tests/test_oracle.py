@@ -214,6 +214,48 @@ def test_discontinuity_mask_hand_derived():
     assert not np.any(mask([0, 0, 0, 0], "tree"))
 
 
+@pytest.mark.parametrize("sched", ["tree", "chain"])
+def test_operand_input_norms_equal_operand_norms_for_orthogonal_inputs(sched):
+    """Orthogonal inputs are summed, so every operand of every node is the
+    plain sum of the inputs under it and its squared norm (the walk's own
+    |a|^2 and |b|^2) equals the summed squared norms of those inputs."""
+    rng = np.random.default_rng(12)
+    for K in (2, 3, 5, 8, 11, 16, 17):
+        q, _ = np.linalg.qr(rng.standard_normal((24, K)))
+        vecs = [q[:, k] * rng.uniform(0.1, 10.0) for k in range(K)]
+        fn = oracle.adasum_chain if sched == "chain" else oracle.adasum_tree
+        _, _, st = fn(vecs)
+        got = oracle.operand_input_norms(vecs, sched)
+        np.testing.assert_allclose(got, np.asarray(st)[:, 1:3], rtol=1e-12)
+
+
+@pytest.mark.parametrize("sched,K", [("tree", 8), ("tree", 13), ("chain", 6)])
+def test_discontinuity_mask_marks_exactly_the_coefficients_that_jump(sched, K):
+    """Inputs 2 and 3 (tree) or 0 and 1 (chain) are u and -u, whose merge is
+    exactly zero (coefficient 1 above it).  Replacing -u by -(1 + 1e-6) u
+    leaves a tiny nonzero merge.  A coefficient that depends continuously on
+    the inputs moves by O(1e-6) (here at most 7e-7); the consumer's
+    coefficient of the tiny operand and both coefficients of every node above
+    it jump by O(1) in the geometry of the inputs (here at least 2.7e-3 in 4
+    dimensions).  Exactly the coefficients that move by more than 3e-5 must
+    be marked, for the exact and for the perturbed inputs."""
+    rng = np.random.default_rng(13)
+    vecs = [rng.standard_normal(4) for _ in range(K)]
+    i = 2 if sched == "tree" else 0
+    fn = oracle.adasum_chain if sched == "chain" else oracle.adasum_tree
+    vecs[i + 1] = -vecs[i]
+    _, c0, s0 = fn(vecs)
+    pert = list(vecs)
+    pert[i + 1] = -(1.0 + 1e-6) * vecs[i]
+    _, c1, s1 = fn(pert)
+    c0, c1 = np.asarray(c0), np.asarray(c1)
+    jumped = np.abs(c1 - c0) > 3e-5 * np.maximum(1.0, np.abs(c0))
+    assert jumped.sum() >= 3
+    for st, v in ((s0, vecs), (s1, pert)):
+        m = oracle.discontinuity_mask(st, oracle.operand_input_norms(v, sched), sched)
+        np.testing.assert_array_equal(m, jumped)
+
+
 def test_symmetry_and_scale_invariance():
     rng = np.random.default_rng(5)
     a, b = rng.standard_normal(50), rng.standard_normal(50)
@@ -280,6 +322,46 @@ def test_plain_sum_exact_order():
     rng = np.random.default_rng(10)
     vecs = [rng.integers(-1000, 1000, size=20).astype(float) for _ in range(6)]
     np.testing.assert_array_equal(oracle.plain_sum(vecs)["out"], np.sum(vecs, axis=0))
+    # values spread over 40 binades, where the order of the additions shows:
+    # each IEEE addition is the exact sum rounded once, float(Fraction + Fraction)
+    vecs = [rng.standard_normal(50) * np.exp2(rng.integers(-20, 20, size=50)) for _ in range(6)]
+    want = []
+    for j in range(50):
+        acc = vecs[0][j]
+        for v in vecs[1:]:
+            acc = float(Fraction(acc) + Fraction(v[j]))
+        want.append(acc)
+    got = oracle.plain_sum(vecs)["out"]
+    assert got.tolist() == want
+    assert oracle.plain_sum(vecs[::-1])["out"].tolist() != want  # the data is order-sensitive
+
+
+def test_plain_sum_left_to_right_rounding():
+    """Worker order decides the fp64 result: 1 + 2^53 is a tie between 2^53
+    and 2^53 + 2 and rounds to the even 2^53, so 1 + 2^53 - 2^53 = 0, while
+    2^53 - 2^53 + 1 = 1 and -2^53 + 2^53 + 1 = 1."""
+    big = 2.0 ** 53
+    assert oracle.plain_sum([np.array([1.0]), np.array([big]), np.array([-big])])["out"][0] == 0.0
+    assert oracle.plain_sum([np.array([big]), np.array([-big]), np.array([1.0])])["out"][0] == 1.0
+    assert oracle.plain_sum([np.array([-big]), np.array([big]), np.array([1.0])])["out"][0] == 1.0
+
+
+def test_orthogonality_closed_forms():
+    """Parallel inputs are averaged, so the pair (u, 3u) gives 2u and the
+    ratio |2u|^2 / (|u|^2 + |3u|^2) = 4/10; an anti-parallel pair of equal
+    norms gives 0; two orthogonal inputs give 1.  The hand-worked tree of
+    four inputs (tests/golden, tree_K4) has result (37/68, 325/136) over
+    inputs of squared norms 1, 2, 4, 2: ratio 111101/166464."""
+    u = np.array([1.0, -2.0, 0.5])
+    assert oracle.orthogonality([u, 3 * u], [0, 3])[0] == pytest.approx(0.4, rel=1e-14)
+    assert oracle.orthogonality([u, -u], [0, 3])[0] == 0.0
+    assert oracle.orthogonality([np.array([3.0, 0.0]), np.array([0.0, 5.0])], [0, 2])[0] == pytest.approx(1.0, rel=1e-15)
+    ex = next(e for e in _golden() if e["name"] == "tree_K4")
+    vecs = [np.array([float(Fraction(v)) for v in vec]) for vec in ex["inputs"]]
+    want = float(sum(Fraction(v) ** 2 for v in ex["result"]) /
+                 sum(Fraction(v) ** 2 for vec in ex["inputs"] for v in vec))
+    assert want == pytest.approx(111101 / 166464, rel=1e-15)
+    assert oracle.orthogonality(vecs, [0, 2])[0] == pytest.approx(want, rel=1e-14)
 
 
 def test_orthogonality_zero_segment_nan():
