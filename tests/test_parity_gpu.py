@@ -130,10 +130,11 @@ def full_check(wl, label, schedule="tree"):
     return got, ref, err
 
 
-def sampled_check(wl, segments, label):
+def sampled_check(wl, segments, label, schedule="tree"):
     """Full-size run; compare the chosen segments one by one with the oracle."""
-    say(label, f"K={wl.K} dtype={wl.dtype} N={wl.N} nseg={wl.nseg} sampled={len(segments)}")
-    out, coeffs, stats = run_gpu(wl)
+    say(label, f"K={wl.K} dtype={wl.dtype} N={wl.N} nseg={wl.nseg} sampled={len(segments)} schedule={schedule}")
+    out, coeffs, stats = run_gpu(wl, schedule)
+    walk = oracle.adasum_chain if schedule == "chain" else oracle.adasum_tree
     c_all = coeffs.cpu().numpy()
     s_all = stats.cpu().numpy()
     worst = 0.0
@@ -141,16 +142,16 @@ def sampled_check(wl, segments, label):
     for s in segments:
         lo, hi = int(wl.seg_offsets[s]), int(wl.seg_offsets[s + 1])
         rows = wl.segment_host(s)
-        res, cf, st = oracle.adasum_tree(rows)
+        res, cf, st = walk(rows)
         ref = oracle.round_to_format(res, wl.dtype)
         got = out[lo:hi].double().cpu().numpy()
         num += float(np.sum((got - ref) ** 2))
         den += float(np.sum(ref ** 2))
         st = np.asarray(st).reshape(-1, 3)
-        opn = oracle.operand_input_norms(rows, "tree")
+        opn = oracle.operand_input_norms(rows, schedule)
         worst = max(worst, check_coeffs(c_all[:, s], np.asarray(cf).reshape(-1, 2), f"{label} seg {s}",
-                                        unstable(st, opn)))
-        check_stats(s_all[:, s], st, f"{label} seg {s}", opn)
+                                        unstable(st, opn, schedule)))
+        check_stats(s_all[:, s], st, f"{label} seg {s}", opn, schedule)
     err = np.sqrt(num / den) if den > 0 else np.sqrt(num)
     say(label, f"sampled relative L2 {err:.3g}, worst coefficient error {worst:.3g}")
     assert err <= TOL[wl.dtype]
@@ -176,12 +177,13 @@ def _spread(nseg, rng, extra=()):
     return sorted(pick)
 
 
-def test_config3_sampled_full_size(gpu):
-    # the BERT-Large workload at full size, as the benchmark runs it
+@pytest.mark.parametrize("schedule", ["tree", "chain"])
+def test_config3_sampled_full_size(gpu, schedule):
+    # the BERT-Large workload at full size, as the benchmark runs it (and as a chain)
     wl = W.make_workload(3, device=gpu)
     lengths = np.diff(wl.seg_offsets)
     segs = _spread(wl.nseg, np.random.default_rng(3), extra=[int(np.argmax(lengths)), 10, 11, 15, 16])
-    sampled_check(wl, segs, "config3")
+    sampled_check(wl, segs, f"config3 {schedule}", schedule=schedule)
 
 
 def test_config4_sampled_full_size(gpu):
@@ -190,7 +192,15 @@ def test_config4_sampled_full_size(gpu):
     sampled_check(wl, segs, "config4")
 
 
-def test_config5_sampled_full_size(gpu):
+def test_config4_sampled_full_size_chain(gpu):
+    # 64 fp16 inputs as a left-to-right chain: five stages, the running result in an fp32 slot
+    wl = W.make_workload(4, device=gpu)
+    segs = _spread(wl.nseg, np.random.default_rng(41), extra=[0, 9, 13])
+    sampled_check(wl, segs, "config4 chain", schedule="chain")
+
+
+@pytest.mark.parametrize("schedule", ["tree", "chain"])
+def test_config5_sampled_full_size(gpu, schedule):
     wl = W.make_workload(5, device=gpu)
     lengths = np.diff(wl.seg_offsets)
     zero = wl.notes["params"]["zero"]
@@ -200,7 +210,7 @@ def test_config5_sampled_full_size(gpu):
     extra = list(flagged[:12]) + list(all_zero[:2]) + [int(np.argmin(lengths)), int(np.argmax(lengths))]
     extra += list(np.flatnonzero(lengths == 1)[:5])
     segs = _spread(wl.nseg, rng, extra=extra)
-    sampled_check(wl, [int(s) for s in segs], "config5")
+    sampled_check(wl, [int(s) for s in segs], f"config5 {schedule}", schedule=schedule)
 
 
 @pytest.mark.parametrize("K,dtype,schedule", [(32, "bf16", "tree"), (32, "f16", "tree"), (16, "bf16", "tree"),
