@@ -103,7 +103,11 @@ typedef enum {
  *                input.  Rounded once, to nearest even, from the fp64 combine.
  *
  * Uses a workspace that the library allocates and caches per (device,
- * stream); the first call for a given shape may therefore allocate.
+ * stream); the first call for a given shape may therefore allocate.  The
+ * cache is keyed by the stream handle and kept until the process ends:
+ * calls on one stream share one buffer in stream order, so a stream with
+ * calls still pending must be synchronized before it is destroyed if a new
+ * stream could be given the same handle.
  * Errors: ADASUM_EINVAL (null pointers with N > 0, K < 1, nseg < 0, bad
  * offsets, unknown dtype, misaligned pointer, out overlapping an input,
  * N > 2^40, K * nseg > 2^31 - 1), ADASUM_ENOMEM, ADASUM_EHIP.
