@@ -478,11 +478,16 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             }
           } else {
             WsumArgs a{};
+            std::memset(a.side_slot, -1, sizeof a.side_slot);
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
               for (size_t k = 0; k < bk.operands.size(); ++k) {
                 a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
                 in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
+                if (bk.operands[k].kind == Ref::Slot && p.short_rows > 0) {
+                  a.side_slot[j][k] = bk.operands[k].idx;
+                  a.side_mask[j] |= 1u << k;
+                }
               }
               a.narrow[j] = block_kind(p, bk).narrow;
               a.y[j] = ref_ptr(p, b, bk.dst);
@@ -495,6 +500,10 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             a.nseg = p.nseg;
             a.weights = weights;
             a.short_off = dt.short_off;
+            if (p.short_rows > 0) {
+              a.side_in = reinterpret_cast<const double*>(b.ws + p.ws_side);
+              a.short_rows = p.short_rows;
+            }
             log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
             e = launch_wsum(in_t, kind0.narrow_t, nbt, out_t, a, ntiles, n, st);

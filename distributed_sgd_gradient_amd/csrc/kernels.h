@@ -81,6 +81,14 @@ struct WsumArgs {
   // (side[j] NULL: not a slot, or no short tiles)
   double* side[kMaxJobs];
   const int64_t* short_off;
+  // operand k of job j is the fp32 slot side_slot[j][k] when bit k of
+  // side_mask[j] is set; in a short tile that operand is read from the
+  // slot's fp64 side buffer, side_in + slot * short_rows + short_off[t], so
+  // a result carried through several stages is rounded only at the root
+  const double* side_in;
+  int64_t short_rows;
+  uint32_t side_mask[kMaxJobs];
+  int32_t side_slot[kMaxJobs][kMaxOps];
 };
 static_assert(sizeof(WsumArgs) <= 4096, "kernel arguments fit 4 KB");
 

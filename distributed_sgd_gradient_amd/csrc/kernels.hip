@@ -1094,21 +1094,26 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
     Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
   };
 
-  if (args.side[j] != nullptr && tile.len <= kExactRows) {
-    // a short tile of a result that feeds a later stage: element by element,
-    // each fp64 sum also kept in the side buffer (row i at side[i + shift])
-    // for that stage's exact Gram sum
+  const uint32_t side_mask = args.side_mask[j];
+  if ((args.side[j] != nullptr || side_mask != 0u) && tile.len <= kExactRows) {
+    // a short tile of a result that feeds a later stage, or of a block that
+    // reads lower results: element by element; a lower result is read from
+    // its fp64 side buffer, and this result's fp64 sum is also kept in its
+    // own (row i at side[i + shift]) for the next stage's exact Gram sum
     double* __restrict__ side = args.side[j];
     const int64_t shift = args.short_off[tile_id] - tile.start;
     for (int64_t i = sp.lo + tid; i < sp.hi; i += kBlock) {
       double acc = 0.0;
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
-        const double t = mul_rn(w[k], (double)load1(k, i));
+        const double v = ((side_mask >> k) & 1u)
+                             ? args.side_in[(int64_t)args.side_slot[j][k] * args.short_rows + shift + i]
+                             : (double)load1(k, i);
+        const double t = mul_rn(w[k], v);
         acc = add_rn(acc, live[k] ? t : 0.0);
       }
       Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
-      side[i + shift] = acc;
+      if (side != nullptr) side[i + shift] = acc;
     }
     return;
   }

@@ -267,11 +267,12 @@ def test_small_K_ragged_segments(gpu, K, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 48, 63, 64, 65, 70, 130])
+@pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 48, 63, 64, 65, 70, 130, 257, 300])
 def test_multistage_K(gpu, K, dtype):
     # more than 16 operands: one block of 32 (at most 32 16-bit inputs), else
     # blocks of 16 with fp32 block results and carried inputs; K = 130 has
-    # stage positions beyond 127
+    # stage positions beyond 127; K = 257 and 300 take three stages (blocks
+    # of lower blocks' results)
     wl = W.random_case(K, [1, 300, 9, 40000, 8], dtype=dtype, seed=100 + K, kind="shared")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"multistage K={K} {dtype}")
@@ -399,8 +400,9 @@ def test_stacked_tensor_input_and_out_argument(gpu):
 # ---------------------------------------------------------------- chain, orthogonality, plain sum
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("K", [2, 3, 5, 16, 17, 32, 33, 40])
+@pytest.mark.parametrize("K", [2, 3, 5, 16, 17, 32, 33, 40, 100, 300])
 def test_chain_schedule(gpu, K, dtype):
+    # K = 300: twenty stages, each the running result (an fp32 slot) and 15 more inputs
     A = _A()
     wl = W.random_case(K, [1, 300, 9, 20000, 8], dtype=dtype, seed=300 + K, kind="shared")
     grads = [g.to(gpu) for g in wl.grads]
