@@ -406,6 +406,8 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
   const int ntiles = (int)p.tiles.size();
   hipError_t e;
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
+  // kept only where there are short tiles (the region is empty otherwise)
+  double* partials_lo = p.short_rows > 0 ? reinterpret_cast<double*>(b.ws + p.ws_plo) : nullptr;
   double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
   uint32_t* flags = reinterpret_cast<uint32_t*>(b.ws + p.ws_flags);
   int stage_no = 0;
@@ -459,6 +461,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             }
             a.tiles = dt.tiles;
             a.partials = partials;
+            a.partials_lo = partials_lo;
             if (p.short_rows > 0 && in_t == DType::F32) {
               a.side = reinterpret_cast<const double*>(b.ws + p.ws_side);
               a.short_off = dt.short_off;
@@ -519,6 +522,8 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         t.merges = dt.merges;
         t.seg_tile = dt.seg_tile;
         t.partials = partials;
+        t.partials_lo = partials_lo;
+        t.tiles = dt.tiles;
         t.desc0 = sg.blocks.front().desc;
         t.nblocks = (int)sg.blocks.size();
         t.nseg = p.nseg;

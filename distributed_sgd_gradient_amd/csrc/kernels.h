@@ -18,6 +18,10 @@ struct GramArgs {
   int64_t poff[kMaxJobs];  // partials of tile t: partials + poff + t * gram_entries(nbt)
   const Tile* tiles;
   double* partials;
+  // short tiles (at most kExactRows rows) sum their entries exactly in
+  // double-double and write the low parts here, at the same index as in
+  // partials (NULL: not kept)
+  double* partials_lo;
   // exact recomputation only: the tiles of (block, segment) pairs whose
   // flags[wrow[j]][segment] is set
   const uint32_t* flags;
@@ -43,6 +47,10 @@ struct TreeArgs {
   const Merge* merges;
   const int32_t* seg_tile;  // nseg + 1
   const double* partials;
+  // a segment of one short tile (tiles[t].len <= kExactRows) takes its Gram
+  // entries as partials + partials_lo (double-double); NULL: fp64 entries only
+  const double* partials_lo;
+  const Tile* tiles;
   int desc0;                // first block of this launch (consecutive descs)
   int nblocks;
   int nblocks_total;        // blocks of the whole plan (rows of weights / leafnorm)
@@ -112,7 +120,7 @@ hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a
                        hipStream_t st);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
 // 16-bit operands: the Gram partials of every tile of a flagged (block,
-// segment) pair, recomputed exactly (fp64 sums of exact products, row order).
+// segment) pair, recomputed exactly (double-double sums of exact products, row order).
 hipError_t launch_gram_exact(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st);
 hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
                        hipStream_t st);

@@ -282,6 +282,45 @@ __device__ __forceinline__ void load_n16x8(const uint16_t* __restrict__ x, int64
   b = load_n16x4<TN>(x, row + 4, lo, hi);
 }
 
+// Double-double values (hi + lo, |lo| <= ulp(hi) / 2) for the merge walk's
+// sums and the Gram entries of short tiles.  A node far smaller than the
+// operands under it (a near-cancellation) makes its quadratic form cancel: summed in fp64, the rounding of the terms
+// would be amplified by the ratio of their size to the result's.  With exact
+// products (a fused multiply-add gives the product's rounding error) and
+// compensated sums, the form is accurate to about 2^-104 of the terms.
+// Terms that mirror each other still cancel exactly.
+struct DD {
+  double hi, lo;
+};
+
+__device__ __forceinline__ DD dd_prod(double a, double b) {
+  const double p = a * b;
+  return DD{p, fma(a, b, -p)};
+}
+
+__device__ __forceinline__ DD dd_add(DD x, DD y) {
+  const double s = x.hi + y.hi;
+  const double bb = s - x.hi;
+  double e = (x.hi - (s - bb)) + (y.hi - bb);
+  e += x.lo + y.lo;
+  const double hi = s + e;
+  return DD{hi, e - (hi - s)};
+}
+
+__device__ __forceinline__ DD dd_scale(DD x, double b) {
+  DD p = dd_prod(x.hi, b);
+  p.lo += x.lo * b;
+  const double hi = p.hi + p.lo;
+  return DD{hi, p.lo - (hi - p.hi)};
+}
+
+__device__ __forceinline__ DD dd_mul(DD x, DD y) {
+  DD p = dd_prod(x.hi, y.hi);
+  p.lo += x.hi * y.lo + x.lo * y.hi;
+  const double hi = p.hi + p.lo;
+  return DD{hi, p.lo - (hi - p.hi)};
+}
+
 // TN = float: every operand is fp32.  Otherwise the lanes of operands that
 // the job's narrow mask marks read them in TN (16-bit inputs carried into a
 // later stage) and widen them exactly; the products stay exact.  Such a
@@ -323,12 +362,14 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
     bool slots = false;
 #pragma unroll
     for (int k = 0; k < NB; ++k) slots = slots || args.side_slot[j][k] >= 0;
-    if (slots) {
-      // a short tile of a stage above the first: slot operands from their
-      // fp64 side buffers (not the fp32-rounded slots), every entry summed
-      // in fp64 row by row
+    if (slots || args.partials_lo != nullptr) {
+      // a short tile: slot operands from their fp64 side buffers (not the
+      // fp32-rounded slots), every entry summed row by row in double-double
+      // from exact products (a fused multiply-add gives each product's
+      // rounding error); the low parts go to partials_lo
       const int64_t so = args.short_off[tile_id];
       double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+      double* out_lo = args.partials_lo != nullptr ? args.partials_lo + args.poff[j] + (int64_t)tile_id * NE : nullptr;
       for (int e = threadIdx.x; e < NE; e += kBlock) {
         int i = 0, rem = e;
         while (rem >= NB - i) {
@@ -336,10 +377,12 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
           ++i;
         }
         const int k = i + rem;
-        double sum = 0.0;
+        DD sum{0.0, 0.0};
         for (int r = 0; r < tile.len; ++r)
-          sum += operand_f64<TN>(args, j, i, lo + r, so + r) * operand_f64<TN>(args, j, k, lo + r, so + r);
-        out[e] = sum;
+          sum = dd_add(sum, dd_prod(operand_f64<TN>(args, j, i, lo + r, so + r),
+                                    operand_f64<TN>(args, j, k, lo + r, so + r)));
+        out[e] = sum.hi;
+        if (out_lo != nullptr) out_lo[e] = sum.lo;
       }
       return;
     }
@@ -587,16 +630,17 @@ __device__ __forceinline__ double widen16<bf16_t>(uint16_t bits) {
 }
 
 // The packed Gram triangle of rows [lo, lo + len) of the operands in
-// `table` (NULL: zero) into out, every entry the fp64 row-order sum of exact
-// products.  The rows pass through sh (NB * kExactRows 16-bit values)
-// kExactRows at a time.  Called by every thread of the workgroup.
+// `table` (NULL: zero) into out, every entry the row-order double-double sum
+// of exact products, its low part into out_lo (NULL: dropped).  The rows
+// pass through sh (NB * kExactRows 16-bit values) kExactRows at a time.
+// Called by every thread of the workgroup.
 template <typename T, int NB>
 __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t len, double* __restrict__ out,
-                                uint16_t* sh) {
+                                double* __restrict__ out_lo, uint16_t* sh) {
   constexpr int NE = gram_entries(NB);
   constexpr int EPT = (NE + kBlock - 1) / kBlock;  // entries per thread
   int ei[EPT], ek[EPT];
-  double acc[EPT];
+  DD acc[EPT];
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
     const int e = threadIdx.x + q * kBlock;
@@ -607,7 +651,7 @@ __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t le
     }
     ei[q] = i;
     ek[q] = i + rem;
-    acc[q] = 0.0;
+    acc[q] = DD{0.0, 0.0};
   }
   for (int64_t c0 = 0; c0 < len; c0 += kExactRows) {
     const int n = (int)min<int64_t>(kExactRows, len - c0);
@@ -623,14 +667,17 @@ __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t le
       if (threadIdx.x + q * kBlock >= NE) continue;
       const uint16_t* x = sh + ei[q] * kExactRows;
       const uint16_t* y = sh + ek[q] * kExactRows;
-      double sum = acc[q];
-      for (int r = 0; r < n; ++r) sum += widen16<T>(x[r]) * widen16<T>(y[r]);  // exact product, one rounding
+      DD sum = acc[q];
+      for (int r = 0; r < n; ++r) sum = dd_add(sum, DD{widen16<T>(x[r]) * widen16<T>(y[r]), 0.0});  // exact product
       acc[q] = sum;
     }
   }
 #pragma unroll
-  for (int q = 0; q < EPT; ++q)
-    if (threadIdx.x + q * kBlock < NE) out[threadIdx.x + q * kBlock] = acc[q];
+  for (int q = 0; q < EPT; ++q) {
+    if (threadIdx.x + q * kBlock >= NE) continue;
+    out[threadIdx.x + q * kBlock] = acc[q].hi;
+    if (out_lo != nullptr) out_lo[threadIdx.x + q * kBlock] = acc[q].lo;
+  }
 }
 
 // Exact recomputation of the Gram partials of every tile of a (block,
@@ -645,8 +692,9 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
   if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] == 0) return;
-  gram_exact_rows<T, NB>(args.x[j], tile.start, tile.len,
-                         args.partials + args.poff[j] + (int64_t)tile_id * gram_entries(NB), sh);
+  const int64_t at = args.poff[j] + (int64_t)tile_id * gram_entries(NB);
+  gram_exact_rows<T, NB>(args.x[j], tile.start, tile.len, args.partials + at,
+                         args.partials_lo != nullptr ? args.partials_lo + at : nullptr, sh);
 }
 
 // Blocks of up to 16 operands use one 16-operand half; the 32-operand block
@@ -670,7 +718,9 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
   const int64_t lo = tile.start, hi = tile.start + tile.len;
   if (tile.len <= kExactRows) {  // workgroup-uniform: a short tile, summed exactly
     static_assert(sizeof(red) >= sizeof(uint16_t) * NB * kExactRows, "staging fits the reduction buffer");
-    gram_exact_rows<T, NB>(args.x[j], lo, tile.len, args.partials + args.poff[j] + (int64_t)tile_id * NE,
+    const int64_t at = args.poff[j] + (int64_t)tile_id * NE;
+    gram_exact_rows<T, NB>(args.x[j], lo, tile.len, args.partials + at,
+                           args.partials_lo != nullptr ? args.partials_lo + at : nullptr,
                            reinterpret_cast<uint16_t*>(&red[0][0][0]));
     return;
   }
@@ -837,45 +887,6 @@ __device__ __forceinline__ double gram_at(const double* G, int n, int i, int k) 
   return i <= k ? G[gram_index(n, i, k)] : G[gram_index(n, k, i)];
 }
 
-// Double-double values (hi + lo, |lo| <= ulp(hi) / 2) for the merge walk's
-// sums.  A node far smaller than the operands under it (a near-cancellation)
-// makes its quadratic form cancel: summed in fp64, the rounding of the terms
-// would be amplified by the ratio of their size to the result's.  With exact
-// products (a fused multiply-add gives the product's rounding error) and
-// compensated sums, the form is accurate to about 2^-104 of the terms.
-// Terms that mirror each other still cancel exactly.
-struct DD {
-  double hi, lo;
-};
-
-__device__ __forceinline__ DD dd_prod(double a, double b) {
-  const double p = a * b;
-  return DD{p, fma(a, b, -p)};
-}
-
-__device__ __forceinline__ DD dd_add(DD x, DD y) {
-  const double s = x.hi + y.hi;
-  const double bb = s - x.hi;
-  double e = (x.hi - (s - bb)) + (y.hi - bb);
-  e += x.lo + y.lo;
-  const double hi = s + e;
-  return DD{hi, e - (hi - s)};
-}
-
-__device__ __forceinline__ DD dd_scale(DD x, double b) {
-  DD p = dd_prod(x.hi, b);
-  p.lo += x.lo * b;
-  const double hi = p.hi + p.lo;
-  return DD{hi, p.lo - (hi - p.hi)};
-}
-
-__device__ __forceinline__ DD dd_mul(DD x, DD y) {
-  DD p = dd_prod(x.hi, y.hi);
-  p.lo += x.hi * y.lo + x.lo * y.hi;
-  const double hi = p.hi + p.lo;
-  return DD{hi, p.lo - (hi - p.hi)};
-}
-
 // sum_{i in [a0,a1)} w_i * (sum_{k in [b0,b1)} w_k G(i,k))
 __device__ double quad_form(const double* G, int n, const double* w, int a0, int a1, int b0, int b1) {
   double total = 0.0;
@@ -927,6 +938,15 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     for (int i = 1; i < kTreeWaves; ++i) sum += part[i][e];
     G[e] = sum;
   }
+  // A segment of one short tile has its Gram entries in double-double (hi:
+  // that tile's partial, taken exactly above); the walk then forms its
+  // quadratic forms from both parts, so their rounding is not amplified by a
+  // merge that cancels.  Workgroup-uniform.
+  const bool exact_g = a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows;
+  double* const Glo = &part[0][0];  // the low parts reuse the consumed wave sums
+  __syncthreads();
+  if (exact_g)
+    for (int e = tid; e < ne; e += kBlock) Glo[e] = a.partials_lo[d.poff + (int64_t)t0 * ne + e];
   if (tid < kMaxOps) w[tid] = DD{1.0, 0.0};
   __syncthreads();
   // Merges run level by level: merges of a block are stored children
@@ -955,8 +975,13 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     if (mine >= 0) {
       const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
       DD sl{0.0, 0.0}, sr{0.0, 0.0};
-      for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_scale(w[k], gram_at(G, n, tid, k)));
-      for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_scale(w[k], gram_at(G, n, tid, k)));
+      if (exact_g) {
+        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
+        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
+      } else {
+        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_scale(w[k], gram_at(G, n, tid, k)));
+        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_scale(w[k], gram_at(G, n, tid, k)));
+      }
       rowL[tid] = sl;
       rowR[tid] = sr;
     }

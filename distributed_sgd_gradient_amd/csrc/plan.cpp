@@ -253,6 +253,8 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   off = align256(off + (size_t)p.nblocks * nseg * sizeof(uint32_t));
   p.ws_side = off;
   off = align256(off + (size_t)p.nslots * (size_t)p.short_rows * sizeof(double));
+  p.ws_plo = off;  // low parts of the short tiles' double-double Gram entries, laid out as the partials
+  off = align256(off + (p.short_rows > 0 ? p.partial_doubles : 0) * sizeof(double));
   p.ws_total = off;
   return p;
 }

@@ -137,7 +137,7 @@ struct Plan {
 
   // workspace layout, byte offsets (each 256-aligned)
   size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_leafnorm = 0, ws_coeffs = 0, ws_stats = 0,
-         ws_flags = 0, ws_side = 0, ws_total = 0;
+         ws_flags = 0, ws_side = 0, ws_plo = 0, ws_total = 0;
   size_t table_bytes(int per_node) const { return (size_t)(K > 1 ? K - 1 : 0) * nseg * per_node * sizeof(double); }
 };
 

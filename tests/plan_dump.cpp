@@ -42,9 +42,9 @@ static void dump(const Plan& p, int dt, int sched, int K) {
   printf("], \"short_off\": [");
   for (size_t t = 0; t < p.short_off.size(); ++t) printf("%s%lld", t ? "," : "", (long long)p.short_off[t]);
   printf("], \"short_rows\": %lld", (long long)p.short_rows);
-  printf(", \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
+  printf(", \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
          p.partial_doubles, p.ws_slots, p.ws_partials, p.ws_weights, p.ws_leafnorm, p.ws_coeffs, p.ws_stats,
-         p.ws_flags, p.ws_side, p.ws_total, p.nblocks);
+         p.ws_flags, p.ws_side, p.ws_plo, p.ws_total, p.nblocks);
 }
 
 int main(int argc, char** argv) {

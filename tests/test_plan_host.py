@@ -207,7 +207,7 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         nodes = max(K - 1, 0)
         sizes = [P["nslots"] * N * 4, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
                  nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4,
-                 P["nslots"] * P["short_rows"] * 8]
+                 P["nslots"] * P["short_rows"] * 8, (P["partial_doubles"] if P["short_rows"] else 0) * 8]
         # short tiles (at most 256 rows) numbered consecutively in the side buffers
         pos = 0
         for (start, length, seg), so in zip(tiles, P["short_off"]):
