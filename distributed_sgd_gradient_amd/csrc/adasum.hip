@@ -524,6 +524,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         t.partials = partials;
         t.partials_lo = partials_lo;
         t.tiles = dt.tiles;
+        t.lo_inputs = p.dtype != DType::F32;
         t.desc0 = sg.blocks.front().desc;
         t.nblocks = (int)sg.blocks.size();
         t.nseg = p.nseg;

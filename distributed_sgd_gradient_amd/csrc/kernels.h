@@ -18,9 +18,9 @@ struct GramArgs {
   int64_t poff[kMaxJobs];  // partials of tile t: partials + poff + t * gram_entries(nbt)
   const Tile* tiles;
   double* partials;
-  // short tiles (at most kExactRows rows) sum their entries exactly in
-  // double-double and write the low parts here, at the same index as in
-  // partials (NULL: not kept)
+  // short tiles (at most kExactRows rows) of 16-bit launches and of blocks
+  // that read a slot sum their entries exactly in double-double and write
+  // the low parts here, at the same index as in partials (NULL: not kept)
   double* partials_lo;
   // exact recomputation only: the tiles of (block, segment) pairs whose
   // flags[wrow[j]][segment] is set
@@ -48,9 +48,11 @@ struct TreeArgs {
   const int32_t* seg_tile;  // nseg + 1
   const double* partials;
   // a segment of one short tile (tiles[t].len <= kExactRows) takes its Gram
-  // entries as partials + partials_lo (double-double); NULL: fp64 entries only
+  // entries as partials + partials_lo (double-double) when its block reads a
+  // slot, or when lo_inputs is set (16-bit inputs); NULL: fp64 entries only
   const double* partials_lo;
   const Tile* tiles;
+  int lo_inputs;
   int desc0;                // first block of this launch (consecutive descs)
   int nblocks;
   int nblocks_total;        // blocks of the whole plan (rows of weights / leafnorm)

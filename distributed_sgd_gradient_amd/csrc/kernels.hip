@@ -362,11 +362,13 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
     bool slots = false;
 #pragma unroll
     for (int k = 0; k < NB; ++k) slots = slots || args.side_slot[j][k] >= 0;
-    if (slots || args.partials_lo != nullptr) {
-      // a short tile: slot operands from their fp64 side buffers (not the
-      // fp32-rounded slots), every entry summed row by row in double-double
-      // from exact products (a fused multiply-add gives each product's
-      // rounding error); the low parts go to partials_lo
+    if (slots) {
+      // a short tile of a stage above the first: slot operands from their
+      // fp64 side buffers (not the fp32-rounded slots), every entry summed
+      // row by row in double-double from exact products (a fused
+      // multiply-add gives each product's rounding error); the low parts go
+      // to partials_lo.  (Short tiles of fp32 inputs alone stay on the
+      // matrix cores, whose products are exact.)
       const int64_t so = args.short_off[tile_id];
       double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
       double* out_lo = args.partials_lo != nullptr ? args.partials_lo + args.poff[j] + (int64_t)tile_id * NE : nullptr;
@@ -939,10 +941,13 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     G[e] = sum;
   }
   // A segment of one short tile has its Gram entries in double-double (hi:
-  // that tile's partial, taken exactly above); the walk then forms its
-  // quadratic forms from both parts, so their rounding is not amplified by a
-  // merge that cancels.  Workgroup-uniform.
-  const bool exact_g = a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows;
+  // that tile's partial, taken exactly above) where an exact path summed
+  // them: blocks that read a lower result, and 16-bit inputs.  The walk then
+  // forms its quadratic forms from both parts, so their rounding is not
+  // amplified by a merge that cancels.  Workgroup-uniform.
+  const uint32_t all_inputs = d.nb >= 32 ? 0xffffffffu : (1u << d.nb) - 1u;
+  const bool exact_g = a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows &&
+                       (a.lo_inputs || d.leafmask != all_inputs);
   double* const Glo = &part[0][0];  // the low parts reuse the consumed wave sums
   __syncthreads();
   if (exact_g)
