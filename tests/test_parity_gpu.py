@@ -751,8 +751,9 @@ def test_random_shapes(gpu, case):
 def test_seeded_random_sweep(gpu):
     """150 seeded random shapes in one test: K log-uniform in [1, 400), all
     three dtypes, tree and chain, i.i.d. / shared-component / per-segment
-    scaled values, some all-zero workers, and segments from empty through
-    one element to 60,000 rows.  Every output and every coefficient away
+    scaled values or values at the edges of the format (fp16 subnormals,
+    bf16 near 2^-100 and 2^60), some all-zero workers, and segments from
+    empty through one element to 60,000 rows.  Every output and every coefficient away
     from the zero discontinuity is compared with the oracle; all failures
     are reported together.  (A wider sweep of this kind found the two
     stage-boundary errors that the one-element chain tests above pin.)"""
@@ -763,7 +764,7 @@ def test_seeded_random_sweep(gpu):
         K = int(np.exp(rng.uniform(0, np.log(400))))
         dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
         schedule = "chain" if rng.random() < 0.4 else "tree"
-        kind = ["normal", "shared", "scaled"][int(rng.integers(0, 3))]
+        kind = ["normal", "shared", "scaled", "edge"][int(rng.integers(0, 4))]
         lengths = []
         for _ in range(int(rng.integers(1, 9))):
             u = rng.random()
@@ -774,7 +775,11 @@ def test_seeded_random_sweep(gpu):
             lengths = [n // 2 for n in lengths]
         zero = tuple(sorted(set(rng.integers(0, K, size=int(rng.integers(1, 4))).tolist()))) \
             if rng.random() < 0.1 else ()
-        wl = W.random_case(K, lengths, dtype=dtype, seed=91000 + case, kind=kind, zero_workers=zero)
+        wl = W.random_case(K, lengths, dtype=dtype, seed=91000 + case, kind="normal" if kind == "edge" else kind,
+                           zero_workers=zero)
+        if kind == "edge":  # exact power-of-two scaling into the format's edge ranges, then rounded to dtype
+            scale = {"f32": 2.0 ** -120, "f16": 2.0 ** -20, "bf16": 2.0 ** (-100 if case % 2 else 60)}[dtype]
+            wl.grads = [(g.double() * scale).to(g.dtype) for g in wl.grads]
         grads = [g.to(gpu) for g in wl.grads]
         out, coeffs, _ = A.combine(grads, wl.seg_offsets, schedule=schedule, return_coeffs=True, return_stats=True)
         torch.cuda.synchronize()
