@@ -794,3 +794,38 @@ def test_seeded_random_sweep(gpu):
             bad.append((case, K, dtype, schedule, kind, lengths, zero, err, worst))
     say("seeded sweep", f"150 cases, {len(bad)} failures")
     assert not bad, bad
+
+
+def test_many_segments_sweep(gpu):
+    """20 seeded shapes of 100 to 5,000 segments each (lengths log-uniform
+    in [1, 10,000], a few empty), K from 2 to 20, all dtypes, both schedules:
+    every output and coefficient against the oracle."""
+    A = _A()
+    bad = []
+    for case in range(20):
+        rng = np.random.default_rng(93000 + case)
+        K = int(rng.integers(2, 21))
+        dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+        schedule = "chain" if rng.random() < 0.4 else "tree"
+        kind = ["normal", "shared", "scaled"][int(rng.integers(0, 3))]
+        nseg = int(np.exp(rng.uniform(np.log(100), np.log(5000))))
+        lengths = np.floor(np.exp(rng.uniform(0, np.log(10000), size=nseg))).astype(int)
+        lengths[rng.random(nseg) < 0.03] = 0
+        lengths = lengths.tolist()
+        while K * max(sum(lengths), 1) > 3e7:
+            lengths = [n // 2 for n in lengths]
+        wl = W.random_case(K, lengths, dtype=dtype, seed=93000 + case, kind=kind)
+        grads = [g.to(gpu) for g in wl.grads]
+        out, coeffs = A.combine(grads, wl.seg_offsets, schedule=schedule, return_coeffs=True)
+        torch.cuda.synchronize()
+        run = oracle.combine_chain if schedule == "chain" else oracle.combine
+        ref = run([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format=dtype)
+        err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
+        c = coeffs.cpu().numpy()
+        cerr = np.abs(c - ref["coeffs"]) / np.maximum(1.0, np.abs(ref["coeffs"]))
+        cerr = np.where(unstable(ref["stats"], segment_opnorms(wl, schedule), schedule), 0.0, cerr)
+        worst = float(cerr.max()) if cerr.size else 0.0
+        if err > TOL[dtype] or worst > COEFF_TOL or not np.all(np.isfinite(c)):
+            bad.append((case, K, dtype, schedule, kind, nseg, err, worst))
+    say("many-segment sweep", f"20 cases, {len(bad)} failures")
+    assert not bad, bad
