@@ -26,6 +26,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <iterator>
 #include <list>
 #include <map>
 #include <memory>
@@ -36,10 +37,10 @@
 
 #include "../../include/adasum.h"
 #include "kernels.h"
+#include "library.h"
 #include "plan.h"
 
 namespace adasum {
-namespace {
 
 thread_local std::string g_last_error;
 
@@ -73,23 +74,11 @@ int fail_hip(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------------- plan cache
 
-struct DeviceTables {
-  Tile* tiles = nullptr;
-  int32_t* seg_tile = nullptr;
-  BlockDesc* descs = nullptr;
-  Merge* merges = nullptr;
-  int64_t* short_off = nullptr;
-};
-
-struct CachedPlan {
-  Plan plan;
-  std::map<int, DeviceTables> per_device;
-};
-
 constexpr size_t kMaxCachedPlans = 64;
 
-std::mutex g_mu;
-std::list<std::shared_ptr<CachedPlan>> g_plans;  // most recently used first
+std::mutex g_mu;  // guards every library-wide table below
+std::list<std::shared_ptr<CachedPlan>> g_plans;    // most recently used first
+std::vector<std::shared_ptr<CachedPlan>> g_retired;  // evicted by a call that may not free; freed later
 
 bool same_shape(const Plan& p, int K, const int64_t* off, int nseg, DType dt, Schedule sc) {
   return p.K == K && p.nseg == nseg && p.dtype == dt && p.schedule == sc &&
@@ -97,6 +86,7 @@ bool same_shape(const Plan& p, int K, const int64_t* off, int nseg, DType dt, Sc
 }
 
 void release_tables(CachedPlan& cp) {
+  if (cp.per_device.empty()) return;
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return;
   for (auto& kv : cp.per_device) {
@@ -108,11 +98,16 @@ void release_tables(CachedPlan& cp) {
     (void)hipFree(kv.second.merges);
     (void)hipFree(kv.second.short_off);
   }
+  cp.per_device.clear();
   (void)hipSetDevice(cur);
 }
 
-// Caller holds g_mu.
-std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType dt, Schedule sc) {
+// may_free = false: for the no-allocation entry point, which calls no hipFree.
+std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType dt, Schedule sc, bool may_free) {
+  if (may_free) {
+    for (auto& r : g_retired) release_tables(*r);
+    g_retired.clear();
+  }
   for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
     if (same_shape((*it)->plan, K, off, nseg, dt, sc)) {
       auto hit = *it;
@@ -126,16 +121,38 @@ std::shared_ptr<CachedPlan> find_plan(int K, const int64_t* off, int nseg, DType
   if (log_enabled()) {
     const Plan& p = cp->plan;
     std::fprintf(stderr, "[adasum] plan K=%d nseg=%d N=%lld dtype=%d schedule=%s: %zu tiles of <= %lld, %zu stages, "
-                 "%d blocks, %d fp32 slots, workspace %zu bytes\n", K, nseg, (long long)p.N, (int)dt,
+                 "%d blocks, %d slots, workspace %zu bytes\n", K, nseg, (long long)p.N, (int)dt,
                  sc == Schedule::Tree ? "tree" : "chain", p.tiles.size(), (long long)p.tile_rows, p.stages.size(),
                  p.nblocks, p.nslots, p.ws_total);
   }
   g_plans.push_front(cp);
-  if (g_plans.size() > kMaxCachedPlans) {
-    release_tables(*g_plans.back());
-    g_plans.pop_back();
+  // evict the least recently used shape that no captured graph refers to
+  size_t unpinned = 0;
+  for (auto& q : g_plans) unpinned += q->pinned ? 0 : 1;
+  if (unpinned > kMaxCachedPlans) {
+    for (auto it = std::prev(g_plans.end());; --it) {
+      if (!(*it)->pinned && *it != cp) {
+        if (may_free)
+          release_tables(**it);
+        else
+          g_retired.push_back(*it);
+        g_plans.erase(it);
+        break;
+      }
+      if (it == g_plans.begin()) break;
+    }
   }
   return cp;
+}
+
+// Whether work enqueued on st now is being captured into a graph.
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &status) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return status != hipStreamCaptureStatusNone;
 }
 
 // Caller holds g_mu.  Uploads the plan tables to `device` once.
@@ -188,6 +205,7 @@ int device_tables(CachedPlan& cp, int device, DeviceTables* out) {
 struct OwnedWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  bool captured = false;  // used under graph capture: never freed (a graph may still refer to it)
 };
 std::map<std::pair<int, void*>, OwnedWorkspace> g_ws;  // (device, stream) -> buffer; guarded by g_mu
 
@@ -359,15 +377,6 @@ int check_devices(const void* const* grads, int K, size_t vec_bytes, const void*
 }
 
 // ---------------------------------------------------------------- scheduler
-
-struct CallBuffers {
-  const void* const* grads;
-  void* out;
-  char* ws;
-  double* coeffs;
-  double* stats;
-  double* ortho;
-};
 
 void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
   switch (r.kind) {
@@ -617,13 +626,18 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
                        device);
     if (rc != ADASUM_OK) return rc;
     OwnedWorkspace& ow = g_ws[{device, stream}];
+    const bool cap = capturing(st);
     if (ow.bytes < p.ws_total) {
+      if (cap)
+        return fail(ADASUM_EINVAL, "adasum_combine would allocate its workspace while the stream is being captured "
+                                   "into a graph; make one call of this shape on this stream before capturing");
       if (ow.ptr) {
         e = hipStreamSynchronize(st);  // earlier calls on this stream may still use the old buffer
         if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize before growing the workspace");
-        (void)hipFree(ow.ptr);
+        if (!ow.captured) (void)hipFree(ow.ptr);  // else a captured graph may still use it: kept
         ow.ptr = nullptr;
         ow.bytes = 0;
+        ow.captured = false;
       }
       e = hipMalloc(&ow.ptr, p.ws_total);
       if (e != hipSuccess) {
@@ -632,6 +646,7 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
       }
       ow.bytes = p.ws_total;
     }
+    if (cap) ow.captured = true;
     workspace = ow.ptr;
     workspace_bytes = ow.bytes;
     // inputs and out were checked above; the library buffer cannot alias them
@@ -647,6 +662,12 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
   }
 
   DeviceTables tables;
+  if (capturing(st)) {
+    if (cp->per_device.find(device) == cp->per_device.end())
+      return fail(ADASUM_EINVAL, "the first call of a shape uploads its tables and may not be captured into a "
+                                 "graph; make one call of this shape before capturing");
+    cp->pinned = true;  // the graph refers to this shape's tables from now on
+  }
   int rc = device_tables(*cp, device, &tables);
   if (rc != ADASUM_OK) return rc;
   char* ws = static_cast<char*>(workspace);
@@ -660,7 +681,6 @@ int combine_impl(const void* const* grads, int K, const int64_t* seg_offsets, in
   return enqueue(p, tables, b, st);
 }
 
-}  // namespace
 }  // namespace adasum
 
 extern "C" {

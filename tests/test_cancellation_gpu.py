@@ -1,0 +1,71 @@
+"""GPU parity under deep cancellation: worker pairs that nearly cancel.
+
+In the operator's properties, parallel gradients are averaged, so an exactly
+anti-parallel pair of equal norms gives zero.  Next to that point a node is
+far smaller than the operands under it, and every merge above it works on a
+near-cancellation.  The inputs here are ``workloads.cancelling_pairs``:
+g_{2m+1} = -(1 + eps) g_{2m} + eps n, so each level-1 node is about eps times
+its operands and the level-2 merges see eps^2 in squared norm.
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from parity import evaluate, passes, say
+
+pytestmark = pytest.mark.gpu
+
+
+def sweep_shape(case):
+    """The shape that seeded sweep case ``case`` draws (K log-uniform in
+    [1, 300), dtype, schedule, value family, 1-6 segments of 0 to 300,000
+    rows, eps log-uniform in [1e-7, 1e-1] for the cancelling family)."""
+    rng = np.random.default_rng(55000 + case)
+    K = int(np.exp(rng.uniform(0, np.log(300))))
+    dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+    schedule = "chain" if rng.random() < 0.4 else "tree"
+    family = ["normal", "shared", "scaled", "cancel", "tiny", "huge"][int(rng.integers(0, 6))]
+    lengths = []
+    for _ in range(int(rng.integers(1, 7))):
+        u = rng.random()
+        if u < 0.05:
+            lengths.append(0)
+        elif u < 0.25:
+            lengths.append(int(rng.integers(1, 9)))
+        elif u < 0.45:
+            lengths.append(int(rng.integers(9, 300)))
+        elif u < 0.70:
+            lengths.append(int(rng.integers(300, 20000)))
+        else:
+            lengths.append(int(rng.integers(20000, 300000)))
+    while K * max(sum(lengths), 1) > 3e7:
+        lengths = [n // 2 for n in lengths]
+    eps = float(np.exp(rng.uniform(np.log(1e-7), np.log(1e-1)))) if family == "cancel" else None
+    return K, dtype, schedule, family, lengths, eps
+
+
+# The sweep cases (of 1,500) whose shapes missed a gate: twelve fp32 shapes
+# whose output missed the 1e-5 relative L2 gate by up to 1.1e-2, and a bf16
+# chain (K = 177) whose third-stage coefficient was off by 3.0e-6.
+FAILED_SWEEP_CASES = [100, 127, 146, 277, 435, 500, 742, 786, 867, 931, 1315, 1427, 1441]
+
+
+@pytest.mark.xfail(reason="merges above a cancelled node take their statistics from quadratic forms in the Gram "
+                          "matrix, whose rounding the cancellation amplifies; not yet flagged for exact "
+                          "recomputation on fp32 and stage-slot operands", strict=True)
+def test_failed_sweep_shapes(gpu):
+    bad = []
+    for case in FAILED_SWEEP_CASES:
+        K, dtype, schedule, family, lengths, eps = sweep_shape(case)
+        assert family == "cancel"
+        wl = W.cancelling_pairs(K, lengths, eps, dtype=dtype, seed=55000 + case)
+        wl.grads = [g.to(gpu) for g in wl.grads]
+        ev = evaluate(wl, schedule)
+        ok = passes(ev, dtype)
+        say(f"sweep case {case}: K={K} {dtype} {schedule} eps={eps:.3g} lengths={lengths}: relative L2 "
+            f"{ev['rel_l2']:.3g}, worst segment {ev['seg_worst']} at {ev['seg_ratio']:.3g} of its budget, "
+            f"coefficient error {ev['coeff_err']:.3g}, {ev['exempt']} exempt{'' if ok else '  FAIL'}")
+        if not ok:
+            bad.append(case)
+    assert not bad, f"cases {bad} miss a gate"

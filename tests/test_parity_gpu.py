@@ -1,19 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Gates (the stated tolerances of the combiner):
-  * output: relative L2 error ||gpu - oracle|| / ||oracle|| <= 1e-5 for fp32
-    inputs and <= 2e-3 for fp16 / bf16 inputs, the oracle rounded once to the
-    output dtype;
-  * coefficients: |c_gpu - c_oracle| <= 1e-6 * max(1, |c_oracle|) for every
-    (node, segment), except at the operator's discontinuity
-    (``oracle.discontinuity_mask``): an operand whose squared norm is below
-    1e-8 of the summed squared norms of the input gradients under it is
-    numerically zero, its coefficient jumps to 1 at exactly zero, and the
-    limit at zero differs from that; there both sides must only agree that
-    the operand is (nearly) zero, and the nodes above it are not compared;
-  * statistics (reported for diagnosis, gated loosely): relative 1e-5.
-Inputs come from the seeded generators in ``workloads`` on the GPU; the
-oracle sees the same tensors copied to the host.
+The gates are those of ``parity`` (tests/parity.py): relative L2 of the whole
+output and of every segment against its own norm (one output ulp per element
+allowed), every coefficient away from the zero discontinuity within 1e-6, and
+the statistics within 1e-5.  Inputs come from the seeded generators in
+``workloads``; the oracle sees the same tensors copied to the host.
 """
 
 import numpy as np
@@ -22,140 +13,15 @@ import torch
 
 import oracle
 import workloads as W
+from parity import (COEFF_TOL, TOL, check_coeffs, check_stats, evaluate, full_check, passes, rel_l2, run_gpu,
+                    sampled_check, say, segment_opnorms, unstable)
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
-COEFF_TOL = 1e-6
-NEAR_ZERO = 1e-8   # operand |a|^2 / (sum of |g_k|^2 under it) at or below: the zero discontinuity
 
 
 def _A():
     import distributed_sgd_gradient_amd as A
     return A
-
-
-def say(*args):
-    print("[parity]", *args, flush=True)
-
-
-def rel_l2(x, ref):
-    den = float(np.linalg.norm(ref))
-    num = float(np.linalg.norm(x - ref))
-    return num / den if den > 0 else num
-
-
-def near_zero(s_ref, opnorms):
-    """[..., 2] mask: operand a (resp. b) of a node is at the zero
-    discontinuity, its oracle |a|^2 at most NEAR_ZERO of the summed squared
-    input norms under it (``oracle.operand_input_norms``), which are not all
-    zero (an operand over all-zero inputs is exactly zero on both sides and
-    its coefficient, exactly 1, stays gated)."""
-    return (s_ref[..., 1:3] <= NEAR_ZERO * opnorms) & (opnorms > 0)
-
-
-def unstable(s_ref, opnorms, schedule="tree"):
-    """``oracle.discontinuity_mask`` of every segment: [K-1, nseg, 2] (or
-    [K-1, 2] for one segment)."""
-    if s_ref.ndim == 2:
-        return oracle.discontinuity_mask(s_ref, opnorms, schedule, NEAR_ZERO)
-    out = np.zeros(s_ref.shape[:2] + (2,), dtype=bool)
-    for s in range(s_ref.shape[1]):
-        out[:, s] = oracle.discontinuity_mask(s_ref[:, s], opnorms[:, s], schedule, NEAR_ZERO)
-    return out
-
-
-def check_coeffs(c_gpu, c_ref, what, exempt=None):
-    err = np.abs(c_gpu - c_ref) / np.maximum(1.0, np.abs(c_ref))
-    assert np.all(np.isfinite(c_gpu)), what
-    if exempt is not None:
-        err = np.where(exempt, 0.0, err)
-    worst = float(err.max()) if err.size else 0.0
-    assert worst <= COEFF_TOL, f"{what}: coefficient error {worst:.3g}"
-    return worst
-
-
-def check_stats(s_gpu, s_ref, what, opnorms=None, schedule="tree"):
-    if s_ref.size == 0:
-        return 0
-    d, A, B = s_ref[..., 0], s_ref[..., 1], s_ref[..., 2]
-    if opnorms is None:
-        zero_a = zero_b = np.zeros(A.shape, dtype=bool)
-    else:
-        direct = near_zero(s_ref, opnorms)
-        # at the discontinuity the GPU must also see the operand as (nearly) zero
-        assert np.all(s_gpu[..., 1][direct[..., 0]] <= 1e-6 * opnorms[..., 0][direct[..., 0]] + 1e-300), what
-        assert np.all(s_gpu[..., 2][direct[..., 1]] <= 1e-6 * opnorms[..., 1][direct[..., 1]] + 1e-300), what
-        mask = unstable(s_ref, opnorms, schedule)
-        zero_a, zero_b = mask[..., 0], mask[..., 1]
-    scale = np.sqrt(np.maximum(A, 0) * np.maximum(B, 0))
-    assert np.all((np.abs(s_gpu[..., 1] - A) <= 1e-5 * A + 1e-300) | zero_a), what
-    assert np.all((np.abs(s_gpu[..., 2] - B) <= 1e-5 * B + 1e-300) | zero_b), what
-    assert np.all((np.abs(s_gpu[..., 0] - d) <= 1e-5 * scale + 1e-300) | zero_a | zero_b), what
-    return int(np.count_nonzero(zero_a | zero_b))
-
-
-def segment_opnorms(wl, schedule="tree"):
-    """operand_input_norms of every segment: [K-1, nseg, 2]."""
-    rows = [g.double().cpu().numpy() for g in wl.grads]
-    out = np.zeros((max(wl.K - 1, 0), wl.nseg, 2))
-    for s in range(wl.nseg):
-        lo, hi = int(wl.seg_offsets[s]), int(wl.seg_offsets[s + 1])
-        out[:, s] = oracle.operand_input_norms([r[lo:hi] for r in rows], schedule)
-    return out
-
-
-def run_gpu(wl, schedule="tree"):
-    A = _A()
-    out, coeffs, stats = A.combine(wl.grads, wl.seg_offsets, schedule=schedule, return_coeffs=True,
-                                   return_stats=True)
-    torch.cuda.synchronize()
-    return out, coeffs, stats
-
-
-def full_check(wl, label, schedule="tree"):
-    """Compare every element and every (node, segment) with the oracle."""
-    say(label, f"K={wl.K} dtype={wl.dtype} N={wl.N} nseg={wl.nseg} schedule={schedule}")
-    out, coeffs, stats = run_gpu(wl, schedule)
-    combine = oracle.combine_chain if schedule == "chain" else oracle.combine
-    ref = combine([g.double().cpu().numpy() for g in wl.grads], wl.seg_offsets, out_format=wl.dtype)
-    got = out.double().cpu().numpy()
-    err = rel_l2(got, ref["out_rounded"])
-    assert err <= TOL[wl.dtype], f"{label}: relative L2 {err:.3g}"
-    opn = segment_opnorms(wl, schedule)
-    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], label, unstable(ref["stats"], opn, schedule))
-    nz = check_stats(stats.cpu().numpy(), ref["stats"], label, opn, schedule)
-    if nz:
-        say(label, f"{nz} node(s) at or above the zero discontinuity, not compared")
-    return got, ref, err
-
-
-def sampled_check(wl, segments, label, schedule="tree"):
-    """Full-size run; compare the chosen segments one by one with the oracle."""
-    say(label, f"K={wl.K} dtype={wl.dtype} N={wl.N} nseg={wl.nseg} sampled={len(segments)} schedule={schedule}")
-    out, coeffs, stats = run_gpu(wl, schedule)
-    walk = oracle.adasum_chain if schedule == "chain" else oracle.adasum_tree
-    c_all = coeffs.cpu().numpy()
-    s_all = stats.cpu().numpy()
-    worst = 0.0
-    num = den = 0.0
-    for s in segments:
-        lo, hi = int(wl.seg_offsets[s]), int(wl.seg_offsets[s + 1])
-        rows = wl.segment_host(s)
-        res, cf, st = walk(rows)
-        ref = oracle.round_to_format(res, wl.dtype)
-        got = out[lo:hi].double().cpu().numpy()
-        num += float(np.sum((got - ref) ** 2))
-        den += float(np.sum(ref ** 2))
-        st = np.asarray(st).reshape(-1, 3)
-        opn = oracle.operand_input_norms(rows, schedule)
-        worst = max(worst, check_coeffs(c_all[:, s], np.asarray(cf).reshape(-1, 2), f"{label} seg {s}",
-                                        unstable(st, opn, schedule)))
-        check_stats(s_all[:, s], st, f"{label} seg {s}", opn, schedule)
-    err = np.sqrt(num / den) if den > 0 else np.sqrt(num)
-    say(label, f"sampled relative L2 {err:.3g}, worst coefficient error {worst:.3g}")
-    assert err <= TOL[wl.dtype]
-    return out
 
 
 # ---------------------------------------------------------------- workloads
@@ -409,37 +275,18 @@ def test_long_chain_one_element_segments(gpu, K, dtype, lengths, seed):
     quadratic forms then cancel by the square of that ratio, and Gram entries
     rounded to fp64 once moved coefficients by up to 5e-6 (found by a seeded
     random sweep).  Short tiles keep their entries in double-double."""
-    A = _A()
     wl = W.random_case(K, lengths, dtype=dtype, seed=seed, kind="shared")
-    grads = [g.to(gpu) for g in wl.grads]
-    say(f"long chain K={K} {dtype}")
-    out, coeffs, stats = A.combine(grads, wl.seg_offsets, schedule="chain", return_coeffs=True,
-                                   return_stats=True)
-    torch.cuda.synchronize()
-    ref = oracle.combine_chain([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format=dtype)
-    err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
-    assert err <= TOL[dtype], f"long chain K={K}: relative L2 {err:.3g}"
-    opn = segment_opnorms(wl, "chain")
-    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], f"long chain K={K}", unstable(ref["stats"], opn, "chain"))
-    check_stats(stats.cpu().numpy(), ref["stats"], f"long chain K={K}", opn, "chain")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"long chain K={K} {dtype}", "chain")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("K", [2, 3, 5, 16, 17, 32, 33, 40, 100, 300])
 def test_chain_schedule(gpu, K, dtype):
     # K = 300: twenty stages, each the running result (an fp32 slot) and 15 more inputs
-    A = _A()
     wl = W.random_case(K, [1, 300, 9, 20000, 8], dtype=dtype, seed=300 + K, kind="shared")
-    grads = [g.to(gpu) for g in wl.grads]
-    say(f"chain K={K} {dtype}")
-    out, coeffs, stats = A.combine(grads, wl.seg_offsets, schedule="chain", return_coeffs=True,
-                                   return_stats=True)
-    torch.cuda.synchronize()
-    ref = oracle.combine_chain([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format=dtype)
-    err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
-    assert err <= TOL[dtype], f"chain K={K}: relative L2 {err:.3g}"
-    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], f"chain K={K}")
-    check_stats(stats.cpu().numpy(), ref["stats"], f"chain K={K}")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"chain K={K} {dtype}", "chain")
 
 
 def test_chain_worked_example(gpu):
@@ -704,6 +551,68 @@ def test_graph_capture_and_replay(gpu):
         assert torch.equal(out, ref), f"replay {r}"
 
 
+def test_captured_shape_survives_cache_eviction(gpu):
+    """A shape used under graph capture stays in the plan cache: after 70
+    other shapes (more than the cache's 64) have been planned and run, the
+    captured graph still replays to the eager result."""
+    A = _A()
+    wl = W.random_case(6, [4000, 1, 70001], dtype="f32", seed=811, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    out = torch.empty_like(grads[0])
+    step = A.Combiner(grads, wl.seg_offsets, out=out)
+    side = torch.cuda.Stream(device=gpu)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    small = [torch.randn(200, device=gpu) for _ in range(3)]
+    for i in range(70):
+        A.combine(small, [0, 10 + i, 200])
+    torch.cuda.synchronize()
+    for x in grads:
+        x.mul_(-0.5)
+    graph.replay()
+    torch.cuda.synchronize()
+    ref = A.combine(grads, wl.seg_offsets)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_captured_library_workspace_survives_growth(gpu):
+    """adasum_combine's cached workspace, once used under graph capture, is
+    not freed when a larger shape on the same stream grows it; the graph
+    still replays to the eager result."""
+    A = _A()
+    wl = W.random_case(5, [3000, 17], dtype="f32", seed=812, kind="shared")
+    grads = [g.to(gpu) for g in wl.grads]
+    out = torch.empty_like(grads[0])
+    s = torch.cuda.Stream(device=gpu)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        A.combine_cached(grads, wl.seg_offsets, out=out)  # plans the shape and sizes the workspace
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        A.combine_cached(grads, wl.seg_offsets, out=out)
+    big = W.random_case(20, [200000, 5], dtype="f32", seed=813, kind="shared")
+    big_grads = [g.to(gpu) for g in big.grads]
+    with torch.cuda.stream(s):
+        A.combine_cached(big_grads, big.seg_offsets)  # a larger workspace on the same stream
+    s.synchronize()
+    for x in grads:
+        x.mul_(2.0).add_(1.0)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ref = A.combine(grads, wl.seg_offsets)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 def test_prepared_combiner_matches_combine(gpu):
     """Combiner marshals once; every call reads the buffers' current contents."""
     A = _A()
@@ -726,7 +635,6 @@ def test_prepared_combiner_matches_combine(gpu):
 def test_random_shapes(gpu, case):
     """Seeded random shapes: K, dtype, schedule and ragged segment lengths
     (empty and length-1 segments included) against the oracle."""
-    A = _A()
     rng = np.random.default_rng(4000 + case)
     K = int(rng.integers(1, 49))
     dtype = ["f32", "f16", "bf16"][case % 3]
@@ -735,17 +643,8 @@ def test_random_shapes(gpu, case):
     lengths = [int(x) for x in np.floor(np.exp(rng.uniform(0, np.log(60000), size=nseg)))]
     lengths[int(rng.integers(0, nseg))] = 0
     wl = W.random_case(K, lengths, dtype=dtype, seed=4000 + case, kind="shared")
-    grads = [g.to(gpu) for g in wl.grads]
-    say(f"random case {case}: K={K} {dtype} {schedule} lengths={lengths}")
-    out, coeffs, stats = A.combine(grads, wl.seg_offsets, schedule=schedule, return_coeffs=True, return_stats=True)
-    torch.cuda.synchronize()
-    host = [g.double().numpy() for g in wl.grads]
-    run = oracle.combine if schedule == "tree" else oracle.combine_chain
-    ref = run(host, wl.seg_offsets, out_format=dtype)
-    err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
-    assert err <= TOL[dtype], f"random case {case}: relative L2 {err:.3g}"
-    check_coeffs(coeffs.cpu().numpy(), ref["coeffs"], f"random case {case}")
-    check_stats(stats.cpu().numpy(), ref["stats"], f"random case {case}")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"random case {case}: lengths={lengths}", schedule)
 
 
 def test_seeded_random_sweep(gpu):
@@ -780,18 +679,11 @@ def test_seeded_random_sweep(gpu):
         if kind == "edge":  # exact power-of-two scaling into the format's edge ranges, then rounded to dtype
             scale = {"f32": 2.0 ** -120, "f16": 2.0 ** -20, "bf16": 2.0 ** (-100 if case % 2 else 60)}[dtype]
             wl.grads = [(g.double() * scale).to(g.dtype) for g in wl.grads]
-        grads = [g.to(gpu) for g in wl.grads]
-        out, coeffs, _ = A.combine(grads, wl.seg_offsets, schedule=schedule, return_coeffs=True, return_stats=True)
-        torch.cuda.synchronize()
-        run = oracle.combine_chain if schedule == "chain" else oracle.combine
-        ref = run([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format=dtype)
-        err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
-        c = coeffs.cpu().numpy()
-        cerr = np.abs(c - ref["coeffs"]) / np.maximum(1.0, np.abs(ref["coeffs"]))
-        cerr = np.where(unstable(ref["stats"], segment_opnorms(wl, schedule), schedule), 0.0, cerr)
-        worst = float(cerr.max()) if cerr.size else 0.0
-        if err > TOL[dtype] or worst > COEFF_TOL or not np.all(np.isfinite(c)):
-            bad.append((case, K, dtype, schedule, kind, lengths, zero, err, worst))
+        wl.grads = [g.to(gpu) for g in wl.grads]
+        ev = evaluate(wl, schedule)
+        if not passes(ev, dtype):
+            bad.append((case, K, dtype, schedule, kind, lengths, zero, ev["rel_l2"], ev["seg_ratio"],
+                        ev["coeff_err"]))
     say("seeded sweep", f"150 cases, {len(bad)} failures")
     assert not bad, bad
 
@@ -815,17 +707,9 @@ def test_many_segments_sweep(gpu):
         while K * max(sum(lengths), 1) > 3e7:
             lengths = [n // 2 for n in lengths]
         wl = W.random_case(K, lengths, dtype=dtype, seed=93000 + case, kind=kind)
-        grads = [g.to(gpu) for g in wl.grads]
-        out, coeffs = A.combine(grads, wl.seg_offsets, schedule=schedule, return_coeffs=True)
-        torch.cuda.synchronize()
-        run = oracle.combine_chain if schedule == "chain" else oracle.combine
-        ref = run([g.double().numpy() for g in wl.grads], wl.seg_offsets, out_format=dtype)
-        err = rel_l2(out.double().cpu().numpy(), ref["out_rounded"])
-        c = coeffs.cpu().numpy()
-        cerr = np.abs(c - ref["coeffs"]) / np.maximum(1.0, np.abs(ref["coeffs"]))
-        cerr = np.where(unstable(ref["stats"], segment_opnorms(wl, schedule), schedule), 0.0, cerr)
-        worst = float(cerr.max()) if cerr.size else 0.0
-        if err > TOL[dtype] or worst > COEFF_TOL or not np.all(np.isfinite(c)):
-            bad.append((case, K, dtype, schedule, kind, nseg, err, worst))
+        wl.grads = [g.to(gpu) for g in wl.grads]
+        ev = evaluate(wl, schedule)
+        if not passes(ev, dtype):
+            bad.append((case, K, dtype, schedule, kind, nseg, ev["rel_l2"], ev["seg_ratio"], ev["coeff_err"]))
     say("many-segment sweep", f"20 cases, {len(bad)} failures")
     assert not bad, bad

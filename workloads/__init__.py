@@ -17,4 +17,4 @@ from .shapes import (  # noqa: F401
     offsets_from_lengths,
     resnet50_lengths,
 )
-from .generate import Workload, make_workload, random_case, segment_params  # noqa: F401
+from .generate import Workload, cancelling_pairs, make_workload, random_case, segment_params  # noqa: F401

@@ -161,3 +161,26 @@ def random_case(K, lengths, dtype="f32", seed=0, device="cpu", kind="normal",
             x.zero_()
         grads.append(x.to(tdt).to(device))
     return Workload(K=K, dtype=dtype, seg_offsets=off, grads=grads, seed=seed)
+
+
+def cancelling_pairs(K, lengths, eps, dtype="f32", seed=0):
+    """Worker pairs that nearly cancel: g_{2m+1} = -(1 + eps) g_{2m} + eps n.
+
+    Every worker starts as i.i.d. N(0,1) in fp64 (one torch generator seeded
+    with ``seed``, workers drawn in order); each odd worker is then replaced
+    by the negative of its even neighbour, stretched by 1 + eps, plus eps
+    times its own draw, and every worker is rounded to ``dtype``.  A level-1
+    node of such a pair is about eps times the size of its operands, so the
+    merges above it see a cancellation of about eps^2 in squared norm.  These
+    are the near anti-parallel pairs of the operator's properties (parallel
+    gradients are averaged; an exactly anti-parallel equal-norm pair gives
+    zero).  Host tensors.
+    """
+    off = offsets_from_lengths(lengths)
+    N = int(off[-1])
+    g = torch.Generator().manual_seed(int(seed))
+    base = [torch.randn(N, generator=g, dtype=torch.float64) for _ in range(K)]
+    for k in range(1, K, 2):
+        base[k] = -(1.0 + eps) * base[k - 1] + eps * base[k]
+    grads = [v.to(TORCH_DTYPES[dtype]) for v in base]
+    return Workload(K=K, dtype=dtype, seg_offsets=off, grads=grads, seed=int(seed), notes={"eps": float(eps)})
