@@ -25,6 +25,8 @@ SIGNATURES = {
     "adasum_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
     "adasum_combine_ex": (ctypes.c_int, [_VP, ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          _VP, _VP, ctypes.c_size_t, _VP, _VP, _VP, _VP]),
+    "adasum_combine_noalloc": (ctypes.c_int, [_VP, ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              _VP, _VP, _VP, _VP, _VP]),
     "adasum_sum": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int64, ctypes.c_int, _VP, _VP, ctypes.c_size_t,
                                   _VP]),
     "adasum_sum_workspace_bytes": (ctypes.c_int64, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),

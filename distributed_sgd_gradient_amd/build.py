@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libadasum.so")
 
-SOURCES = ["adasum.hip", "kernels.hip", "plan.cpp"]
+SOURCES = ["adasum.hip", "kernels.hip", "noalloc.hip", "plan.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -69,6 +69,9 @@ int check_devices(const void* const* grads, int K, size_t vec_bytes, const void*
                   size_t ws_needed, const double* coeffs, const double* stats, const double* ortho, size_t nodes,
                   int nseg, int device);
 
+// Whether work enqueued on st now is being captured into a graph.
+bool capturing(hipStream_t st);
+
 // Enqueue every stage of a plan on st.
 int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStream_t st);
 

@@ -161,6 +161,29 @@ ADASUM_API int adasum_combine_ex(const void* const* grads, int K, const int64_t*
                                  void* stream);
 
 /*
+ * adasum_combine_noalloc - adasum_combine_ex for callers that cannot allocate
+ * device memory (tight serving loops, harnesses that forbid hipMalloc).  It
+ * allocates nothing: the call's workspace and plan tables live in a fixed
+ * array of device memory that the library holds on every GPU it runs on,
+ * 64 MiB each, kept until the process ends.  The tables are copied into it
+ * on `stream` from host memory with hipMemcpyAsync, so a call cannot be
+ * captured into a HIP graph (refused with ADASUM_EINVAL; capture
+ * adasum_combine_ex with a workspace allocated before the capture instead).
+ *
+ *   Arguments as for adasum_combine_ex, without the workspace.
+ *   Errors: as adasum_combine_ex, and ADASUM_EINVAL when the shape's
+ *   workspace and tables need more than the array holds (the message gives
+ *   the bytes needed; adasum_combine_ex then serves the shape).
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind: calls that overlap on one GPU (on different streams, or from
+ *   different threads without ordering) race and give wrong results.
+ *   Calls ordered on one stream are safe.
+ */
+ADASUM_API int adasum_combine_noalloc(const void* const* grads, int K, const int64_t* seg_offsets, int nseg,
+                                      int dtype, int schedule, void* out, double* coeffs, double* stats,
+                                      double* ortho, void* stream);
+
+/*
  * adasum_sum - the synchronous-SGD combination the text compares against:
  * out = g_0 + g_1 + ... + g_{K-1}, element by element, accumulated in fp64 in
  * worker order and rounded once to dtype (Sec. 2 of the text: the allreduce

@@ -200,3 +200,30 @@ def test_k_times_nseg_bound():
     assert lib.adasum_workspace_bytes(1000, p, nseg, 0, 0) == _native.EINVAL
     assert "exceeds 2^31 - 1" in lib.adasum_last_error().decode()
     assert lib.adasum_workspace_bytes(999, p, nseg - 10, 0, 0) > 0
+
+
+def _call_noalloc(K=2, off=(0, 8, 16), dtype=0, grads=None, out=FAKE + (1 << 30), coeffs=None, schedule=0):
+    lib = _native.lib()
+    arr, p = _off(*off)
+    if grads is None:
+        grads = [FAKE + (k << 20) for k in range(K)]
+    ptrs = (ctypes.c_void_p * max(len(grads), 1))(*grads)
+    rc = lib.adasum_combine_noalloc(ptrs, K, p, arr.size - 1, dtype, schedule, out, coeffs, None, None, None)
+    return rc, lib.adasum_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,needle", [
+    (dict(K=0), "K must be >= 1"),
+    (dict(out=None), "out is NULL"),
+    (dict(out=FAKE + 16), "overlaps input"),
+    (dict(grads=[FAKE, 0]), "grads[1] is NULL"),
+    (dict(coeffs=FAKE + (1 << 30) + 8), "overlaps"),
+    # 40 fp32 inputs of 2^24 elements: fp32 slots of the second stage alone
+    # need far more than the fixed scratch array holds
+    (dict(K=40, off=(0, 1 << 24)), "bytes of scratch"),
+])
+def test_noalloc_rejects_before_any_launch(kwargs, needle):
+    """The no-allocation entry point validates like adasum_combine_ex and
+    refuses shapes whose workspace and tables exceed its fixed array."""
+    rc, msg = _call_noalloc(**kwargs)
+    assert rc == _native.EINVAL and needle in msg, msg
