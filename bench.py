@@ -170,6 +170,78 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, 
     return base, parity
 
 
+def time_steps(step, steps, profile):
+    """Run `steps` combines back to back on the current stream, bracketed by
+    synchronisations.  Returns (mean ms per step from the host clock, the
+    per-step GPU times from events recorded at every step boundary on the
+    launch stream, per-kernel rows of HIP events around every launch or
+    None)."""
+    import torch
+
+    from distributed_sgd_gradient_amd import _native
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    if profile:
+        _native.profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = _native.profile_end() if profile else None
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return (t1 - t0) * 1e3 / steps, per_step, kernels
+
+
+def step_stats(ms, per_step):
+    srt = sorted(per_step)
+    return {"mean": ms, "median": srt[len(srt) // 2], "min": srt[0], "max": srt[-1]}
+
+
+def kernel_table(kernels, steps):
+    return {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / steps,
+                "bytes_per_step": v["bytes"] / steps,
+                "achieved_GBps": v["bytes"] / (v["milliseconds"] * 1e-3) / 1e9 if v["milliseconds"] > 0 else 0.0,
+                "frac": (v["bytes"] / (v["milliseconds"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+                         if v["milliseconds"] > 0 else 0.0)} for k, v in kernels.items()}
+
+
+def other_workload(config, steps, warmup, dev, budget_s):
+    """A compact record of another workload in the same run: step time
+    (mean, median, min), path roofline, per-kernel times and parity against
+    the oracle on a bounded sample of its segments."""
+    import torch
+
+    import distributed_sgd_gradient_amd as A
+    import workloads as W
+
+    log(f"other workload {config} ({WORKLOAD_NAMES[config]})")
+    wl = W.make_workload(config, device=dev)
+    K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
+    out = torch.empty_like(wl.grads[0])
+    step = A.Combiner(wl.grads, wl.seg_offsets, out=out, return_coeffs=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms, per_step, kernels = time_steps(step, steps, profile=True)
+    b_min = K * N * esz + N * esz
+    st = step_stats(ms, per_step)
+    log(f"  {steps} steps: {ms:.3f} ms/step (median {st['median']:.3f}, min {st['min']:.3f})")
+    _, parity = cpu_baseline(wl, budget_s, "tree", 1, gpu_out=out, gpu_coeffs=step.coeffs)
+    log(f"  parity on {parity['segments']} segments: relative L2 {parity['rel_l2']:.3g}, "
+        f"coefficient error {parity['max_coeff_err']}")
+    rec = {"workload": WORKLOAD_NAMES[config], "K": K, "N": N, "nseg": wl.nseg, "io_dtype": wl.dtype,
+           "ms_per_step": st, "gradient_GBps": K * N * esz / (ms * 1e-3) / 1e9,
+           "path_frac": b_min / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "B_min_bytes": b_min,
+           "kernels": kernel_table(kernels, steps), "parity": parity}
+    del step, out, wl
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +254,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of one-thread oracle time that bound the CPU baseline's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--others", default="2,4",
+                    help="comma-separated workloads also timed in the same run (compact records under "
+                         "'other_workloads'); only with the default workload; '' for none")
     ap.add_argument("--cold", action="store_true",
                     help="also time each step alone after writing a 1 GiB scratch buffer (caches cold); "
                          "reported under 'cold', the headline value stays the back-to-back rate")
@@ -199,7 +274,6 @@ def main():
     import torch
 
     import distributed_sgd_gradient_amd as A
-    from distributed_sgd_gradient_amd import _native
     import workloads as W
 
     dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", "0")))
@@ -226,16 +300,15 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    _native.profile_begin()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernels = _native.profile_end()
-    ms = (t1 - t0) * 1e3 / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    # the timed region: HIP events around every launch (per-kernel times)
+    # and at every step boundary (per-step times)
+    ms, per_step, kernels = time_steps(step, args.steps, profile=True)
+    steps_ms = step_stats(ms, per_step)
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {steps_ms['median']:.3f}, min {steps_ms['min']:.3f})")
+    # the same steps again without the per-launch events, for comparison
+    ms_bare, per_step_bare, _ = time_steps(step, args.steps, profile=False)
+    bare_ms = step_stats(ms_bare, per_step_bare)
+    log(f"again without per-launch events: {ms_bare:.3f} ms/step (median {bare_ms['median']:.3f})")
 
     grad_bytes = K * N * esz
     b_min = grad_bytes + N * esz
@@ -247,9 +320,12 @@ def main():
     achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(WORKLOAD_NAMES[args.config], dom_name),
-                "kernel": dom_name, "launch_ms": per_launch_ms, "algorithmic_bytes_per_launch": per_launch_bytes}
+                "kernel": dom_name, "launch_ms": per_launch_ms, "algorithmic_bytes_per_launch": per_launch_bytes,
+                "scope": f"the dominant kernel ({dom_name}) alone; the whole path's fraction of the HBM "
+                         f"roofline, the metric's figure, is path_roofline.frac"}
     path = {"B_min_bytes": b_min, "achieved": b_min / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": b_min / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "frac": b_min / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "frac_median_step": b_min / (steps_ms["median"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
     for name, k in sorted(kernels.items()):
         log(f"  {name:12s} launches {k['launches']:5d}  {k['milliseconds'] / args.steps:8.3f} ms/step  "
             f"{k['bytes'] / (k['milliseconds'] * 1e-3) / 1e9 if k['milliseconds'] > 0 else 0:8.1f} GB/s")
@@ -282,12 +358,9 @@ def main():
     for _ in range(args.warmup):
         A.plain_sum(wl.grads, out=out_sum)
     torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        A.plain_sum(wl.grads, out=out_sum)
-    torch.cuda.synchronize()
-    sum_ms = (time.perf_counter() - t2) * 1e3 / args.steps
-    plain_sum = {"ms_per_step": sum_ms, "gradient_GBps": grad_bytes / (sum_ms * 1e-3) / 1e9,
+    sum_ms, sum_steps, _ = time_steps(lambda: A.plain_sum(wl.grads, out=out_sum), args.steps, profile=False)
+    plain_sum = {"ms_per_step": sum_ms, "ms_per_step_median": sorted(sum_steps)[len(sum_steps) // 2],
+                 "gradient_GBps": grad_bytes / (sum_ms * 1e-3) / 1e9,
                  "path_frac": b_min / (sum_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "adasum_over_sum_time": ms / sum_ms}
     log(f"plain sum on the same buffers: {sum_ms:.3f} ms/step; Adasum takes {ms / sum_ms:.2f}x as long")
     del out_sum
@@ -302,20 +375,26 @@ def main():
         log(f"parity on {parity['segments']} segments: relative L2 {parity['rel_l2']:.3g}, "
             f"coefficient error {parity['max_coeff_err']}")
 
+    config = {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg, "io_dtype": wl.dtype,
+              "seed": wl.seed, "schedule": args.schedule, "parallelism": "none (one GPU)"}
+    others = {}
+    if args.others and args.config == 3 and args.seed is None and args.schedule == "tree":
+        del step, wl
+        torch.cuda.empty_cache()
+        for c in [int(x) for x in args.others.split(",") if x]:
+            others[WORKLOAD_NAMES[c]] = other_workload(c, args.steps, args.warmup, dev,
+                                                       0.0 if args.no_cpu_baseline else 5.0)
+
     line = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f64", "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "K": K, "N": N, "nseg": wl.nseg,
-                   "io_dtype": wl.dtype, "seed": wl.seed, "schedule": args.schedule,
-                   "parallelism": "none (one GPU)"},
-        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "parity": parity, "plain_sum": plain_sum,
+        "config": config,
+        "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "parity": parity,
+        "step_ms": steps_ms, "step_ms_without_launch_events": bare_ms, "plain_sum": plain_sum,
         **({"cold": cold} if cold is not None else {}),
-        "kernels": {k: {"launches": v["launches"], "ms_per_step": v["milliseconds"] / args.steps,
-                        "bytes_per_step": v["bytes"] / args.steps,
-                        "achieved_GBps": v["bytes"] / (v["milliseconds"] * 1e-3) / 1e9 if v["milliseconds"] > 0 else 0.0,
-                        "frac": (v["bytes"] / (v["milliseconds"] * 1e-3) / 1e9 / PEAK_HBM_GBS
-                                 if v["milliseconds"] > 0 else 0.0)} for k, v in kernels.items()},
+        "kernels": kernel_table(kernels, args.steps),
+        **({"other_workloads": others} if others else {}),
     }
     print(json.dumps(line), flush=True)
 
