@@ -75,11 +75,6 @@ def cpu_model():
 
 TOL_REL_L2 = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
 TOL_COEFF = 1e-6
-# an operand whose squared norm is at most this fraction of the (nonzero)
-# summed squared norms of the input gradients under it sits at the operator's
-# discontinuity (coefficient 1 at exactly zero, another limit next to it); its
-# coefficient and those of the nodes above it are not gated
-NEAR_ZERO = 1e-8
 
 
 def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, gpu_out=None, gpu_coeffs=None):
@@ -109,7 +104,7 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, 
     used, elems, spent = [], 0, 0.0
     err2 = ref2 = 0.0
     cerr = 0.0
-    exempt = 0
+    exempt = unsettled_segments = 0
     coeffs_host = gpu_coeffs.cpu().numpy() if gpu_coeffs is not None else None
     with threadpool_limits(limits=1):
         for s in order:
@@ -119,7 +114,15 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, 
             spent += time.perf_counter() - t0
             used.append(s)
             elems += rows[0].size
-            if gpu_out is not None:
+            if gpu_out is not None or coeffs_host is not None:
+                # outside the timed call: which coefficients, and whether this
+                # segment's output, the oracle itself determines (one-ulp noise
+                # on the inputs moves them by less than a tenth of their
+                # tolerance); the rest is reported, not gated
+                stab = oracle.stability(rows, [0, rows[0].size], schedule)
+                seg_ok = stab["output_motion"][0] <= TOL_REL_L2[wl.dtype] / 10
+                unsettled_segments += 0 if seg_ok else 1
+            if gpu_out is not None and seg_ok:
                 lo, hi = int(wl.seg_offsets[s]), int(wl.seg_offsets[s + 1])
                 ref = oracle.round_to_format(res, wl.dtype)
                 got = gpu_out[lo:hi].double().cpu().numpy()
@@ -127,9 +130,7 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, 
                 ref2 += float(np.sum(ref ** 2))
             if coeffs_host is not None and len(coeffs):
                 c = np.asarray(coeffs, dtype=np.float64)
-                st = np.asarray(stats, dtype=np.float64)
-                zero = oracle.discontinuity_mask(st, oracle.operand_input_norms(rows, schedule), schedule,
-                                                 NEAR_ZERO)
+                zero = stab["coeff_motion"][:, 0, :] > TOL_COEFF / 10
                 exempt += int(np.count_nonzero(zero))
                 err = np.where(zero, 0.0, np.abs(coeffs_host[:, s, :] - c) / np.maximum(1.0, np.abs(c)))
                 cerr = max(cerr, float(np.max(err)))
@@ -165,7 +166,8 @@ def cpu_baseline(wl, budget_s, schedule="tree", threads=1, batch_bytes=8 << 30, 
         parity = {"against": "fp64 oracle, rounded to the output dtype", "segments": len(used),
                   "elements_per_worker": elems, "rel_l2": rel, "tol_rel_l2": tol,
                   "max_coeff_err": cerr if coeffs_host is not None else None, "tol_coeff": TOL_COEFF,
-                  "coeffs_at_or_above_zero_discontinuity": exempt if coeffs_host is not None else None,
+                  "coeffs_not_determined_by_the_oracle": exempt if coeffs_host is not None else None,
+                  "segments_not_determined_by_the_oracle": unsettled_segments,
                   "pass": bool(rel <= tol and (coeffs_host is None or cerr <= TOL_COEFF))}
     return base, parity
 

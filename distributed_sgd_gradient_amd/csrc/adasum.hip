@@ -96,7 +96,6 @@ void release_tables(CachedPlan& cp) {
     (void)hipFree(kv.second.seg_tile);
     (void)hipFree(kv.second.descs);
     (void)hipFree(kv.second.merges);
-    (void)hipFree(kv.second.short_off);
   }
   cp.per_device.clear();
   (void)hipSetDevice(cur);
@@ -173,7 +172,6 @@ int device_tables(CachedPlan& cp, int device, DeviceTables* out) {
       {reinterpret_cast<void**>(&t.seg_tile), p.seg_tile.data(), sizeof(int32_t) * p.seg_tile.size()},
       {reinterpret_cast<void**>(&t.descs), p.descs.data(), sizeof(BlockDesc) * p.descs.size()},
       {reinterpret_cast<void**>(&t.merges), p.merges.data(), sizeof(Merge) * p.merges.size()},
-      {reinterpret_cast<void**>(&t.short_off), p.short_off.data(), sizeof(int64_t) * p.short_off.size()},
   };
   int rc = ADASUM_OK;
   for (Upload& u : ups) {
@@ -381,33 +379,29 @@ int check_devices(const void* const* grads, int K, size_t vec_bytes, const void*
 void* ref_ptr(const Plan& p, const CallBuffers& b, Ref r) {
   switch (r.kind) {
     case Ref::Input: return const_cast<void*>(b.grads[r.idx]);
-    case Ref::Slot: return b.ws + p.ws_slots + (size_t)r.idx * (size_t)p.N * sizeof(float);
+    case Ref::Slot: return b.ws + p.ws_slots + (size_t)r.idx * (size_t)p.N * sizeof(double);
     case Ref::Out: return b.out;
   }
   return nullptr;
 }
 
-DType ref_type(const Plan& p, Ref r) { return r.kind == Ref::Slot ? DType::F32 : p.dtype; }
+DType ref_type(const Plan& p, Ref r) { return r.kind == Ref::Slot ? DType::F64 : p.dtype; }
 
-// The kernels a block needs: its operands' type, and, for an fp32 block that
-// also reads 16-bit inputs (carried up from below), the inputs' type and
-// which operands they are.
+// The kernels a block needs: its operands' type (the inputs' dtype in the
+// first stage, F64 once it reads a slot) and, for a block over slots, which
+// operands are inputs carried up (read in the inputs' dtype).
 struct BlockKind {
-  DType in_t;        // operand type of the launch
-  DType narrow_t;    // 16-bit type of the marked operands, or F32 for none
-  uint32_t narrow;   // bit k: operand k is read in narrow_t
+  DType in_t;
+  uint32_t narrow;  // bit k: operand k is an input (only with in_t == F64)
 };
 
 BlockKind block_kind(const Plan& p, const Block& b) {
   bool any_slot = false;
   for (const Ref& r : b.operands) any_slot |= r.kind == Ref::Slot;
-  if (!any_slot) return {p.dtype, DType::F32, 0u};  // inputs only, in their own type
-  BlockKind k{DType::F32, DType::F32, 0u};
-  if (p.dtype != DType::F32) {
-    for (size_t i = 0; i < b.operands.size(); ++i)
-      if (b.operands[i].kind == Ref::Input) k.narrow |= 1u << i;
-    if (k.narrow) k.narrow_t = p.dtype;
-  }
+  if (!any_slot) return {p.dtype, 0u};
+  BlockKind k{DType::F64, 0u};
+  for (size_t i = 0; i < b.operands.size(); ++i)
+    if (b.operands[i].kind == Ref::Input) k.narrow |= 1u << i;
   return k;
 }
 
@@ -415,38 +409,60 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
   const int ntiles = (int)p.tiles.size();
   hipError_t e;
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
-  // kept only where there are short tiles (the region is empty otherwise)
-  double* partials_lo = p.short_rows > 0 ? reinterpret_cast<double*>(b.ws + p.ws_plo) : nullptr;
+  double* partials_lo = reinterpret_cast<double*>(b.ws + p.ws_plo);
   double* weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
+  double* weights_lo = reinterpret_cast<double*>(b.ws + p.ws_weights_lo);
   uint32_t* flags = reinterpret_cast<uint32_t*>(b.ws + p.ws_flags);
   int stage_no = 0;
   for (const Stage& sg : p.stages) {
     ++stage_no;
-    // 16-bit Gram launches of this stage (the only inexact ones), for the
-    // exact recomputation of flagged (block, segment) pairs
-    struct Narrow {
+    TreeArgs t{};
+    t.descs = dt.descs;
+    t.merges = dt.merges;
+    t.seg_tile = dt.seg_tile;
+    t.partials = partials;
+    t.partials_lo = partials_lo;
+    t.tiles = dt.tiles;
+    t.lo_inputs = p.dtype != DType::F32;
+    t.desc0 = sg.blocks.front().desc;
+    t.nblocks = (int)sg.blocks.size();
+    t.nseg = p.nseg;
+    t.weights = weights;
+    t.weights_lo = weights_lo;
+    t.coeffs = b.coeffs;
+    t.stats = b.stats;
+    t.ortho = b.ortho;
+    t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
+    t.nblocks_total = p.nblocks;
+    if (ntiles == 0) {  // every segment empty: coefficients 1, statistics 0
+      if (p.nseg > 0) {
+        e = launch_tree(t, st);
+        if (e != hipSuccess) return fail_hip(e, "launching tree");
+      }
+      continue;
+    }
+    // The Gram launches of this stage, kept for the exact recomputation of
+    // flagged (block, segment) pairs
+    struct GramLaunch {
       GramArgs args;
-      DType t;
+      DType in_t;
       int nbt, njobs;
     };
-    std::vector<Narrow> narrow_grams;
-    // 1. Gram partials, blocks grouped by (operand types, Gram size)
-    // 3. weighted sums, grouped by (operand types, Gram size, result type)
+    std::vector<GramLaunch> grams;
+    // 1. Gram partials, blocks grouped by (operand type, Gram size)
+    // 3. weighted sums, grouped by (operand type, Gram size, result type)
     for (int pass = 0; pass < 2; ++pass) {
-      if (ntiles == 0) break;
       std::vector<char> done(sg.blocks.size(), 0);
       for (size_t i = 0; i < sg.blocks.size(); ++i) {
         if (done[i]) continue;
         const Block& b0 = sg.blocks[i];
-        const BlockKind kind0 = block_kind(p, b0);
-        const DType in_t = kind0.in_t;
+        const DType in_t = block_kind(p, b0).in_t;
         const DType out_t = ref_type(p, b0.dst);
         const int nbt = p.descs[b0.desc].nbt;
         std::vector<const Block*> group;
         for (size_t k = i; k < sg.blocks.size(); ++k) {
           const Block& bk = sg.blocks[k];
-          const BlockKind kk = block_kind(p, bk);
-          if (done[k] || p.descs[bk.desc].nbt != nbt || kk.in_t != in_t || kk.narrow_t != kind0.narrow_t) continue;
+          if (done[k] || p.descs[bk.desc].nbt != nbt || block_kind(p, bk).in_t != in_t) continue;
           if (pass == 1 && ref_type(p, bk.dst) != out_t) continue;
           done[k] = 1;
           group.push_back(&bk);
@@ -456,97 +472,60 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
           double in_bytes = 0, out_bytes = 0;
           if (pass == 0) {
             GramArgs a{};
-            std::memset(a.side_slot, -1, sizeof a.side_slot);
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
               for (size_t k = 0; k < bk.operands.size(); ++k) {
                 a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
                 in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
-                if (bk.operands[k].kind == Ref::Slot) a.side_slot[j][k] = bk.operands[k].idx;
               }
               a.narrow[j] = block_kind(p, bk).narrow;
               a.poff[j] = p.descs[bk.desc].poff;
+              a.wrow[j] = p.descs[bk.desc].wrow;
               out_bytes += 8.0 * gram_entries(nbt) * ntiles;
             }
             a.tiles = dt.tiles;
             a.partials = partials;
             a.partials_lo = partials_lo;
-            if (p.short_rows > 0 && in_t == DType::F32) {
-              a.side = reinterpret_cast<const double*>(b.ws + p.ws_side);
-              a.short_off = dt.short_off;
-              a.short_rows = p.short_rows;
-            }
+            a.flags = flags;
+            a.nseg = p.nseg;
             log_launch("gram", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kGram, in_bytes + out_bytes, st);
-            e = launch_gram(in_t, kind0.narrow_t, nbt, a, ntiles, n, st);
+            e = launch_gram(in_t, p.dtype, nbt, a, ntiles, n, st);
             prof_stop(pr, st);
             if (e != hipSuccess) return fail_hip(e, "launching gram");
-            if (in_t != DType::F32) {
-              Narrow nw{a, in_t, nbt, n};
-              for (int j = 0; j < n; ++j) nw.args.wrow[j] = p.descs[group[c + j]->desc].wrow;
-              nw.args.flags = flags;
-              nw.args.nseg = p.nseg;
-              narrow_grams.push_back(nw);
-            }
+            grams.push_back(GramLaunch{a, in_t, nbt, n});
           } else {
             WsumArgs a{};
-            std::memset(a.side_slot, -1, sizeof a.side_slot);
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
               for (size_t k = 0; k < bk.operands.size(); ++k) {
                 a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
                 in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
-                if (bk.operands[k].kind == Ref::Slot && p.short_rows > 0) {
-                  a.side_slot[j][k] = bk.operands[k].idx;
-                  a.side_mask[j] |= 1u << k;
-                }
               }
               a.narrow[j] = block_kind(p, bk).narrow;
               a.y[j] = ref_ptr(p, b, bk.dst);
               a.wrow[j] = p.descs[bk.desc].wrow;
               out_bytes += (double)p.N * dtype_size(out_t);
-              if (bk.dst.kind == Ref::Slot && p.short_rows > 0)
-                a.side[j] = reinterpret_cast<double*>(b.ws + p.ws_side) + (size_t)bk.dst.idx * (size_t)p.short_rows;
             }
             a.tiles = dt.tiles;
             a.nseg = p.nseg;
             a.weights = weights;
-            a.short_off = dt.short_off;
-            if (p.short_rows > 0) {
-              a.side_in = reinterpret_cast<const double*>(b.ws + p.ws_side);
-              a.short_rows = p.short_rows;
-            }
+            a.weights_lo = weights_lo;
+            a.flags = flags;
             log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
-            e = launch_wsum(in_t, kind0.narrow_t, nbt, out_t, a, ntiles, n, st);
+            e = launch_wsum(in_t, p.dtype, nbt, out_t, a, ntiles, n, st);
             prof_stop(pr, st);
             if (e != hipSuccess) return fail_hip(e, "launching wsum");
           }
         }
       }
       if (pass == 0 && p.nseg > 0) {
-        // 3. per (block, segment): statistics, coefficients, operand weights
-        TreeArgs t{};
-        t.descs = dt.descs;
-        t.merges = dt.merges;
-        t.seg_tile = dt.seg_tile;
-        t.partials = partials;
-        t.partials_lo = partials_lo;
-        t.tiles = dt.tiles;
-        t.lo_inputs = p.dtype != DType::F32;
-        t.desc0 = sg.blocks.front().desc;
-        t.nblocks = (int)sg.blocks.size();
-        t.nseg = p.nseg;
-        t.weights = weights;
-        t.coeffs = b.coeffs;
-        t.stats = b.stats;
-        t.ortho = b.ortho;
-        t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
-        t.nblocks_total = p.nblocks;
-        // the matrix cores round each 32-row sum of exact 16-bit products to
-        // fp32 once (relative error 2^-24), with a margin for the fp64
-        // accumulation of the partials
-        t.gram_err = narrow_grams.empty() ? 0.0 : std::ldexp(1.0, -24) * (1.0 + std::ldexp(1.0, -10));
+        // 2. per (block, segment): statistics, coefficients, operand weights,
+        // and a flag on every pair whose coefficients the rounding of its
+        // Gram entries could move beyond tolerance (a merge under deep
+        // cancellation); those pairs' tiles are then recomputed exactly and
+        // walked again
         t.flags = flags;
         double bytes = 0;
         for (const Block& bk : sg.blocks) bytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
@@ -555,48 +534,25 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         e = launch_tree(t, st);
         prof_stop(pr, st);
         if (e != hipSuccess) return fail_hip(e, "launching tree");
-        if (!narrow_grams.empty()) {
-          // pairs whose coefficients the fp32 rounding could move by more
-          // than kRefineTol: their tiles recomputed exactly, then walked again
-          for (const Narrow& nw : narrow_grams) {
-            // algorithmic bytes: the flag of every tile (flagged tiles, none in
-            // the usual case, also re-read their operands)
-            const double fbytes = 4.0 * ntiles * nw.njobs;
-            log_launch("exact", stage_no, ntiles, nw.njobs, nw.nbt, fbytes);
-            const int pe = prof_start(kExact, fbytes, st);
-            e = launch_gram_exact(nw.t, nw.nbt, nw.args, ntiles, nw.njobs, st);
-            prof_stop(pe, st);
-            if (e != hipSuccess) return fail_hip(e, "launching exact gram");
-          }
-          TreeArgs r = t;
-          r.gram_err = 0.0;
-          r.refine = 1;
-          const double rbytes = 4.0 * t.nblocks * p.nseg;  // the flags
-          log_launch("tree", stage_no, t.nblocks * p.nseg, 1, 0, rbytes);
-          const int pt = prof_start(kTree, rbytes, st);
-          e = launch_tree(r, st);
-          prof_stop(pt, st);
-          if (e != hipSuccess) return fail_hip(e, "launching tree");
+        for (const GramLaunch& g : grams) {
+          // algorithmic bytes: the flag of every tile (flagged tiles, none in
+          // the usual case, also re-read their operands)
+          const double fbytes = 4.0 * ntiles * g.njobs;
+          log_launch("exact", stage_no, ntiles, g.njobs, g.nbt, fbytes);
+          const int pe = prof_start(kExact, fbytes, st);
+          e = launch_gram_exact(g.in_t, p.dtype, g.nbt, g.args, ntiles, g.njobs, st);
+          prof_stop(pe, st);
+          if (e != hipSuccess) return fail_hip(e, "launching exact gram");
         }
+        TreeArgs r = t;
+        r.refine = 1;
+        const double rbytes = 4.0 * t.nblocks * p.nseg;  // the flags
+        log_launch("tree", stage_no, t.nblocks * p.nseg, 1, 0, rbytes);
+        const int pt = prof_start(kTree, rbytes, st);
+        e = launch_tree(r, st);
+        prof_stop(pt, st);
+        if (e != hipSuccess) return fail_hip(e, "launching tree");
       }
-    }
-    if (ntiles == 0 && p.nseg > 0) {
-      TreeArgs t{};
-      t.descs = dt.descs;
-      t.merges = dt.merges;
-      t.seg_tile = dt.seg_tile;
-      t.partials = partials;
-      t.desc0 = sg.blocks.front().desc;
-      t.nblocks = (int)sg.blocks.size();
-      t.nseg = p.nseg;
-      t.weights = weights;
-      t.coeffs = b.coeffs;
-      t.stats = b.stats;
-      t.ortho = b.ortho;
-      t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
-      t.nblocks_total = p.nblocks;
-      e = launch_tree(t, st);
-      if (e != hipSuccess) return fail_hip(e, "launching tree");
     }
   }
   return ADASUM_OK;

@@ -82,6 +82,7 @@ __device__ __forceinline__ T gload(const T* p) {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef double v2d __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Elem;
@@ -195,8 +196,22 @@ struct Elem<bf16_t> {
   }
 };
 
-// A 16-bit input gradient read by an fp32 launch (an input carried into a
-// later stage), widened exactly to fp32.
+// An fp64 slot: the block result that feeds a later stage, kept unrounded.
+template <>
+struct Elem<double> {
+  static __device__ __forceinline__ double round(double x, double* stored) {
+    *stored = x;
+    return x;
+  }
+  static __device__ __forceinline__ void store1(double* p, double v) { *p = v; }
+  static __device__ __forceinline__ void store8(double* p, const double (&v)[kGroup]) {
+#pragma unroll
+    for (int i = 0; i < kGroup; i += 2) *reinterpret_cast<v2d*>(p + i) = v2d{v[i], v[i + 1]};
+  }
+};
+
+// A 16-bit input gradient read by a launch over fp64 slots (an input carried
+// into a later stage), widened exactly to fp32.
 template <typename TN>
 __device__ __forceinline__ float narrow_to_f32(uint32_t bits16);
 template <>
@@ -252,36 +267,6 @@ __device__ __forceinline__ v4f load_f32x4(const float* __restrict__ x, int64_t r
   return v4f{w[0], w[1], w[2], w[3]};
 }
 
-// The same for an operand stored in the 16-bit type TN, widened.
-template <typename TN>
-__device__ __forceinline__ v4f load_n16x4(const uint16_t* __restrict__ x, int64_t row, int64_t lo, int64_t hi) {
-  if (row >= lo && row + 4 <= hi) {
-    const v2u w = gload(reinterpret_cast<const v2u*>(x + row));
-    return v4f{narrow_to_f32<TN>(w.x & 0xffffu), narrow_to_f32<TN>(w.x >> 16), narrow_to_f32<TN>(w.y & 0xffffu),
-               narrow_to_f32<TN>(w.y >> 16)};
-  }
-  float w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = (row + e >= lo && row + e < hi) ? narrow_to_f32<TN>(gload(x + row + e)) : 0.f;
-  return v4f{w[0], w[1], w[2], w[3]};
-}
-
-// Eight consecutive values at rows [row, row + 8) of a 16-bit operand, widened, zero outside [lo, hi).
-template <typename TN>
-__device__ __forceinline__ void load_n16x8(const uint16_t* __restrict__ x, int64_t row, int64_t lo, int64_t hi,
-                                           v4f& a, v4f& b) {
-  if (row >= lo && row + 8 <= hi) {
-    const v4u w = gload(reinterpret_cast<const v4u*>(x + row));
-    a = v4f{narrow_to_f32<TN>(w.x & 0xffffu), narrow_to_f32<TN>(w.x >> 16), narrow_to_f32<TN>(w.y & 0xffffu),
-            narrow_to_f32<TN>(w.y >> 16)};
-    b = v4f{narrow_to_f32<TN>(w.z & 0xffffu), narrow_to_f32<TN>(w.z >> 16), narrow_to_f32<TN>(w.w & 0xffffu),
-            narrow_to_f32<TN>(w.w >> 16)};
-    return;
-  }
-  a = load_n16x4<TN>(x, row, lo, hi);
-  b = load_n16x4<TN>(x, row + 4, lo, hi);
-}
-
 // Double-double values (hi + lo, |lo| <= ulp(hi) / 2) for the merge walk's
 // sums and the Gram entries of short tiles.  A node far smaller than the
 // operands under it (a near-cancellation) makes its quadratic form cancel: summed in fp64, the rounding of the terms
@@ -321,171 +306,18 @@ __device__ __forceinline__ DD dd_mul(DD x, DD y) {
   return DD{hi, p.lo - (hi - p.hi)};
 }
 
-// TN = float: every operand is fp32.  Otherwise the lanes of operands that
-// the job's narrow mask marks read them in TN (16-bit inputs carried into a
-// later stage) and widen them exactly; the products stay exact.  Such a
-// launch takes 32-row chunks with eight consecutive rows per lane, so that a
-// 16-bit lane reads 16 bytes at once (an fp32 lane two times 16); any
-// assignment of rows to the instruction steps gives the same Gram matrix, as
-// long as every operand lane uses the same row at each step.
-// Operand op of job j at a row of a short tile, in fp64: from the slot's
-// side buffer (srow: the row's position there) when it is a slot, else the
-// operand itself (fp32, or a 16-bit input marked narrow), widened exactly.
-template <typename TN>
-__device__ __forceinline__ double operand_f64(const GramArgs& a, int j, int op, int64_t row, int64_t srow) {
-  const int slot = a.side_slot[j][op];
-  if (slot >= 0) return a.side[(int64_t)slot * a.short_rows + srow];
-  const void* p = a.x[j][op];
-  if (p == nullptr) return 0.0;
-  if constexpr (!std::is_same<TN, float>::value) {
-    if ((a.narrow[j] >> op) & 1u) return (double)narrow_to_f32<TN>(gload(static_cast<const uint16_t*>(p) + row));
-  }
-  return (double)gload(static_cast<const float*>(p) + row);
-}
-
-template <int NB, typename TN>
-__global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
-  constexpr bool kMixed = !std::is_same<TN, float>::value;
-  constexpr int SETS = 16 / NB;          // row sets packed into the 16 operand lanes
-  constexpr int U = kF64Unroll;
-  constexpr int RC = 16 * SETS;          // rows per chunk
-  constexpr int R = RC * U;              // rows per wave per iteration
+// Sum the four waves' 16 x 16 blocks (and the row sets' diagonal NB x NB
+// blocks) in a fixed order; write the packed triangle to out.  Lane l,
+// register r of a wave holds D[l % 16][4 r + l / 16].
+template <int NB>
+__device__ __forceinline__ void f64_gram_reduce(double (*red)[64 * 4], const f64x4& acc, double* out) {
+  constexpr int SETS = 16 / NB;
   constexpr int NE = gram_entries(NB);
-  static_assert(NB * SETS == 16, "NB divides 16");
-  __shared__ double red[kGramWaves][64 * 4];
-
-  const int tile_id = blockIdx.x;
-  const int j = blockIdx.y;
-  const Tile tile = args.tiles[tile_id];
-  const int64_t lo = tile.start, hi = tile.start + tile.len;
-  if (args.short_off != nullptr && tile.len <= kExactRows) {  // workgroup-uniform
-    bool slots = false;
-#pragma unroll
-    for (int k = 0; k < NB; ++k) slots = slots || args.side_slot[j][k] >= 0;
-    if (slots) {
-      // a short tile of a stage above the first: slot operands from their
-      // fp64 side buffers (not the fp32-rounded slots), every entry summed
-      // row by row in double-double from exact products (a fused
-      // multiply-add gives each product's rounding error); the low parts go
-      // to partials_lo.  (Short tiles of fp32 inputs alone stay on the
-      // matrix cores, whose products are exact.)
-      const int64_t so = args.short_off[tile_id];
-      double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
-      double* out_lo = args.partials_lo != nullptr ? args.partials_lo + args.poff[j] + (int64_t)tile_id * NE : nullptr;
-      for (int e = threadIdx.x; e < NE; e += kBlock) {
-        int i = 0, rem = e;
-        while (rem >= NB - i) {
-          rem -= NB - i;
-          ++i;
-        }
-        const int k = i + rem;
-        DD sum{0.0, 0.0};
-        for (int r = 0; r < tile.len; ++r)
-          sum = dd_add(sum, dd_prod(operand_f64<TN>(args, j, i, lo + r, so + r),
-                                    operand_f64<TN>(args, j, k, lo + r, so + r)));
-        out[e] = sum.hi;
-        if (out_lo != nullptr) out_lo[e] = sum.lo;
-      }
-      return;
-    }
-  }
-  const int64_t first = lo & ~int64_t(kGroup - 1);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int op = (lane & 15) % NB, set = (lane & 15) / NB, grp = lane >> 4;
-
-  // a NULL operand (beyond the block's count) reads operand 0, masked to zero
-  const void* mine = args.x[j][op];
-  const bool live = mine != nullptr;
-  const float* xp = static_cast<const float*>(live ? mine : args.x[j][0]);
-  // a masked operand reads operand 0, in operand 0's type
-  const bool narrow = kMixed && ((args.narrow[j] >> (live ? op : 0)) & 1u);
-  const uint16_t* xn = reinterpret_cast<const uint16_t*>(xp);
-
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  const int64_t niter = (hi - first + R - 1) / R;
-  if constexpr (!kMixed) {
-    const int64_t lane_row = (int64_t)set * 16 + 4 * grp;  // first row of this lane in a chunk
-    for (int64_t it = wave; it < niter; it += kGramWaves) {
-      const int64_t r0 = first + it * R;
-      v4f v[U];
-      if (r0 >= lo && r0 + R <= hi) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4f*>(xp + r0 + u * RC + lane_row));
-      } else {
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load_f32x4(xp, r0 + u * RC + lane_row, lo, hi);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!live) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].x, (double)v[u].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].y, (double)v[u].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].z, (double)v[u].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].w, (double)v[u].w, acc, 0, 0, 0);
-      }
-    }
-  } else {
-    constexpr int RC2 = 32 * SETS;  // rows per chunk: eight per lane
-    constexpr int U2 = U / 2;       // chunks per iteration (the same R rows)
-    static_assert(RC2 * U2 == R, "same rows per iteration");
-    const int64_t lane_row = (int64_t)set * 32 + 8 * grp;
-    for (int64_t it = wave; it < niter; it += kGramWaves) {
-      const int64_t r0 = first + it * R;
-      v4f va[U2], vb[U2];
-      if (r0 >= lo && r0 + R <= hi) {  // the whole iteration inside the tile: no per-row checks
-        if (narrow) {
-          v4u w[U2];
-#pragma unroll
-          for (int u = 0; u < U2; ++u) w[u] = gload(reinterpret_cast<const v4u*>(xn + r0 + u * RC2 + lane_row));
-#pragma unroll
-          for (int u = 0; u < U2; ++u) {
-            va[u] = v4f{narrow_to_f32<TN>(w[u].x & 0xffffu), narrow_to_f32<TN>(w[u].x >> 16),
-                        narrow_to_f32<TN>(w[u].y & 0xffffu), narrow_to_f32<TN>(w[u].y >> 16)};
-            vb[u] = v4f{narrow_to_f32<TN>(w[u].z & 0xffffu), narrow_to_f32<TN>(w[u].z >> 16),
-                        narrow_to_f32<TN>(w[u].w & 0xffffu), narrow_to_f32<TN>(w[u].w >> 16)};
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < U2; ++u) {
-            const float* p = xp + r0 + u * RC2 + lane_row;
-            va[u] = gload(reinterpret_cast<const v4f*>(p));
-            vb[u] = gload(reinterpret_cast<const v4f*>(p + 4));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < U2; ++u) {
-          const int64_t row = r0 + u * RC2 + lane_row;
-          if (narrow) {
-            load_n16x8<TN>(xn, row, lo, hi, va[u], vb[u]);
-          } else {
-            va[u] = load_f32x4(xp, row, lo, hi);
-            vb[u] = load_f32x4(xp, row + 4, lo, hi);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U2; ++u) {
-        if (!live) va[u] = vb[u] = v4f{0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].x, (double)va[u].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].y, (double)va[u].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].z, (double)va[u].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va[u].w, (double)va[u].w, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].x, (double)vb[u].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].y, (double)vb[u].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].z, (double)vb[u].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vb[u].w, (double)vb[u].w, acc, 0, 0, 0);
-      }
-    }
-  }
-
-  // Sum the four waves' matrices (and the row sets' diagonal blocks) in a
-  // fixed order; write the packed triangle.
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = acc[r];
   __syncthreads();
-  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
   for (int e = threadIdx.x; e < NE; e += kBlock) {
     int i = 0, rem = e;
     while (rem >= NB - i) {
@@ -503,6 +335,143 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
       }
     out[e] = sum;
   }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
+  constexpr int SETS = 16 / NB;          // row sets packed into the 16 operand lanes
+  constexpr int U = kF64Unroll;
+  constexpr int RC = 16 * SETS;          // rows per chunk
+  constexpr int R = RC * U;              // rows per wave per iteration
+  constexpr int NE = gram_entries(NB);
+  static_assert(NB * SETS == 16, "NB divides 16");
+  __shared__ double red[kGramWaves][64 * 4];
+
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = (lane & 15) % NB, set = (lane & 15) / NB, grp = lane >> 4;
+
+  // a NULL operand (beyond the block's count) reads operand 0, masked to zero
+  const void* mine = args.x[j][op];
+  const bool live = mine != nullptr;
+  const float* xp = static_cast<const float*>(live ? mine : args.x[j][0]);
+
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  const int64_t niter = (hi - first + R - 1) / R;
+  const int64_t lane_row = (int64_t)set * 16 + 4 * grp;  // first row of this lane in a chunk
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+    const int64_t r0 = first + it * R;
+    v4f v[U];
+    if (r0 >= lo && r0 + R <= hi) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = gload(reinterpret_cast<const v4f*>(xp + r0 + u * RC + lane_row));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = load_f32x4(xp, r0 + u * RC + lane_row, lo, hi);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!live) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].x, (double)v[u].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].y, (double)v[u].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].z, (double)v[u].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)v[u].w, (double)v[u].w, acc, 0, 0, 0);
+    }
+  }
+  f64_gram_reduce<NB>(red, acc, args.partials + args.poff[j] + (int64_t)tile_id * NE);
+}
+
+// ----------------------------------------------------------------- Gram pass, stages above the first
+
+// Operands of a later stage are fp64 slots (results of lower blocks) and, in
+// lanes that the job's narrow mask marks, input gradients of type TN carried
+// up (widened exactly).  Products of fp64 values are rounded by the matrix
+// cores (an entry then errs by a few units of 2^-53 of the sum of |x_i x_j|,
+// the bound the tree walk's flags assume), and flagged pairs are recomputed
+// exactly.  Lane l reads four consecutive rows of its operand per 16-row
+// chunk, as in the fp32 pass.
+constexpr int kStageUnroll = 8;  // 16-row chunks per wave per iteration
+
+// Four consecutive rows [row, row + 4) of an fp64 slot or a TN input,
+// widened to fp64, zero outside [lo, hi).
+template <typename TN>
+__device__ __forceinline__ void load_stage4(const void* p, bool narrow, int64_t row, int64_t lo, int64_t hi,
+                                            double (&v)[4]) {
+  const bool whole = row >= lo && row + 4 <= hi;
+  if (!narrow) {
+    const double* x = static_cast<const double*>(p);
+    if (whole) {
+      const v2d a = gload(reinterpret_cast<const v2d*>(x + row));
+      const v2d b = gload(reinterpret_cast<const v2d*>(x + row + 2));
+      v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (row + e >= lo && row + e < hi) ? gload(x + row + e) : 0.0;
+    }
+  } else if constexpr (std::is_same<TN, float>::value) {
+    const v4f f = load_f32x4(static_cast<const float*>(p), row, lo, hi);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const uint16_t* x = static_cast<const uint16_t*>(p);
+    if (whole) {
+      const v2u w = gload(reinterpret_cast<const v2u*>(x + row));
+      v[0] = narrow_to_f32<TN>(w.x & 0xffffu); v[1] = narrow_to_f32<TN>(w.x >> 16);
+      v[2] = narrow_to_f32<TN>(w.y & 0xffffu); v[3] = narrow_to_f32<TN>(w.y >> 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = (row + e >= lo && row + e < hi) ? (double)narrow_to_f32<TN>(gload(x + row + e)) : 0.0;
+    }
+  }
+}
+
+template <int NB, typename TN>
+__global__ __launch_bounds__(kBlock) void gram_stage_kernel(GramArgs args) {
+  constexpr int SETS = 16 / NB;
+  constexpr int U = kStageUnroll;
+  constexpr int RC = 16 * SETS;
+  constexpr int R = RC * U;
+  constexpr int NE = gram_entries(NB);
+  static_assert(NB * SETS == 16, "NB divides 16");
+  __shared__ double red[kGramWaves][64 * 4];
+
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = (lane & 15) % NB, set = (lane & 15) / NB, grp = lane >> 4;
+  const void* mine = args.x[j][op];
+  const bool live = mine != nullptr;
+  const void* xp = live ? mine : args.x[j][0];
+  // a masked operand reads operand 0, in operand 0's type
+  const bool narrow = (args.narrow[j] >> (live ? op : 0)) & 1u;
+
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  const int64_t niter = (hi - first + R - 1) / R;
+  const int64_t lane_row = (int64_t)set * 16 + 4 * grp;
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+    const int64_t r0 = first + it * R;
+    double v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_stage4<TN>(xp, narrow, r0 + u * RC + lane_row, lo, hi, v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double x = live ? v[u][e] : 0.0;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(x, x, acc, 0, 0, 0);
+      }
+    }
+  }
+  f64_gram_reduce<NB>(red, acc, args.partials + args.poff[j] + (int64_t)tile_id * NE);
 }
 
 // ----------------------------------------------------------------- Gram pass, 16-bit operands
@@ -683,20 +652,84 @@ __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t le
 }
 
 // Exact recomputation of the Gram partials of every tile of a (block,
-// segment) pair that the tree walk flagged (see TreeArgs): the matrix-core
-// pass rounds each 32-row sum to fp32, which an ill-conditioned merge (a node
-// far smaller than the operands under it) could amplify beyond the
-// coefficient tolerance.  Tiles of other pairs return at once.
-template <typename T, int NB>
+// segment) pair that the tree walk flagged (see TreeArgs): a merge far
+// smaller than the operands under it (a near-cancellation) amplifies the
+// rounding of the Gram entries into its statistics.  Every entry of such a
+// tile is recomputed as the row-order double-double sum of exact products (a
+// fused multiply-add gives each product's rounding error, so even products of
+// fp64 slot values are exact), its high part written to partials and its low
+// part to partials_lo; the refining walk then sums tiles in double-double.
+// The rows pass through LDS kExactChunk at a time, in fp64.  Operand k is of
+// type TIn, or TN where the job's narrow mask marks it (launches over fp64
+// slots).  Tiles of other pairs return at once.
+constexpr int kExactChunk = 128;
+
+template <typename T>
+__device__ __forceinline__ double widen_any(const void* p, int64_t i) {
+  if constexpr (std::is_same<T, double>::value) return gload(static_cast<const double*>(p) + i);
+  else if constexpr (std::is_same<T, float>::value) return (double)gload(static_cast<const float*>(p) + i);
+  else return (double)narrow_to_f32<T>(gload(static_cast<const uint16_t*>(p) + i));
+}
+
+template <typename TIn, typename TN, int NB>
 __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
-  __shared__ uint16_t sh[NB * kExactRows];
+  constexpr int NE = gram_entries(NB);
+  constexpr int EPT = (NE + kBlock - 1) / kBlock;  // entries per thread
+  __shared__ double sh[NB][kExactChunk];
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
-  if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] == 0) return;
-  const int64_t at = args.poff[j] + (int64_t)tile_id * gram_entries(NB);
-  gram_exact_rows<T, NB>(args.x[j], tile.start, tile.len, args.partials + at,
-                         args.partials_lo != nullptr ? args.partials_lo + at : nullptr, sh);
+  if ((args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] & 1u) == 0) return;  // workgroup-uniform
+  int ei[EPT], ek[EPT];
+  DD acc[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = threadIdx.x + q * kBlock;
+    int i = 0, rem = e < NE ? e : 0;
+    while (rem >= NB - i) {
+      rem -= NB - i;
+      ++i;
+    }
+    ei[q] = i;
+    ek[q] = i + rem;
+    acc[q] = DD{0.0, 0.0};
+  }
+  for (int64_t c0 = 0; c0 < tile.len; c0 += kExactChunk) {
+    const int n = (int)min<int64_t>(kExactChunk, tile.len - c0);
+    if (c0 > 0) __syncthreads();  // the previous chunk is consumed
+    for (int idx = threadIdx.x; idx < NB * n; idx += kBlock) {
+      const int k = idx / n, r = idx - k * n;
+      const void* x = args.x[j][k];
+      const int64_t row = tile.start + c0 + r;
+      double v = 0.0;
+      if (x != nullptr) {
+        if constexpr (std::is_same<TIn, TN>::value) {
+          v = widen_any<TIn>(x, row);
+        } else {
+          v = ((args.narrow[j] >> k) & 1u) ? widen_any<TN>(x, row) : widen_any<TIn>(x, row);
+        }
+      }
+      sh[k][r] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      if (threadIdx.x + q * kBlock >= NE) continue;
+      const double* x = sh[ei[q]];
+      const double* y = sh[ek[q]];
+      DD sum = acc[q];
+      for (int r = 0; r < n; ++r) sum = dd_add(sum, dd_prod(x[r], y[r]));
+      acc[q] = sum;
+    }
+  }
+  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+  double* out_lo = args.partials_lo + args.poff[j] + (int64_t)tile_id * NE;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    if (threadIdx.x + q * kBlock >= NE) continue;
+    out[threadIdx.x + q * kBlock] = acc[q].hi;
+    out_lo[threadIdx.x + q * kBlock] = acc[q].lo;
+  }
 }
 
 // Blocks of up to 16 operands use one 16-operand half; the 32-operand block
@@ -905,9 +938,13 @@ constexpr int kTreeWaves = kBlock / 64;
 // One workgroup per (block, segment).  Wave q sums the tile partials of the
 // q-th quarter of the segment's tiles (lanes over Gram entries, tiles in
 // order); the four quarter sums are then added in wave order.  The split
-// depends only on the tile count, so the result is reproducible.
+// depends only on the tile count, so the result is reproducible.  The
+// refining walk (kRefine) visits only flagged pairs, whose tiles hold
+// double-double entries, and sums them in double-double.
+template <bool kRefine>
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   __shared__ double part[kTreeWaves][gram_entries(kMaxOps)];
+  __shared__ double part_lo[kRefine ? kTreeWaves : 1][kRefine ? gram_entries(kMaxOps) : 1];
   __shared__ double G[gram_entries(kMaxOps)];
   // operand weights: products of the coefficients of the merges above each
   // operand, in double-double (a chain multiplies up to K - 1 of them, and a
@@ -918,7 +955,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   const int b = item / a.nseg;
   const int s = item % a.nseg;
   const BlockDesc d = a.descs[a.desc0 + b];
-  if (a.refine && a.flags[(int64_t)d.wrow * a.nseg + s] == 0) return;  // workgroup-uniform
+  if (kRefine && (a.flags[(int64_t)d.wrow * a.nseg + s] & 1u) == 0) return;  // workgroup-uniform
   const int n = d.nbt;
   const int ne = gram_entries(n);
   const int tid = threadIdx.x;
@@ -928,32 +965,53 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   const int q0 = min(t1, t0 + q * chunk), q1 = min(t1, q0 + chunk);
   for (int e = lane; e < ne; e += 64) {
     const double* p = a.partials + d.poff + e;
-    double sum = 0.0;
+    if constexpr (kRefine) {
+      const double* pl = a.partials_lo + d.poff + e;
+      DD sum{0.0, 0.0};
+      for (int t = q0; t < q1; ++t) sum = dd_add(sum, DD{p[(int64_t)t * ne], pl[(int64_t)t * ne]});
+      part[q][e] = sum.hi;
+      part_lo[q][e] = sum.lo;
+    } else {
+      double sum = 0.0;
 #pragma unroll 8
-    for (int t = q0; t < q1; ++t) sum += p[(int64_t)t * ne];
-    part[q][e] = sum;
+      for (int t = q0; t < q1; ++t) sum += p[(int64_t)t * ne];
+      part[q][e] = sum;
+    }
   }
   __syncthreads();
-  for (int e = tid; e < ne; e += kBlock) {
-    double sum = part[0][e];
-#pragma unroll
-    for (int i = 1; i < kTreeWaves; ++i) sum += part[i][e];
-    G[e] = sum;
-  }
-  // A segment of one short tile has its Gram entries in double-double (hi:
-  // that tile's partial, taken exactly above) where an exact path summed
-  // them: blocks that read a lower result, and 16-bit inputs.  The walk then
+  // A segment of one short tile of 16-bit inputs has its Gram entries in
+  // double-double (hi: that tile's partial, taken exactly above) from the
+  // exact short-tile sums; a refined pair has all of them so.  The walk then
   // forms its quadratic forms from both parts, so their rounding is not
   // amplified by a merge that cancels.  Workgroup-uniform.
   const uint32_t all_inputs = d.nb >= 32 ? 0xffffffffu : (1u << d.nb) - 1u;
-  const bool exact_g = a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows &&
-                       (a.lo_inputs || d.leafmask != all_inputs);
-  double* const Glo = &part[0][0];  // the low parts reuse the consumed wave sums
-  __syncthreads();
-  if (exact_g)
+  const bool exact_g = kRefine || (a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows &&
+                                   a.lo_inputs && d.leafmask == all_inputs);
+  // the normal walk keeps the low parts in the consumed wave sums
+  __shared__ double glo_refine[kRefine ? gram_entries(kMaxOps) : 1];
+  double* const Glo = kRefine ? &glo_refine[0] : &part[0][0];
+  for (int e = tid; e < ne; e += kBlock) {
+    if constexpr (kRefine) {
+      DD sum{part[0][e], part_lo[0][e]};
+#pragma unroll
+      for (int i = 1; i < kTreeWaves; ++i) sum = dd_add(sum, DD{part[i][e], part_lo[i][e]});
+      G[e] = sum.hi;
+      Glo[e] = sum.lo;
+    } else {
+      double sum = part[0][e];
+#pragma unroll
+      for (int i = 1; i < kTreeWaves; ++i) sum += part[i][e];
+      G[e] = sum;
+    }
+  }
+  if (!kRefine && exact_g) {
+    __syncthreads();  // every wave sum is consumed
     for (int e = tid; e < ne; e += kBlock) Glo[e] = a.partials_lo[d.poff + (int64_t)t0 * ne + e];
+  }
   if (tid < kMaxOps) w[tid] = DD{1.0, 0.0};
   __syncthreads();
+  // entries already exact (double-double) are not flagged again
+  const double gram_err = exact_g ? 0.0 : d.gram_err;
   // Merges run level by level: merges of a block are stored children
   // before parents, and the merges of one level cover disjoint operand
   // ranges (a batch ends where a merge starts left of the previous one).
@@ -966,7 +1024,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   __shared__ DD rowL[kMaxOps], rowR[kMaxOps];
   __shared__ double cab[kMaxOps][2];
   __shared__ Merge ms[kMaxOps];
-  __shared__ int unsure;  // some coefficient may be off by more than kRefineTol (gram_err > 0)
+  __shared__ int unsure;  // some coefficient may be off by more than kRefineTol
   if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
   if (tid == 0) unsure = 0;
   __syncthreads();
@@ -1003,7 +1061,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
       cab[m0 + tid][0] = ca;
       cab[m0 + tid][1] = cb;
-      if (a.gram_err > 0.0) {
+      if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
         // The rounding errors of separate chunk sums are independent, so a
         // quadratic form over an operand with weights w errs by about
         // gram_err S, S = sum w_i^2 G_ii (the norm the operand would have if
@@ -1017,7 +1075,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
         double sl = 0.0, sr = 0.0;
         for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
         for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
-        const double eA = a.gram_err * sl, eB = a.gram_err * sr, ed = a.gram_err * sqrt(fmax(sl * sr, 0.0));
+        const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
         bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
         if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
         if (B > eB) bad = bad || (ed + fabs(dd) * eB / B) / (2.0 * B) > kRefineTol * fmax(1.0, fabs(cb));
@@ -1054,24 +1112,72 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     }
   }
   __syncthreads();
-  if (tid < kMaxOps) a.weights[((int64_t)d.wrow * a.nseg + s) * kMaxOps + tid] = wf[tid];
-  if (tid == 0 && a.flags != nullptr && !a.refine) a.flags[(int64_t)d.wrow * a.nseg + s] = unsure;
+  const int64_t wat = ((int64_t)d.wrow * a.nseg + s) * kMaxOps;
+  if (tid < kMaxOps) {
+    a.weights[wat + tid] = wf[tid];
+    a.weights_lo[wat + tid] = w[tid].lo;
+  }
+  if (!kRefine && a.flags != nullptr) {
+    // Bit 1: the block's result is summed in double-double.  Where it is far
+    // smaller than its weighted parts, sum_k w_k x_k in fp64 would lose the
+    // ratio of the two to rounding, and a later stage could amplify that loss
+    // again; every pair flagged for recomputation (bit 0) is summed so too.
+    __shared__ double rows_w[kMaxOps];
+    if (tid < d.nb) {
+      double r = 0.0;
+      for (int k = 0; k < d.nb; ++k) r += wf[k] * gram_at(G, n, tid, k);
+      rows_w[tid] = r;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double out2 = 0.0, parts = 0.0;
+      for (int k = 0; k < d.nb; ++k) {
+        out2 += wf[k] * rows_w[k];
+        parts += wf[k] * wf[k] * G[gram_index(n, k, k)];
+      }
+      uint32_t f = unsure ? 3u : 0u;
+      if (parts > 0.0 && !(out2 > kSumCancel * parts)) f |= 2u;
+      a.flags[(int64_t)d.wrow * a.nseg + s] = f;
+    }
+  }
 }
 
 // ----------------------------------------------------------------- weighted sum
 
+// A (block, segment) pair whose walk set bit 1 of its flag: every element's
+// sum_k w_k x_k in double-double, with the walk's double-double weights and
+// exact products, rounded once.  Operands one at a time (rare, so compact);
+// operand k is of type TIn, or TN where the job's narrow mask marks it.
+template <typename TIn, typename TN, int NB, typename TOut>
+__device__ void wsum_exact_range(const WsumArgs& args, int j, int64_t lo, int64_t hi, const double* w_hi,
+                                 const double* w_lo) {
+  TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
+  double unused;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+    DD acc{0.0, 0.0};
+#pragma unroll 1
+    for (int k = 0; k < NB; ++k) {
+      const void* x = args.x[j][k];
+      if (x == nullptr) continue;
+      double v;
+      if constexpr (std::is_same<TIn, TN>::value) {
+        v = widen_any<TIn>(x, i);
+      } else {
+        v = ((args.narrow[j] >> k) & 1u) ? widen_any<TN>(x, i) : widen_any<TIn>(x, i);
+      }
+      acc = dd_add(acc, dd_mul(DD{w_hi[k], w_lo[k]}, DD{v, 0.0}));
+    }
+    Elem<TOut>::store1(y + i, Elem<TOut>::round(acc.hi, &unused));  // normalised: hi is the rounded sum
+  }
+}
+
 // Operands at or beyond the block's count are NULL in the argument table;
 // they alias operand 0 (cache hits, no extra HBM traffic) and their terms are
 // masked to zero, so the loop has no branches and every load of a step is in
-// flight at once.
-//
-// TN = TIn: every operand is TIn.  Otherwise (TIn = float) the operands that
-// the job's narrow mask marks are 16-bit inputs in TN, read as such (16 bytes
-// per 8 elements) and widened exactly.
-template <typename TIn, int NB, typename TOut, typename TN = TIn>
+// flight at once.  First stage: every operand is an input of type TIn; the
+// result is the output (TOut = TIn) or an fp64 slot (TOut = double).
+template <typename TIn, int NB, typename TOut>
 __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
-  constexpr bool kMixed = !std::is_same<TN, TIn>::value;
-  static_assert(!kMixed || std::is_same<TIn, float>::value, "narrow operands only in fp32 launches");
   constexpr int kSplit = wsum_split(sizeof(TIn));
   const int tile_id = blockIdx.x / kSplit;
   const int part = blockIdx.x % kSplit;
@@ -1090,63 +1196,35 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
     sp.body_lo = b0;
     sp.body_hi = b1;
   }
-  const double* wrow = args.weights + ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  const int64_t wat = ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  const double* wrow = args.weights + wat;
+  if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] & 2u) {  // workgroup-uniform
+    wsum_exact_range<TIn, TIn, NB, TOut>(args, j, sp.lo, sp.hi, wrow, args.weights_lo + wat);
+    return;
+  }
   const TIn* x0 = static_cast<const TIn*>(args.x[j][0]);
   const TIn* xs[NB];
   bool live[NB];
-  bool nk[NB];  // read in TN (a masked operand reads operand 0, in operand 0's type)
   double w[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
     live[k] = args.x[j][k] != nullptr;
     xs[k] = live[k] ? static_cast<const TIn*>(args.x[j][k]) : x0;
-    nk[k] = kMixed && ((args.narrow[j] >> (live[k] ? k : 0)) & 1u);
     w[k] = wrow[k];
   }
   TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
   const int tid = threadIdx.x;
   double unused;
 
-
-  auto load1 = [&](int k, int64_t i) -> float {
-    if constexpr (kMixed) {
-      if (nk[k]) return narrow_to_f32<TN>(gload(reinterpret_cast<const uint16_t*>(xs[k]) + i));
-    }
-    return Elem<TIn>::load1(xs[k] + i);
-  };
   auto one = [&](int64_t i) {
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const double t = mul_rn(w[k], (double)load1(k, i));
+      const double t = mul_rn(w[k], (double)Elem<TIn>::load1(xs[k] + i));
       acc = add_rn(acc, live[k] ? t : 0.0);
     }
     Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
   };
-
-  const uint32_t side_mask = args.side_mask[j];
-  if ((args.side[j] != nullptr || side_mask != 0u) && tile.len <= kExactRows) {
-    // a short tile of a result that feeds a later stage, or of a block that
-    // reads lower results: element by element; a lower result is read from
-    // its fp64 side buffer, and this result's fp64 sum is also kept in its
-    // own (row i at side[i + shift]) for the next stage's exact Gram sum
-    double* __restrict__ side = args.side[j];
-    const int64_t shift = args.short_off[tile_id] - tile.start;
-    for (int64_t i = sp.lo + tid; i < sp.hi; i += kBlock) {
-      double acc = 0.0;
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const double v = ((side_mask >> k) & 1u)
-                             ? args.side_in[(int64_t)args.side_slot[j][k] * args.short_rows + shift + i]
-                             : (double)load1(k, i);
-        const double t = mul_rn(w[k], v);
-        acc = add_rn(acc, live[k] ? t : 0.0);
-      }
-      Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
-      if (side != nullptr) side[i + shift] = acc;
-    }
-    return;
-  }
 
   if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
   // Operand-outer: the raw loads of all operands are in flight together,
@@ -1155,30 +1233,14 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
   for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
     typename Elem<TIn>::Raw8 raw[NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if constexpr (kMixed) {
-        if (nk[k]) {  // eight 16-bit values, in the first half of the slot
-          raw[k].a = __builtin_bit_cast(v4f, gload(reinterpret_cast<const v4u*>(
-                                                 reinterpret_cast<const uint16_t*>(xs[k]) + g)));
-          continue;
-        }
-      }
-      raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
-    }
+    for (int k = 0; k < NB; ++k) raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
     double acc[kGroup];
 #pragma unroll
     for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       float v[kGroup];
-      bool unpacked = false;
-      if constexpr (kMixed) {
-        if (nk[k]) {
-          Elem<TN>::unpack8(__builtin_bit_cast(v4u, raw[k].a), v);
-          unpacked = true;
-        }
-      }
-      if (!unpacked) Elem<TIn>::unpack8(raw[k], v);
+      Elem<TIn>::unpack8(raw[k], v);
 #pragma unroll
       for (int e = 0; e < kGroup; ++e) {
         const double t = mul_rn(w[k], (double)v[e]);
@@ -1189,6 +1251,93 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
 #pragma unroll
     for (int e = 0; e < kGroup; ++e) r[e] = Elem<TOut>::round(acc[e], &unused);
     Elem<TOut>::store8(y + g, r);
+  }
+  if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
+}
+
+// Weighted sum of a stage above the first: operands are fp64 slots or, where
+// the job's narrow mask marks them, inputs of type TN carried up; the result
+// is an fp64 slot (TOut = double) or the output (TOut = TN).  Each thread
+// takes runs of four elements (the body starts at a multiple of kGroup, so
+// every fp64 run is 32-byte aligned); an operand's type is the same for the
+// whole workgroup.
+template <typename TN>
+__device__ __forceinline__ void load_run4(const void* p, bool narrow, int64_t g, double (&v)[4]) {
+  if (!narrow) {
+    const v2d a = gload(reinterpret_cast<const v2d*>(static_cast<const double*>(p) + g));
+    const v2d b = gload(reinterpret_cast<const v2d*>(static_cast<const double*>(p) + g + 2));
+    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+  } else if constexpr (std::is_same<TN, float>::value) {
+    const v4f f = gload(reinterpret_cast<const v4f*>(static_cast<const float*>(p) + g));
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const v2u w = gload(reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(p) + g));
+    v[0] = narrow_to_f32<TN>(w.x & 0xffffu); v[1] = narrow_to_f32<TN>(w.x >> 16);
+    v[2] = narrow_to_f32<TN>(w.y & 0xffffu); v[3] = narrow_to_f32<TN>(w.y >> 16);
+  }
+}
+
+template <int NB, typename TN, typename TOut>
+__global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
+  constexpr int kSplit = kWsumSplitMax;
+  constexpr int kRun = 4;
+  const int tile_id = blockIdx.x / kSplit;
+  const int part = blockIdx.x % kSplit;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  TileSpan sp = span_of(tile);
+  {
+    const int64_t groups = (sp.body_hi - sp.body_lo) / kGroup;
+    const int64_t per = (groups + kSplit - 1) / kSplit * kGroup;
+    const int64_t b0 = min(sp.body_lo + part * per, sp.body_hi);
+    const int64_t b1 = min(b0 + per, sp.body_hi);
+    if (part > 0) sp.lo = b0;
+    if (part < kSplit - 1) sp.hi = b1;
+    sp.body_lo = b0;
+    sp.body_hi = b1;
+  }
+  const int64_t wat = ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  const double* wrow = args.weights + wat;
+  if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] & 2u) {  // workgroup-uniform
+    wsum_exact_range<double, TN, NB, TOut>(args, j, sp.lo, sp.hi, wrow, args.weights_lo + wat);
+    return;
+  }
+  const void* xs[NB];
+  bool live[NB], nk[NB];
+  double w[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    live[k] = args.x[j][k] != nullptr;
+    xs[k] = live[k] ? args.x[j][k] : args.x[j][0];
+    nk[k] = (args.narrow[j] >> (live[k] ? k : 0)) & 1u;  // a masked operand reads operand 0, in its type
+    w[k] = wrow[k];
+  }
+  TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
+  const int tid = threadIdx.x;
+  double unused;
+
+  auto one = [&](int64_t i) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const double v = nk[k] ? widen_any<TN>(xs[k], i) : widen_any<double>(xs[k], i);
+      acc = add_rn(acc, live[k] ? mul_rn(w[k], v) : 0.0);
+    }
+    Elem<TOut>::store1(y + i, Elem<TOut>::round(acc, &unused));
+  };
+
+  if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
+  for (int64_t g = sp.body_lo + (int64_t)tid * kRun; g < sp.body_hi; g += (int64_t)kBlock * kRun) {
+    double v[NB][kRun];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) load_run4<TN>(xs[k], nk[k], g, v[k]);
+    double acc[kRun] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+      for (int e = 0; e < kRun; ++e) acc[e] = add_rn(acc[e], live[k] ? mul_rn(w[k], v[k][e]) : 0.0);
+#pragma unroll
+    for (int e = 0; e < kRun; ++e) Elem<TOut>::store1(y + g + e, Elem<TOut>::round(acc[e], &unused));
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
 }
@@ -1322,6 +1471,7 @@ hipError_t by_type(DType t, Args&&... args) {
     case DType::F32: return F<float>::run(args...);
     case DType::F16: return F<_Float16>::run(args...);
     case DType::BF16: return F<bf16_t>::run(args...);
+    case DType::F64: break;  // not an input dtype
   }
   return hipErrorInvalidValue;
 }
@@ -1338,15 +1488,27 @@ struct RunSum {
   }
 };
 
+hipError_t run_gram_f64(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+  const dim3 grid(ntiles, njobs);
+  switch (nbt) {
+    case 2: hipLaunchKernelGGL((gram_f64mfma_kernel<2>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gram_f64mfma_kernel<4>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16>), grid, dim3(kBlock), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename TN>
-struct RunGramF64 {
+struct RunGramStage {
   static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
     const dim3 grid(ntiles, njobs);
     switch (nbt) {
-      case 2: hipLaunchKernelGGL((gram_f64mfma_kernel<2, TN>), grid, dim3(kBlock), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((gram_f64mfma_kernel<4, TN>), grid, dim3(kBlock), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8, TN>), grid, dim3(kBlock), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((gram_stage_kernel<2, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((gram_stage_kernel<4, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((gram_stage_kernel<8, TN>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_stage_kernel<16, TN>), grid, dim3(kBlock), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1369,17 +1531,35 @@ struct RunGramMfma {
   }
 };
 
-template <typename TIn, typename TOut, typename TN = TIn>
+template <typename TIn, typename TN>
+hipError_t run_gram_exact(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+  const dim3 grid(ntiles, njobs);
+  switch (nbt) {
+    case 2: hipLaunchKernelGGL((gram_exact_kernel<TIn, TN, 2>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gram_exact_kernel<TIn, TN, 4>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gram_exact_kernel<TIn, TN, 8>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((gram_exact_kernel<TIn, TN, 16>), grid, dim3(kBlock), 0, st, a); break;
+    case 32:
+      if constexpr (sizeof(TIn) == 2) {  // 32-operand blocks exist only over 16-bit inputs
+        hipLaunchKernelGGL((gram_exact_kernel<TIn, TN, 32>), grid, dim3(kBlock), 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
 hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
   const dim3 grid((unsigned)ntiles * wsum_split(sizeof(TIn)), njobs);
   switch (nbt) {
-    case 2: hipLaunchKernelGGL((wsum_kernel<TIn, 2, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((wsum_kernel<TIn, 8, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((wsum_kernel<TIn, 16, TOut, TN>), grid, dim3(kBlock), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((wsum_kernel<TIn, 2, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((wsum_kernel<TIn, 4, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((wsum_kernel<TIn, 8, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((wsum_kernel<TIn, 16, TOut>), grid, dim3(kBlock), 0, st, a); break;
     case 32:
-      // 32-operand blocks exist only over 16-bit inputs, with an fp32 or same-type result
-      if constexpr (sizeof(TIn) == 2 && (sizeof(TOut) == 4 || std::is_same<TIn, TOut>::value)) {
+      if constexpr (sizeof(TIn) == 2) {  // 32-operand blocks exist only over 16-bit inputs
         hipLaunchKernelGGL((wsum_kernel<TIn, 32, TOut>), grid, dim3(kBlock), 0, st, a);
         break;
       }
@@ -1389,27 +1569,49 @@ hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream
   return hipGetLastError();
 }
 
+// First stage: inputs of type TIn; the result is an fp64 slot or the output.
 template <typename TIn>
 struct RunWsum {
   static hipError_t run(int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
-    switch (out_t) {
-      case DType::F32: return run_wsum<TIn, float>(nbt, a, ntiles, njobs, st);
-      case DType::F16: return run_wsum<TIn, _Float16>(nbt, a, ntiles, njobs, st);
-      case DType::BF16: return run_wsum<TIn, bf16_t>(nbt, a, ntiles, njobs, st);
-    }
-    return hipErrorInvalidValue;
+    if (out_t == DType::F64) return run_wsum<TIn, double>(nbt, a, ntiles, njobs, st);
+    return run_wsum<TIn, TIn>(nbt, a, ntiles, njobs, st);
   }
 };
 
-// fp32 launches with 16-bit inputs among the operands: the result is an fp32
-// slot or, at the root, the inputs' own type.
+template <typename TN, typename TOut>
+hipError_t run_wsum_stage(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
+  const dim3 grid((unsigned)ntiles * kWsumSplitMax, njobs);
+  switch (nbt) {
+    case 2: hipLaunchKernelGGL((wsum_stage_kernel<2, TN, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((wsum_stage_kernel<4, TN, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((wsum_stage_kernel<8, TN, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((wsum_stage_kernel<16, TN, TOut>), grid, dim3(kBlock), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Later stages: fp64 slots and inputs of type TN; the result is an fp64 slot
+// or the output.
 template <typename TN>
-struct RunWsumNarrow {
+struct RunWsumStage {
   static hipError_t run(int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs, hipStream_t st) {
-    if (out_t == DType::F32) return run_wsum<float, float, TN>(nbt, a, ntiles, njobs, st);
-    if (sizeof(TN) == 2 && out_t == (std::is_same<TN, _Float16>::value ? DType::F16 : DType::BF16))
-      return run_wsum<float, TN, TN>(nbt, a, ntiles, njobs, st);
-    return hipErrorInvalidValue;
+    if (out_t == DType::F64) return run_wsum_stage<TN, double>(nbt, a, ntiles, njobs, st);
+    return run_wsum_stage<TN, TN>(nbt, a, ntiles, njobs, st);
+  }
+};
+
+template <typename TN>
+struct RunExactStage {
+  static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+    return run_gram_exact<double, TN>(nbt, a, ntiles, njobs, st);
+  }
+};
+
+template <typename TIn>
+struct RunExactFirst {
+  static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+    return run_gram_exact<TIn, TIn>(nbt, a, ntiles, njobs, st);
   }
 };
 
@@ -1418,13 +1620,8 @@ struct RunWsumNarrow {
 hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
                        hipStream_t st) {
   switch (operand) {
-    case DType::F32:
-      switch (narrow_t) {
-        case DType::F32: return RunGramF64<float>::run(nbt, a, ntiles, njobs, st);
-        case DType::F16: return RunGramF64<_Float16>::run(nbt, a, ntiles, njobs, st);
-        case DType::BF16: return RunGramF64<bf16_t>::run(nbt, a, ntiles, njobs, st);
-      }
-      return hipErrorInvalidValue;
+    case DType::F64: return by_type<RunGramStage>(narrow_t, nbt, a, ntiles, njobs, st);
+    case DType::F32: return run_gram_f64(nbt, a, ntiles, njobs, st);
     case DType::F16: return RunGramMfma<_Float16>::run(nbt, a, ntiles, njobs, st);
     case DType::BF16: return RunGramMfma<bf16_t>::run(nbt, a, ntiles, njobs, st);
   }
@@ -1432,39 +1629,23 @@ hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a
 }
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(tree_kernel, dim3((unsigned)((int64_t)a.nblocks * a.nseg)), dim3(kBlock), 0, st, a);
+  const dim3 grid((unsigned)((int64_t)a.nblocks * a.nseg));
+  if (a.refine)
+    hipLaunchKernelGGL(tree_kernel<true>, grid, dim3(kBlock), 0, st, a);
+  else
+    hipLaunchKernelGGL(tree_kernel<false>, grid, dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t run_gram_exact(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
-  const dim3 grid(ntiles, njobs);
-  switch (nbt) {
-    case 2: hipLaunchKernelGGL((gram_exact_kernel<T, 2>), grid, dim3(kBlock), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gram_exact_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gram_exact_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((gram_exact_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((gram_exact_kernel<T, 32>), grid, dim3(kBlock), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gram_exact(DType operand, int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
-  switch (operand) {
-    case DType::F16: return run_gram_exact<_Float16>(nbt, a, ntiles, njobs, st);
-    case DType::BF16: return run_gram_exact<bf16_t>(nbt, a, ntiles, njobs, st);
-    case DType::F32: break;  // the fp32 pass is exact already
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_gram_exact(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
+                             hipStream_t st) {
+  if (operand == DType::F64) return by_type<RunExactStage>(narrow_t, nbt, a, ntiles, njobs, st);
+  return by_type<RunExactFirst>(operand, nbt, a, ntiles, njobs, st);
 }
 
 hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
                        hipStream_t st) {
-  if (in_t == DType::F32 && narrow_t == DType::F16)
-    return RunWsumNarrow<_Float16>::run(nbt, out_t, a, ntiles, njobs, st);
-  if (in_t == DType::F32 && narrow_t == DType::BF16)
-    return RunWsumNarrow<bf16_t>::run(nbt, out_t, a, ntiles, njobs, st);
+  if (in_t == DType::F64) return by_type<RunWsumStage>(narrow_t, nbt, out_t, a, ntiles, njobs, st);
   return by_type<RunWsum>(in_t, nbt, out_t, a, ntiles, njobs, st);
 }
 

@@ -23,7 +23,6 @@ struct DeviceTables {
   int32_t* seg_tile = nullptr;
   BlockDesc* descs = nullptr;
   Merge* merges = nullptr;
-  int64_t* short_off = nullptr;
 };
 
 struct CachedPlan {

@@ -51,7 +51,7 @@ int scratch_of(int device, char** out) {
 // Where a call's plan tables go in the array: behind its workspace, each
 // table 256-byte aligned.
 struct ScratchLayout {
-  size_t tiles, seg_tile, descs, merges, short_off, total;
+  size_t tiles, seg_tile, descs, merges, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -67,8 +67,6 @@ ScratchLayout scratch_layout(const Plan& p) {
   off = align256(off + sizeof(BlockDesc) * p.descs.size());
   L.merges = off;
   off = align256(off + sizeof(Merge) * p.merges.size());
-  L.short_off = off;
-  off = align256(off + sizeof(int64_t) * p.short_off.size());
   L.total = off;
   return L;
 }
@@ -110,8 +108,8 @@ int combine_noalloc(const void* const* grads, int K, const int64_t* seg_offsets,
   // The tables are copied from the host plan on the call's stream; a copy
   // from pageable host memory has consumed its source when it returns.
   // Nothing in the workspace needs to start at zero: every kernel writes the
-  // regions it reads before reading them (Gram partials, weights, flags, the
-  // lower stages' slots and side buffers).
+  // regions it reads before reading them (Gram partials and their low parts,
+  // weights, flags, the lower stages' slots).
   const struct {
     size_t at;
     const void* src;
@@ -121,7 +119,6 @@ int combine_noalloc(const void* const* grads, int K, const int64_t* seg_offsets,
       {L.seg_tile, p.seg_tile.data(), sizeof(int32_t) * p.seg_tile.size()},
       {L.descs, p.descs.data(), sizeof(BlockDesc) * p.descs.size()},
       {L.merges, p.merges.data(), sizeof(Merge) * p.merges.size()},
-      {L.short_off, p.short_off.data(), sizeof(int64_t) * p.short_off.size()},
   };
   for (const auto& c : copies) {
     if (c.bytes == 0) continue;
@@ -133,7 +130,6 @@ int combine_noalloc(const void* const* grads, int K, const int64_t* seg_offsets,
   tables.seg_tile = reinterpret_cast<int32_t*>(base + L.seg_tile);
   tables.descs = reinterpret_cast<BlockDesc*>(base + L.descs);
   tables.merges = reinterpret_cast<Merge*>(base + L.merges);
-  tables.short_off = reinterpret_cast<int64_t*>(base + L.short_off);
   CallBuffers b;
   b.grads = grads;
   b.out = out;

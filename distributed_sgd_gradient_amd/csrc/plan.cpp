@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 
 namespace adasum {
@@ -146,16 +147,9 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   }
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
   const size_t ntiles = p.tiles.size();
-  p.short_off.assign(ntiles, -1);
-  for (size_t t = 0; t < ntiles; ++t) {
-    if (p.tiles[t].len <= kExactRows) {
-      p.short_off[t] = p.short_rows;
-      p.short_rows += p.tiles[t].len;
-    }
-  }
 
   // ---- blocks, stage by stage.  An operand of a stage above the first is
-  // an fp32 slot (the result of a lower block) or an input gradient that the
+  // an fp64 slot (the result of a lower block) or an input gradient that the
   // stage reads where it is, in its own dtype.
   std::vector<Ref> operands(K);
   std::vector<char> is_leaf(K, 1);   // per operand of the current stage
@@ -173,7 +167,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     std::vector<Elem> cur;
     for (int i = 0; i < (int)operands.size(); ++i) cur.push_back(Elem{i, i + 1, false});
     std::vector<StageMerge> stage_merges;
-    // the first stage reads only inputs; later ones read fp32 slots (and inputs carried up)
+    // the first stage reads only inputs; later ones read fp64 slots (and inputs carried up)
     const int ops = first ? first_stage_ops(dtype, K) : kMaxOps32;
     if (schedule == Schedule::Tree)
       tree_stage(cur, stage_merges, node, ops == 32 ? 5 : 4);
@@ -206,6 +200,15 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
       for (int k = e.lo; k < e.hi; ++k)
         if (is_leaf[k]) d.leafmask |= 1u << (k - e.lo);
       d.root = last ? 1 : 0;
+      // fp64 sums on the fp64 matrix cores (fp32 inputs; stages that read
+      // fp64 slots, any inputs among them widened exactly): a bound on the
+      // rounding of a lane's running sum and of the reductions behind it.
+      // 16-bit inputs of the first stage: each 32-row chunk rounded to fp32
+      // once by the matrix cores, with a margin for the fp64 accumulation.
+      bool reads_slot = false;
+      for (int k = e.lo; k < e.hi; ++k) reads_slot |= operands[k].kind == Ref::Slot;
+      d.gram_err = (dtype == DType::F32 || reads_slot) ? std::ldexp(1.0, -44)
+                                                        : std::ldexp(1.0, -24) * (1.0 + std::ldexp(1.0, -10));
       b.desc = (int)p.descs.size();
       p.descs.push_back(d);
       st.blocks.push_back(b);
@@ -238,10 +241,12 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   // ---- workspace layout
   size_t off = 0;
   p.ws_slots = off;
-  off = align256(off + (size_t)p.nslots * (size_t)p.N * sizeof(float));
+  off = align256(off + (size_t)p.nslots * (size_t)p.N * sizeof(double));
   p.ws_partials = off;
   off = align256(off + p.partial_doubles * sizeof(double));
   p.ws_weights = off;
+  off = align256(off + (size_t)p.nblocks * nseg * kMaxOps * sizeof(double));
+  p.ws_weights_lo = off;
   off = align256(off + (size_t)p.nblocks * nseg * kMaxOps * sizeof(double));
   p.ws_leafnorm = off;
   off = align256(off + (size_t)p.nblocks * nseg * sizeof(double));
@@ -251,10 +256,8 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   off = align256(off + p.table_bytes(3));
   p.ws_flags = off;
   off = align256(off + (size_t)p.nblocks * nseg * sizeof(uint32_t));
-  p.ws_side = off;
-  off = align256(off + (size_t)p.nslots * (size_t)p.short_rows * sizeof(double));
-  p.ws_plo = off;  // low parts of the short tiles' double-double Gram entries, laid out as the partials
-  off = align256(off + (p.short_rows > 0 ? p.partial_doubles : 0) * sizeof(double));
+  p.ws_plo = off;  // low parts of exactly recomputed Gram partials (double-double), laid out as the partials
+  off = align256(off + p.partial_doubles * sizeof(double));
   p.ws_total = off;
   return p;
 }

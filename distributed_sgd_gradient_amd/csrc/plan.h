@@ -14,13 +14,13 @@
 //     operands, because every node is a linear combination of them; so a
 //     block needs one Gram pass over its operands, a small per-segment walk
 //     of its merges, and one weighted-sum pass that writes its result;
-//   * the workspace layout: fp32 slots for block results that feed a later
-//     stage, fp64 per-tile Gram partials, leaf weights, the coefficient and
-//     statistic tables, per-(block, segment) flags of pairs whose Gram
-//     matrix is recomputed exactly, and the fp64 side buffers of the fp32
-//     slots (their rows in short tiles).  An input that a later stage reads (an
+//   * the workspace layout: fp64 slots for block results that feed a later
+//     stage, fp64 per-tile Gram partials and the low parts of their
+//     double-double recomputation, leaf weights, the coefficient and
+//     statistic tables, and per-(block, segment) flags of pairs whose Gram
+//     matrix is recomputed exactly.  An input that a later stage reads (an
 //     odd vector carried up the tree, or the chain's next inputs) is read
-//     where it is, in its own dtype, next to the fp32 slots.
+//     where it is, in its own dtype, next to the fp64 slots.
 //
 // Pure C++: it makes no HIP call, so it can be exercised without a GPU.
 #pragma once
@@ -40,10 +40,9 @@ constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
 constexpr int kMaxOps = 32;      // operands per block over 16-bit inputs: five tree levels
 constexpr int kMaxOps32 = 16;    // operands per block over fp32 operands: four tree levels
 constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
-// Tiles of at most kExactRows rows are short: their Gram matrices are summed
-// exactly, and a block result that feeds a later stage also keeps their rows
-// in fp64 (the side buffer), since short segments are where merges nearly
-// cancel by chance.
+// Tiles of at most kExactRows rows of 16-bit inputs are short: their Gram
+// matrices are summed exactly (double-double) instead of on the matrix cores,
+// since short segments are where merges nearly cancel by chance.
 constexpr int kExactRows = 256;
 // The weighted sum cuts every tile into aligned parts, one workgroup each,
 // so that a workgroup's range holds 16 KB of every operand of a full tile:
@@ -53,14 +52,16 @@ constexpr int kExactRows = 256;
 constexpr int wsum_split(int elem_bytes) { return elem_bytes == 4 ? 8 : 4; }
 constexpr int kWsumSplitMax = 8;
 
-enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+// F64 is internal: the type of the slots that carry block results between
+// stages (never a dtype of the C ABI).
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2, F64 = 3 };
 
 // Order in which the pairwise operator is applied to the K gradients.
 //   Tree:  level by level, pairs (v0,v1), (v2,v3), ..., odd last carried;
 //   Chain: left to right, acc = Adasum(acc, g_{i+1}).
 enum class Schedule : int { Tree = 0, Chain = 1 };
 
-inline size_t dtype_size(DType t) { return t == DType::F32 ? 4 : 2; }
+inline size_t dtype_size(DType t) { return t == DType::F64 ? 8 : t == DType::F32 ? 4 : 2; }
 
 // Largest block of the first stage.  32-operand blocks (16-bit inputs only)
 // pay off only where they finish the whole combine in one stage: above 32
@@ -98,6 +99,12 @@ struct BlockDesc {  // device-visible description of one block
   uint32_t leafmask;  // bit k: operand k is one of the K input gradients
   int32_t root;       // 1 for the block whose result is the output
   int32_t pad;
+  // Relative rounding error of this block's Gram entries, against the sum of
+  // |x_i x_j| that each entry adds up: the fp64 sums of the fp64 matrix cores
+  // (fp32 inputs, fp64 slots) or the fp32 rounding of the 16-bit matrix
+  // cores' 32-row chunks.  The tree walk flags the merges whose coefficients
+  // such errors could move beyond tolerance.
+  double gram_err;
 };
 
 // Where an operand or result lives.
@@ -126,18 +133,16 @@ struct Plan {
   std::vector<int64_t> offsets;   // nseg + 1
   std::vector<Tile> tiles;
   std::vector<int32_t> seg_tile;  // nseg + 1: tiles of segment s are [seg_tile[s], seg_tile[s+1])
-  std::vector<int64_t> short_off; // per tile: first row of a short tile in the side buffers, else -1
-  int64_t short_rows = 0;         // rows of all short tiles
   std::vector<Stage> stages;
   std::vector<BlockDesc> descs;
   std::vector<Merge> merges;
-  int nslots = 0;                 // fp32 vectors of N elements
+  int nslots = 0;                 // fp64 vectors of N elements
   int nblocks = 0;                // rows of the leaf-weight table
   size_t partial_doubles = 0;     // largest per-stage Gram partials footprint
 
   // workspace layout, byte offsets (each 256-aligned)
-  size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_leafnorm = 0, ws_coeffs = 0, ws_stats = 0,
-         ws_flags = 0, ws_side = 0, ws_plo = 0, ws_total = 0;
+  size_t ws_slots = 0, ws_partials = 0, ws_weights = 0, ws_weights_lo = 0, ws_leafnorm = 0, ws_coeffs = 0, ws_stats = 0,
+         ws_flags = 0, ws_plo = 0, ws_total = 0;
   size_t table_bytes(int per_node) const { return (size_t)(K > 1 ? K - 1 : 0) * nseg * per_node * sizeof(double); }
 };
 

@@ -17,10 +17,11 @@ emulated sequential orders, it is applied per layer, it is not elementwise).
 
 Modules
   adasum    fp64 NumPy oracle: pairwise operator, binary tree, per-segment
-            combine, orthogonality ratio, plain sum, linear chain, and the
-            input norms under each node's operands with the mask of the
-            coefficients at (or above) the operator's discontinuity at a
-            zero operand.
+            combine, orthogonality ratio, plain sum, linear chain, the input
+            norms under each node's operands, and the stability of the
+            oracle's own results under rounding-size noise (which coefficients
+            and outputs fp64 arithmetic does not determine, at the operator's
+            discontinuity and under deep cancellation).
   exact     the same definitions in exact rational arithmetic (fractions),
             for brute force on tiny inputs.
   rounding  IEEE round-to-nearest-even from fp64 to fp32 / fp16 / bf16.
@@ -31,6 +32,7 @@ brute force, library cross-checks, invariants).  No function is unpinned.
 """
 
 from .adasum import (  # noqa: F401
+    ZERO_FLOOR,
     adasum_pair,
     adasum_tree,
     adasum_chain,
@@ -39,7 +41,8 @@ from .adasum import (  # noqa: F401
     plain_sum,
     orthogonality,
     operand_input_norms,
-    discontinuity_mask,
+    node_parents,
+    stability,
     tree_schedule,
 )
 from .rounding import round_to_format  # noqa: F401

@@ -244,39 +244,127 @@ def operand_input_norms(vectors, schedule="tree"):
     return np.asarray(out, dtype=np.float64).reshape(-1, 2)
 
 
-def discontinuity_mask(stats, opnorms, schedule="tree", rel=1e-8):
-    """[K-1, 2] mask of the coefficients that are not stable quantities.
+def _ulp_noise(rows, rng):
+    """Every nonzero finite element moved to an adjacent fp64 value, toward
+    or away from zero at random (one unit in the last place: plus or minus 1
+    on the bit pattern); zeros (exact data, such as an all-zero worker) stay
+    as they are, and so do infinities, NaNs and the largest finite
+    magnitudes."""
+    big = np.finfo(np.float64).max
+    out = []
+    for r in rows:
+        r = np.ascontiguousarray(r, dtype=np.float64)
+        bits = r.view(np.int64)
+        coin = np.unpackbits(np.frombuffer(rng.bytes((r.size + 7) // 8), dtype=np.uint8), count=r.size)
+        step = coin.astype(np.int64)
+        step <<= 1
+        step -= 1
+        moved = bits + step
+        if not (np.isfinite(r).all() and float(np.abs(r).max(initial=0.0)) < big):
+            keep = ~np.isfinite(r) | (np.abs(r) == big)
+            moved[keep] = bits[keep]
+        zero = r == 0.0
+        moved[zero] = bits[zero]
+        out.append(moved.view(np.float64))
+    return out
 
-    The operator takes coefficient 1 at an exactly zero operand, but
-    Adasum(eps*u, c) tends to c - (u.c) u / 2 as eps -> 0: a zero operand that
-    carries rounding noise gets an arbitrary coefficient, and the node's value
-    moves by O(|c|).  Marked: the coefficient of every operand whose squared
-    norm (``stats`` [K-1, 3], (a.b, |a|^2, |b|^2)) is at most ``rel`` times
-    the summed squared norms of the input gradients under it (``opnorms``
-    [K-1, 2], nonzero), and both coefficients of every node that consumes
-    such a merge's result, directly or through later nodes.
-    """
-    stats = np.asarray(stats, dtype=np.float64).reshape(-1, 3)
-    opnorms = np.asarray(opnorms, dtype=np.float64).reshape(-1, 2)
-    n = stats.shape[0]
-    mask = (stats[:, 1:3] <= rel * opnorms) & (opnorms > 0)
-    parent = [-1] * n
+
+def node_parents(n_nodes, schedule="tree"):
+    """Parent node of every node (-1 for the root), in node order."""
+    parent = [-1] * n_nodes
     if schedule == "chain":
-        for i in range(n - 1):
+        for i in range(n_nodes - 1):
             parent[i] = i + 1
-    else:
-        node = 0
-        for level in tree_schedule(n + 1):
-            for left, right in level:
-                for kind, i in (left, right):
-                    if kind == "node":
-                        parent[i] = node
-                node += 1
-    for i in range(n):
-        if mask[i].any():
-            j = parent[i]
-            while j >= 0:
-                mask[j] = True
-                j = parent[j]
-    return mask
+        return parent
+    node = 0
+    for level in tree_schedule(n_nodes + 1):
+        for left, right in level:
+            for kind, i in (left, right):
+                if kind == "node":
+                    parent[i] = node
+            node += 1
+    return parent
 
+
+# An operand whose squared norm is at most this fraction of the summed squared
+# norms of the input gradients under it is below about 2^-45 of their size, a
+# few hundred units of fp64 rounding: to fp64 arithmetic it is zero, whether
+# or not the rounding happened to leave it exactly zero.
+ZERO_FLOOR = 2.0 ** -90
+
+
+def stability(inputs, seg_offsets, schedule="tree", trials=2, seed=0):
+    """How far this oracle's own results move under rounding-size noise.
+
+    The operator is discontinuous at a zero operand (coefficient 1 there,
+    another limit next to it), and under deep cancellation (a node far
+    smaller than the inputs under it) fp64 arithmetic no longer determines
+    the coefficients above it, nor, in a long chain, the results built on
+    them.  This reruns the per-segment combine ``trials`` times, each time
+    with every nonzero input element moved by one fp64 ulp in a random
+    direction (seeded).  An operand whose squared norm is at most
+    ZERO_FLOOR of the inputs under it (which are not all zero) sits at the
+    discontinuity itself, whatever the noise does (an exact negation can
+    survive it, rounding can absorb it, and a rounding residue can be as
+    stable as it is wrong): its consumer's coefficient of it, both
+    coefficients of every node above that consumer and the segment's output
+    count as not determined.
+    Returns
+
+      ``base``           the unperturbed result (as ``combine`` or
+                         ``combine_chain`` returns it);
+      ``coeff_motion``   [K-1, nseg, 2], the largest
+                         |c' - c| / max(1, |c|) over the trials (inf at an
+                         exact zero and above it);
+      ``output_motion``  [nseg], the largest ||out' - out|| / ||out|| of
+                         each segment (0 for an all-zero or empty segment,
+                         inf above an exact zero).
+
+    A coefficient or output that moves by a sizeable fraction of its
+    tolerance is not determined by the data through fp64 arithmetic, so this
+    oracle is no reference for it.
+    """
+    rows, n = _as_rows(inputs)
+    off = _check_offsets(seg_offsets, n)
+    fn = combine_chain if schedule == "chain" else combine
+    base = fn(rows, off)
+    rng = np.random.default_rng(seed)
+    nseg = off.size - 1
+    cmov = np.zeros_like(base["coeffs"])
+    omov = np.zeros(nseg)
+    for _ in range(trials):
+        res = fn(_ulp_noise(rows, rng), off)
+        with np.errstate(invalid="ignore"):
+            d = np.abs(res["coeffs"] - base["coeffs"]) / np.maximum(1.0, np.abs(base["coeffs"]))
+        cmov = np.fmax(cmov, np.where(np.isnan(d) & ~np.isnan(base["coeffs"]), np.inf, d))
+        for s in range(nseg):
+            lo, hi = int(off[s]), int(off[s + 1])
+            ref = base["out"][lo:hi]
+            den = float(np.linalg.norm(ref))
+            num = float(np.linalg.norm(res["out"][lo:hi] - ref))
+            omov[s] = max(omov[s], num / den if den > 0 else num)
+    # operands that are zero to fp64 over inputs that are not all zero, and
+    # everything above them; the segment's summed input norms bound those
+    # under any operand, so only segments with a candidate are looked at
+    if base["stats"].size:
+        nonempty = off[1:] > off[:-1]
+        total = np.zeros(nseg)
+        for r in rows:
+            total[nonempty] += np.add.reduceat(r * r, off[:-1][nonempty]) if r.size else 0.0
+        candidate = base["stats"][:, :, 1:3] <= ZERO_FLOOR * total[None, :, None]
+    else:
+        candidate = np.zeros(base["stats"].shape[:2] + (2,), dtype=bool)
+    if candidate.any():
+        parent = node_parents(base["stats"].shape[0], schedule)
+        for s in np.flatnonzero(candidate.any(axis=(0, 2))):
+            lo, hi = int(off[s]), int(off[s + 1])
+            opn = operand_input_norms([r[lo:hi] for r in rows], schedule)
+            at_zero = (base["stats"][:, s, 1:3] <= ZERO_FLOOR * opn) & (opn > 0)
+            for i, side in zip(*np.nonzero(at_zero)):
+                cmov[i, s, side] = np.inf
+                j = parent[i]
+                while j >= 0:
+                    cmov[j, s, :] = np.inf
+                    j = parent[j]
+                omov[s] = np.inf
+    return {"base": base, "coeff_motion": cmov, "output_motion": omov}

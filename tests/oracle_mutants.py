@@ -12,8 +12,9 @@ zero-norm rule, the order of the returned coefficients or statistics, the
 carry or the pairing of the tree, the chain's operand order, statistics
 taken over the whole vector instead of per layer, a rounding mode, the
 subnormal range, the orthogonality ratio's squares, the plain sum's order,
-and the two parity helpers (the discontinuity mask's ancestors, the chain's
-accumulated input norms).
+and the parity helpers (the stability check's noise taken in ulps of fp32
+instead of fp64, or no noise at all, its zero floor at exact zeros only or
+as wide as 1e-8; the chain's accumulated input norms).
 """
 
 import json
@@ -181,10 +182,18 @@ def _plain_sum_reversed(inputs, seg_offsets=None, out_format=None):
     return _orig["plain_sum"](list(inputs)[::-1], seg_offsets, out_format)
 
 
-def _mask_without_ancestors(stats, opnorms, schedule="tree", rel=1e-8):
-    stats = np.asarray(stats, dtype=np.float64).reshape(-1, 3)
-    opnorms = np.asarray(opnorms, dtype=np.float64).reshape(-1, 2)
-    return (stats[:, 1:3] <= rel * opnorms) & (opnorms > 0)
+def _noise_in_fp32_ulps(rows, rng):
+    out = []
+    for r in rows:
+        f = np.ascontiguousarray(r, dtype=np.float32)
+        step = np.where(rng.random(r.size) < 0.5, 1, -1).astype(np.int32)
+        moved = (f.view(np.int32) + step).view(np.float32).astype(np.float64)
+        out.append(np.where(np.isfinite(r) & (r != 0.0), moved, r))
+    return out
+
+
+def _no_noise(rows, rng):
+    return [np.array(r, copy=True) for r in rows]
 
 
 def _chain_norms_not_accumulated(vectors, schedule="tree"):
@@ -213,7 +222,10 @@ MUTANTS = {
     "rounding_flushes_subnormal_range": {"round_to_format": _round_with(np.rint, subnormals=False)},
     "orthogonality_unsquared": {"orthogonality": _orthogonality_unsquared},
     "plain_sum_reversed": {"plain_sum": _plain_sum_reversed},
-    "mask_without_ancestors": {"discontinuity_mask": _mask_without_ancestors},
+    "stability_noise_in_fp32_ulps": {"_ulp_noise": _noise_in_fp32_ulps},
+    "stability_without_noise": {"_ulp_noise": _no_noise},
+    "stability_exact_zeros_only": {"ZERO_FLOOR": 0.0},
+    "stability_zero_floor_too_wide": {"ZERO_FLOOR": 1e-8},
     "chain_norms_not_accumulated": {"operand_input_norms": _chain_norms_not_accumulated},
 }
 

@@ -24,8 +24,9 @@ static void dump(const Plan& p, int dt, int sched, int K) {
       printf("%s{\"ops\": [", b ? "," : "");
       for (size_t k = 0; k < bk.operands.size(); ++k)
         printf("%s[%d,%d]", k ? "," : "", (int)bk.operands[k].kind, bk.operands[k].idx);
-      printf("], \"dst\": [%d,%d], \"nb\": %d, \"nbt\": %d, \"leafmask\": %llu, \"root\": %d, \"poff\": %lld, "
-             "\"merges\": [", (int)bk.dst.kind, bk.dst.idx, d.nb, d.nbt, (unsigned long long)d.leafmask, (int)d.root, (long long)d.poff);
+      printf("], \"dst\": [%d,%d], \"desc\": %d, \"nb\": %d, \"nbt\": %d, \"leafmask\": %llu, \"root\": %d, "
+             "\"poff\": %lld, \"merges\": [", (int)bk.dst.kind, bk.dst.idx, bk.desc, d.nb, d.nbt,
+             (unsigned long long)d.leafmask, (int)d.root, (long long)d.poff);
       for (int m = 0; m < d.nmerges; ++m) {
         const Merge& mg = p.merges[d.merge0 + m];
         printf("%s[%d,%d,%d,%d]", m ? "," : "", mg.llo, mg.lhi, mg.rhi, mg.node);
@@ -39,12 +40,11 @@ static void dump(const Plan& p, int dt, int sched, int K) {
     printf("%s[%lld,%d,%d]", t ? "," : "", (long long)p.tiles[t].start, p.tiles[t].len, p.tiles[t].seg);
   printf("], \"seg_tile\": [");
   for (size_t s = 0; s < p.seg_tile.size(); ++s) printf("%s%d", s ? "," : "", p.seg_tile[s]);
-  printf("], \"short_off\": [");
-  for (size_t t = 0; t < p.short_off.size(); ++t) printf("%s%lld", t ? "," : "", (long long)p.short_off[t]);
-  printf("], \"short_rows\": %lld", (long long)p.short_rows);
-  printf(", \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
-         p.partial_doubles, p.ws_slots, p.ws_partials, p.ws_weights, p.ws_leafnorm, p.ws_coeffs, p.ws_stats,
-         p.ws_flags, p.ws_side, p.ws_plo, p.ws_total, p.nblocks);
+  printf("], \"gram_err\": [");
+  for (size_t b = 0; b < p.descs.size(); ++b) printf("%s%.17g", b ? "," : "", p.descs[b].gram_err);
+  printf("], \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
+         p.partial_doubles, p.ws_slots, p.ws_partials, p.ws_weights, p.ws_weights_lo, p.ws_leafnorm, p.ws_coeffs,
+         p.ws_stats, p.ws_flags, p.ws_plo, p.ws_total, p.nblocks);
 }
 
 int main(int argc, char** argv) {

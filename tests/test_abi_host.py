@@ -105,21 +105,21 @@ def test_workspace_size_properties():
 
     n = 1 << 20
     assert 0 < ws(1, (0, 1000)) < 4096           # K = 1: one single-operand block
-    # up to 16 operands form one block: no fp32 intermediates, only
-    # Gram partials and tables
+    # up to 16 operands form one block: no intermediates, only Gram partials
+    # (with room for the low parts of an exact recomputation) and tables
     for K in (2, 3, 9, 16):
-        assert 0 < ws(K, (0, n)) < n
-    # 17 = a block of 16 (its result in one fp32 slot) and the carried input,
+        assert 0 < ws(K, (0, n)) < 2 * n
+    # 17 = a block of 16 (its result in one fp64 slot) and the carried input,
     # which the second stage reads where it is
-    assert n * 4 <= ws(17, (0, n)) < 2 * n * 4
-    assert 4 * n * 4 <= ws(64, (0, n)) < 5 * n * 4   # four blocks of 16
+    assert n * 8 <= ws(17, (0, n)) < 2 * n * 8
+    assert 4 * n * 8 <= ws(64, (0, n)) < 5 * n * 8   # four blocks of 16
     assert ws(16, (0, 64 * n)) > ws(16, (0, n))
     assert ws(16, (0, 0)) >= 0 and ws(2, (0,)) >= 0
-    # chain: 16 inputs, then the running result (an fp32 slot) and up to 15
+    # chain: 16 inputs, then the running result (an fp64 slot) and up to 15
     # more inputs, read where they are, per stage
-    assert ws(16, (0, n), 0, 1) < n
-    assert n * 4 <= ws(17, (0, n), 0, 1) < 2 * n * 4
-    assert 4 * n * 4 <= ws(64, (0, n), 0, 1) < 5 * n * 4   # four stages below the root
+    assert ws(16, (0, n), 0, 1) < 2 * n
+    assert n * 8 <= ws(17, (0, n), 0, 1) < 2 * n * 8
+    assert 4 * n * 8 <= ws(64, (0, n), 0, 1) < 5 * n * 8   # four stages below the root
 
 
 def test_sum_entry_point_validation():

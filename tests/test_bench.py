@@ -56,7 +56,7 @@ def test_bench_json_line(gpu):
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["achieved"] > 0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) <= 1e-12 * roof["frac"]
-    assert roof["kernel"] in ("gram", "tree", "wsum")
+    assert roof["kernel"] in ("gram", "tree", "exact", "wsum")
 
     cpu = rec["cpu_baseline"]
     for key in ("value", "unit", "cores", "kind", "sample"):
@@ -69,6 +69,12 @@ def test_bench_json_line(gpu):
     assert par["segments"] >= 1 and par["tol_rel_l2"] == 1e-5 and par["tol_coeff"] == 1e-6
     assert par["rel_l2"] <= par["tol_rel_l2"] and par["max_coeff_err"] <= par["tol_coeff"] and par["pass"] is True
 
-    # one combine is three launches: gram, tree, weighted sum
-    assert set(rec["kernels"]) == {"gram", "tree", "wsum"}
-    assert all(k["launches"] == 3 for k in rec["kernels"].values())
+    # one combine is five launches: gram, the tree walk, the exact
+    # recomputation of flagged tiles, the walk again over flagged pairs (the
+    # last two return at once when nothing is flagged), weighted sum
+    assert set(rec["kernels"]) == {"gram", "tree", "exact", "wsum"}
+    launches = {k: v["launches"] for k, v in rec["kernels"].items()}
+    assert launches == {"gram": 3, "tree": 6, "exact": 3, "wsum": 3}, launches
+    for key in ("mean", "median", "min", "max"):
+        assert rec["step_ms"][key] > 0 and rec["step_ms_without_launch_events"][key] > 0
+    assert rec["step_ms"]["min"] <= rec["step_ms"]["median"] <= rec["step_ms"]["max"]

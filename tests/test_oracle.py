@@ -192,26 +192,33 @@ def test_operand_input_norms_hand_derived():
             assert abs(root.sum() - total) <= 1e-12 * total
 
 
-def test_discontinuity_mask_hand_derived():
-    """Scalars 1, -1 make the exactly zero node n0 = Adasum(1, -1) = 3/2 - 3/2.
-    Tree of (1, -1, 2, 3): n2 = (n0, n1), so only n2's left coefficient is
-    marked.  Tree of (1, -1, 2, 3, 4, 5, 6, 7): n4 = (n0, n1) is marked on
-    the left, and n6 = (n4, n5), which consumes n4, on both sides.  Chain of
-    (1, -1, 2, 3): n1 = (n0, 2) on the left, then n2 = (n1, 3) on both.
-    Inputs with no cancellation mark nothing; all-zero inputs mark nothing
-    (their coefficients are exactly 1)."""
-    def mask(vals, sched):
-        rows = [np.array([float(v)]) for v in vals]
-        fn = oracle.adasum_chain if sched == "chain" else oracle.adasum_tree
-        _, _, st = fn(rows)
-        return oracle.discontinuity_mask(st, oracle.operand_input_norms(rows, sched), sched).tolist()
+UNSTABLE = 1e-7  # a tenth of the coefficient tolerance
 
-    assert mask([1, -1, 2, 3], "tree") == [[False, False], [False, False], [True, False]]
-    m8 = mask([1, -1, 2, 3, 4, 5, 6, 7], "tree")
+
+def _unstable(vals, sched, trials=3):
+    rows = [np.atleast_1d(np.asarray(v, dtype=np.float64)) for v in vals]
+    st = oracle.stability(rows, [0, rows[0].size], sched, trials=trials)
+    return (st["coeff_motion"][:, 0] > UNSTABLE).tolist(), st
+
+
+def test_stability_hand_derived():
+    """Scalars 1, -1 make the exactly zero node n0 = Adasum(1, -1) = 3/2 - 3/2;
+    one-ulp noise makes it a tiny nonzero scalar, and for scalars Adasum(a, b)
+    is (a + b) / 2 unless a is exactly zero, when it is b.  Tree of
+    (1, -1, 2, 3): n2 = (n0, n1), so only n2's left coefficient moves (its
+    right one stays 1 - n0 n1 / (2 n1^2)).  Tree of (1, -1, 2, 3, 4, 5, 6, 7):
+    n4 = (n0, n1) moves on the left, and n6 = (n4, n5), whose operand n4 jumps
+    from n1 to about n1 / 2, on both sides.  Chain of (1, -1, 2, 3): n1 =
+    (n0, 2) on the left, then n2 = (n1, 3) on both.  Inputs with no
+    cancellation move nothing; all-zero inputs stay exactly zero (their
+    coefficients are exactly 1)."""
+    assert _unstable([1, -1, 2, 3], "tree")[0] == [[False, False], [False, False], [True, False]]
+    m8 = _unstable([1, -1, 2, 3, 4, 5, 6, 7], "tree")[0]
     assert m8 == [[False, False]] * 4 + [[True, False], [False, False], [True, True]]
-    assert mask([1, -1, 2, 3], "chain") == [[False, False], [True, False], [True, True]]
-    assert not np.any(mask([1, 2, 3, 4, 5], "tree"))
-    assert not np.any(mask([0, 0, 0, 0], "tree"))
+    assert _unstable([1, -1, 2, 3], "chain")[0] == [[False, False], [True, False], [True, True]]
+    assert not np.any(_unstable([1, 2, 3, 4, 5], "tree")[0])
+    m, st = _unstable([0, 0, 0, 0], "tree")
+    assert not np.any(m) and np.all(st["coeff_motion"] == 0.0) and np.all(st["base"]["coeffs"] == 1.0)
 
 
 @pytest.mark.parametrize("sched", ["tree", "chain"])
@@ -230,30 +237,151 @@ def test_operand_input_norms_equal_operand_norms_for_orthogonal_inputs(sched):
 
 
 @pytest.mark.parametrize("sched,K", [("tree", 8), ("tree", 13), ("chain", 6)])
-def test_discontinuity_mask_marks_exactly_the_coefficients_that_jump(sched, K):
+def test_stability_marks_exactly_the_coefficients_that_jump(sched, K):
     """Inputs 2 and 3 (tree) or 0 and 1 (chain) are u and -u, whose merge is
     exactly zero (coefficient 1 above it).  Replacing -u by -(1 + 1e-6) u
     leaves a tiny nonzero merge.  A coefficient that depends continuously on
     the inputs moves by O(1e-6) (here at most 7e-7); the consumer's
     coefficient of the tiny operand and both coefficients of every node above
     it jump by O(1) in the geometry of the inputs (here at least 2.7e-3 in 4
-    dimensions).  Exactly the coefficients that move by more than 3e-5 must
-    be marked, for the exact and for the perturbed inputs."""
+    dimensions).  At the exact zero, one-ulp noise moves exactly the
+    coefficients that jump.  Once perturbed, the tiny operand (|a|^2 about
+    1e-12 of its inputs) is resolved by fp64 arithmetic: its coefficients are
+    well defined there, and noise moves none of them."""
     rng = np.random.default_rng(13)
     vecs = [rng.standard_normal(4) for _ in range(K)]
     i = 2 if sched == "tree" else 0
     fn = oracle.adasum_chain if sched == "chain" else oracle.adasum_tree
     vecs[i + 1] = -vecs[i]
-    _, c0, s0 = fn(vecs)
+    _, c0, _ = fn(vecs)
     pert = list(vecs)
     pert[i + 1] = -(1.0 + 1e-6) * vecs[i]
-    _, c1, s1 = fn(pert)
+    _, c1, _ = fn(pert)
     c0, c1 = np.asarray(c0), np.asarray(c1)
     jumped = np.abs(c1 - c0) > 3e-5 * np.maximum(1.0, np.abs(c0))
     assert jumped.sum() >= 3
-    for st, v in ((s0, vecs), (s1, pert)):
-        m = oracle.discontinuity_mask(st, oracle.operand_input_norms(v, sched), sched)
-        np.testing.assert_array_equal(m, jumped)
+    m0 = oracle.stability(vecs, [0, 4], sched, trials=3)["coeff_motion"][:, 0] > UNSTABLE
+    np.testing.assert_array_equal(m0, jumped)
+    m1 = oracle.stability(pert, [0, 4], sched, trials=3)["coeff_motion"][:, 0] > UNSTABLE
+    assert not m1.any()
+
+
+def test_stability_keeps_exact_zeros():
+    """Zeros are exact data, not rounding: all-zero workers and an all-zero
+    segment stay exactly zero under the noise, so their coefficients (exactly
+    1) and that segment's output (exactly 0) do not move at all, while the
+    other coefficients move by rounding only."""
+    rng = np.random.default_rng(31)
+    vecs = [rng.standard_normal(40) for _ in range(8)]
+    for k in (0, 3):
+        vecs[k][:] = 0.0
+    for v in vecs:
+        v[30:] = 0.0  # segment 1, [30, 40), is zero in every worker
+    st = oracle.stability(vecs, [0, 30, 40], "tree", trials=3)
+    c = st["base"]["coeffs"]
+    assert np.all(c[:, 1] == 1.0) and np.all(st["coeff_motion"][:, 1] == 0.0)
+    assert st["output_motion"][1] == 0.0
+    zero_operand = c[:, 0] == 1.0
+    assert zero_operand.sum() >= 2 and np.all(st["coeff_motion"][:, 0][zero_operand] == 0.0)
+    assert 0.0 < float(st["coeff_motion"][:, 0].max()) < 1e-12
+
+
+@pytest.mark.parametrize("vals", [[7, 0, -7, 1, 3, -7, 0, -2, 3, 3, -8],
+                                  [0, 6, -4, 1, 3, -2, -6, 0, -7, 3, 1, 3]])
+def test_stability_treats_rounding_residues_as_zero(vals):
+    """Scalars at fp16's subnormal scale (multiples of 2^-24) whose trees
+    have operands that are exactly zero in exact arithmetic (the Fraction
+    oracle) but rounding residues of a few 1e-45 in fp64, about 1e-32 of the
+    inputs under them.  Their coefficients are garbage on any fp64 path, and
+    the nodes above inherit that however stable it is under noise; below
+    ZERO_FLOOR they count as zero.  The coefficients marked as not determined
+    at the discontinuity are exactly: the consumer's coefficient of every
+    operand that is zero in exact arithmetic over inputs that are not all
+    zero, and both coefficients of every node above it; and the output."""
+    from fractions import Fraction
+
+    from oracle import exact
+
+    rows = [np.array([v * 2.0 ** -24]) for v in vals]
+    _, _, st = oracle.adasum_tree(rows)
+    _, _, st_exact = exact.adasum_tree([[Fraction(v, 2 ** 24)] for v in vals])
+    opn = oracle.operand_input_norms(rows, "tree")
+    exact_zero = (np.array([[s[1] == 0, s[2] == 0] for s in st_exact])) & (opn > 0)
+    residue = exact_zero & (np.asarray(st)[:, 1:3] > 0)
+    assert residue.any()  # fp64 left a nonzero residue where the exact value is zero
+    parents = oracle.node_parents(len(vals) - 1, "tree")
+    expect = exact_zero.copy()
+    for i in np.flatnonzero(exact_zero.any(axis=1)):
+        j = parents[i]
+        while j >= 0:
+            expect[j] = True
+            j = parents[j]
+    res = oracle.stability(rows, [0, 1], "tree")
+    np.testing.assert_array_equal(np.isinf(res["coeff_motion"][:, 0]), expect)
+    assert np.isinf(res["output_motion"][0])
+
+
+def _planted(eps, K=4, n=300, seed=21):
+    """Tree inputs with g1 = -(1 + eps) g0 + eps v: the level-1 node (g0, g1)
+    is about eps of its operands, so the merge above sees |a|^2 / S of about
+    2.25 eps^2."""
+    rng = np.random.default_rng(seed)
+    vecs = [rng.standard_normal(n) for _ in range(K)]
+    vecs[1] = -(1.0 + eps) * vecs[0] + eps * vecs[1]
+    return vecs
+
+
+@pytest.mark.parametrize("eps2", [1e-10, 1e-12, 1e-14])
+def test_resolved_cancellations_are_stable(eps2):
+    """Planted cancellations with eps^2 = 1e-10, 1e-12, 1e-14: one-ulp noise
+    on every input element moves the oracle's coefficients above them by less
+    than 1e-8 of max(1, |c|), so every one of them is gated."""
+    vecs = _planted(np.sqrt(eps2))
+    _, _, st = oracle.adasum_tree(vecs)
+    ratio = st[2][1] / oracle.operand_input_norms(vecs, "tree")[2][0]
+    assert 1.0 * eps2 < ratio < 5.0 * eps2
+    motion = oracle.stability(vecs, [0, 300], "tree", trials=4)["coeff_motion"]
+    assert float(motion.max()) < 1e-8
+
+
+def test_unresolved_cancellations_are_unstable():
+    """Below the floor fp64 rounding decides the coefficient: with
+    eps^2 = 1e-22 one-ulp noise moves the coefficient of the tiny operand by
+    more than 1e-7 of it, and nothing else in the two-level tree."""
+    motion = oracle.stability(_planted(1e-11), [0, 300], "tree", trials=4)["coeff_motion"][:, 0]
+    assert (motion > UNSTABLE).tolist() == [[False, False], [False, False], [True, False]]
+
+
+def test_stability_covers_every_coefficient_the_oracle_gets_wrong():
+    """A chain of 40 two-element inputs in cancelling pairs (relative gap
+    5e-8): later merges meet operands that are tiny against the inputs under
+    them, with coefficients far from 1, and the fp64 oracle's own rounding
+    moves them.  Against the same chain in 50-digit arithmetic, every
+    coefficient the oracle has wrong by more than 1e-7 of max(1, |c|) is one
+    that one-ulp noise moves by more than 1e-7 (and some are wrong)."""
+    import mpmath as mp
+
+    rng = np.random.default_rng(3)
+    vecs = [rng.standard_normal(2) for _ in range(40)]
+    for k in range(1, 40, 2):
+        vecs[k] = -(1.0 + 5e-8) * vecs[k - 1] + 5e-8 * vecs[k]
+    mp.mp.dps = 50
+    acc = [mp.mpf(float(x)) for x in vecs[0]]
+    ref = []
+    for v in vecs[1:]:
+        v = [mp.mpf(float(x)) for x in v]
+        d = mp.fsum(a * b for a, b in zip(acc, v))
+        A, B = mp.fsum(a * a for a in acc), mp.fsum(b * b for b in v)
+        ca = mp.mpf(1) if A == 0 else 1 - d / (2 * A)
+        cb = mp.mpf(1) if B == 0 else 1 - d / (2 * B)
+        ref.append((float(ca), float(cb)))
+        acc = [ca * a + cb * b for a, b in zip(acc, v)]
+    ref = np.asarray(ref)
+    st = oracle.stability(vecs, [0, 2], "chain", trials=3)
+    got = st["base"]["coeffs"][:, 0]
+    wrong = np.abs(got - ref) / np.maximum(1.0, np.abs(ref)) > UNSTABLE
+    assert wrong.any()
+    assert np.all(st["coeff_motion"][:, 0][wrong] > UNSTABLE)
 
 
 def test_symmetry_and_scale_invariance():

@@ -13,8 +13,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import (COEFF_TOL, TOL, check_coeffs, check_stats, evaluate, full_check, passes, rel_l2, run_gpu,
-                    sampled_check, say, segment_opnorms, unstable)
+from parity import TOL, check_coeffs, evaluate, full_check, passes, rel_l2, run_gpu, sampled_check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -647,23 +646,25 @@ def test_random_shapes(gpu, case):
     full_check(wl, f"random case {case}: lengths={lengths}", schedule)
 
 
-def test_seeded_random_sweep(gpu):
-    """150 seeded random shapes in one test: K log-uniform in [1, 400), all
+@pytest.mark.parametrize("chunk", range(10))
+def test_seeded_random_sweep(gpu, chunk):
+    """150 seeded random shapes, in ten chunks of 15: K log-uniform in [1, 400), all
     three dtypes, tree and chain, i.i.d. / shared-component / per-segment
-    scaled values or values at the edges of the format (fp16 subnormals,
-    bf16 near 2^-100 and 2^60), some all-zero workers, and segments from
+    scaled values, values at the edges of the format (fp16 subnormals, bf16
+    near 2^-100 and 2^60) or worker pairs that nearly cancel (relative gap
+    log-uniform in [1e-7, 1e-1]), some all-zero workers, and segments from
     empty through one element to 60,000 rows.  Every output and every coefficient away
     from the zero discontinuity is compared with the oracle; all failures
     are reported together.  (A wider sweep of this kind found the two
     stage-boundary errors that the one-element chain tests above pin.)"""
     A = _A()
     bad = []
-    for case in range(150):
+    for case in range(15 * chunk, 15 * chunk + 15):
         rng = np.random.default_rng(91000 + case)
         K = int(np.exp(rng.uniform(0, np.log(400))))
         dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
         schedule = "chain" if rng.random() < 0.4 else "tree"
-        kind = ["normal", "shared", "scaled", "edge"][int(rng.integers(0, 4))]
+        kind = ["normal", "shared", "scaled", "edge", "cancel"][int(rng.integers(0, 5))]
         lengths = []
         for _ in range(int(rng.integers(1, 9))):
             u = rng.random()
@@ -674,8 +675,12 @@ def test_seeded_random_sweep(gpu):
             lengths = [n // 2 for n in lengths]
         zero = tuple(sorted(set(rng.integers(0, K, size=int(rng.integers(1, 4))).tolist()))) \
             if rng.random() < 0.1 else ()
-        wl = W.random_case(K, lengths, dtype=dtype, seed=91000 + case, kind="normal" if kind == "edge" else kind,
-                           zero_workers=zero)
+        if kind == "cancel":  # worker pairs cancelling to eps, eps log-uniform in [1e-7, 1e-1]
+            eps = float(np.exp(rng.uniform(np.log(1e-7), np.log(1e-1))))
+            wl = W.cancelling_pairs(K, lengths, eps, dtype=dtype, seed=91000 + case)
+        else:
+            wl = W.random_case(K, lengths, dtype=dtype, seed=91000 + case,
+                               kind="normal" if kind == "edge" else kind, zero_workers=zero)
         if kind == "edge":  # exact power-of-two scaling into the format's edge ranges, then rounded to dtype
             scale = {"f32": 2.0 ** -120, "f16": 2.0 ** -20, "bf16": 2.0 ** (-100 if case % 2 else 60)}[dtype]
             wl.grads = [(g.double() * scale).to(g.dtype) for g in wl.grads]
@@ -684,17 +689,18 @@ def test_seeded_random_sweep(gpu):
         if not passes(ev, dtype):
             bad.append((case, K, dtype, schedule, kind, lengths, zero, ev["rel_l2"], ev["seg_ratio"],
                         ev["coeff_err"]))
-    say("seeded sweep", f"150 cases, {len(bad)} failures")
+    say("seeded sweep", f"cases {15 * chunk}..{15 * chunk + 14}: {len(bad)} failures")
     assert not bad, bad
 
 
-def test_many_segments_sweep(gpu):
-    """20 seeded shapes of 100 to 5,000 segments each (lengths log-uniform
+@pytest.mark.parametrize("chunk", range(4))
+def test_many_segments_sweep(gpu, chunk):
+    """20 seeded shapes (four chunks of 5) of 100 to 5,000 segments each (lengths log-uniform
     in [1, 10,000], a few empty), K from 2 to 20, all dtypes, both schedules:
     every output and coefficient against the oracle."""
     A = _A()
     bad = []
-    for case in range(20):
+    for case in range(5 * chunk, 5 * chunk + 5):
         rng = np.random.default_rng(93000 + case)
         K = int(rng.integers(2, 21))
         dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
@@ -711,5 +717,5 @@ def test_many_segments_sweep(gpu):
         ev = evaluate(wl, schedule)
         if not passes(ev, dtype):
             bad.append((case, K, dtype, schedule, kind, nseg, ev["rel_l2"], ev["seg_ratio"], ev["coeff_err"]))
-    say("many-segment sweep", f"20 cases, {len(bad)} failures")
+    say("many-segment sweep", f"cases {5 * chunk}..{5 * chunk + 4}: {len(bad)} failures")
     assert not bad, bad

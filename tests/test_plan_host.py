@@ -205,17 +205,16 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         ws = P["ws"]
         assert all(x % 256 == 0 for x in ws) and ws == sorted(ws)
         nodes = max(K - 1, 0)
-        sizes = [P["nslots"] * N * 4, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
-                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4,
-                 P["nslots"] * P["short_rows"] * 8, (P["partial_doubles"] if P["short_rows"] else 0) * 8]
-        # short tiles (at most 256 rows) numbered consecutively in the side buffers
-        pos = 0
-        for (start, length, seg), so in zip(tiles, P["short_off"]):
-            if length <= 256:
-                assert so == pos
-                pos += length
-            else:
-                assert so == -1
-        assert pos == P["short_rows"]
+        sizes = [P["nslots"] * N * 8, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8,
+                 P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
+                 nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4, P["partial_doubles"] * 8]
+        # every block carries the error bound of its Gram entries: fp64 sums
+        # (fp32 inputs, or a stage over fp64 slots), else the fp32 rounding of
+        # the 16-bit matrix cores' chunks
+        for si, stg in enumerate(P["stages"]):
+            for b in stg["blocks"]:
+                reads_slot = any(kind == 1 for kind, _ in b["ops"])
+                want = 2.0 ** -44 if (dt == 0 or reads_slot) else 2.0 ** -24 * (1 + 2.0 ** -10)
+                assert P["gram_err"][b["desc"]] == want, (K, si)
         for r, size in enumerate(sizes):
             assert ws[r] + size <= ws[r + 1], (K, r)
