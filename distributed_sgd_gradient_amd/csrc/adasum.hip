@@ -3,22 +3,23 @@
 // The tree is cut into stages of at most four levels (five when at most 32
 // 16-bit inputs make it one stage); each stage is a set of blocks (subtrees
 // of at most 16 operands, or that one 32-operand block).  A block above the
-// first stage reads fp32 slots and, where an input is carried up, that input
-// in its own dtype.  One call enqueues, stage by stage:
-//   1. gram: one launch per (block size, operand types) over every block and
+// first stage reads fp64 slots (lower blocks' results) and, where an input is
+// carried up, that input in its own dtype.  One call enqueues, stage by stage:
+//   1. gram: one launch per (block size, operand type) over every block and
 //      every tile: the Gram partials of each block's operands, in fp64;
 //   2. tree: one launch over every (block, segment): tile partials summed in
 //      tile order, every merge of the block evaluated on the Gram matrix
-//      (statistics, coefficients), the final operand weights written.  In a
-//      stage over 16-bit inputs the walk also flags the pairs whose
-//      coefficients the matrix cores' fp32 rounding could move beyond
-//      tolerance; one launch per Gram launch recomputes their tiles exactly
-//      (the others return at once) and a second walk redoes only them;
+//      (statistics, coefficients), the final operand weights written, and a
+//      flag on every pair whose coefficients the rounding of its Gram
+//      entries could move beyond tolerance (a merge under deep
+//      cancellation); one launch per Gram launch recomputes the flagged
+//      pairs' tiles exactly (the others return at once) and a second walk
+//      redoes only them;
 //   3. wsum: one launch per (block size, types) over every block and tile:
-//      the block's result, sum_k w_k x_k, into an fp32 slot or into out.
-// So a combine of K <= 16 gradients (K <= 32 for 16-bit ones) is three
-// launches (five for 16-bit inputs) and two passes over the inputs, whatever
-// the number of segments.
+//      the block's result, sum_k w_k x_k (in double-double for flagged
+//      pairs), into an fp64 slot or into out.
+// So a combine of K <= 16 gradients (K <= 32 for 16-bit ones) is five
+// launches and two passes over the inputs, whatever the number of segments.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -7,23 +7,27 @@
 // statistics of a subtree are quadratic forms in the Gram matrix of its
 // operands.  A block (a subtree of at most 16 operands, four levels; 32
 // operands and five levels for 16-bit inputs that fit one block) is
-// therefore combined in three launches:
+// therefore combined in three passes:
 //   gram  - one pass over the operands: per tile, the Gram matrix (packed
 //           upper triangle) on the matrix cores: fp64 instructions on the
-//           widened values (exact products, fp64 sums) for fp32 operands,
-//           32-row sums of exact products added in fp64 for 16-bit
-//           operands (tiles of at most 256 rows: exact products summed in
-//           fp64); reduced across the workgroup in a fixed order;
+//           widened values (exact products, fp64 sums) for fp32 operands and
+//           for the fp64 slots of later stages, 32-row sums of exact
+//           products added in fp64 for 16-bit operands (tiles of at most
+//           256 rows: exact products summed in double-double); reduced
+//           across the workgroup in a fixed order;
 //   tree  - per segment: the tile partials summed in tile order, then the
 //           block's merges evaluated on the Gram matrix level by level:
 //           d = wL.G.wR, A = wL.G.wL, B = wR.G.wR, ca = 1 - d/(2A),
 //           cb = 1 - d/(2B) (coefficient 1 for a zero norm), and the
 //           weights of the merged operands scaled by ca and cb;
 //   wsum  - one pass: y = sum_k w_k x_k in fp64, rounded once.
-// Over 16-bit operands the walk also flags the (block, segment) pairs whose
-// coefficients the fp32 rounding of the matrix-core sums could move beyond
-// tolerance (a merge under cancellation); gram_exact recomputes their Gram
-// partials exactly and the walk is repeated for them alone.
+// Each block's Gram entries carry a known rounding bound; the walk flags the
+// (block, segment) pairs whose coefficients that rounding could move beyond
+// tolerance (a merge under deep cancellation, where the quadratic forms
+// amplify it); gram_exact recomputes their partials as double-double sums of
+// exact products, the walk is repeated for them alone on double-double tile
+// sums, and their weighted sums (with those of any block whose result is far
+// smaller than its parts) are summed in double-double.
 // The merge walk's quadratic forms are summed in double-double from exact
 // products, and the weighted sum uses separately rounded products and sums
 // (no fused multiply-add); either way mirrored terms cancel exactly: an

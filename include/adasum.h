@@ -68,8 +68,12 @@
 extern "C" {
 #endif
 
-/* Element type of the inputs and of the result.  Intermediate tree levels
- * are always held in fp32; statistics and coefficients in fp64. */
+/* Element type of the inputs and of the result.  Inside a block of up to 16
+ * operands (32 for at most 32 16-bit inputs) nothing intermediate is stored:
+ * statistics are quadratic forms in the block's fp64 Gram matrix and the
+ * block's result is one weighted sum; a block result that feeds a later
+ * stage (K above 16, or above 32 for 16-bit inputs) is kept in fp64.
+ * Statistics and coefficients are fp64. */
 typedef enum {
   ADASUM_F32 = 0,
   ADASUM_F16 = 1,
@@ -145,8 +149,9 @@ ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int
  *                32 operands and five levels when at most 32 16-bit inputs
  *                make the whole tree one block) the statistics are evaluated
  *                from the Gram matrix of the block's operands, accumulated
- *                in fp64; above a block, from the fp32 values its result was
- *                stored in.  coeffs, stats and ortho must be 8-byte aligned
+ *                in fp64 (double-double where a merge cancels deeply enough
+ *                for the fp64 rounding to matter); above a block, from its
+ *                result kept in fp64.  coeffs, stats and ortho must be 8-byte aligned
  *                and overlap no other argument.
  *   ortho        device fp64 array [nseg] receiving, per segment, the
  *                orthogonality ratio |result|^2 / sum_k |g_k|^2 of Figure 1
