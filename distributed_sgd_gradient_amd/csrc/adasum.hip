@@ -468,15 +468,16 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
           done[k] = 1;
           group.push_back(&bk);
         }
-        for (size_t c = 0; c < group.size(); c += kMaxJobs) {
-          const int n = (int)std::min<size_t>(kMaxJobs, group.size() - c);
+        const int per_launch = max_jobs(nbt);
+        for (size_t c = 0; c < group.size(); c += per_launch) {
+          const int n = (int)std::min<size_t>(per_launch, group.size() - c);
           double in_bytes = 0, out_bytes = 0;
           if (pass == 0) {
             GramArgs a{};
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
               for (size_t k = 0; k < bk.operands.size(); ++k) {
-                a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+                a.x[j * op_stride(nbt) + k] = ref_ptr(p, b, bk.operands[k]);
                 in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
               }
               a.narrow[j] = block_kind(p, bk).narrow;
@@ -500,7 +501,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             for (int j = 0; j < n; ++j) {
               const Block& bk = *group[c + j];
               for (size_t k = 0; k < bk.operands.size(); ++k) {
-                a.x[j][k] = ref_ptr(p, b, bk.operands[k]);
+                a.x[j * op_stride(nbt) + k] = ref_ptr(p, b, bk.operands[k]);
                 in_bytes += (double)p.N * dtype_size(ref_type(p, bk.operands[k]));
               }
               a.narrow[j] = block_kind(p, bk).narrow;
@@ -528,6 +529,15 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         // cancellation); those pairs' tiles are then recomputed exactly and
         // walked again
         t.flags = flags;
+        if (p.descs[sg.blocks.front().desc].nbt > kArgOps) {
+          // 64-operand blocks (a stage of its own): tile groups of long segments
+          const double gbytes = 8.0 * gram_entries(kMaxOps) * ntiles * t.nblocks;
+          log_launch("groups", stage_no, ntiles, t.nblocks, kMaxOps, gbytes);
+          const int pg = prof_start(kTree, gbytes, st);
+          e = launch_tile_groups(t, ntiles, st);
+          prof_stop(pg, st);
+          if (e != hipSuccess) return fail_hip(e, "launching tile groups");
+        }
         double bytes = 0;
         for (const Block& bk : sg.blocks) bytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
         log_launch("tree", stage_no, t.nblocks * p.nseg, 1, 0, bytes);

@@ -8,13 +8,14 @@
 namespace adasum {
 
 // Gram pass: per (block, tile), the packed upper triangle of the fp64 Gram
-// matrix of the block's operands over the tile.  Operands x[j][k] with k at
-// or beyond the block's operand count are NULL and read as zero.  In a launch
+// matrix of the block's operands over the tile.  Operand k of job j is
+// x[j * op_stride(nbt) + k]; those at or beyond the block's operand count are
+// NULL and read as zero.  In a launch
 // over fp64 slots (a stage above the first), bit k of narrow[j] marks operand
 // k of job j as an input gradient, read in the inputs' dtype and widened
 // exactly.
 struct GramArgs {
-  const void* x[kMaxJobs][kMaxOps];
+  const void* x[kMaxJobs * kArgOps];
   uint32_t narrow[kMaxJobs];
   int64_t poff[kMaxJobs];  // partials of tile t: partials + poff + t * gram_entries(nbt)
   const Tile* tiles;
@@ -79,7 +80,7 @@ constexpr double kSumCancel = 1e-2;
 // to the result's type (an fp64 slot keeps the sum as it is); narrow as for
 // the Gram pass.
 struct WsumArgs {
-  const void* x[kMaxJobs][kMaxOps];
+  const void* x[kMaxJobs * kArgOps];  // laid out as in GramArgs
   uint32_t narrow[kMaxJobs];
   void* y[kMaxJobs];
   int wrow[kMaxJobs];
@@ -110,6 +111,11 @@ struct SumArgs {
 hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
                        hipStream_t st);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
+// For the 64-operand blocks of a launch (descs desc0 .. desc0 + nblocks - 1):
+// the Gram partials of each group of kTileGroup consecutive tiles of a
+// segment with more than one tile, added in tile order in fp64 into the
+// group's first tile.
+hipError_t launch_tile_groups(const TreeArgs& a, int ntiles, hipStream_t st);
 // The Gram partials of every tile of a flagged (block, segment) pair,
 // recomputed exactly: double-double sums of exact products in row order,
 // high parts to partials, low parts to partials_lo.  Other tiles return at once.

@@ -361,9 +361,9 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
   const int op = (lane & 15) % NB, set = (lane & 15) / NB, grp = lane >> 4;
 
   // a NULL operand (beyond the block's count) reads operand 0, masked to zero
-  const void* mine = args.x[j][op];
+  const void* mine = args.x[j * op_stride(NB) + op];
   const bool live = mine != nullptr;
-  const float* xp = static_cast<const float*>(live ? mine : args.x[j][0]);
+  const float* xp = static_cast<const float*>(live ? mine : args.x[j * op_stride(NB)]);
 
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
   const int64_t niter = (hi - first + R - 1) / R;
@@ -452,9 +452,9 @@ __global__ __launch_bounds__(kBlock) void gram_stage_kernel(GramArgs args) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int op = (lane & 15) % NB, set = (lane & 15) / NB, grp = lane >> 4;
-  const void* mine = args.x[j][op];
+  const void* mine = args.x[j * op_stride(NB) + op];
   const bool live = mine != nullptr;
-  const void* xp = live ? mine : args.x[j][0];
+  const void* xp = live ? mine : args.x[j * op_stride(NB)];
   // a masked operand reads operand 0, in operand 0's type
   const bool narrow = (args.narrow[j] >> (live ? op : 0)) & 1u;
 
@@ -609,16 +609,16 @@ __device__ __forceinline__ double widen16<bf16_t>(uint16_t bits) {
 // of exact products, its low part into out_lo (NULL: dropped).  The rows
 // pass through sh (NB * kExactRows 16-bit values) kExactRows at a time.
 // Called by every thread of the workgroup.
-template <typename T, int NB>
+template <typename T, int NB, int NT = kBlock>
 __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t len, double* __restrict__ out,
                                 double* __restrict__ out_lo, uint16_t* sh) {
   constexpr int NE = gram_entries(NB);
-  constexpr int EPT = (NE + kBlock - 1) / kBlock;  // entries per thread
+  constexpr int EPT = (NE + NT - 1) / NT;  // entries per thread
   int ei[EPT], ek[EPT];
   DD acc[EPT];
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
-    const int e = threadIdx.x + q * kBlock;
+    const int e = threadIdx.x + q * NT;
     int i = 0, rem = e < NE ? e : 0;
     while (rem >= NB - i) {
       rem -= NB - i;
@@ -631,7 +631,7 @@ __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t le
   for (int64_t c0 = 0; c0 < len; c0 += kExactRows) {
     const int n = (int)min<int64_t>(kExactRows, len - c0);
     if (c0 > 0) __syncthreads();  // the previous chunk is consumed
-    for (int idx = threadIdx.x; idx < NB * n; idx += kBlock) {
+    for (int idx = threadIdx.x; idx < NB * n; idx += NT) {
       const int k = idx / n, r = idx - k * n;
       const uint16_t* x = static_cast<const uint16_t*>(table[k]);
       sh[k * kExactRows + r] = x != nullptr ? gload(x + lo + c0 + r) : (uint16_t)0;
@@ -639,7 +639,7 @@ __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t le
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
-      if (threadIdx.x + q * kBlock >= NE) continue;
+      if (threadIdx.x + q * NT >= NE) continue;
       const uint16_t* x = sh + ei[q] * kExactRows;
       const uint16_t* y = sh + ek[q] * kExactRows;
       DD sum = acc[q];
@@ -649,9 +649,9 @@ __device__ void gram_exact_rows(const void* const* table, int64_t lo, int64_t le
   }
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
-    if (threadIdx.x + q * kBlock >= NE) continue;
-    out[threadIdx.x + q * kBlock] = acc[q].hi;
-    if (out_lo != nullptr) out_lo[threadIdx.x + q * kBlock] = acc[q].lo;
+    if (threadIdx.x + q * NT >= NE) continue;
+    out[threadIdx.x + q * NT] = acc[q].hi;
+    if (out_lo != nullptr) out_lo[threadIdx.x + q * NT] = acc[q].lo;
   }
 }
 
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
     if (c0 > 0) __syncthreads();  // the previous chunk is consumed
     for (int idx = threadIdx.x; idx < NB * n; idx += kBlock) {
       const int k = idx / n, r = idx - k * n;
-      const void* x = args.x[j][k];
+      const void* x = args.x[j * op_stride(NB) + k];
       const int64_t row = tile.start + c0 + r;
       double v = 0.0;
       if (x != nullptr) {
@@ -736,20 +736,27 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
   }
 }
 
-// Blocks of up to 16 operands use one 16-operand half; the 32-operand block
+// Blocks of up to 16 operands use one 16-operand group; the 32-operand block
 // (at most 32 16-bit inputs, one stage) uses two, with three instructions
-// per 32-row chunk: the two diagonal 16 x 16 blocks and the cross block
-// (A from the first half, B from the second).  Lane l, output register r of
-// sub-block q = (h1, h2) holds G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].
+// per 32-row chunk: the two diagonal 16 x 16 blocks and the cross block (A
+// from the first group, B from the second); the 64-operand block (33 to 64
+// 16-bit inputs, one stage) uses four, with ten instructions per chunk.
+// Lane l, output register r of sub-block q = (h1, h2) holds
+// G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].  A 64-operand wave keeps forty
+// fp64 sums, so it runs at two waves per SIMD, with eight chunks (32 KB) in
+// flight per iteration to keep as many bytes in flight per CU as the
+// smaller blocks do at four waves per SIMD (bf16: four chunks, within the
+// registers that its range check and scaled path take).
+constexpr int kWideUnroll = 8;  // 32-row chunks per wave per iteration of a 64-operand block
 template <typename T, int NB>
 __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
-  constexpr int NH = NB > 16 ? 2 : 1;  // 16-operand halves
+  constexpr int NH = NB > 32 ? 4 : NB > 16 ? 2 : 1;  // 16-operand groups
   constexpr int NP = NH * (NH + 1) / 2;  // sub-blocks (h1 <= h2)
-  constexpr int U = kMfmaUnroll / NH;  // 32-row chunks per wave per iteration
+  constexpr int U = NB > 32 ? (Mfma<T>::kGuard ? kWideUnroll / 2 : kWideUnroll) : kMfmaUnroll / NH;  // chunks per wave per iteration
   constexpr int R = 32 * U;            // rows per wave per iteration
   constexpr int NE = gram_entries(NB);
-  static_assert(NB <= 32, "at most two halves");
-  __shared__ double red[kGramWaves][NP][64 * 4];
+  // the wave sums of every sub-block; for 64 operands those of waves 1-3 only
+  __shared__ double red[NB > 32 ? kGramWaves - 1 : kGramWaves][NP][64 * 4];
 
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
@@ -758,7 +765,7 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
   if (tile.len <= kExactRows) {  // workgroup-uniform: a short tile, summed exactly
     static_assert(sizeof(red) >= sizeof(uint16_t) * NB * kExactRows, "staging fits the reduction buffer");
     const int64_t at = args.poff[j] + (int64_t)tile_id * NE;
-    gram_exact_rows<T, NB>(args.x[j], lo, tile.len, args.partials + at,
+    gram_exact_rows<T, NB>(args.x + j * op_stride(NB), lo, tile.len, args.partials + at,
                            args.partials_lo != nullptr ? args.partials_lo + at : nullptr,
                            reinterpret_cast<uint16_t*>(&red[0][0][0]));
     return;
@@ -770,7 +777,7 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
 
   // Lanes of absent operands (index >= NB, or a NULL slot) read operand 0
   // and are masked to zero, so every load of an iteration is unconditional.
-  const void* const* table = args.x[j];
+  const void* const* table = args.x + j * op_stride(NB);
   const uint16_t* xp[NH];
   bool live[NH];
 #pragma unroll
@@ -892,13 +899,41 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
     }
   }
 
+  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+  if constexpr (NB > 32) {
+    // Waves 1-3 pass their matrices through LDS; wave 0 adds them to its own
+    // in wave order and writes its lanes' entries of the packed triangle.
+    if (wave > 0) {
+#pragma unroll
+      for (int q = 0; q < NP; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave - 1][q][r * 64 + lane] = acc[q][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int q = 0;
+#pragma unroll
+      for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+        for (int h2 = h1; h2 < NH; ++h2, ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * h1 + 4 * grp + r, k = 16 * h2 + op;
+            if (i > k) continue;
+            double sum = acc[q][r];
+#pragma unroll
+            for (int w = 0; w < kGramWaves - 1; ++w) sum += red[w][q][r * 64 + lane];
+            out[gram_index(NB, i, k)] = sum;
+          }
+    }
+    return;
+  }
   // Sum the four waves' matrices in wave order; write the packed triangle.
 #pragma unroll
   for (int q = 0; q < NP; ++q)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][q][lane * 4 + r] = acc[q][r];
   __syncthreads();
-  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
   for (int e = threadIdx.x; e < NE; e += kBlock) {
     int i = 0, rem = e;
     while (rem >= NB - i) {
@@ -938,17 +973,43 @@ __device__ double quad_form(const double* G, int n, const double* w, int a0, int
 }
 
 constexpr int kTreeWaves = kBlock / 64;
+// Per-wave tile sums of blocks of up to 32 operands (528 Gram entries); the
+// 2080 entries of a 64-operand block fit the same space.
+constexpr int kPartStride = gram_entries(kArgOps);
+static_assert(kTreeWaves * kPartStride >= gram_entries(kMaxOps), "a 64-operand Gram matrix fits the wave sums");
 
-// One workgroup per (block, segment).  Wave q sums the tile partials of the
-// q-th quarter of the segment's tiles (lanes over Gram entries, tiles in
-// order); the four quarter sums are then added in wave order.  The split
-// depends only on the tile count, so the result is reproducible.  The
+// Groups of kTileGroup tiles of the segments of 64-operand blocks: see
+// launch_tile_groups.  One workgroup per (tile, block); a tile that starts
+// no group, or lies in a segment of one tile, returns at once.
+__global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
+  const int t = blockIdx.x;
+  const BlockDesc d = a.descs[a.desc0 + blockIdx.y];
+  const int s = a.tiles[t].seg;
+  const int t0 = a.seg_tile[s], t1 = a.seg_tile[s + 1];
+  if (t1 - t0 < 2 || (t - t0) % kTileGroup != 0) return;  // workgroup-uniform
+  const int ne = gram_entries(d.nbt);
+  const int n = min(t1 - t, kTileGroup);
+  // the partials live in the workspace; only the walk reads them as const
+  double* p = const_cast<double*>(a.partials) + d.poff + (int64_t)t * ne;
+  for (int e = threadIdx.x; e < ne; e += kBlock) {
+    double sum = 0.0;
+    for (int u = 0; u < n; ++u) sum += p[(int64_t)u * ne + e];
+    p[e] = sum;
+  }
+}
+
+// One workgroup per (block, segment).  Blocks of up to 32 operands: wave q
+// sums the tile partials of the q-th quarter of the segment's tiles (lanes
+// over Gram entries, tiles in order); the four quarter sums are then added
+// in wave order.  64-operand blocks: one thread per entry adds the
+// segment's tile groups in order (see launch_tile_groups).  Either way the
+// split depends only on the tile count, so the result is reproducible.  The
 // refining walk (kRefine) visits only flagged pairs, whose tiles hold
-// double-double entries, and sums them in double-double.
+// double-double entries, and sums them in double-double, tile by tile.
 template <bool kRefine>
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
-  __shared__ double part[kTreeWaves][gram_entries(kMaxOps)];
-  __shared__ double part_lo[kRefine ? kTreeWaves : 1][kRefine ? gram_entries(kMaxOps) : 1];
+  __shared__ double part[kTreeWaves * kPartStride];
+  __shared__ double part_lo[kRefine ? kTreeWaves * kPartStride : 1];
   __shared__ double G[gram_entries(kMaxOps)];
   // operand weights: products of the coefficients of the merges above each
   // operand, in double-double (a chain multiplies up to K - 1 of them, and a
@@ -963,51 +1024,74 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   const int n = d.nbt;
   const int ne = gram_entries(n);
   const int tid = threadIdx.x;
-  const int q = tid >> 6, lane = tid & 63;
   const int t0 = a.seg_tile[s], t1 = a.seg_tile[s + 1];
-  const int chunk = (t1 - t0 + kTreeWaves - 1) / kTreeWaves;
-  const int q0 = min(t1, t0 + q * chunk), q1 = min(t1, q0 + chunk);
-  for (int e = lane; e < ne; e += 64) {
-    const double* p = a.partials + d.poff + e;
-    if constexpr (kRefine) {
-      const double* pl = a.partials_lo + d.poff + e;
-      DD sum{0.0, 0.0};
-      for (int t = q0; t < q1; ++t) sum = dd_add(sum, DD{p[(int64_t)t * ne], pl[(int64_t)t * ne]});
-      part[q][e] = sum.hi;
-      part_lo[q][e] = sum.lo;
-    } else {
-      double sum = 0.0;
+  // The low parts of the Gram entries, where the walk has them: the refining
+  // walk's tile sums, or below the exact entries of a single short tile.
+  // Entry e of either is written only after every wave sum of entry e is
+  // read, by the thread that read them, and above all wave sums' first
+  // quarter-stride, so the space can be shared.
+  double* const Glo = kRefine ? &part_lo[0] : &part[0];
+  if (n > kArgOps) {
+    const int step = (!kRefine && t1 - t0 > 1) ? kTileGroup : 1;
+    for (int e = tid; e < ne; e += kBlock) {
+      const double* p = a.partials + d.poff + e;
+      if constexpr (kRefine) {
+        const double* pl = a.partials_lo + d.poff + e;
+        DD sum{0.0, 0.0};
+        for (int t = t0; t < t1; ++t) sum = dd_add(sum, DD{p[(int64_t)t * ne], pl[(int64_t)t * ne]});
+        G[e] = sum.hi;
+        Glo[e] = sum.lo;
+      } else {
+        double sum = 0.0;
 #pragma unroll 8
-      for (int t = q0; t < q1; ++t) sum += p[(int64_t)t * ne];
-      part[q][e] = sum;
+        for (int t = t0; t < t1; t += step) sum += p[(int64_t)t * ne];
+        G[e] = sum;
+      }
+    }
+    __syncthreads();
+  } else {
+    const int q = tid >> 6, lane = tid & 63;
+    const int chunk = (t1 - t0 + kTreeWaves - 1) / kTreeWaves;
+    const int q0 = min(t1, t0 + q * chunk), q1 = min(t1, q0 + chunk);
+    for (int e = lane; e < ne; e += 64) {
+      const double* p = a.partials + d.poff + e;
+      if constexpr (kRefine) {
+        const double* pl = a.partials_lo + d.poff + e;
+        DD sum{0.0, 0.0};
+        for (int t = q0; t < q1; ++t) sum = dd_add(sum, DD{p[(int64_t)t * ne], pl[(int64_t)t * ne]});
+        part[q * kPartStride + e] = sum.hi;
+        part_lo[q * kPartStride + e] = sum.lo;
+      } else {
+        double sum = 0.0;
+#pragma unroll 8
+        for (int t = q0; t < q1; ++t) sum += p[(int64_t)t * ne];
+        part[q * kPartStride + e] = sum;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < ne; e += kBlock) {
+      if constexpr (kRefine) {
+        DD sum{part[e], part_lo[e]};
+#pragma unroll
+        for (int i = 1; i < kTreeWaves; ++i) sum = dd_add(sum, DD{part[i * kPartStride + e], part_lo[i * kPartStride + e]});
+        G[e] = sum.hi;
+        Glo[e] = sum.lo;
+      } else {
+        double sum = part[e];
+#pragma unroll
+        for (int i = 1; i < kTreeWaves; ++i) sum += part[i * kPartStride + e];
+        G[e] = sum;
+      }
     }
   }
-  __syncthreads();
   // A segment of one short tile of 16-bit inputs has its Gram entries in
   // double-double (hi: that tile's partial, taken exactly above) from the
   // exact short-tile sums; a refined pair has all of them so.  The walk then
   // forms its quadratic forms from both parts, so their rounding is not
   // amplified by a merge that cancels.  Workgroup-uniform.
-  const uint32_t all_inputs = d.nb >= 32 ? 0xffffffffu : (1u << d.nb) - 1u;
+  const uint64_t all_inputs = d.nb >= 64 ? ~uint64_t(0) : (uint64_t(1) << d.nb) - 1u;
   const bool exact_g = kRefine || (a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows &&
                                    a.lo_inputs && d.leafmask == all_inputs);
-  // the normal walk keeps the low parts in the consumed wave sums
-  __shared__ double glo_refine[kRefine ? gram_entries(kMaxOps) : 1];
-  double* const Glo = kRefine ? &glo_refine[0] : &part[0][0];
-  for (int e = tid; e < ne; e += kBlock) {
-    if constexpr (kRefine) {
-      DD sum{part[0][e], part_lo[0][e]};
-#pragma unroll
-      for (int i = 1; i < kTreeWaves; ++i) sum = dd_add(sum, DD{part[i][e], part_lo[i][e]});
-      G[e] = sum.hi;
-      Glo[e] = sum.lo;
-    } else {
-      double sum = part[0][e];
-#pragma unroll
-      for (int i = 1; i < kTreeWaves; ++i) sum += part[i][e];
-      G[e] = sum;
-    }
-  }
   if (!kRefine && exact_g) {
     __syncthreads();  // every wave sum is consumed
     for (int e = tid; e < ne; e += kBlock) Glo[e] = a.partials_lo[d.poff + (int64_t)t0 * ne + e];
@@ -1103,7 +1187,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     // sum of |g_k|^2 over the block's input operands, in operand order
     double leaf = 0.0;
     for (int k = 0; k < d.nb; ++k)
-      if ((d.leafmask >> k) & 1) leaf += G[gram_index(n, k, k)];
+      if ((d.leafmask >> k) & 1u) leaf += G[gram_index(n, k, k)];
     a.leafnorm[(int64_t)d.wrow * a.nseg + s] = leaf;
     if (d.root && a.ortho != nullptr) {
       // orthogonality of the segment's gradients: |result|^2 over the sum
@@ -1161,7 +1245,7 @@ __device__ void wsum_exact_range(const WsumArgs& args, int j, int64_t lo, int64_
     DD acc{0.0, 0.0};
 #pragma unroll 1
     for (int k = 0; k < NB; ++k) {
-      const void* x = args.x[j][k];
+      const void* x = args.x[j * op_stride(NB) + k];
       if (x == nullptr) continue;
       double v;
       if constexpr (std::is_same<TIn, TN>::value) {
@@ -1206,14 +1290,14 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
     wsum_exact_range<TIn, TIn, NB, TOut>(args, j, sp.lo, sp.hi, wrow, args.weights_lo + wat);
     return;
   }
-  const TIn* x0 = static_cast<const TIn*>(args.x[j][0]);
+  const TIn* x0 = static_cast<const TIn*>(args.x[j * op_stride(NB)]);
   const TIn* xs[NB];
   bool live[NB];
   double w[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    live[k] = args.x[j][k] != nullptr;
-    xs[k] = live[k] ? static_cast<const TIn*>(args.x[j][k]) : x0;
+    live[k] = args.x[j * op_stride(NB) + k] != nullptr;
+    xs[k] = live[k] ? static_cast<const TIn*>(args.x[j * op_stride(NB) + k]) : x0;
     w[k] = wrow[k];
   }
   TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
@@ -1255,6 +1339,113 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
 #pragma unroll
     for (int e = 0; e < kGroup; ++e) r[e] = Elem<TOut>::round(acc[e], &unused);
     Elem<TOut>::store8(y + g, r);
+  }
+  if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
+}
+
+// Weighted sum of a 64-operand block (16-bit inputs of type T, one stage, so
+// the result is the output).  The four waves of a workgroup take the same
+// 512 elements, wave w the operands 16 w .. 16 w + 15, as wsum_kernel takes
+// a 16-operand block (eight elements per lane, all sixteen loads in flight,
+// terms in operand order from zero); waves 1-3 pass their sums through LDS
+// and wave 0 adds them to its own in wave order, rounds once and stores.
+// So each element is (((s0 + s1) + s2) + s3), s_w the fp64 sum of wave w's
+// sixteen terms.
+template <typename T>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void wsum_wide_kernel(WsumArgs args) {
+  constexpr int NB = 64;
+  constexpr int NG = 16;  // operands per wave
+  constexpr int kSplit = wsum_split(sizeof(T));
+  constexpr int kStep = 64 * kGroup;  // elements per iteration
+  __shared__ double sums[kGramWaves - 1][kStep];
+  const int tile_id = blockIdx.x / kSplit;
+  const int part = blockIdx.x % kSplit;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  TileSpan sp = span_of(tile);
+  {
+    const int64_t groups = (sp.body_hi - sp.body_lo) / kGroup;
+    const int64_t per = (groups + kSplit - 1) / kSplit * kGroup;
+    const int64_t b0 = min(sp.body_lo + part * per, sp.body_hi);
+    const int64_t b1 = min(b0 + per, sp.body_hi);
+    if (part > 0) sp.lo = b0;
+    if (part < kSplit - 1) sp.hi = b1;
+    sp.body_lo = b0;
+    sp.body_hi = b1;
+  }
+  const int64_t wat = ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  const double* wrow = args.weights + wat;
+  if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] & 2u) {  // workgroup-uniform
+    wsum_exact_range<T, T, NB, T>(args, j, sp.lo, sp.hi, wrow, args.weights_lo + wat);
+    return;
+  }
+  const void* const* table = args.x + j * op_stride(NB);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: pointers and weights in scalars
+  const T* x0 = static_cast<const T*>(table[0]);
+  const T* xs[NG];
+  bool live[NG];
+  double w[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int k = NG * wave + i;
+    live[i] = table[k] != nullptr;
+    xs[i] = live[i] ? static_cast<const T*>(table[k]) : x0;
+    w[i] = wrow[k];
+  }
+  T* __restrict__ y = static_cast<T*>(args.y[j]);
+  double unused;
+
+  auto one = [&](int64_t i) {
+    double acc = 0.0;
+    for (int k = 0; k < NB; ++k) {
+      const void* x = table[k];
+      if (x != nullptr) acc = add_rn(acc, mul_rn(wrow[k], (double)Elem<T>::load1(static_cast<const T*>(x) + i)));
+    }
+    Elem<T>::store1(y + i, Elem<T>::round(acc, &unused));
+  };
+
+  if (tid < sp.body_lo - sp.lo) one(sp.lo + tid);
+  for (int64_t g0 = sp.body_lo; g0 < sp.body_hi; g0 += kStep) {
+    // the body is a whole number of groups; lanes past its end read its last
+    // group again (so every load is unconditional) and store nothing
+    const int64_t gl = g0 + (int64_t)lane * kGroup;
+    const bool in = gl < sp.body_hi;
+    const int64_t g = in ? gl : sp.body_hi - kGroup;
+    typename Elem<T>::Raw8 raw[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) raw[i] = Elem<T>::load_raw8(xs[i] + g);
+    double acc[kGroup];
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      float v[kGroup];
+      Elem<T>::unpack8(raw[i], v);
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) {
+        const double t = mul_rn(w[i], (double)v[e]);
+        acc[e] = add_rn(acc[e], live[i] ? t : 0.0);
+      }
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) sums[wave - 1][e * 64 + lane] = acc[e];
+    }
+    __syncthreads();
+    if (wave == 0 && in) {
+      T r[kGroup];
+#pragma unroll
+      for (int e = 0; e < kGroup; ++e) {
+        double t = acc[e];
+#pragma unroll
+        for (int q = 0; q < kGramWaves - 1; ++q) t = add_rn(t, sums[q][e * 64 + lane]);
+        r[e] = Elem<T>::round(t, &unused);
+      }
+      Elem<T>::store8(y + g, r);
+    }
+    __syncthreads();  // the sums are consumed before the next iteration writes its own
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
 }
@@ -1311,8 +1502,8 @@ __global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
   double w[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) {
-    live[k] = args.x[j][k] != nullptr;
-    xs[k] = live[k] ? args.x[j][k] : args.x[j][0];
+    live[k] = args.x[j * op_stride(NB) + k] != nullptr;
+    xs[k] = live[k] ? args.x[j * op_stride(NB) + k] : args.x[j * op_stride(NB)];
     nk[k] = (args.narrow[j] >> (live[k] ? k : 0)) & 1u;  // a masked operand reads operand 0, in its type
     w[k] = wrow[k];
   }
@@ -1529,6 +1720,7 @@ struct RunGramMfma {
       case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
       case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
       case 32: hipLaunchKernelGGL((gram_mfma_kernel<T, 32>), grid, dim3(kBlock), 0, st, a); break;
+      case 64: hipLaunchKernelGGL((gram_mfma_kernel<T, 64>), grid, dim3(kBlock), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1549,6 +1741,12 @@ hipError_t run_gram_exact(int nbt, const GramArgs& a, int ntiles, int njobs, hip
         break;
       }
       return hipErrorInvalidValue;
+    case 64:
+      if constexpr (sizeof(TIn) == 2 && std::is_same<TIn, TN>::value) {  // so are 64-operand blocks, one stage
+        hipLaunchKernelGGL((gram_exact_kernel<TIn, TN, 64>), grid, dim3(kBlock), 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1565,6 +1763,12 @@ hipError_t run_wsum(int nbt, const WsumArgs& a, int ntiles, int njobs, hipStream
     case 32:
       if constexpr (sizeof(TIn) == 2) {  // 32-operand blocks exist only over 16-bit inputs
         hipLaunchKernelGGL((wsum_kernel<TIn, 32, TOut>), grid, dim3(kBlock), 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    case 64:
+      if constexpr (sizeof(TIn) == 2 && std::is_same<TIn, TOut>::value) {  // one stage: the result is the output
+        hipLaunchKernelGGL((wsum_wide_kernel<TIn>), grid, dim3(kBlock), 0, st, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -1638,6 +1842,11 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(tree_kernel<true>, grid, dim3(kBlock), 0, st, a);
   else
     hipLaunchKernelGGL(tree_kernel<false>, grid, dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_groups(const TreeArgs& a, int ntiles, hipStream_t st) {
+  hipLaunchKernelGGL(tile_group_kernel, dim3((unsigned)ntiles, (unsigned)a.nblocks), dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }
 

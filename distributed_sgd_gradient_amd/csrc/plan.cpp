@@ -170,7 +170,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     // the first stage reads only inputs; later ones read fp64 slots (and inputs carried up)
     const int ops = first ? first_stage_ops(dtype, K) : kMaxOps32;
     if (schedule == Schedule::Tree)
-      tree_stage(cur, stage_merges, node, ops == 32 ? 5 : 4);
+      tree_stage(cur, stage_merges, node, ops == 64 ? 6 : ops == 32 ? 5 : 4);
     else
       chain_stage(cur, stage_merges, node);
     const bool last = cur.size() == 1 && next_leaf == K;
@@ -188,7 +188,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
       b.dst = last ? Ref{Ref::Out, 0} : Ref{Ref::Slot, p.nslots++};
       BlockDesc d{};
       d.nb = e.hi - e.lo;
-      d.nbt = d.nb <= 2 ? 2 : d.nb <= 4 ? 4 : d.nb <= 8 ? 8 : d.nb <= 16 ? 16 : 32;
+      d.nbt = d.nb <= 2 ? 2 : d.nb <= 4 ? 4 : d.nb <= 8 ? 8 : d.nb <= 16 ? 16 : d.nb <= 32 ? 32 : 64;
       d.merge0 = (int)p.merges.size();
       for (const StageMerge& m : stage_merges) {
         if (m.llo >= e.lo && m.rhi <= e.hi) {
@@ -198,7 +198,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
       d.nmerges = (int)p.merges.size() - d.merge0;
       d.wrow = p.nblocks++;
       for (int k = e.lo; k < e.hi; ++k)
-        if (is_leaf[k]) d.leafmask |= 1u << (k - e.lo);
+        if (is_leaf[k]) d.leafmask |= uint64_t(1) << (k - e.lo);
       d.root = last ? 1 : 0;
       // fp64 sums on the fp64 matrix cores (fp32 inputs; stages that read
       // fp64 slots, any inputs among them widened exactly): a bound on the

@@ -6,9 +6,9 @@
 //     tile at a multiple of kGroup elements, so that vector loads inside a
 //     tile are 16-byte aligned whatever the segment boundaries are;
 //   * the tree, cut into stages.  Within a stage, every maximal subtree is a
-//     block of up to four levels (16 operands); with at most 32 16-bit
+//     block of up to four levels (16 operands); with at most 64 16-bit
 //     inputs, whose Gram pass runs on the matrix cores, the single stage
-//     takes five levels (32 operands).  Every
+//     takes five levels (32 operands) or six (64 operands).  Every
 //     statistic a node of the block needs (a.b, |a|^2, |b|^2 of its two
 //     children) is a quadratic form in the Gram matrix of the block's
 //     operands, because every node is a linear combination of them; so a
@@ -37,9 +37,20 @@ constexpr int kTile = 32768;     // largest tile, elements (a multiple of kGroup
 constexpr int kMinTile = 2048;   // smallest tile a large segment is cut into
 constexpr int kTargetTiles = 4096;  // tiles a workload is cut into when it is small
 constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
-constexpr int kMaxOps = 32;      // operands per block over 16-bit inputs: five tree levels
+constexpr int kMaxOps = 64;      // operands per block over 16-bit inputs: up to six tree levels
 constexpr int kMaxOps32 = 16;    // operands per block over fp32 operands: four tree levels
 constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
+// Operand pointers of a launch sit in one table, job j's operand k at
+// j * op_stride(nbt) + k: 32 per job, or 64 for a launch of 64-operand
+// blocks (then at most kArgOps * kMaxJobs / 64 jobs).
+constexpr int kArgOps = 32;
+constexpr int op_stride(int nbt) { return nbt > kArgOps ? 64 : kArgOps; }
+constexpr int max_jobs(int nbt) { return kArgOps * kMaxJobs / op_stride(nbt); }
+// The walk of a 64-operand block sums its 2080 Gram entries over the tiles
+// of a segment.  Where a segment has many tiles, a separate launch first
+// adds up groups of kTileGroup consecutive tiles, in place into each group's
+// first tile, so that the walk reads one partial per group.
+constexpr int kTileGroup = 16;
 // Tiles of at most kExactRows rows of 16-bit inputs are short: their Gram
 // matrices are summed exactly (double-double) instead of on the matrix cores,
 // since short segments are where merges nearly cancel by chance.
@@ -63,11 +74,14 @@ enum class Schedule : int { Tree = 0, Chain = 1 };
 
 inline size_t dtype_size(DType t) { return t == DType::F64 ? 8 : t == DType::F32 ? 4 : 2; }
 
-// Largest block of the first stage.  32-operand blocks (16-bit inputs only)
-// pay off only where they finish the whole combine in one stage: above 32
-// inputs the tree needs a second stage anyway, and 16-operand blocks stream
-// faster (half the concurrent streams per pass).
-inline int first_stage_ops(DType t, int K) { return (t != DType::F32 && K <= kMaxOps) ? kMaxOps : kMaxOps32; }
+// Largest block of the first stage.  Blocks of 32 or 64 operands (16-bit
+// inputs only) pay off only where they finish the whole combine in one stage,
+// without the fp64 intermediates of a second: above 64 inputs the tree needs
+// a second stage anyway, and 16-operand blocks stream faster.
+inline int first_stage_ops(DType t, int K) {
+  if (t == DType::F32 || K > kMaxOps) return kMaxOps32;
+  return K <= 32 ? 32 : kMaxOps;
+}
 
 // Number of distinct entries of the symmetric n x n Gram matrix.
 constexpr int gram_entries(int n) { return n * (n + 1) / 2; }
@@ -90,15 +104,14 @@ struct Merge {
 };
 
 struct BlockDesc {  // device-visible description of one block
-  int32_t nb;       // operands (1..32; 1 only for K = 1)
-  int32_t nbt;      // Gram size the kernels use: 2, 4, 8, 16 or 32 (operands >= nb are zero)
+  int32_t nb;       // operands (1..64; 1 only for K = 1)
+  int32_t nbt;      // Gram size the kernels use: 2, 4, 8, 16, 32 or 64 (operands >= nb are zero)
   int32_t merge0;   // first merge in the merge table
   int32_t nmerges;  // merges of this block, children before parents
   int64_t poff;     // Gram partials of tile t start at partials + poff + t * gram_entries(nbt)
   int32_t wrow;     // row of this block in the leaf-weight table
-  uint32_t leafmask;  // bit k: operand k is one of the K input gradients
-  int32_t root;       // 1 for the block whose result is the output
-  int32_t pad;
+  int32_t root;     // 1 for the block whose result is the output
+  uint64_t leafmask;  // bit k: operand k is one of the K input gradients
   // Relative rounding error of this block's Gram entries, against the sum of
   // |x_i x_j| that each entry adds up: the fp64 sums of the fp64 matrix cores
   // (fp32 inputs, fp64 slots) or the fp32 rounding of the 16-bit matrix

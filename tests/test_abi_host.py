@@ -141,11 +141,11 @@ def test_adasum_log_reports_the_plan():
             "from distributed_sgd_gradient_amd import _native\n"
             "off = np.array([0, 1000, 70000], dtype=np.int64)\n"
             "p = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))\n"
-            "print(_native.lib().adasum_workspace_bytes(40, p, 2, 2, 0))\n")
+            "print(_native.lib().adasum_workspace_bytes(70, p, 2, 2, 0))\n")
     env = dict(os.environ, ADASUM_LOG="1")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
     assert r.returncode == 0, r.stderr
-    assert "[adasum] plan K=40 nseg=2 N=70000" in r.stderr
+    assert "[adasum] plan K=70 nseg=2 N=70000" in r.stderr
     assert "2 stages" in r.stderr and int(r.stdout.strip()) > 0
 
 

@@ -58,7 +58,7 @@ def test_config4_sampled_full_size(gpu):
 
 
 def test_config4_sampled_full_size_chain(gpu):
-    # 64 fp16 inputs as a left-to-right chain: five stages, the running result in an fp32 slot
+    # 64 fp16 inputs as a left-to-right chain: one 64-operand block whose walk takes the 63 merges in order
     wl = W.make_workload(4, device=gpu)
     segs = _spread(wl.nseg, np.random.default_rng(41), extra=[0, 9, 13])
     sampled_check(wl, segs, "config4 chain", schedule="chain")
@@ -80,7 +80,8 @@ def test_config5_sampled_full_size(gpu, schedule):
 
 @pytest.mark.parametrize("K,dtype,schedule", [(32, "bf16", "tree"), (32, "f16", "tree"), (16, "bf16", "tree"),
                                               (16, "f16", "tree"), (16, "f32", "tree"), (32, "bf16", "chain"),
-                                              (16, "f32", "chain")])
+                                              (16, "f32", "chain"), (48, "bf16", "tree"), (64, "f16", "tree"),
+                                              (40, "bf16", "chain")])
 def test_short_random_segments(gpu, K, dtype, schedule):
     """Hundreds of segments of 1..8 i.i.d. N(0,1) elements, plus tiles on
     both sides of the short-tile limit (256 rows): a short random vector is
@@ -97,7 +98,7 @@ def test_short_random_segments(gpu, K, dtype, schedule):
     full_check(wl, f"short K={K} {dtype} {schedule}", schedule)
 
 
-@pytest.mark.parametrize("K,dtype", [(4, "bf16"), (4, "f16"), (32, "bf16"), (32, "f16")])
+@pytest.mark.parametrize("K,dtype", [(4, "bf16"), (4, "f16"), (32, "bf16"), (32, "f16"), (64, "bf16"), (48, "f16")])
 def test_long_near_cancelling_pairs_16bit(gpu, K, dtype):
     """Long segments (tens of thousands of elements, many matrix-core tiles)
     where every odd worker nearly cancels its even neighbour:
@@ -134,8 +135,8 @@ def test_small_K_ragged_segments(gpu, K, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("K", [17, 20, 31, 32, 33, 48, 63, 64, 65, 70, 130, 257, 300])
 def test_multistage_K(gpu, K, dtype):
-    # more than 16 operands: one block of 32 (at most 32 16-bit inputs), else
-    # blocks of 16 with fp32 block results and carried inputs; K = 130 has
+    # more than 16 operands: one block of 32 or 64 (at most 32 or 64 16-bit
+    # inputs), else blocks of 16 with fp64 block results and carried inputs; K = 130 has
     # stage positions beyond 127; K = 257 and 300 take three stages (blocks
     # of lower blocks' results)
     wl = W.random_case(K, [1, 300, 9, 40000, 8], dtype=dtype, seed=100 + K, kind="shared")
@@ -143,21 +144,33 @@ def test_multistage_K(gpu, K, dtype):
     full_check(wl, f"multistage K={K} {dtype}")
 
 
-@pytest.mark.parametrize("K", [8, 29])
+@pytest.mark.parametrize("K,dtype,schedule", [(40, "f16", "tree"), (64, "bf16", "tree"), (33, "bf16", "chain")])
+def test_wide_block_many_tiles(gpu, K, dtype, schedule):
+    """33 to 64 16-bit inputs: one 64-operand block.  A segment of about 980
+    tiles (the walk reads its partials in groups of 16 tiles), segments of
+    exactly 16, 17 and 33 tiles (group boundaries), a short tile and a few
+    rows."""
+    lengths = [2_000_000, 16 * 2048, 17 * 2048, 33 * 2048 + 5, 300, 3]
+    wl = W.random_case(K, lengths, dtype=dtype, seed=300 + K, kind="shared")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"wide K={K} {dtype} {schedule}", schedule)
+
+
+@pytest.mark.parametrize("K", [8, 29, 50])
 def test_fp16_subnormal_scales(gpu, K):
     wl = W.random_case(K, [3000] * 16 + [7, 1], dtype="f16", seed=11, kind="scaled")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"fp16 scaled K={K}")
 
 
-@pytest.mark.parametrize("K", [8, 24])
+@pytest.mark.parametrize("K", [8, 24, 48])
 def test_bf16_exponent_extremes(gpu, K):
     """bf16 segments at magnitudes near and past the limits of fp32 products.
 
     Per-segment scales 2^-120 (bf16 subnormals), 2^-57 and 2^61 (values on
     both sides of the range whose pairwise products are exact in fp32),
     2^-40, 1 and 2^100, plus one segment that mixes 2^-100 and 2^90 values.
-    K = 24 runs the 32-operand Gram pass.
+    K = 24 runs the 32-operand Gram pass, K = 48 the 64-operand one.
     """
     lengths = [5000, 5000, 5000, 5000, 5000, 5000, 3001]
     scales = [2.0 ** -120, 2.0 ** -57, 2.0 ** -40, 1.0, 2.0 ** 61, 2.0 ** 100]

@@ -5,9 +5,9 @@ together with the library's plan.cpp and prints every plan for K = 1..70 and
 some larger K (up to 300), in both schedules, for fp32 and for 16-bit
 inputs.  Every merge the GPU path will evaluate must be exactly the node the
 oracle defines: same two children (as leaf ranges), same position in the
-node order, every input used once, stage operands fp32 above stage 1; blocks
-hold at most 16 operands, or 32 when at most 32 16-bit inputs make the
-whole combine one stage.
+node order, every input used once, stage operands fp64 above stage 1; blocks
+hold at most 16 operands, or 32 (64) when at most 32 (64) 16-bit inputs make
+the whole combine one stage.
 """
 
 import json
@@ -64,8 +64,10 @@ def oracle_nodes(K, schedule):
 
 def block_limit(stage, dtype, K):
     """Largest block the planner may form: 16 operands, except the single
-    stage over at most 32 16-bit inputs (32)."""
-    return 32 if (stage == 0 and dtype != 0 and K <= 32) else 16
+    stage over at most 32 16-bit inputs (32) or at most 64 (64)."""
+    if stage == 0 and dtype != 0 and K <= 64:
+        return 32 if K <= 32 else 64
+    return 16
 
 
 def plan_nodes(P):
@@ -113,22 +115,26 @@ def test_plan_nodes_match_oracle(plans, schedule, dtype):
 
 
 def test_16bit_blocks_are_larger(plans):
-    """Up to 32 16-bit inputs (fp16 or bf16) finish in one stage of one
-    32-operand block; beyond that the first stage uses 16-operand blocks."""
+    """Up to 64 16-bit inputs (fp16 or bf16) finish in one stage of one
+    block, of 32 operands up to 32 inputs and of 64 above; beyond that the
+    first stage uses 16-operand blocks.  Both schedules."""
     seen = set()
     for P in plans:
-        if P["schedule"] == 0 and P["K"] in (17, 32, 33, 64, 65):
+        if P["K"] in (17, 32, 33, 64, 65):
             K, dt = P["K"], P["dtype"]
-            one = dt != 0 and K <= 32
+            one = dt != 0 and K <= 64
             nstages = len(P["stages"])
-            assert nstages == (1 if one else 2), (K, dt, nstages)
+            if P["schedule"] == 0:
+                assert nstages == (1 if one else 2), (K, dt, nstages)
             blocks = P["stages"][0]["blocks"]
             if one:
-                assert len(blocks) == 1 and blocks[0]["nb"] == K and blocks[0]["nbt"] == 32
+                assert nstages == 1
+                assert len(blocks) == 1 and blocks[0]["nb"] == K and blocks[0]["nbt"] == (32 if K <= 32 else 64)
+                assert blocks[0]["leafmask"] == (1 << K) - 1
             else:
                 assert all(b["nb"] <= 16 for b in blocks)
-            seen.add((K, dt))
-    assert len(seen) == 15
+            seen.add((K, dt, P["schedule"]))
+    assert len(seen) == 30
 
 
 def test_tiles_cover_segments_exactly(plans):
@@ -195,7 +201,7 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         for si, stg in enumerate(P["stages"]):
             regions = []
             for b in stg["blocks"]:
-                assert b["nb"] <= block_limit(si, dt, K) and b["nbt"] in (2, 4, 8, 16, 32) and b["nbt"] >= b["nb"]
+                assert b["nb"] <= block_limit(si, dt, K) and b["nbt"] in (2, 4, 8, 16, 32, 64) and b["nbt"] >= b["nb"]
                 entries = b["nbt"] * (b["nbt"] + 1) // 2
                 assert 0 <= b["poff"] and b["poff"] + entries * len(tiles) <= P["partial_doubles"]
                 regions.append((b["poff"], b["poff"] + entries * len(tiles)))
@@ -205,8 +211,8 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         ws = P["ws"]
         assert all(x % 256 == 0 for x in ws) and ws == sorted(ws)
         nodes = max(K - 1, 0)
-        sizes = [P["nslots"] * N * 8, P["partial_doubles"] * 8, P["nblocks"] * nseg * 32 * 8,
-                 P["nblocks"] * nseg * 32 * 8, P["nblocks"] * nseg * 8,
+        sizes = [P["nslots"] * N * 8, P["partial_doubles"] * 8, P["nblocks"] * nseg * 64 * 8,
+                 P["nblocks"] * nseg * 64 * 8, P["nblocks"] * nseg * 8,
                  nodes * nseg * 2 * 8, nodes * nseg * 3 * 8, P["nblocks"] * nseg * 4, P["partial_doubles"] * 8]
         # every block carries the error bound of its Gram entries: fp64 sums
         # (fp32 inputs, or a stage over fp64 slots), else the fp32 rounding of
