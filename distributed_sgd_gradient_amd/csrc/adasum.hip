@@ -435,6 +435,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
     t.ortho = b.ortho;
     t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
     t.nblocks_total = p.nblocks;
+    for (const Block& bk : sg.blocks) t.wide |= p.descs[bk.desc].nbt > kArgOps ? 1 : 0;
     if (ntiles == 0) {  // every segment empty: coefficients 1, statistics 0
       if (p.nseg > 0) {
         e = launch_tree(t, st);

@@ -65,6 +65,7 @@ struct TreeArgs {
   // The weighted sum adds up pairs with bit 1 in double-double.
   uint32_t* flags;          // [nblocks total][nseg]
   int refine;
+  int wide;                 // some block of the launch has 64 operands (nbt = 64)
 };
 
 // Relative coefficient error bound above which a pair's Gram matrix is

@@ -973,6 +973,7 @@ __device__ double quad_form(const double* G, int n, const double* w, int a0, int
 }
 
 constexpr int kTreeWaves = kBlock / 64;
+constexpr int kSerialMerge = 16;  // widest merge whose sums one thread adds in operand order
 // Per-wave tile sums of blocks of up to 32 operands (528 Gram entries); the
 // 2080 entries of a 64-operand block fit the same space.
 constexpr int kPartStride = gram_entries(kArgOps);
@@ -1006,16 +1007,19 @@ __global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
 // split depends only on the tile count, so the result is reproducible.  The
 // refining walk (kRefine) visits only flagged pairs, whose tiles hold
 // double-double entries, and sums them in double-double, tile by tile.
-template <bool kRefine>
+// kWide: the launch holds a 64-operand block (its Gram matrix takes 2080
+// entries of LDS; the other variant, 528, keeps more workgroups per CU).
+template <bool kRefine, bool kWide>
 __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   __shared__ double part[kTreeWaves * kPartStride];
   __shared__ double part_lo[kRefine ? kTreeWaves * kPartStride : 1];
-  __shared__ double G[gram_entries(kMaxOps)];
+  constexpr int MO = kWide ? kMaxOps : kArgOps;  // operands of the launch's largest block
+  __shared__ double G[gram_entries(MO)];
   // operand weights: products of the coefficients of the merges above each
   // operand, in double-double (a chain multiplies up to K - 1 of them, and a
   // node that nearly cancels would amplify their fp64 rounding)
-  __shared__ DD w[kMaxOps];
-  __shared__ double wf[kMaxOps];  // the weights rounded to fp64
+  __shared__ DD w[MO];
+  __shared__ double wf[MO];  // the weights rounded to fp64
   const int item = blockIdx.x;
   const int b = item / a.nseg;
   const int s = item % a.nseg;
@@ -1031,7 +1035,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // read, by the thread that read them, and above all wave sums' first
   // quarter-stride, so the space can be shared.
   double* const Glo = kRefine ? &part_lo[0] : &part[0];
-  if (n > kArgOps) {
+  if (kWide && n > kArgOps) {
     const int step = (!kRefine && t1 - t0 > 1) ? kTileGroup : 1;
     for (int e = tid; e < ne; e += kBlock) {
       const double* p = a.partials + d.poff + e;
@@ -1096,7 +1100,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     __syncthreads();  // every wave sum is consumed
     for (int e = tid; e < ne; e += kBlock) Glo[e] = a.partials_lo[d.poff + (int64_t)t0 * ne + e];
   }
-  if (tid < kMaxOps) w[tid] = DD{1.0, 0.0};
+  if (tid < MO) w[tid] = DD{1.0, 0.0};
   __syncthreads();
   // entries already exact (double-double) are not flagged again
   const double gram_err = exact_g ? 0.0 : d.gram_err;
@@ -1109,9 +1113,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order,
   // all in double-double, and rounds them to fp64.  That is the same
   // arithmetic, term for term, as a serial evaluation.
-  __shared__ DD rowL[kMaxOps], rowR[kMaxOps];
-  __shared__ double cab[kMaxOps][2];
-  __shared__ Merge ms[kMaxOps];
+  __shared__ DD rowL[MO], rowR[MO];
+  __shared__ double cab[MO][2];
+  __shared__ Merge ms[MO];
   __shared__ int unsure;  // some coefficient may be off by more than kRefineTol
   if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
   if (tid == 0) unsure = 0;
@@ -1137,18 +1141,15 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       rowR[tid] = sr;
     }
     __syncthreads();
-    if (tid < m1 - m0) {
-      const Merge mg = ms[m0 + tid];
-      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
-      DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
-      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_mul(rowL[i], w[i]));
-      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_mul(rowR[i], w[i]));
-      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_mul(rowR[i], w[i]));
+    // A merge's statistics from its five sums: A, B, d (double-double) and,
+    // for the rounding estimate, sl = sum_{i in L} w_i^2 G_ii and sr over R.
+    auto finish = [&](int mi, DD a2, DD b2, DD ab, double sl, double sr) {
+      const Merge mg = ms[mi];
       const double A = a2.hi, B = b2.hi, dd = ab.hi;  // normalised: hi is the rounded sum
       const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
-      cab[m0 + tid][0] = ca;
-      cab[m0 + tid][1] = cb;
+      cab[mi][0] = ca;
+      cab[mi][1] = cb;
       if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
         // The rounding errors of separate chunk sums are independent, so a
         // quadratic form over an operand with weights w errs by about
@@ -1160,9 +1161,6 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
         // data.)  c = 1 - d / (2A) then moves by about
         // (|d err| + |d| |A err| / A) / (2A).  An operand whose norm the
         // estimate cannot tell from zero is flagged too.
-        double sl = 0.0, sr = 0.0;
-        for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
-        for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
         const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
         bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
         if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
@@ -1175,13 +1173,57 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
       a.stats[at * 3] = dd;
       a.stats[at * 3 + 1] = A;
       a.stats[at * 3 + 2] = B;
+    };
+    // Merges over at most kSerialMerge operands: one thread each, terms in
+    // operand order.  Wider ones (the top of a 64-operand tree, a chain of
+    // more than 16): one wave each, a lane per operand, the terms added by a
+    // butterfly across the wave, so that a 64-operand chain is not 63 serial
+    // sums of up to 63 terms.
+    if (tid < m1 - m0 && ms[m0 + tid].rhi - ms[m0 + tid].llo <= kSerialMerge) {
+      const Merge mg = ms[m0 + tid];
+      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
+      DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
+      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_mul(rowL[i], w[i]));
+      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_mul(rowR[i], w[i]));
+      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_mul(rowR[i], w[i]));
+      double sl = 0.0, sr = 0.0;
+      for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
+      for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
+      finish(m0 + tid, a2, b2, ab, sl, sr);
+    }
+    {
+      const int q = tid >> 6, lane = tid & 63;
+      int nth = 0;  // wide merges of this batch seen so far
+      for (int mi = m0; mi < m1; ++mi) {
+        const Merge mg = ms[mi];
+        if (mg.rhi - mg.llo <= kSerialMerge) continue;
+        if ((nth++ & (kTreeWaves - 1)) != q) continue;  // wave-uniform
+        const int i0 = mg.llo + lane;  // a wide merge spans at most 64 operands
+        const bool inL = i0 < mg.lhi, inR = i0 >= mg.lhi && i0 < mg.rhi;
+        const int i = (inL || inR) ? i0 : mg.llo;  // lanes past the merge read a valid entry, unused
+        const DD zero{0.0, 0.0};
+        DD a2 = inL ? dd_mul(rowL[i], w[i]) : zero;
+        DD b2 = inR ? dd_mul(rowR[i], w[i]) : zero;
+        DD ab = inL ? dd_mul(rowR[i], w[i]) : zero;
+        const double wg = (inL || inR) ? w[i].hi * w[i].hi * G[gram_index(n, i, i)] : 0.0;
+        double sl = inL ? wg : 0.0, sr = inR ? wg : 0.0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          a2 = dd_add(a2, DD{__shfl_xor(a2.hi, off), __shfl_xor(a2.lo, off)});
+          b2 = dd_add(b2, DD{__shfl_xor(b2.hi, off), __shfl_xor(b2.lo, off)});
+          ab = dd_add(ab, DD{__shfl_xor(ab.hi, off), __shfl_xor(ab.lo, off)});
+          sl += __shfl_xor(sl, off);
+          sr += __shfl_xor(sr, off);
+        }
+        if (lane == 0) finish(mi, a2, b2, ab, sl, sr);
+      }
     }
     __syncthreads();
     if (mine >= 0) w[tid] = dd_scale(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
     __syncthreads();
     m0 = m1;
   }
-  if (tid < kMaxOps) wf[tid] = w[tid].hi;  // normalised: hi is the rounded value
+  if (tid < MO) wf[tid] = w[tid].hi;  // normalised: hi is the rounded value
   __syncthreads();
   if (tid == 0) {
     // sum of |g_k|^2 over the block's input operands, in operand order
@@ -1201,7 +1243,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   }
   __syncthreads();
   const int64_t wat = ((int64_t)d.wrow * a.nseg + s) * kMaxOps;
-  if (tid < kMaxOps) {
+  if (tid < MO) {
     a.weights[wat + tid] = wf[tid];
     a.weights_lo[wat + tid] = w[tid].lo;
   }
@@ -1210,7 +1252,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     // smaller than its weighted parts, sum_k w_k x_k in fp64 would lose the
     // ratio of the two to rounding, and a later stage could amplify that loss
     // again; every pair flagged for recomputation (bit 0) is summed so too.
-    __shared__ double rows_w[kMaxOps];
+    __shared__ double rows_w[MO];
     if (tid < d.nb) {
       double r = 0.0;
       for (int k = 0; k < d.nb; ++k) r += wf[k] * gram_at(G, n, tid, k);
@@ -1838,10 +1880,17 @@ hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a
 
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.nblocks * a.nseg));
-  if (a.refine)
-    hipLaunchKernelGGL(tree_kernel<true>, grid, dim3(kBlock), 0, st, a);
-  else
-    hipLaunchKernelGGL(tree_kernel<false>, grid, dim3(kBlock), 0, st, a);
+  if (a.refine) {
+    if (a.wide)
+      hipLaunchKernelGGL((tree_kernel<true, true>), grid, dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((tree_kernel<true, false>), grid, dim3(kBlock), 0, st, a);
+  } else {
+    if (a.wide)
+      hipLaunchKernelGGL((tree_kernel<false, true>), grid, dim3(kBlock), 0, st, a);
+    else
+      hipLaunchKernelGGL((tree_kernel<false, false>), grid, dim3(kBlock), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -157,7 +157,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   int node = 0;
   int next_leaf = K;                 // chain: first input not yet in any stage
   if (schedule == Schedule::Chain) {
-    next_leaf = std::min(K, first_stage_ops(dtype, K));
+    next_leaf = std::min(K, first_stage_ops(dtype, K, schedule));
     operands.resize(next_leaf);
     is_leaf.resize(next_leaf);
   }
@@ -168,7 +168,7 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
     for (int i = 0; i < (int)operands.size(); ++i) cur.push_back(Elem{i, i + 1, false});
     std::vector<StageMerge> stage_merges;
     // the first stage reads only inputs; later ones read fp64 slots (and inputs carried up)
-    const int ops = first ? first_stage_ops(dtype, K) : kMaxOps32;
+    const int ops = first ? first_stage_ops(dtype, K, schedule) : kMaxOps32;
     if (schedule == Schedule::Tree)
       tree_stage(cur, stage_merges, node, ops == 64 ? 6 : ops == 32 ? 5 : 4);
     else

@@ -77,8 +77,10 @@ inline size_t dtype_size(DType t) { return t == DType::F64 ? 8 : t == DType::F32
 // Largest block of the first stage.  Blocks of 32 or 64 operands (16-bit
 // inputs only) pay off only where they finish the whole combine in one stage,
 // without the fp64 intermediates of a second: above 64 inputs the tree needs
-// a second stage anyway, and 16-operand blocks stream faster.
-inline int first_stage_ops(DType t, int K) {
+// a second stage anyway, and 16-operand blocks stream faster.  (A chain
+// takes the same blocks: its stages of 16 would write and read an fp64
+// running result between stages.)
+inline int first_stage_ops(DType t, int K, Schedule) {
   if (t == DType::F32 || K > kMaxOps) return kMaxOps32;
   return K <= 32 ? 32 : kMaxOps;
 }

@@ -62,9 +62,10 @@ def oracle_nodes(K, schedule):
     return nodes
 
 
-def block_limit(stage, dtype, K):
+def block_limit(stage, dtype, K, schedule=0):
     """Largest block the planner may form: 16 operands, except the single
-    stage over at most 32 16-bit inputs (32) or at most 64 (64)."""
+    stage over at most 32 16-bit inputs (32) or at most 64 (64), in either
+    schedule."""
     if stage == 0 and dtype != 0 and K <= 64:
         return 32 if K <= 32 else 64
     return 16
@@ -82,7 +83,7 @@ def plan_nodes(P):
                 assert all(kind in (0, 1) for kind, _ in b["ops"])
                 assert any(kind == 1 for kind, _ in b["ops"]), "a later block holds a lower block's result"
             rng = [(i, i + 1) if kind == 0 else slot_range[i] for kind, i in b["ops"]]
-            limit = block_limit(si, P["dtype"], P["K"])
+            limit = block_limit(si, P["dtype"], P["K"], P["schedule"])
             assert len(rng) == b["nb"] <= limit and b["nbt"] >= b["nb"]
             for i in range(len(rng) - 1):
                 assert rng[i][1] == rng[i + 1][0], "block operands must be adjacent leaf ranges"
@@ -116,8 +117,8 @@ def test_plan_nodes_match_oracle(plans, schedule, dtype):
 
 def test_16bit_blocks_are_larger(plans):
     """Up to 64 16-bit inputs (fp16 or bf16) finish in one stage of one
-    block, of 32 operands up to 32 inputs and of 64 above; beyond that the
-    first stage uses 16-operand blocks.  Both schedules."""
+    block, of 32 operands up to 32 inputs and of 64 above, in both
+    schedules; beyond that the first stage uses 16-operand blocks."""
     seen = set()
     for P in plans:
         if P["K"] in (17, 32, 33, 64, 65):
@@ -201,7 +202,7 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         for si, stg in enumerate(P["stages"]):
             regions = []
             for b in stg["blocks"]:
-                assert b["nb"] <= block_limit(si, dt, K) and b["nbt"] in (2, 4, 8, 16, 32, 64) and b["nbt"] >= b["nb"]
+                assert b["nb"] <= block_limit(si, dt, K, sc) and b["nbt"] in (2, 4, 8, 16, 32, 64) and b["nbt"] >= b["nb"]
                 entries = b["nbt"] * (b["nbt"] + 1) // 2
                 assert 0 <= b["poff"] and b["poff"] + entries * len(tiles) <= P["partial_doubles"]
                 regions.append((b["poff"], b["poff"] + entries * len(tiles)))
