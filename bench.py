@@ -244,6 +244,123 @@ def other_workload(config, steps, warmup, dev, budget_s):
     return rec
 
 
+def _median_ms(fn, reps=5):
+    """Median of `reps` timed calls of fn (HIP events on the current stream)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return sorted(ms)[len(ms) // 2]
+
+
+def probe(name, dev):
+    """Measurements behind design decisions, run with the library's own
+    kernels (one JSON line per case):
+
+    cache  - the K = 16 fp32 plain sum of one group of buffers repeated 32
+             times in a HIP graph (its inputs were just read: the memory-side
+             cache can serve them) against 32 different groups in turn, for
+             groups of 8 MiB to 512 MiB of inputs;
+    groups - the combine of 2^26 elements per worker (K = 16 fp32) as one
+             call, against the same segments cut into groups combined one
+             after another (a HIP graph of all groups, on one stream and
+             alternating over two), so that each group's second read could
+             come from the memory-side cache;
+    launch - back-to-back plain sums of 8 elements (K = 1) in a graph: the
+             cost of a dependent launch."""
+    import torch
+
+    import distributed_sgd_gradient_amd as A
+
+    K, T = 16, 1 << 26
+    out_lines = []
+    if name in ("cache", "groups"):
+        gen = torch.Generator(device=dev).manual_seed(5)
+        big = [torch.randn(T, device=dev, generator=gen) for _ in range(K)]
+        out = torch.empty(T, device=dev)
+    if name == "cache":
+        R = 32
+        for lg in range(17, 24):
+            ng = 1 << lg
+            ngroups = T // ng
+            sl = [slice((g % ngroups) * ng, (g % ngroups + 1) * ng) for g in range(R)]
+            A.plain_sum([b[sl[0]] for b in big], out=out[sl[0]])
+            torch.cuda.synchronize()
+            same, cyc = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(same):
+                for _ in range(R):
+                    A.plain_sum([b[sl[0]] for b in big], out=out[sl[0]])
+            with torch.cuda.graph(cyc):
+                for r in range(R):
+                    A.plain_sum([b[sl[r]] for b in big], out=out[sl[r]])
+            t_same, t_cyc = _median_ms(same.replay) / R, _median_ms(cyc.replay) / R
+            nbytes = (K + 1) * ng * 4
+            out_lines.append({"probe": "cache", "input_MiB": K * ng * 4 >> 20, "same_group_us": t_same * 1e3,
+                              "same_group_GBps": nbytes / (t_same * 1e-3) / 1e9, "groups_in_turn": min(ngroups, R),
+                              "in_turn_us": t_cyc * 1e3, "in_turn_GBps": nbytes / (t_cyc * 1e-3) / 1e9})
+            del same, cyc
+    elif name == "groups":
+        bmin = (K + 1) * T * 4
+        for lg in (19, 21, 23):
+            ng, nper = 1 << lg, 4
+            ngroups = T // ng
+            off = [i * (ng // nper) for i in range(ngroups * nper + 1)]
+            whole = A.Combiner(big, off, out=out)
+            t_whole = _median_ms(whole)
+            del whole
+            groups = []
+            for g in range(ngroups):
+                sl = slice(g * ng, (g + 1) * ng)
+                groups.append(A.Combiner([b[sl] for b in big], [i * (ng // nper) for i in range(nper + 1)],
+                                         out=out[sl]))
+            for c in groups:
+                c()
+            torch.cuda.synchronize()
+            one, two = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(one):
+                for c in groups:
+                    c()
+            side = torch.cuda.Stream()
+            with torch.cuda.graph(two):
+                cur = torch.cuda.current_stream()
+                side.wait_stream(cur)
+                for i, c in enumerate(groups):
+                    if i % 2:
+                        with torch.cuda.stream(side):
+                            c()
+                    else:
+                        c()
+                cur.wait_stream(side)
+            t_one, t_two = _median_ms(one.replay), _median_ms(two.replay)
+            out_lines.append({"probe": "groups", "group_input_MiB": K * ng * 4 >> 20, "groups": ngroups,
+                              "one_call_ms": t_whole, "groups_one_stream_ms": t_one, "groups_two_streams_ms": t_two,
+                              "one_call_path_frac": bmin / (t_whole * 1e-3) / 1e9 / PEAK_HBM_GBS})
+            del one, two, groups
+            torch.cuda.synchronize()
+    elif name == "launch":
+        x = torch.ones(8, device=dev)
+        y = torch.empty_like(x)
+        A.plain_sum([x], out=y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(100):
+                A.plain_sum([x], out=y)
+        out_lines.append({"probe": "launch", "us_per_dependent_launch": _median_ms(g.replay) * 10})
+    else:
+        raise SystemExit(f"unknown probe {name!r} (cache, groups, launch)")
+    for ln in out_lines:
+        print(json.dumps(ln), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +379,8 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time each step alone after writing a 1 GiB scratch buffer (caches cold); "
                          "reported under 'cold', the headline value stays the back-to-back rate")
+    ap.add_argument("--probe", choices=["cache", "groups", "launch"], default=None,
+                    help="instead of the benchmark, print the measurements behind a design decision (see probe())")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 3 plain fp32 copies of MIB MiB (read MIB, write MIB) "
                          "so that rocprofv3 counters can be scaled against a kernel of known traffic")
@@ -280,6 +399,9 @@ def main():
 
     dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", "0")))
     torch.cuda.set_device(dev)
+    if args.probe:
+        probe(args.probe, dev)
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
