@@ -515,6 +515,16 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             a.weights = weights;
             a.weights_lo = weights_lo;
             a.flags = flags;
+            if (p.fused) {
+              // the walk, any exact recomputation and the weighted sum in one launch
+              t.flags = flags;
+              log_launch("walk+wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
+              const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
+              e = launch_fused(in_t, nbt, t, a, ntiles, st);
+              prof_stop(pr, st);
+              if (e != hipSuccess) return fail_hip(e, "launching the fused walk and weighted sum");
+              continue;
+            }
             log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
             e = launch_wsum(in_t, p.dtype, nbt, out_t, a, ntiles, n, st);
@@ -523,7 +533,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
           }
         }
       }
-      if (pass == 0 && p.nseg > 0) {
+      if (pass == 0 && p.nseg > 0 && !p.fused) {
         // 2. per (block, segment): statistics, coefficients, operand weights,
         // and a flag on every pair whose coefficients the rounding of its
         // Gram entries could move beyond tolerance (a merge under deep

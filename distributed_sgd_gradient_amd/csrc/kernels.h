@@ -126,5 +126,10 @@ hipError_t launch_gram_exact(DType operand, DType narrow_t, int nbt, const GramA
 hipError_t launch_wsum(DType in_t, DType narrow_t, int nbt, DType out_t, const WsumArgs& a, int ntiles, int njobs,
                        hipStream_t st);
 hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st);
+// A one-stage plan of one block of at most 32 operands whose segments have
+// few tiles (Plan::fused): after its Gram pass, the walk, any exact
+// recomputation and the weighted sum in one launch over the weighted sum's
+// grid (t as for launch_tree, w as for launch_wsum of that block).
+hipError_t launch_fused(DType in_t, int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st);
 
 }  // namespace adasum

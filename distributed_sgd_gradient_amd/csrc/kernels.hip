@@ -1007,6 +1007,196 @@ __global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
 // split depends only on the tile count, so the result is reproducible.  The
 // refining walk (kRefine) visits only flagged pairs, whose tiles hold
 // double-double entries, and sums them in double-double, tile by tile.
+// The merge walk of block d over segment s on its Gram matrix G (and, where
+// exact_g, its double-double low parts Glo): every merge's statistics and
+// coefficients, the operands' weights w (double-double) and wf (rounded),
+// and the block's flags (see TreeArgs), returned to every thread.  Where
+// outputs is set, the coefficients, statistics, weights, input norms,
+// orthogonality and flags are also written out.  Called by every thread of
+// the workgroup; G and Glo are in LDS.
+template <bool kRefine, int MO>
+__device__ __forceinline__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, const double* G,
+                                               const double* Glo, bool exact_g, DD* w, double* wf, bool outputs) {
+  const int tid = threadIdx.x;
+  const int n = d.nbt;
+  if (tid < MO) w[tid] = DD{1.0, 0.0};
+  __syncthreads();
+  // entries already exact (double-double) are not flagged again
+  const double gram_err = exact_g ? 0.0 : d.gram_err;
+  // Merges run level by level: merges of a block are stored children
+  // before parents, and the merges of one level cover disjoint operand
+  // ranges (a batch ends where a merge starts left of the previous one).
+  // For merge (L, R), thread i in L u R forms its row sums
+  // rowL_i = sum_{k in L} w_k G(i,k) and rowR_i = sum_{k in R} w_k G(i,k) in
+  // k order; one thread per merge then forms A = sum_{i in L} w_i rowL_i,
+  // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order,
+  // all in double-double, and rounds them to fp64.  That is the same
+  // arithmetic, term for term, as a serial evaluation.
+  __shared__ DD rowL[MO], rowR[MO];
+  __shared__ double cab[MO][2];
+  __shared__ Merge ms[MO];
+  __shared__ int unsure;  // some coefficient may be off by more than kRefineTol
+  if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
+  if (tid == 0) unsure = 0;
+  __syncthreads();
+  for (int m0 = 0; m0 < d.nmerges;) {
+    int m1 = m0 + 1;
+    while (m1 < d.nmerges && ms[m1].llo >= ms[m1 - 1].rhi) ++m1;
+    // the merge of this batch that holds operand tid, if any
+    int mine = -1;
+    for (int m = m0; m < m1; ++m)
+      if (tid >= ms[m].llo && tid < ms[m].rhi) mine = m;
+    if (mine >= 0) {
+      const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
+      DD sl{0.0, 0.0}, sr{0.0, 0.0};
+      if (exact_g) {
+        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
+        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
+      } else {
+        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_scale(w[k], gram_at(G, n, tid, k)));
+        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_scale(w[k], gram_at(G, n, tid, k)));
+      }
+      rowL[tid] = sl;
+      rowR[tid] = sr;
+    }
+    __syncthreads();
+    // A merge's statistics from its five sums: A, B, d (double-double) and,
+    // for the rounding estimate, sl = sum_{i in L} w_i^2 G_ii and sr over R.
+    auto finish = [&](int mi, DD a2, DD b2, DD ab, double sl, double sr) {
+      const Merge mg = ms[mi];
+      const double A = a2.hi, B = b2.hi, dd = ab.hi;  // normalised: hi is the rounded sum
+      const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
+      const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
+      cab[mi][0] = ca;
+      cab[mi][1] = cb;
+      if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
+        // The rounding errors of separate chunk sums are independent, so a
+        // quadratic form over an operand with weights w errs by about
+        // gram_err S, S = sum w_i^2 G_ii (the norm the operand would have if
+        // its parts were orthogonal): S <= A for parallel parts, S ~ A for
+        // orthogonal ones, S >> A only under cancellation.  (The worst case,
+        // with every error aligned, replaces S by (sum |w_i| sqrt(G_ii))^2,
+        // which exceeds A for any orthogonal parts and would flag ordinary
+        // data.)  c = 1 - d / (2A) then moves by about
+        // (|d err| + |d| |A err| / A) / (2A).  An operand whose norm the
+        // estimate cannot tell from zero is flagged too.
+        const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
+        bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
+        if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
+        if (B > eB) bad = bad || (ed + fabs(dd) * eB / B) / (2.0 * B) > kRefineTol * fmax(1.0, fabs(cb));
+        if (bad) unsure = 1;
+      }
+      if (!outputs) return;
+      const int64_t at = (int64_t)mg.node * a.nseg + s;
+      a.coeffs[at * 2] = ca;
+      a.coeffs[at * 2 + 1] = cb;
+      a.stats[at * 3] = dd;
+      a.stats[at * 3 + 1] = A;
+      a.stats[at * 3 + 2] = B;
+    };
+    // Merges over at most kSerialMerge operands: one thread each, terms in
+    // operand order.  Wider ones (the top of a 64-operand tree, a chain of
+    // more than 16): one wave each, a lane per operand, the terms added by a
+    // butterfly across the wave, so that a 64-operand chain is not 63 serial
+    // sums of up to 63 terms.
+    if (tid < m1 - m0 && ms[m0 + tid].rhi - ms[m0 + tid].llo <= kSerialMerge) {
+      const Merge mg = ms[m0 + tid];
+      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
+      DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
+      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_mul(rowL[i], w[i]));
+      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_mul(rowR[i], w[i]));
+      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_mul(rowR[i], w[i]));
+      double sl = 0.0, sr = 0.0;
+      for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
+      for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
+      finish(m0 + tid, a2, b2, ab, sl, sr);
+    }
+    {
+      const int q = tid >> 6, lane = tid & 63;
+      int nth = 0;  // wide merges of this batch seen so far
+      for (int mi = m0; mi < m1; ++mi) {
+        const Merge mg = ms[mi];
+        if (mg.rhi - mg.llo <= kSerialMerge) continue;
+        if ((nth++ & (kTreeWaves - 1)) != q) continue;  // wave-uniform
+        const int i0 = mg.llo + lane;  // a wide merge spans at most 64 operands
+        const bool inL = i0 < mg.lhi, inR = i0 >= mg.lhi && i0 < mg.rhi;
+        const int i = (inL || inR) ? i0 : mg.llo;  // lanes past the merge read a valid entry, unused
+        const DD zero{0.0, 0.0};
+        DD a2 = inL ? dd_mul(rowL[i], w[i]) : zero;
+        DD b2 = inR ? dd_mul(rowR[i], w[i]) : zero;
+        DD ab = inL ? dd_mul(rowR[i], w[i]) : zero;
+        const double wg = (inL || inR) ? w[i].hi * w[i].hi * G[gram_index(n, i, i)] : 0.0;
+        double sl = inL ? wg : 0.0, sr = inR ? wg : 0.0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          a2 = dd_add(a2, DD{__shfl_xor(a2.hi, off), __shfl_xor(a2.lo, off)});
+          b2 = dd_add(b2, DD{__shfl_xor(b2.hi, off), __shfl_xor(b2.lo, off)});
+          ab = dd_add(ab, DD{__shfl_xor(ab.hi, off), __shfl_xor(ab.lo, off)});
+          sl += __shfl_xor(sl, off);
+          sr += __shfl_xor(sr, off);
+        }
+        if (lane == 0) finish(mi, a2, b2, ab, sl, sr);
+      }
+    }
+    __syncthreads();
+    if (mine >= 0) w[tid] = dd_scale(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
+    __syncthreads();
+    m0 = m1;
+  }
+  if (tid < MO) wf[tid] = w[tid].hi;  // normalised: hi is the rounded value
+  __syncthreads();
+  if (outputs && tid == 0) {
+    // sum of |g_k|^2 over the block's input operands, in operand order
+    double leaf = 0.0;
+    for (int k = 0; k < d.nb; ++k)
+      if ((d.leafmask >> k) & 1u) leaf += G[gram_index(n, k, k)];
+    a.leafnorm[(int64_t)d.wrow * a.nseg + s] = leaf;
+    if (d.root && a.ortho != nullptr) {
+      // orthogonality of the segment's gradients: |result|^2 over the sum
+      // of their squared norms (lower blocks finished in earlier launches)
+      double total = 0.0;
+      for (int r = 0; r < a.nblocks_total; ++r)
+        total += (r == d.wrow) ? leaf : a.leafnorm[(int64_t)r * a.nseg + s];
+      const double out2 = quad_form(G, n, wf, 0, d.nb, 0, d.nb);
+      a.ortho[s] = (total == 0.0) ? __builtin_nan("") : out2 / total;
+    }
+  }
+  __syncthreads();
+  const int64_t wat = ((int64_t)d.wrow * a.nseg + s) * kMaxOps;
+  if (outputs && tid < MO) {
+    a.weights[wat + tid] = wf[tid];
+    a.weights_lo[wat + tid] = w[tid].lo;
+  }
+  __shared__ uint32_t fl;
+  if (!kRefine) {
+    // Bit 1: the block's result is summed in double-double.  Where it is far
+    // smaller than its weighted parts, sum_k w_k x_k in fp64 would lose the
+    // ratio of the two to rounding, and a later stage could amplify that loss
+    // again; every pair flagged for recomputation (bit 0) is summed so too.
+    __shared__ double rows_w[MO];
+    if (tid < d.nb) {
+      double r = 0.0;
+      for (int k = 0; k < d.nb; ++k) r += wf[k] * gram_at(G, n, tid, k);
+      rows_w[tid] = r;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double out2 = 0.0, parts = 0.0;
+      for (int k = 0; k < d.nb; ++k) {
+        out2 += wf[k] * rows_w[k];
+        parts += wf[k] * wf[k] * G[gram_index(n, k, k)];
+      }
+      uint32_t f = unsure ? 3u : 0u;
+      if (parts > 0.0 && !(out2 > kSumCancel * parts)) f |= 2u;
+      fl = f;
+      if (outputs && a.flags != nullptr) a.flags[(int64_t)d.wrow * a.nseg + s] = f;
+    }
+    __syncthreads();
+    return fl;
+  }
+  return 3u;  // a refined pair is summed in double-double
+}
+
 // kWide: the launch holds a 64-operand block (its Gram matrix takes 2080
 // entries of LDS; the other variant, 528, keeps more workgroups per CU).
 template <bool kRefine, bool kWide>
@@ -1100,176 +1290,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     __syncthreads();  // every wave sum is consumed
     for (int e = tid; e < ne; e += kBlock) Glo[e] = a.partials_lo[d.poff + (int64_t)t0 * ne + e];
   }
-  if (tid < MO) w[tid] = DD{1.0, 0.0};
-  __syncthreads();
-  // entries already exact (double-double) are not flagged again
-  const double gram_err = exact_g ? 0.0 : d.gram_err;
-  // Merges run level by level: merges of a block are stored children
-  // before parents, and the merges of one level cover disjoint operand
-  // ranges (a batch ends where a merge starts left of the previous one).
-  // For merge (L, R), thread i in L u R forms its row sums
-  // rowL_i = sum_{k in L} w_k G(i,k) and rowR_i = sum_{k in R} w_k G(i,k) in
-  // k order; one thread per merge then forms A = sum_{i in L} w_i rowL_i,
-  // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order,
-  // all in double-double, and rounds them to fp64.  That is the same
-  // arithmetic, term for term, as a serial evaluation.
-  __shared__ DD rowL[MO], rowR[MO];
-  __shared__ double cab[MO][2];
-  __shared__ Merge ms[MO];
-  __shared__ int unsure;  // some coefficient may be off by more than kRefineTol
-  if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
-  if (tid == 0) unsure = 0;
-  __syncthreads();
-  for (int m0 = 0; m0 < d.nmerges;) {
-    int m1 = m0 + 1;
-    while (m1 < d.nmerges && ms[m1].llo >= ms[m1 - 1].rhi) ++m1;
-    // the merge of this batch that holds operand tid, if any
-    int mine = -1;
-    for (int m = m0; m < m1; ++m)
-      if (tid >= ms[m].llo && tid < ms[m].rhi) mine = m;
-    if (mine >= 0) {
-      const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
-      DD sl{0.0, 0.0}, sr{0.0, 0.0};
-      if (exact_g) {
-        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
-        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
-      } else {
-        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_scale(w[k], gram_at(G, n, tid, k)));
-        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_scale(w[k], gram_at(G, n, tid, k)));
-      }
-      rowL[tid] = sl;
-      rowR[tid] = sr;
-    }
-    __syncthreads();
-    // A merge's statistics from its five sums: A, B, d (double-double) and,
-    // for the rounding estimate, sl = sum_{i in L} w_i^2 G_ii and sr over R.
-    auto finish = [&](int mi, DD a2, DD b2, DD ab, double sl, double sr) {
-      const Merge mg = ms[mi];
-      const double A = a2.hi, B = b2.hi, dd = ab.hi;  // normalised: hi is the rounded sum
-      const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
-      const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
-      cab[mi][0] = ca;
-      cab[mi][1] = cb;
-      if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
-        // The rounding errors of separate chunk sums are independent, so a
-        // quadratic form over an operand with weights w errs by about
-        // gram_err S, S = sum w_i^2 G_ii (the norm the operand would have if
-        // its parts were orthogonal): S <= A for parallel parts, S ~ A for
-        // orthogonal ones, S >> A only under cancellation.  (The worst case,
-        // with every error aligned, replaces S by (sum |w_i| sqrt(G_ii))^2,
-        // which exceeds A for any orthogonal parts and would flag ordinary
-        // data.)  c = 1 - d / (2A) then moves by about
-        // (|d err| + |d| |A err| / A) / (2A).  An operand whose norm the
-        // estimate cannot tell from zero is flagged too.
-        const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
-        bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
-        if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
-        if (B > eB) bad = bad || (ed + fabs(dd) * eB / B) / (2.0 * B) > kRefineTol * fmax(1.0, fabs(cb));
-        if (bad) unsure = 1;
-      }
-      const int64_t at = (int64_t)mg.node * a.nseg + s;
-      a.coeffs[at * 2] = ca;
-      a.coeffs[at * 2 + 1] = cb;
-      a.stats[at * 3] = dd;
-      a.stats[at * 3 + 1] = A;
-      a.stats[at * 3 + 2] = B;
-    };
-    // Merges over at most kSerialMerge operands: one thread each, terms in
-    // operand order.  Wider ones (the top of a 64-operand tree, a chain of
-    // more than 16): one wave each, a lane per operand, the terms added by a
-    // butterfly across the wave, so that a 64-operand chain is not 63 serial
-    // sums of up to 63 terms.
-    if (tid < m1 - m0 && ms[m0 + tid].rhi - ms[m0 + tid].llo <= kSerialMerge) {
-      const Merge mg = ms[m0 + tid];
-      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
-      DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
-      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_mul(rowL[i], w[i]));
-      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_mul(rowR[i], w[i]));
-      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_mul(rowR[i], w[i]));
-      double sl = 0.0, sr = 0.0;
-      for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
-      for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
-      finish(m0 + tid, a2, b2, ab, sl, sr);
-    }
-    {
-      const int q = tid >> 6, lane = tid & 63;
-      int nth = 0;  // wide merges of this batch seen so far
-      for (int mi = m0; mi < m1; ++mi) {
-        const Merge mg = ms[mi];
-        if (mg.rhi - mg.llo <= kSerialMerge) continue;
-        if ((nth++ & (kTreeWaves - 1)) != q) continue;  // wave-uniform
-        const int i0 = mg.llo + lane;  // a wide merge spans at most 64 operands
-        const bool inL = i0 < mg.lhi, inR = i0 >= mg.lhi && i0 < mg.rhi;
-        const int i = (inL || inR) ? i0 : mg.llo;  // lanes past the merge read a valid entry, unused
-        const DD zero{0.0, 0.0};
-        DD a2 = inL ? dd_mul(rowL[i], w[i]) : zero;
-        DD b2 = inR ? dd_mul(rowR[i], w[i]) : zero;
-        DD ab = inL ? dd_mul(rowR[i], w[i]) : zero;
-        const double wg = (inL || inR) ? w[i].hi * w[i].hi * G[gram_index(n, i, i)] : 0.0;
-        double sl = inL ? wg : 0.0, sr = inR ? wg : 0.0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          a2 = dd_add(a2, DD{__shfl_xor(a2.hi, off), __shfl_xor(a2.lo, off)});
-          b2 = dd_add(b2, DD{__shfl_xor(b2.hi, off), __shfl_xor(b2.lo, off)});
-          ab = dd_add(ab, DD{__shfl_xor(ab.hi, off), __shfl_xor(ab.lo, off)});
-          sl += __shfl_xor(sl, off);
-          sr += __shfl_xor(sr, off);
-        }
-        if (lane == 0) finish(mi, a2, b2, ab, sl, sr);
-      }
-    }
-    __syncthreads();
-    if (mine >= 0) w[tid] = dd_scale(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
-    __syncthreads();
-    m0 = m1;
-  }
-  if (tid < MO) wf[tid] = w[tid].hi;  // normalised: hi is the rounded value
-  __syncthreads();
-  if (tid == 0) {
-    // sum of |g_k|^2 over the block's input operands, in operand order
-    double leaf = 0.0;
-    for (int k = 0; k < d.nb; ++k)
-      if ((d.leafmask >> k) & 1u) leaf += G[gram_index(n, k, k)];
-    a.leafnorm[(int64_t)d.wrow * a.nseg + s] = leaf;
-    if (d.root && a.ortho != nullptr) {
-      // orthogonality of the segment's gradients: |result|^2 over the sum
-      // of their squared norms (lower blocks finished in earlier launches)
-      double total = 0.0;
-      for (int r = 0; r < a.nblocks_total; ++r)
-        total += (r == d.wrow) ? leaf : a.leafnorm[(int64_t)r * a.nseg + s];
-      const double out2 = quad_form(G, n, wf, 0, d.nb, 0, d.nb);
-      a.ortho[s] = (total == 0.0) ? __builtin_nan("") : out2 / total;
-    }
-  }
-  __syncthreads();
-  const int64_t wat = ((int64_t)d.wrow * a.nseg + s) * kMaxOps;
-  if (tid < MO) {
-    a.weights[wat + tid] = wf[tid];
-    a.weights_lo[wat + tid] = w[tid].lo;
-  }
-  if (!kRefine && a.flags != nullptr) {
-    // Bit 1: the block's result is summed in double-double.  Where it is far
-    // smaller than its weighted parts, sum_k w_k x_k in fp64 would lose the
-    // ratio of the two to rounding, and a later stage could amplify that loss
-    // again; every pair flagged for recomputation (bit 0) is summed so too.
-    __shared__ double rows_w[MO];
-    if (tid < d.nb) {
-      double r = 0.0;
-      for (int k = 0; k < d.nb; ++k) r += wf[k] * gram_at(G, n, tid, k);
-      rows_w[tid] = r;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double out2 = 0.0, parts = 0.0;
-      for (int k = 0; k < d.nb; ++k) {
-        out2 += wf[k] * rows_w[k];
-        parts += wf[k] * wf[k] * G[gram_index(n, k, k)];
-      }
-      uint32_t f = unsure ? 3u : 0u;
-      if (parts > 0.0 && !(out2 > kSumCancel * parts)) f |= 2u;
-      a.flags[(int64_t)d.wrow * a.nseg + s] = f;
-    }
-  }
+  walk_block<kRefine, MO>(a, d, s, G, Glo, exact_g, w, wf, true);
 }
 
 // ----------------------------------------------------------------- weighted sum
@@ -1306,30 +1327,29 @@ __device__ void wsum_exact_range(const WsumArgs& args, int j, int64_t lo, int64_
 // masked to zero, so the loop has no branches and every load of a step is in
 // flight at once.  First stage: every operand is an input of type TIn; the
 // result is the output (TOut = TIn) or an fp64 slot (TOut = double).
-template <typename TIn, int NB, typename TOut>
-__global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
-  constexpr int kSplit = wsum_split(sizeof(TIn));
-  const int tile_id = blockIdx.x / kSplit;
-  const int part = blockIdx.x % kSplit;
-  const int j = blockIdx.y;
-  const Tile tile = args.tiles[tile_id];
+// Part `part` of kSplit of a tile: the p-th share of the aligned body; the
+// unaligned head goes with part 0 and the tail with the last part.
+__device__ __forceinline__ TileSpan tile_part(const Tile& tile, int part, int kSplit) {
   TileSpan sp = span_of(tile);
-  {
-    // part p takes the p-th share of the aligned body; the unaligned head
-    // goes with part 0 and the tail with the last part
-    const int64_t groups = (sp.body_hi - sp.body_lo) / kGroup;
-    const int64_t per = (groups + kSplit - 1) / kSplit * kGroup;
-    const int64_t b0 = min(sp.body_lo + part * per, sp.body_hi);
-    const int64_t b1 = min(b0 + per, sp.body_hi);
-    if (part > 0) sp.lo = b0;
-    if (part < kSplit - 1) sp.hi = b1;
-    sp.body_lo = b0;
-    sp.body_hi = b1;
-  }
-  const int64_t wat = ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
-  const double* wrow = args.weights + wat;
-  if (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] & 2u) {  // workgroup-uniform
-    wsum_exact_range<TIn, TIn, NB, TOut>(args, j, sp.lo, sp.hi, wrow, args.weights_lo + wat);
+  const int64_t groups = (sp.body_hi - sp.body_lo) / kGroup;
+  const int64_t per = (groups + kSplit - 1) / kSplit * kGroup;
+  const int64_t b0 = min(sp.body_lo + part * per, sp.body_hi);
+  const int64_t b1 = min(b0 + per, sp.body_hi);
+  if (part > 0) sp.lo = b0;
+  if (part < kSplit - 1) sp.hi = b1;
+  sp.body_lo = b0;
+  sp.body_hi = b1;
+  return sp;
+}
+
+// The weighted sum of job j over the range sp, with weights wrow (and their
+// double-double low parts wlo, used where dd is set).  Called by every
+// thread of the workgroup.
+template <typename TIn, int NB, typename TOut>
+__device__ __forceinline__ void wsum_tile_range(const WsumArgs& args, int j, const TileSpan& sp, const double* wrow,
+                                                const double* wlo, bool dd) {
+  if (dd) {  // workgroup-uniform
+    wsum_exact_range<TIn, TIn, NB, TOut>(args, j, sp.lo, sp.hi, wrow, wlo);
     return;
   }
   const TIn* x0 = static_cast<const TIn*>(args.x[j * op_stride(NB)]);
@@ -1383,6 +1403,18 @@ __global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
     Elem<TOut>::store8(y + g, r);
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
+}
+
+template <typename TIn, int NB, typename TOut>
+__global__ __launch_bounds__(kBlock) void wsum_kernel(WsumArgs args) {
+  constexpr int kSplit = wsum_split(sizeof(TIn));
+  const int tile_id = blockIdx.x / kSplit;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const TileSpan sp = tile_part(tile, blockIdx.x % kSplit, kSplit);
+  const int64_t wat = ((int64_t)args.wrow[j] * args.nseg + tile.seg) * kMaxOps;
+  wsum_tile_range<TIn, NB, TOut>(args, j, sp, args.weights + wat, args.weights_lo + wat,
+                                 (args.flags[(int64_t)args.wrow[j] * args.nseg + tile.seg] & 2u) != 0);
 }
 
 // Weighted sum of a 64-operand block (16-bit inputs of type T, one stage, so
@@ -1577,6 +1609,126 @@ __global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
     for (int e = 0; e < kRun; ++e) Elem<TOut>::store1(y + g + e, Elem<TOut>::round(acc[e], &unused));
   }
   if (tid < sp.hi - sp.body_hi) one(sp.body_hi + tid);
+}
+
+// ----------------------------------------------------------------- small combines: walk and weighted sum in one launch
+
+// The double-double Gram matrix of rows [lo, hi) of the block's operands
+// (table; NULL: zero), every entry the row-order sum of exact products, high
+// parts into G and low parts into Glo; the rows pass through sh
+// (NB x kFusedChunk doubles).  Called by every thread of the workgroup.
+constexpr int kFusedChunk = 64;
+
+template <typename TIn, int NB>
+__device__ void segment_exact_gram(const void* const* table, int64_t lo, int64_t hi, double* G, double* Glo,
+                                   double* sh) {
+  constexpr int NE = gram_entries(NB);
+  constexpr int EPT = (NE + kBlock - 1) / kBlock;  // entries per thread
+  int ei[EPT], ek[EPT];
+  DD acc[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const int e = threadIdx.x + q * kBlock;
+    int i = 0, rem = e < NE ? e : 0;
+    while (rem >= NB - i) {
+      rem -= NB - i;
+      ++i;
+    }
+    ei[q] = i;
+    ek[q] = i + rem;
+    acc[q] = DD{0.0, 0.0};
+  }
+  for (int64_t c0 = lo; c0 < hi; c0 += kFusedChunk) {
+    const int n = (int)min<int64_t>(kFusedChunk, hi - c0);
+    if (c0 > lo) __syncthreads();  // the previous chunk is consumed
+    for (int idx = threadIdx.x; idx < NB * n; idx += kBlock) {
+      const int k = idx / n, r = idx - k * n;
+      const void* x = table[k];
+      sh[k * kFusedChunk + r] = x != nullptr ? widen_any<TIn>(x, c0 + r) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      if (threadIdx.x + q * kBlock >= NE) continue;
+      const double* x = sh + ei[q] * kFusedChunk;
+      const double* y = sh + ek[q] * kFusedChunk;
+      DD sum = acc[q];
+      for (int r = 0; r < n; ++r) sum = dd_add(sum, dd_prod(x[r], y[r]));
+      acc[q] = sum;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    if (threadIdx.x + q * kBlock >= NE) continue;
+    G[threadIdx.x + q * kBlock] = acc[q].hi;
+    Glo[threadIdx.x + q * kBlock] = acc[q].lo;
+  }
+}
+
+// A one-stage combine whose segments have few tiles, after its Gram pass,
+// in one launch instead of four (walk, exact recomputation, second walk,
+// weighted sum).  Each workgroup of the weighted sum first walks its own
+// segment's block on the segment's tile partials, summed as tree_kernel sums
+// them, so every workgroup of a segment takes the same walk and the same
+// weights; the segment's first workgroup writes the tables.  A pair the walk
+// flags is recomputed exactly by each of its workgroups over the whole
+// segment (rare, and bounded by the plan's limits on these combines) and
+// walked again.
+template <typename TIn, int NB>
+__global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa) {
+  constexpr int kSplit = wsum_split(sizeof(TIn));
+  constexpr int MO = kArgOps;
+  static_assert(NB <= MO, "blocks of at most 32 operands");
+  static_assert(kTreeWaves * kPartStride >= NB * kFusedChunk, "the exact rows fit the wave sums");
+  __shared__ double part[kTreeWaves * kPartStride];
+  __shared__ double G[gram_entries(MO)];
+  __shared__ double glo[gram_entries(MO)];
+  __shared__ DD w[MO];
+  __shared__ double wf[MO];
+  __shared__ double wlo[MO];
+  const int tile_id = blockIdx.x / kSplit;
+  const int part_id = blockIdx.x % kSplit;
+  const Tile tile = wa.tiles[tile_id];
+  const int s = tile.seg;
+  const BlockDesc d = ta.descs[ta.desc0];
+  const int ne = gram_entries(d.nbt);
+  const int tid = threadIdx.x;
+  const int t0 = ta.seg_tile[s], t1 = ta.seg_tile[s + 1];
+  {
+    // the tile partials: for Q = kBlock / ne (at least 1), thread (q, e)
+    // adds tiles t0 + q, t0 + q + Q, ... of entry e in order, and the Q sums
+    // of each entry are added in q order; every thread has few tiles to read
+    const int Q = max(1, kBlock / ne);
+    for (int x = tid; x < Q * ne; x += kBlock) {
+      const int q = x / ne, e = x - q * ne;
+      const double* p = ta.partials + d.poff + e;
+      double sum = 0.0;
+      for (int t = t0 + q; t < t1; t += Q) sum += p[(int64_t)t * ne];
+      part[x] = sum;
+    }
+    __syncthreads();
+    for (int e = tid; e < ne; e += kBlock) {
+      double sum = part[e];
+      for (int q = 1; q < Q; ++q) sum += part[q * ne + e];
+      G[e] = sum;
+    }
+  }
+  const uint64_t all_inputs = (uint64_t(1) << d.nb) - 1u;
+  const bool exact_g = ta.partials_lo != nullptr && t1 - t0 == 1 && tile.len <= kExactRows && ta.lo_inputs &&
+                       d.leafmask == all_inputs;
+  if (exact_g)
+    for (int e = tid; e < ne; e += kBlock) glo[e] = ta.partials_lo[d.poff + (int64_t)t0 * ne + e];
+  const bool first = tile_id == t0 && part_id == 0;
+  uint32_t f = walk_block<false, MO>(ta, d, s, G, glo, exact_g, w, wf, first);
+  if (f & 1u) {  // workgroup-uniform
+    const Tile last = ta.tiles[t1 - 1];
+    segment_exact_gram<TIn, NB>(wa.x, ta.tiles[t0].start, last.start + last.len, G, glo, part);
+    __syncthreads();
+    f = walk_block<true, MO>(ta, d, s, G, glo, true, w, wf, first);
+  }
+  if (tid < MO) wlo[tid] = w[tid].lo;
+  __syncthreads();
+  wsum_tile_range<TIn, NB, TIn>(wa, 0, tile_part(tile, part_id, kSplit), wf, wlo, (f & 2u) != 0);
 }
 
 // ----------------------------------------------------------------- plain sum
@@ -1865,6 +2017,27 @@ struct RunExactFirst {
   }
 };
 
+template <typename TIn>
+struct RunFused {
+  static hipError_t run(int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st) {
+    const dim3 grid((unsigned)ntiles * wsum_split(sizeof(TIn)));
+    switch (nbt) {
+      case 2: hipLaunchKernelGGL((fused_kernel<TIn, 2>), grid, dim3(kBlock), 0, st, t, w); break;
+      case 4: hipLaunchKernelGGL((fused_kernel<TIn, 4>), grid, dim3(kBlock), 0, st, t, w); break;
+      case 8: hipLaunchKernelGGL((fused_kernel<TIn, 8>), grid, dim3(kBlock), 0, st, t, w); break;
+      case 16: hipLaunchKernelGGL((fused_kernel<TIn, 16>), grid, dim3(kBlock), 0, st, t, w); break;
+      case 32:
+        if constexpr (sizeof(TIn) == 2) {  // 32-operand blocks exist only over 16-bit inputs
+          hipLaunchKernelGGL((fused_kernel<TIn, 32>), grid, dim3(kBlock), 0, st, t, w);
+          break;
+        }
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+};
+
 }  // namespace
 
 hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
@@ -1892,6 +2065,10 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((tree_kernel<false, false>), grid, dim3(kBlock), 0, st, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fused(DType in_t, int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st) {
+  return by_type<RunFused>(in_t, nbt, t, w, ntiles, st);
 }
 
 hipError_t launch_tile_groups(const TreeArgs& a, int ntiles, hipStream_t st) {

@@ -51,6 +51,15 @@ constexpr int max_jobs(int nbt) { return kArgOps * kMaxJobs / op_stride(nbt); }
 // adds up groups of kTileGroup consecutive tiles, in place into each group's
 // first tile, so that the walk reads one partial per group.
 constexpr int kTileGroup = 16;
+// A one-stage plan of one block of at most 32 operands, with at most
+// kFusedMaxRows elements and no empty segment, runs its walk and weighted
+// sum in one launch after the Gram pass: every weighted-sum workgroup walks
+// its own segment, so the small, launch-bound combines take two launches
+// instead of five.  Each workgroup then reads its segment's tile partials,
+// so the plan must keep sum_s (workgroups of s) x (tiles of s) x (Gram
+// entries) within kFusedMaxReads.
+constexpr int64_t kFusedMaxRows = int64_t(1) << 22;
+constexpr int64_t kFusedMaxReads = int64_t(1) << 24;
 // Tiles of at most kExactRows rows of 16-bit inputs are short: their Gram
 // matrices are summed exactly (double-double) instead of on the matrix cores,
 // since short segments are where merges nearly cancel by chance.
@@ -151,6 +160,7 @@ struct Plan {
   std::vector<Stage> stages;
   std::vector<BlockDesc> descs;
   std::vector<Merge> merges;
+  bool fused = false;             // see kFusedMaxRows
   int nslots = 0;                 // fp64 vectors of N elements
   int nblocks = 0;                // rows of the leaf-weight table
   size_t partial_doubles = 0;     // largest per-stage Gram partials footprint

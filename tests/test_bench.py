@@ -69,12 +69,11 @@ def test_bench_json_line(gpu):
     assert par["segments"] >= 1 and par["tol_rel_l2"] == 1e-5 and par["tol_coeff"] == 1e-6
     assert par["rel_l2"] <= par["tol_rel_l2"] and par["max_coeff_err"] <= par["tol_coeff"] and par["pass"] is True
 
-    # one combine is five launches: gram, the tree walk, the exact
-    # recomputation of flagged tiles, the walk again over flagged pairs (the
-    # last two return at once when nothing is flagged), weighted sum
-    assert set(rec["kernels"]) == {"gram", "tree", "exact", "wsum"}
+    # this small one-stage combine is two launches: gram, then the walk
+    # (with any exact recomputation) and the weighted sum in one
+    assert set(rec["kernels"]) == {"gram", "wsum"}
     launches = {k: v["launches"] for k, v in rec["kernels"].items()}
-    assert launches == {"gram": 3, "tree": 6, "exact": 3, "wsum": 3}, launches
+    assert launches == {"gram": 3, "wsum": 3}, launches
     for key in ("mean", "median", "min", "max"):
         assert rec["step_ms"][key] > 0 and rec["step_ms_without_launch_events"][key] > 0
     assert rec["step_ms"]["min"] <= rec["step_ms"]["median"] <= rec["step_ms"]["max"]
