@@ -491,6 +491,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             a.partials_lo = partials_lo;
             a.flags = flags;
             a.nseg = p.nseg;
+            a.short_tiles = p.tile_rows <= kMinTile;
             log_launch("gram", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kGram, in_bytes + out_bytes, st);
             e = launch_gram(in_t, p.dtype, nbt, a, ntiles, n, st);

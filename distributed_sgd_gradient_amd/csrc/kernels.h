@@ -29,6 +29,7 @@ struct GramArgs {
   const uint32_t* flags;
   int32_t wrow[kMaxJobs];
   int nseg;
+  int short_tiles;  // every tile has at most kMinTile rows
 };
 static_assert(sizeof(GramArgs) <= 4096, "kernel arguments fit 4 KB");
 

@@ -341,10 +341,12 @@ __device__ __forceinline__ void f64_gram_reduce(double (*red)[64 * 4], const f64
   }
 }
 
-template <int NB>
+// U: 16-row chunks per wave per iteration.  Plans of short tiles (at most
+// kMinTile rows) take fewer chunks for blocks of 2 or 4 operands, so that
+// the four waves share a tile's rows instead of one wave taking them all.
+template <int NB, int U = kF64Unroll>
 __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
   constexpr int SETS = 16 / NB;          // row sets packed into the 16 operand lanes
-  constexpr int U = kF64Unroll;
   constexpr int RC = 16 * SETS;          // rows per chunk
   constexpr int R = RC * U;              // rows per wave per iteration
   constexpr int NE = gram_entries(NB);
@@ -957,23 +959,10 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
 __device__ __forceinline__ double mul_rn(double a, double b) { return __dmul_rn(a, b); }
 __device__ __forceinline__ double add_rn(double a, double b) { return __dadd_rn(a, b); }
 
-__device__ __forceinline__ double gram_at(const double* G, int n, int i, int k) {
-  return i <= k ? G[gram_index(n, i, k)] : G[gram_index(n, k, i)];
-}
-
-// sum_{i in [a0,a1)} w_i * (sum_{k in [b0,b1)} w_k G(i,k))
-__device__ double quad_form(const double* G, int n, const double* w, int a0, int a1, int b0, int b1) {
-  double total = 0.0;
-  for (int i = a0; i < a1; ++i) {
-    double row = 0.0;
-    for (int k = b0; k < b1; ++k) row = add_rn(row, mul_rn(w[k], gram_at(G, n, i, k)));
-    total = add_rn(total, mul_rn(w[i], row));
-  }
-  return total;
-}
+// Packed index of entry (i, k) of a symmetric n x n matrix, either order.
+__device__ __forceinline__ int sym_index(int n, int i, int k) { return i <= k ? gram_index(n, i, k) : gram_index(n, k, i); }
 
 constexpr int kTreeWaves = kBlock / 64;
-constexpr int kSerialMerge = 16;  // widest merge whose sums one thread adds in operand order
 // Per-wave tile sums of blocks of up to 32 operands (528 Gram entries); the
 // 2080 entries of a 64-operand block fit the same space.
 constexpr int kPartStride = gram_entries(kArgOps);
@@ -999,6 +988,199 @@ __global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
   }
 }
 
+// The merge walk of block d over segment s.  On entry N holds the block's
+// Gram matrix (packed upper triangle, nbt x nbt) and, where exact_g, Nlo its
+// double-double low parts (otherwise the walk zeroes Nlo).  Every node of
+// the block is a linear combination of its operands, and a merge P = ca L +
+// cb R of two current nodes changes the dot products with P linearly:
+// P.Y = ca L.Y + cb R.Y for every other current node Y, and
+// |P|^2 = ca (ca A + cb d) + cb (ca d + cb B).  So the walk keeps the dot
+// products of the current nodes, in double-double, in N itself (node X is
+// stored at the index of its first operand): a merge reads A = |L|^2,
+// B = |R|^2 and d = L.R directly, and a level's updates take a constant
+// number of steps whatever the block size.  Products of the fp64
+// coefficients with double-double entries are exact up to the double-double
+// rounding, so a node that nearly cancels keeps about 2^-104 of its terms'
+// size, and nodes that mirror each other cancel exactly, as the plain
+// definition does (rounding is symmetric under negation).
+// Returns the block's flags (see TreeArgs) to every thread, and leaves the
+// operands' weights, products of the coefficients above them in
+// double-double, in w (and rounded, in wf).  Where outputs is set, the
+// coefficients, statistics, weights, input norms, orthogonality and flags
+// are also written out.  Called by every thread of the workgroup; ms (the
+// block's merges, loaded by the caller before a barrier), N, Nlo, w and wf
+// are in LDS, and N and Nlo are overwritten.
+template <bool kRefine, int MO>
+__device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, const Merge* ms, double* N, double* Nlo,
+                               bool exact_g, DD* w, double* wf, bool outputs) {
+  const int tid = threadIdx.x;
+  const int n = d.nbt;
+  const int nm = d.nmerges;
+  // the updates of one level: at most MO / 2 merges times MO nodes
+  constexpr int kPairs = (MO / 2 * MO + kBlock - 1) / kBlock;
+  __shared__ double cab[MO][2];  // coefficients of each merge
+  // per node (operand index of its first operand): sum_i w_i^2 G_ii over its
+  // operands, the scale of its Gram entries' rounding
+  __shared__ double S[MO];
+  __shared__ double diag[MO];    // the Gram diagonal: the operands' squared norms
+  __shared__ int own[MO];        // the last merge that took in operand i
+  __shared__ int alive[MO];      // node i is current (not merged into another)
+  __shared__ int unsure;         // some coefficient may be off by more than kRefineTol
+  __shared__ uint32_t fl;
+  // entries already exact (double-double) are not flagged again
+  const double gram_err = exact_g ? 0.0 : d.gram_err;
+  __syncthreads();  // N (and Nlo) are complete
+  if (!exact_g)
+    for (int e = tid; e < gram_entries(n); e += kBlock) Nlo[e] = 0.0;
+  if (tid < MO) {
+    const double g = tid < n ? N[gram_index(n, tid, tid)] : 0.0;
+    diag[tid] = g;
+    S[tid] = g;
+    own[tid] = -1;
+    alive[tid] = tid < d.nb;
+  }
+  if (tid == 0) unsure = 0;
+  __syncthreads();
+  // Merges are stored children before parents; a level (a batch) ends where
+  // a merge overlaps the one before it.  Bit m: merge m starts a batch.
+  const int lane = tid & 63;
+  const uint64_t starts = __ballot(lane < nm && (lane == 0 || ms[lane].llo < ms[lane - 1].rhi));
+  DD wi{1.0, 0.0};  // weight of operand tid
+  for (int m0 = 0; m0 < nm;) {
+    const uint64_t later = starts & ~((uint64_t(2) << m0) - 1u);
+    const int m1 = later != 0 ? (int)__builtin_ctzll(later) : nm;
+    // the statistics and coefficients, one thread per merge
+    if (tid < m1 - m0) {
+      const int mi = m0 + tid;
+      const Merge mg = ms[mi];
+      const int L = mg.llo, R = mg.lhi;
+      const int eLL = gram_index(n, L, L), eRR = gram_index(n, R, R), eLR = gram_index(n, L, R);
+      const double A = N[eLL], B = N[eRR], dd = N[eLR];  // double-double: hi is the rounded value
+      const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
+      const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
+      cab[mi][0] = ca;
+      cab[mi][1] = cb;
+      const double sl = S[L], sr = S[R];
+      if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
+        // The rounding errors of separate chunk sums are independent, so a
+        // quadratic form over a node errs by about gram_err S (S: the norm
+        // the node would have if its operands were orthogonal): S <= A for
+        // parallel parts, S ~ A for orthogonal ones, S >> A only under
+        // cancellation.  (The worst case, with every error aligned, replaces
+        // S by (sum |w_i| sqrt(G_ii))^2, which exceeds A for any orthogonal
+        // parts and would flag ordinary data.)  c = 1 - d / (2A) then moves
+        // by about (|d err| + |d| |A err| / A) / (2A).  A node whose norm the
+        // estimate cannot tell from zero is flagged too.
+        // (Compared multiplied out by A^2 and B^2, both positive there.)
+        const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
+        bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
+        if (A > eA) bad = bad || ed * A + fabs(dd) * eA > 2.0 * kRefineTol * fmax(1.0, fabs(ca)) * A * A;
+        if (B > eB) bad = bad || ed * B + fabs(dd) * eB > 2.0 * kRefineTol * fmax(1.0, fabs(cb)) * B * B;
+        if (bad) unsure = 1;
+      }
+      S[L] = ca * ca * sl + cb * cb * sr;
+      alive[R] = 0;
+      for (int i = L; i < mg.rhi; ++i) own[i] = mi;
+      if (outputs) {
+        const int64_t at = (int64_t)mg.node * a.nseg + s;
+        a.coeffs[at * 2] = ca;
+        a.coeffs[at * 2 + 1] = cb;
+        a.stats[at * 3] = dd;
+        a.stats[at * 3 + 1] = A;
+        a.stats[at * 3 + 2] = B;
+      }
+    }
+    __syncthreads();
+    // The merged nodes' dot products, from the entries before this level:
+    // pair (m, Y) gives P_m.Y for a current node Y that no merge of the level
+    // takes in, and P_m.P_m' for Y = L_m' with m <= m' (P_m'.Y' expanded the
+    // same way); a node R_m is gone.
+    DD val[kPairs];
+    int at[kPairs];
+    const int npairs = (m1 - m0) * n;
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+      at[q] = -1;
+      const int x = tid + q * kBlock;
+      if (x >= npairs) continue;
+      const int m = m0 + x / n, Y = x - (x / n) * n;
+      // the reads this pair may need, issued together (o < 0: merge 0, unused)
+      const int live = alive[Y], o = own[Y];
+      const Merge mg = ms[m], mo = ms[max(o, 0)];
+      const double ca = cab[m][0], cb = cab[m][1], ca2 = cab[max(o, 0)][0], cb2 = cab[max(o, 0)][1];
+      const bool cross = o >= m0;  // Y is L_o of a merge of this level
+      if (!live || (cross && o < m)) continue;
+      const int L = mg.llo, R = mg.lhi;
+      const int Y1 = cross ? mo.llo : Y, Y2 = cross ? mo.lhi : Y;
+      const int e1 = sym_index(n, L, Y1), e2 = sym_index(n, R, Y1), e3 = sym_index(n, L, Y2), e4 = sym_index(n, R, Y2);
+      const DD n1{N[e1], Nlo[e1]}, n2{N[e2], Nlo[e2]}, n3{N[e3], Nlo[e3]}, n4{N[e4], Nlo[e4]};
+      const DD pl = dd_add(dd_scale(n1, ca), dd_scale(n2, cb));  // P_m.Y, or P_m.L_o
+      if (cross) {
+        const DD pr = dd_add(dd_scale(n3, ca), dd_scale(n4, cb));  // P_m.R_o
+        val[q] = dd_add(dd_scale(pl, ca2), dd_scale(pr, cb2));
+      } else {
+        val[q] = pl;
+      }
+      at[q] = sym_index(n, L, Y);
+    }
+    // this thread's operand weight: scaled by the coefficient of its side
+    if (tid < MO) {
+      const int o = own[tid];
+      if (o >= m0) wi = dd_scale(wi, tid < ms[o].lhi ? cab[o][0] : cab[o][1]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q)
+      if (at[q] >= 0) {
+        N[at[q]] = val[q].hi;
+        Nlo[at[q]] = val[q].lo;
+      }
+    __syncthreads();
+    m0 = m1;
+  }
+  if (tid < MO) {
+    w[tid] = wi;
+    wf[tid] = wi.hi;  // normalised: hi is the rounded value
+  }
+  // The block's result is node 0: its squared norm and its scale S[0].
+  if (tid == 0) {
+    const double out2 = N[0], parts = S[0];
+    if (outputs) {
+      // sum of |g_k|^2 over the block's input operands, in operand order
+      double leaf = 0.0;
+      for (int k = 0; k < d.nb; ++k)
+        if ((d.leafmask >> k) & 1u) leaf += diag[k];
+      a.leafnorm[(int64_t)d.wrow * a.nseg + s] = leaf;
+      if (d.root && a.ortho != nullptr) {
+        // orthogonality of the segment's gradients: |result|^2 over the sum
+        // of their squared norms (lower blocks finished in earlier launches)
+        double total = 0.0;
+        for (int r = 0; r < a.nblocks_total; ++r)
+          total += (r == d.wrow) ? leaf : a.leafnorm[(int64_t)r * a.nseg + s];
+        a.ortho[s] = (total == 0.0) ? __builtin_nan("") : out2 / total;
+      }
+    }
+    if (!kRefine) {
+      // Bit 1: the block's result is summed in double-double.  Where it is
+      // far smaller than its weighted parts, sum_k w_k x_k in fp64 would lose
+      // the ratio of the two to rounding, and a later stage could amplify
+      // that loss again; every pair flagged for recomputation (bit 0) is
+      // summed so too.
+      uint32_t f = unsure ? 3u : 0u;
+      if (parts > 0.0 && !(out2 > kSumCancel * parts)) f |= 2u;
+      fl = f;
+      if (outputs && a.flags != nullptr) a.flags[(int64_t)d.wrow * a.nseg + s] = f;
+    }
+  }
+  if (outputs && tid < MO) {
+    const int64_t wat = ((int64_t)d.wrow * a.nseg + s) * kMaxOps;
+    a.weights[wat + tid] = wi.hi;
+    a.weights_lo[wat + tid] = wi.lo;
+  }
+  __syncthreads();
+  return kRefine ? 3u : fl;  // a refined pair is summed in double-double
+}
+
 // One workgroup per (block, segment).  Blocks of up to 32 operands: wave q
 // sums the tile partials of the q-th quarter of the segment's tiles (lanes
 // over Gram entries, tiles in order); the four quarter sums are then added
@@ -1007,195 +1189,6 @@ __global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
 // split depends only on the tile count, so the result is reproducible.  The
 // refining walk (kRefine) visits only flagged pairs, whose tiles hold
 // double-double entries, and sums them in double-double, tile by tile.
-// The merge walk of block d over segment s on its Gram matrix G (and, where
-// exact_g, its double-double low parts Glo): every merge's statistics and
-// coefficients, the operands' weights w (double-double) and wf (rounded),
-// and the block's flags (see TreeArgs), returned to every thread.  Where
-// outputs is set, the coefficients, statistics, weights, input norms,
-// orthogonality and flags are also written out.  Called by every thread of
-// the workgroup; G and Glo are in LDS.
-template <bool kRefine, int MO>
-__device__ __forceinline__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, const double* G,
-                                               const double* Glo, bool exact_g, DD* w, double* wf, bool outputs) {
-  const int tid = threadIdx.x;
-  const int n = d.nbt;
-  if (tid < MO) w[tid] = DD{1.0, 0.0};
-  __syncthreads();
-  // entries already exact (double-double) are not flagged again
-  const double gram_err = exact_g ? 0.0 : d.gram_err;
-  // Merges run level by level: merges of a block are stored children
-  // before parents, and the merges of one level cover disjoint operand
-  // ranges (a batch ends where a merge starts left of the previous one).
-  // For merge (L, R), thread i in L u R forms its row sums
-  // rowL_i = sum_{k in L} w_k G(i,k) and rowR_i = sum_{k in R} w_k G(i,k) in
-  // k order; one thread per merge then forms A = sum_{i in L} w_i rowL_i,
-  // B = sum_{i in R} w_i rowR_i and d = sum_{i in L} w_i rowR_i in i order,
-  // all in double-double, and rounds them to fp64.  That is the same
-  // arithmetic, term for term, as a serial evaluation.
-  __shared__ DD rowL[MO], rowR[MO];
-  __shared__ double cab[MO][2];
-  __shared__ Merge ms[MO];
-  __shared__ int unsure;  // some coefficient may be off by more than kRefineTol
-  if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];
-  if (tid == 0) unsure = 0;
-  __syncthreads();
-  for (int m0 = 0; m0 < d.nmerges;) {
-    int m1 = m0 + 1;
-    while (m1 < d.nmerges && ms[m1].llo >= ms[m1 - 1].rhi) ++m1;
-    // the merge of this batch that holds operand tid, if any
-    int mine = -1;
-    for (int m = m0; m < m1; ++m)
-      if (tid >= ms[m].llo && tid < ms[m].rhi) mine = m;
-    if (mine >= 0) {
-      const int l0 = ms[mine].llo, l1 = ms[mine].lhi, r1 = ms[mine].rhi;
-      DD sl{0.0, 0.0}, sr{0.0, 0.0};
-      if (exact_g) {
-        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
-        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_mul(w[k], DD{gram_at(G, n, tid, k), gram_at(Glo, n, tid, k)}));
-      } else {
-        for (int k = l0; k < l1; ++k) sl = dd_add(sl, dd_scale(w[k], gram_at(G, n, tid, k)));
-        for (int k = l1; k < r1; ++k) sr = dd_add(sr, dd_scale(w[k], gram_at(G, n, tid, k)));
-      }
-      rowL[tid] = sl;
-      rowR[tid] = sr;
-    }
-    __syncthreads();
-    // A merge's statistics from its five sums: A, B, d (double-double) and,
-    // for the rounding estimate, sl = sum_{i in L} w_i^2 G_ii and sr over R.
-    auto finish = [&](int mi, DD a2, DD b2, DD ab, double sl, double sr) {
-      const Merge mg = ms[mi];
-      const double A = a2.hi, B = b2.hi, dd = ab.hi;  // normalised: hi is the rounded sum
-      const double ca = (A == 0.0) ? 1.0 : 1.0 - dd / (2.0 * A);
-      const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
-      cab[mi][0] = ca;
-      cab[mi][1] = cb;
-      if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
-        // The rounding errors of separate chunk sums are independent, so a
-        // quadratic form over an operand with weights w errs by about
-        // gram_err S, S = sum w_i^2 G_ii (the norm the operand would have if
-        // its parts were orthogonal): S <= A for parallel parts, S ~ A for
-        // orthogonal ones, S >> A only under cancellation.  (The worst case,
-        // with every error aligned, replaces S by (sum |w_i| sqrt(G_ii))^2,
-        // which exceeds A for any orthogonal parts and would flag ordinary
-        // data.)  c = 1 - d / (2A) then moves by about
-        // (|d err| + |d| |A err| / A) / (2A).  An operand whose norm the
-        // estimate cannot tell from zero is flagged too.
-        const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
-        bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
-        if (A > eA) bad = bad || (ed + fabs(dd) * eA / A) / (2.0 * A) > kRefineTol * fmax(1.0, fabs(ca));
-        if (B > eB) bad = bad || (ed + fabs(dd) * eB / B) / (2.0 * B) > kRefineTol * fmax(1.0, fabs(cb));
-        if (bad) unsure = 1;
-      }
-      if (!outputs) return;
-      const int64_t at = (int64_t)mg.node * a.nseg + s;
-      a.coeffs[at * 2] = ca;
-      a.coeffs[at * 2 + 1] = cb;
-      a.stats[at * 3] = dd;
-      a.stats[at * 3 + 1] = A;
-      a.stats[at * 3 + 2] = B;
-    };
-    // Merges over at most kSerialMerge operands: one thread each, terms in
-    // operand order.  Wider ones (the top of a 64-operand tree, a chain of
-    // more than 16): one wave each, a lane per operand, the terms added by a
-    // butterfly across the wave, so that a 64-operand chain is not 63 serial
-    // sums of up to 63 terms.
-    if (tid < m1 - m0 && ms[m0 + tid].rhi - ms[m0 + tid].llo <= kSerialMerge) {
-      const Merge mg = ms[m0 + tid];
-      const int l0 = mg.llo, l1 = mg.lhi, r1 = mg.rhi;
-      DD a2{0.0, 0.0}, b2{0.0, 0.0}, ab{0.0, 0.0};
-      for (int i = l0; i < l1; ++i) a2 = dd_add(a2, dd_mul(rowL[i], w[i]));
-      for (int i = l1; i < r1; ++i) b2 = dd_add(b2, dd_mul(rowR[i], w[i]));
-      for (int i = l0; i < l1; ++i) ab = dd_add(ab, dd_mul(rowR[i], w[i]));
-      double sl = 0.0, sr = 0.0;
-      for (int i = l0; i < l1; ++i) sl += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
-      for (int i = l1; i < r1; ++i) sr += w[i].hi * w[i].hi * G[gram_index(n, i, i)];
-      finish(m0 + tid, a2, b2, ab, sl, sr);
-    }
-    {
-      const int q = tid >> 6, lane = tid & 63;
-      int nth = 0;  // wide merges of this batch seen so far
-      for (int mi = m0; mi < m1; ++mi) {
-        const Merge mg = ms[mi];
-        if (mg.rhi - mg.llo <= kSerialMerge) continue;
-        if ((nth++ & (kTreeWaves - 1)) != q) continue;  // wave-uniform
-        const int i0 = mg.llo + lane;  // a wide merge spans at most 64 operands
-        const bool inL = i0 < mg.lhi, inR = i0 >= mg.lhi && i0 < mg.rhi;
-        const int i = (inL || inR) ? i0 : mg.llo;  // lanes past the merge read a valid entry, unused
-        const DD zero{0.0, 0.0};
-        DD a2 = inL ? dd_mul(rowL[i], w[i]) : zero;
-        DD b2 = inR ? dd_mul(rowR[i], w[i]) : zero;
-        DD ab = inL ? dd_mul(rowR[i], w[i]) : zero;
-        const double wg = (inL || inR) ? w[i].hi * w[i].hi * G[gram_index(n, i, i)] : 0.0;
-        double sl = inL ? wg : 0.0, sr = inR ? wg : 0.0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          a2 = dd_add(a2, DD{__shfl_xor(a2.hi, off), __shfl_xor(a2.lo, off)});
-          b2 = dd_add(b2, DD{__shfl_xor(b2.hi, off), __shfl_xor(b2.lo, off)});
-          ab = dd_add(ab, DD{__shfl_xor(ab.hi, off), __shfl_xor(ab.lo, off)});
-          sl += __shfl_xor(sl, off);
-          sr += __shfl_xor(sr, off);
-        }
-        if (lane == 0) finish(mi, a2, b2, ab, sl, sr);
-      }
-    }
-    __syncthreads();
-    if (mine >= 0) w[tid] = dd_scale(w[tid], tid < ms[mine].lhi ? cab[mine][0] : cab[mine][1]);
-    __syncthreads();
-    m0 = m1;
-  }
-  if (tid < MO) wf[tid] = w[tid].hi;  // normalised: hi is the rounded value
-  __syncthreads();
-  if (outputs && tid == 0) {
-    // sum of |g_k|^2 over the block's input operands, in operand order
-    double leaf = 0.0;
-    for (int k = 0; k < d.nb; ++k)
-      if ((d.leafmask >> k) & 1u) leaf += G[gram_index(n, k, k)];
-    a.leafnorm[(int64_t)d.wrow * a.nseg + s] = leaf;
-    if (d.root && a.ortho != nullptr) {
-      // orthogonality of the segment's gradients: |result|^2 over the sum
-      // of their squared norms (lower blocks finished in earlier launches)
-      double total = 0.0;
-      for (int r = 0; r < a.nblocks_total; ++r)
-        total += (r == d.wrow) ? leaf : a.leafnorm[(int64_t)r * a.nseg + s];
-      const double out2 = quad_form(G, n, wf, 0, d.nb, 0, d.nb);
-      a.ortho[s] = (total == 0.0) ? __builtin_nan("") : out2 / total;
-    }
-  }
-  __syncthreads();
-  const int64_t wat = ((int64_t)d.wrow * a.nseg + s) * kMaxOps;
-  if (outputs && tid < MO) {
-    a.weights[wat + tid] = wf[tid];
-    a.weights_lo[wat + tid] = w[tid].lo;
-  }
-  __shared__ uint32_t fl;
-  if (!kRefine) {
-    // Bit 1: the block's result is summed in double-double.  Where it is far
-    // smaller than its weighted parts, sum_k w_k x_k in fp64 would lose the
-    // ratio of the two to rounding, and a later stage could amplify that loss
-    // again; every pair flagged for recomputation (bit 0) is summed so too.
-    __shared__ double rows_w[MO];
-    if (tid < d.nb) {
-      double r = 0.0;
-      for (int k = 0; k < d.nb; ++k) r += wf[k] * gram_at(G, n, tid, k);
-      rows_w[tid] = r;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double out2 = 0.0, parts = 0.0;
-      for (int k = 0; k < d.nb; ++k) {
-        out2 += wf[k] * rows_w[k];
-        parts += wf[k] * wf[k] * G[gram_index(n, k, k)];
-      }
-      uint32_t f = unsure ? 3u : 0u;
-      if (parts > 0.0 && !(out2 > kSumCancel * parts)) f |= 2u;
-      fl = f;
-      if (outputs && a.flags != nullptr) a.flags[(int64_t)d.wrow * a.nseg + s] = f;
-    }
-    __syncthreads();
-    return fl;
-  }
-  return 3u;  // a refined pair is summed in double-double
-}
 
 // kWide: the launch holds a 64-operand block (its Gram matrix takes 2080
 // entries of LDS; the other variant, 528, keeps more workgroups per CU).
@@ -1210,6 +1203,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // node that nearly cancels would amplify their fp64 rounding)
   __shared__ DD w[MO];
   __shared__ double wf[MO];  // the weights rounded to fp64
+  __shared__ Merge ms[MO];
   const int item = blockIdx.x;
   const int b = item / a.nseg;
   const int s = item % a.nseg;
@@ -1218,6 +1212,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   const int n = d.nbt;
   const int ne = gram_entries(n);
   const int tid = threadIdx.x;
+  if (tid < d.nmerges) ms[tid] = a.merges[d.merge0 + tid];  // read by the walk, after the barriers below
   const int t0 = a.seg_tile[s], t1 = a.seg_tile[s + 1];
   // The low parts of the Gram entries, where the walk has them: the refining
   // walk's tile sums, or below the exact entries of a single short tile.
@@ -1290,7 +1285,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     __syncthreads();  // every wave sum is consumed
     for (int e = tid; e < ne; e += kBlock) Glo[e] = a.partials_lo[d.poff + (int64_t)t0 * ne + e];
   }
-  walk_block<kRefine, MO>(a, d, s, G, Glo, exact_g, w, wf, true);
+  walk_block<kRefine, MO>(a, d, s, ms, G, Glo, exact_g, w, wf, true);
 }
 
 // ----------------------------------------------------------------- weighted sum
@@ -1618,6 +1613,7 @@ __global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
 // parts into G and low parts into Glo; the rows pass through sh
 // (NB x kFusedChunk doubles).  Called by every thread of the workgroup.
 constexpr int kFusedChunk = 64;
+constexpr int kFusedRuns = 16;  // runs of tiles whose partials one workgroup sums in parallel
 
 template <typename TIn, int NB>
 __device__ void segment_exact_gram(const void* const* table, int64_t lo, int64_t hi, double* G, double* Glo,
@@ -1676,7 +1672,7 @@ __device__ void segment_exact_gram(const void* const* table, int64_t lo, int64_t
 // walked again.
 template <typename TIn, int NB>
 __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa) {
-  constexpr int kSplit = wsum_split(sizeof(TIn));
+  constexpr int kSplit = kFusedSplit;
   constexpr int MO = kArgOps;
   static_assert(NB <= MO, "blocks of at most 32 operands");
   static_assert(kTreeWaves * kPartStride >= NB * kFusedChunk, "the exact rows fit the wave sums");
@@ -1686,6 +1682,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa)
   __shared__ DD w[MO];
   __shared__ double wf[MO];
   __shared__ double wlo[MO];
+  __shared__ Merge ms[MO];
   const int tile_id = blockIdx.x / kSplit;
   const int part_id = blockIdx.x % kSplit;
   const Tile tile = wa.tiles[tile_id];
@@ -1694,21 +1691,27 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa)
   const int ne = gram_entries(d.nbt);
   const int tid = threadIdx.x;
   const int t0 = ta.seg_tile[s], t1 = ta.seg_tile[s + 1];
+  if (tid < d.nmerges) ms[tid] = ta.merges[d.merge0 + tid];  // read by the walk, after the barrier below
   {
-    // the tile partials: for Q = kBlock / ne (at least 1), thread (q, e)
-    // adds tiles t0 + q, t0 + q + Q, ... of entry e in order, and the Q sums
-    // of each entry are added in q order; every thread has few tiles to read
-    const int Q = max(1, kBlock / ne);
+    // the tile partials: the segment's tiles cut into Q runs of consecutive
+    // tiles (Q = kBlock / ne, at most kFusedRuns, at least 1); thread (q, e)
+    // adds run q of entry e in tile order, and the Q run sums of each entry
+    // are added in q order
+    const int Q = min(kFusedRuns, max(1, kBlock / ne));
+    const int run = (t1 - t0 + Q - 1) / Q;
     for (int x = tid; x < Q * ne; x += kBlock) {
       const int q = x / ne, e = x - q * ne;
       const double* p = ta.partials + d.poff + e;
+      const int r0 = t0 + q * run, r1 = min(t1, r0 + run);
       double sum = 0.0;
-      for (int t = t0 + q; t < t1; t += Q) sum += p[(int64_t)t * ne];
+#pragma unroll 8
+      for (int t = r0; t < r1; ++t) sum += p[(int64_t)t * ne];
       part[x] = sum;
     }
     __syncthreads();
     for (int e = tid; e < ne; e += kBlock) {
       double sum = part[e];
+#pragma unroll 4
       for (int q = 1; q < Q; ++q) sum += part[q * ne + e];
       G[e] = sum;
     }
@@ -1719,12 +1722,12 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa)
   if (exact_g)
     for (int e = tid; e < ne; e += kBlock) glo[e] = ta.partials_lo[d.poff + (int64_t)t0 * ne + e];
   const bool first = tile_id == t0 && part_id == 0;
-  uint32_t f = walk_block<false, MO>(ta, d, s, G, glo, exact_g, w, wf, first);
+  uint32_t f = walk_block<false, MO>(ta, d, s, ms, G, glo, exact_g, w, wf, first);
   if (f & 1u) {  // workgroup-uniform
     const Tile last = ta.tiles[t1 - 1];
     segment_exact_gram<TIn, NB>(wa.x, ta.tiles[t0].start, last.start + last.len, G, glo, part);
     __syncthreads();
-    f = walk_block<true, MO>(ta, d, s, G, glo, true, w, wf, first);
+    f = walk_block<true, MO>(ta, d, s, ms, G, glo, true, w, wf, first);
   }
   if (tid < MO) wlo[tid] = w[tid].lo;
   __syncthreads();
@@ -1879,9 +1882,21 @@ struct RunSum {
 
 hipError_t run_gram_f64(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
   const dim3 grid(ntiles, njobs);
+  // short tiles: at most kMinTile rows, 4 x 16 x (16 / nbt) x U rows per workgroup iteration
+  static_assert(kMinTile <= 4 * 16 * 8 * 4 && kMinTile <= 4 * 16 * 4 * 8, "short tiles take one iteration per wave");
   switch (nbt) {
-    case 2: hipLaunchKernelGGL((gram_f64mfma_kernel<2>), grid, dim3(kBlock), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gram_f64mfma_kernel<4>), grid, dim3(kBlock), 0, st, a); break;
+    case 2:
+      if (a.short_tiles)
+        hipLaunchKernelGGL((gram_f64mfma_kernel<2, 4>), grid, dim3(kBlock), 0, st, a);
+      else
+        hipLaunchKernelGGL((gram_f64mfma_kernel<2>), grid, dim3(kBlock), 0, st, a);
+      break;
+    case 4:
+      if (a.short_tiles)
+        hipLaunchKernelGGL((gram_f64mfma_kernel<4, 8>), grid, dim3(kBlock), 0, st, a);
+      else
+        hipLaunchKernelGGL((gram_f64mfma_kernel<4>), grid, dim3(kBlock), 0, st, a);
+      break;
     case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8>), grid, dim3(kBlock), 0, st, a); break;
     case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16>), grid, dim3(kBlock), 0, st, a); break;
     default: return hipErrorInvalidValue;
@@ -2020,7 +2035,7 @@ struct RunExactFirst {
 template <typename TIn>
 struct RunFused {
   static hipError_t run(int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st) {
-    const dim3 grid((unsigned)ntiles * wsum_split(sizeof(TIn)));
+    const dim3 grid((unsigned)ntiles * kFusedSplit);
     switch (nbt) {
       case 2: hipLaunchKernelGGL((fused_kernel<TIn, 2>), grid, dim3(kBlock), 0, st, t, w); break;
       case 4: hipLaunchKernelGGL((fused_kernel<TIn, 4>), grid, dim3(kBlock), 0, st, t, w); break;

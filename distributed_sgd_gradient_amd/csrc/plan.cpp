@@ -242,14 +242,11 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   if (p.stages.size() == 1 && p.stages[0].blocks.size() == 1 && p.descs[0].nbt <= kArgOps && p.N <= kFusedMaxRows &&
       !p.tiles.empty()) {
     p.fused = true;
-    int64_t reads = 0;
-    const int64_t split = wsum_split((int)dtype_size(dtype)), ne = gram_entries(p.descs[0].nbt);
+    const int64_t ne = gram_entries(p.descs[0].nbt);
     for (int s = 0; s < nseg; ++s) {
       const int64_t nt = p.seg_tile[s + 1] - p.seg_tile[s];
-      if (nt < 1) p.fused = false;
-      reads += nt * split * nt * ne;
+      if (nt < 1 || nt * ne > kFusedMaxReads) p.fused = false;
     }
-    if (reads > kFusedMaxReads) p.fused = false;
   }
 
   // ---- workspace layout

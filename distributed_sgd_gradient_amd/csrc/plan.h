@@ -55,11 +55,14 @@ constexpr int kTileGroup = 16;
 // kFusedMaxRows elements and no empty segment, runs its walk and weighted
 // sum in one launch after the Gram pass: every weighted-sum workgroup walks
 // its own segment, so the small, launch-bound combines take two launches
-// instead of five.  Each workgroup then reads its segment's tile partials,
-// so the plan must keep sum_s (workgroups of s) x (tiles of s) x (Gram
-// entries) within kFusedMaxReads.
+// instead of five.  Each workgroup then reads all its segment's tile
+// partials, so every segment must have at most kFusedMaxReads of them
+// ((tiles of s) x (Gram entries)).
 constexpr int64_t kFusedMaxRows = int64_t(1) << 22;
-constexpr int64_t kFusedMaxReads = int64_t(1) << 24;
+constexpr int64_t kFusedMaxReads = int64_t(1) << 13;
+// Workgroups per tile of that launch.  Its tiles have at most kMinTile rows
+// (see Plan::tile_rows), which one workgroup covers in one vector step.
+constexpr int kFusedSplit = 1;
 // Tiles of at most kExactRows rows of 16-bit inputs are short: their Gram
 // matrices are summed exactly (double-double) instead of on the matrix cores,
 // since short segments are where merges nearly cancel by chance.

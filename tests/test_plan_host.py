@@ -199,11 +199,14 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
             assert (st[s + 1] > st[s]) == (off[s + 1] > off[s])
         # small one-stage combines of one block of at most 32 operands, no
         # empty segment and few partials for every weighted-sum workgroup to
-        # read, take the walk and weighted sum in one launch
+        # read (at most 2^13 per segment), take the walk and weighted sum in
+        # one launch
         nbt0 = P["stages"][0]["blocks"][0]["nbt"]
-        reads = sum((st[s + 1] - st[s]) ** 2 * (8 if dt == 0 else 4) * nbt0 * (nbt0 + 1) // 2 for s in range(nseg))
+        reads = max([(st[s + 1] - st[s]) * nbt0 * (nbt0 + 1) // 2 for s in range(nseg)] or [0])
         small = (len(P["stages"]) == 1 and len(P["stages"][0]["blocks"]) == 1 and nbt0 <= 32 and N <= 1 << 22
-                 and len(tiles) > 0 and all(st[s + 1] > st[s] for s in range(nseg)) and reads <= 1 << 24)
+                 and len(tiles) > 0 and all(st[s + 1] > st[s] for s in range(nseg)) and reads <= 1 << 13)
+        if small:
+            assert T <= 2048  # one weighted-sum workgroup per tile covers it in one vector step
         assert bool(P["fused"]) == small, (K, dt, sc, off[:5])
         # the tree (or chain) is the oracle's, with the block size limits
         assert plan_nodes(P) == oracle_nodes(K, sc), (K, dt, sc)
