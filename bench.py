@@ -198,6 +198,43 @@ def time_steps(step, steps, profile):
     return (t1 - t0) * 1e3 / steps, per_step, kernels
 
 
+def time_bare(step, steps):
+    """Mean ms per step of `steps` combines back to back with no event inside
+    the loop (host clock, bracketed by synchronisations)."""
+    import torch
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_graph(step, steps, per_graph=10):
+    """Mean ms per step when `per_graph` combines are captured into one HIP
+    graph and the graph is replayed: the same kernels without the host's
+    launch cost (the earlier calls have uploaded the shape's tables)."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            step()
+    reps = max(1, steps // per_graph)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * per_graph)
+    del g
+    return ms
+
+
 def step_stats(ms, per_step):
     srt = sorted(per_step)
     return {"mean": ms, "median": srt[len(srt) // 2], "min": srt[0], "max": srt[-1]}
@@ -232,11 +269,15 @@ def other_workload(config, steps, warmup, dev, budget_s):
     b_min = K * N * esz + N * esz
     st = step_stats(ms, per_step)
     log(f"  {steps} steps: {ms:.3f} ms/step (median {st['median']:.3f}, min {st['min']:.3f})")
+    bare = time_bare(step, steps)
+    graph = time_graph(step, steps)
+    log(f"  without events: {bare * 1e3:.1f} us/step; graph replay: {graph * 1e3:.1f} us/step")
     _, parity = cpu_baseline(wl, budget_s, "tree", 1, gpu_out=out, gpu_coeffs=step.coeffs)
     log(f"  parity on {parity['segments']} segments: relative L2 {parity['rel_l2']:.3g}, "
         f"coefficient error {parity['max_coeff_err']}")
     rec = {"workload": WORKLOAD_NAMES[config], "K": K, "N": N, "nseg": wl.nseg, "io_dtype": wl.dtype,
-           "ms_per_step": st, "gradient_GBps": K * N * esz / (ms * 1e-3) / 1e9,
+           "ms_per_step": st, "ms_per_step_without_events": bare, "ms_per_step_graph_replay": graph,
+           "gradient_GBps": K * N * esz / (ms * 1e-3) / 1e9,
            "path_frac": b_min / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "B_min_bytes": b_min,
            "kernels": kernel_table(kernels, steps), "parity": parity}
     del step, out, wl
@@ -433,6 +474,10 @@ def main():
     ms_bare, per_step_bare, _ = time_steps(step, args.steps, profile=False)
     bare_ms = step_stats(ms_bare, per_step_bare)
     log(f"again without per-launch events: {ms_bare:.3f} ms/step (median {bare_ms['median']:.3f})")
+    ms_noev = time_bare(step, args.steps)
+    ms_graph = time_graph(step, args.steps)
+    log(f"again without any event in the loop: {ms_noev * 1e3:.1f} us/step; "
+        f"as HIP graph replays: {ms_graph * 1e3:.1f} us/step")
 
     grad_bytes = K * N * esz
     b_min = grad_bytes + N * esz
@@ -515,7 +560,8 @@ def main():
         "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": config,
         "roofline": roofline, "path_roofline": path, "cpu_baseline": cpu, "parity": parity,
-        "step_ms": steps_ms, "step_ms_without_launch_events": bare_ms, "plain_sum": plain_sum,
+        "step_ms": steps_ms, "step_ms_without_launch_events": bare_ms,
+        "step_ms_without_events": ms_noev, "step_ms_graph_replay": ms_graph, "plain_sum": plain_sum,
         **({"cold": cold} if cold is not None else {}),
         "kernels": kernel_table(kernels, args.steps),
         **({"other_workloads": others} if others else {}),

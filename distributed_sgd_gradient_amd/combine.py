@@ -13,6 +13,15 @@ import torch
 
 from . import _native
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_raw_stream(index):
+    """Handle of the current stream of device ``index``."""
+    if _raw_stream is not None:
+        return _raw_stream(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
 DTYPE_CODES = {torch.float32: _native.F32, torch.float16: _native.F16, torch.bfloat16: _native.BF16}
 SCHEDULES = {"tree": _native.TREE, "chain": _native.CHAIN}
 
@@ -178,9 +187,9 @@ class Combiner:
         self._index = dev.index if dev.index is not None else torch.cuda.current_device()
 
     def __call__(self, stream=None):
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
-        st = ctypes.c_void_p(stream.cuda_stream)
+        # the stream as a raw handle: torch's current-stream object costs
+        # more host time than a small combine's launches
+        st = _current_raw_stream(self._index) if stream is None else stream.cuda_stream
         if torch.cuda.current_device() == self._index:
             _native.check(self._fn(*self._args, st))
         else:

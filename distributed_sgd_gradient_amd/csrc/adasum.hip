@@ -406,7 +406,74 @@ BlockKind block_kind(const Plan& p, const Block& b) {
   return k;
 }
 
+// A small combine (Plan::fused: one stage of one block, at most kArgOps
+// operands): the Gram pass, then the walk and weighted sum in one launch,
+// both with one-job arguments.  Such combines are bound by the host's cost
+// of their launches.
+int enqueue_fused(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStream_t st) {
+  const int ntiles = (int)p.tiles.size();
+  const Block& bk = p.stages[0].blocks[0];
+  const BlockDesc& d = p.descs[bk.desc];
+  const int nbt = d.nbt;
+  double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
+  double* partials_lo = reinterpret_cast<double*>(b.ws + p.ws_plo);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(b.ws + p.ws_flags);
+  GramArgs1 g{};
+  WsumArgs1 w{};
+  for (size_t k = 0; k < bk.operands.size(); ++k) g.x[k] = w.x[k] = ref_ptr(p, b, bk.operands[k]);
+  const double in_bytes = (double)p.N * dtype_size(p.dtype) * bk.operands.size();
+  g.poff[0] = d.poff;
+  g.tiles = dt.tiles;
+  g.partials = partials;
+  g.partials_lo = partials_lo;
+  g.flags = flags;
+  g.wrow[0] = d.wrow;
+  g.nseg = p.nseg;
+  g.short_tiles = p.tile_rows <= kMinTile;
+  const double gbytes = in_bytes + 8.0 * gram_entries(nbt) * ntiles;
+  log_launch("gram", 1, ntiles, 1, nbt, gbytes);
+  const int pg = prof_start(kGram, gbytes, st);
+  hipError_t e = launch_gram1(p.dtype, nbt, g, ntiles, st);
+  prof_stop(pg, st);
+  if (e != hipSuccess) return fail_hip(e, "launching gram");
+
+  TreeArgs t{};
+  t.descs = dt.descs;
+  t.merges = dt.merges;
+  t.seg_tile = dt.seg_tile;
+  t.partials = partials;
+  t.partials_lo = partials_lo;
+  t.tiles = dt.tiles;
+  t.lo_inputs = p.dtype != DType::F32;
+  t.desc0 = bk.desc;
+  t.nblocks = 1;
+  t.nseg = p.nseg;
+  t.weights = reinterpret_cast<double*>(b.ws + p.ws_weights);
+  t.weights_lo = reinterpret_cast<double*>(b.ws + p.ws_weights_lo);
+  t.coeffs = b.coeffs;
+  t.stats = b.stats;
+  t.ortho = b.ortho;
+  t.leafnorm = reinterpret_cast<double*>(b.ws + p.ws_leafnorm);
+  t.nblocks_total = p.nblocks;
+  t.flags = flags;
+  w.y[0] = ref_ptr(p, b, bk.dst);
+  w.wrow[0] = d.wrow;
+  w.tiles = dt.tiles;
+  w.nseg = p.nseg;
+  w.weights = t.weights;
+  w.weights_lo = t.weights_lo;
+  w.flags = flags;
+  const double wbytes = in_bytes + (double)p.N * dtype_size(p.dtype);
+  log_launch("walk+wsum", 1, ntiles, 1, nbt, wbytes);
+  const int pw = prof_start(kWsum, wbytes, st);
+  e = launch_fused(p.dtype, nbt, t, w, ntiles, st);
+  prof_stop(pw, st);
+  if (e != hipSuccess) return fail_hip(e, "launching the fused walk and weighted sum");
+  return ADASUM_OK;
+}
+
 int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStream_t st) {
+  if (p.fused) return enqueue_fused(p, dt, b, st);
   const int ntiles = (int)p.tiles.size();
   hipError_t e;
   double* partials = reinterpret_cast<double*>(b.ws + p.ws_partials);
@@ -516,16 +583,6 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
             a.weights = weights;
             a.weights_lo = weights_lo;
             a.flags = flags;
-            if (p.fused) {
-              // the walk, any exact recomputation and the weighted sum in one launch
-              t.flags = flags;
-              log_launch("walk+wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
-              const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
-              e = launch_fused(in_t, nbt, t, a, ntiles, st);
-              prof_stop(pr, st);
-              if (e != hipSuccess) return fail_hip(e, "launching the fused walk and weighted sum");
-              continue;
-            }
             log_launch("wsum", stage_no, ntiles, n, nbt, in_bytes + out_bytes);
             const int pr = prof_start(kWsum, in_bytes + out_bytes, st);
             e = launch_wsum(in_t, p.dtype, nbt, out_t, a, ntiles, n, st);
@@ -534,7 +591,7 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
           }
         }
       }
-      if (pass == 0 && p.nseg > 0 && !p.fused) {
+      if (pass == 0 && p.nseg > 0) {
         // 2. per (block, segment): statistics, coefficients, operand weights,
         // and a flag on every pair whose coefficients the rounding of its
         // Gram entries could move beyond tolerance (a merge under deep

@@ -94,6 +94,33 @@ struct WsumArgs {
 };
 static_assert(sizeof(WsumArgs) <= 4096, "kernel arguments fit 4 KB");
 
+// The same arguments for a launch of one job of at most kArgOps operands
+// (the small combines of Plan::fused).  The host's cost of a launch grows
+// with the size of its arguments, and these launches are bound by it.
+struct GramArgs1 {
+  const void* x[kArgOps];
+  uint32_t narrow[1];
+  int64_t poff[1];
+  const Tile* tiles;
+  double* partials;
+  double* partials_lo;
+  const uint32_t* flags;
+  int32_t wrow[1];
+  int nseg;
+  int short_tiles;
+};
+struct WsumArgs1 {
+  const void* x[kArgOps];
+  uint32_t narrow[1];
+  void* y[1];
+  int wrow[1];
+  const Tile* tiles;
+  int nseg;
+  const double* weights;
+  const double* weights_lo;
+  const uint32_t* flags;
+};
+
 // Plain sum of up to kSumOps operands, element by element in fp64, in
 // operand order: acc = (acc_in ? acc_in : 0) + x0 + x1 + ...; the result goes
 // to acc_out (fp64) or, rounded once, to out.
@@ -131,6 +158,8 @@ hipError_t launch_sum(DType t, const SumArgs& a, hipStream_t st);
 // few tiles (Plan::fused): after its Gram pass, the walk, any exact
 // recomputation and the weighted sum in one launch over the weighted sum's
 // grid (t as for launch_tree, w as for launch_wsum of that block).
-hipError_t launch_fused(DType in_t, int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st);
+hipError_t launch_fused(DType in_t, int nbt, const TreeArgs& t, const WsumArgs1& w, int ntiles, hipStream_t st);
+// The Gram pass of that plan's one block (inputs of type operand).
+hipError_t launch_gram1(DType operand, int nbt, const GramArgs1& a, int ntiles, hipStream_t st);
 
 }  // namespace adasum

@@ -344,8 +344,8 @@ __device__ __forceinline__ void f64_gram_reduce(double (*red)[64 * 4], const f64
 // U: 16-row chunks per wave per iteration.  Plans of short tiles (at most
 // kMinTile rows) take fewer chunks for blocks of 2 or 4 operands, so that
 // the four waves share a tile's rows instead of one wave taking them all.
-template <int NB, int U = kF64Unroll>
-__global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GramArgs args) {
+template <int NB, int U = kF64Unroll, typename GA = GramArgs>
+__global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GA args) {
   constexpr int SETS = 16 / NB;          // row sets packed into the 16 operand lanes
   constexpr int RC = 16 * SETS;          // rows per chunk
   constexpr int R = RC * U;              // rows per wave per iteration
@@ -750,8 +750,8 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
 // smaller blocks do at four waves per SIMD (bf16: four chunks, within the
 // registers that its range check and scaled path take).
 constexpr int kWideUnroll = 8;  // 32-row chunks per wave per iteration of a 64-operand block
-template <typename T, int NB>
-__global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GramArgs args) {
+template <typename T, int NB, typename GA = GramArgs>
+__global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GA args) {
   constexpr int NH = NB > 32 ? 4 : NB > 16 ? 2 : 1;  // 16-operand groups
   constexpr int NP = NH * (NH + 1) / 2;  // sub-blocks (h1 <= h2)
   constexpr int U = NB > 32 ? (Mfma<T>::kGuard ? kWideUnroll / 2 : kWideUnroll) : kMfmaUnroll / NH;  // chunks per wave per iteration
@@ -1045,10 +1045,14 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
   // a merge overlaps the one before it.  Bit m: merge m starts a batch.
   const int lane = tid & 63;
   const uint64_t starts = __ballot(lane < nm && (lane == 0 || ms[lane].llo < ms[lane - 1].rhi));
+  // |root|^2 in double-double: the last merge (the block's root, alone in
+  // its level) forms it itself, since no other node is left to update
+  __shared__ DD root2;
   DD wi{1.0, 0.0};  // weight of operand tid
   for (int m0 = 0; m0 < nm;) {
     const uint64_t later = starts & ~((uint64_t(2) << m0) - 1u);
     const int m1 = later != 0 ? (int)__builtin_ctzll(later) : nm;
+    const bool last = m1 == nm;  // workgroup-uniform
     // the statistics and coefficients, one thread per merge
     if (tid < m1 - m0) {
       const int mi = m0 + tid;
@@ -1060,6 +1064,12 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
       const double cb = (B == 0.0) ? 1.0 : 1.0 - dd / (2.0 * B);
       cab[mi][0] = ca;
       cab[mi][1] = cb;
+      if (last) {
+        const DD nA{A, Nlo[eLL]}, nB{B, Nlo[eRR]}, nd{dd, Nlo[eLR]};
+        const DD pl = dd_add(dd_scale(nA, ca), dd_scale(nd, cb));  // P.L
+        const DD pr = dd_add(dd_scale(nd, ca), dd_scale(nB, cb));  // P.R
+        root2 = dd_add(dd_scale(pl, ca), dd_scale(pr, cb));
+      }
       const double sl = S[L], sr = S[R];
       if (!kRefine && a.flags != nullptr && gram_err > 0.0) {
         // The rounding errors of separate chunk sums are independent, so a
@@ -1091,6 +1101,13 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
       }
     }
     __syncthreads();
+    if (last) {
+      if (tid < MO) {
+        const int o = own[tid];
+        if (o >= m0) wi = dd_scale(wi, tid < ms[o].lhi ? cab[o][0] : cab[o][1]);
+      }
+      break;
+    }
     // The merged nodes' dot products, from the entries before this level:
     // pair (m, Y) gives P_m.Y for a current node Y that no merge of the level
     // takes in, and P_m.P_m' for Y = L_m' with m <= m' (P_m'.Y' expanded the
@@ -1144,7 +1161,7 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
   }
   // The block's result is node 0: its squared norm and its scale S[0].
   if (tid == 0) {
-    const double out2 = N[0], parts = S[0];
+    const double out2 = nm > 0 ? root2.hi : N[0], parts = S[0];
     if (outputs) {
       // sum of |g_k|^2 over the block's input operands, in operand order
       double leaf = 0.0;
@@ -1294,8 +1311,8 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 // sum_k w_k x_k in double-double, with the walk's double-double weights and
 // exact products, rounded once.  Operands one at a time (rare, so compact);
 // operand k is of type TIn, or TN where the job's narrow mask marks it.
-template <typename TIn, typename TN, int NB, typename TOut>
-__device__ void wsum_exact_range(const WsumArgs& args, int j, int64_t lo, int64_t hi, const double* w_hi,
+template <typename TIn, typename TN, int NB, typename TOut, typename WA = WsumArgs>
+__device__ void wsum_exact_range(const WA& args, int j, int64_t lo, int64_t hi, const double* w_hi,
                                  const double* w_lo) {
   TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
   double unused;
@@ -1339,12 +1356,14 @@ __device__ __forceinline__ TileSpan tile_part(const Tile& tile, int part, int kS
 
 // The weighted sum of job j over the range sp, with weights wrow (and their
 // double-double low parts wlo, used where dd is set).  Called by every
-// thread of the workgroup.
-template <typename TIn, int NB, typename TOut>
-__device__ __forceinline__ void wsum_tile_range(const WsumArgs& args, int j, const TileSpan& sp, const double* wrow,
-                                                const double* wlo, bool dd) {
+// thread of the workgroup.  kPre: pre holds this thread's first group of
+// every operand, already loaded.
+template <typename TIn, int NB, typename TOut, typename WA = WsumArgs, bool kPre = false>
+__device__ __forceinline__ void wsum_tile_range(const WA& args, int j, const TileSpan& sp, const double* wrow,
+                                                const double* wlo, bool dd,
+                                                const typename Elem<TIn>::Raw8* pre = nullptr) {
   if (dd) {  // workgroup-uniform
-    wsum_exact_range<TIn, TIn, NB, TOut>(args, j, sp.lo, sp.hi, wrow, wlo);
+    wsum_exact_range<TIn, TIn, NB, TOut, WA>(args, j, sp.lo, sp.hi, wrow, wlo);
     return;
   }
   const TIn* x0 = static_cast<const TIn*>(args.x[j * op_stride(NB)]);
@@ -1375,10 +1394,16 @@ __device__ __forceinline__ void wsum_tile_range(const WsumArgs& args, int j, con
   // Operand-outer: the raw loads of all operands are in flight together,
   // but only one operand is widened at a time; every element still sums
   // its terms in operand order, starting from zero.
-  for (int64_t g = sp.body_lo + (int64_t)tid * kGroup; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
+  const int64_t g0 = sp.body_lo + (int64_t)tid * kGroup;
+  for (int64_t g = g0; g < sp.body_hi; g += (int64_t)kBlock * kGroup) {
     typename Elem<TIn>::Raw8 raw[NB];
+    if (kPre && g == g0) {
 #pragma unroll
-    for (int k = 0; k < NB; ++k) raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
+      for (int k = 0; k < NB; ++k) raw[k] = pre[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) raw[k] = Elem<TIn>::load_raw8(xs[k] + g);
+    }
     double acc[kGroup];
 #pragma unroll
     for (int e = 0; e < kGroup; ++e) acc[e] = 0.0;
@@ -1671,7 +1696,7 @@ __device__ void segment_exact_gram(const void* const* table, int64_t lo, int64_t
 // segment (rare, and bounded by the plan's limits on these combines) and
 // walked again.
 template <typename TIn, int NB>
-__global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa) {
+__global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs1 wa) {
   constexpr int kSplit = kFusedSplit;
   constexpr int MO = kArgOps;
   static_assert(NB <= MO, "blocks of at most 32 operands");
@@ -1692,6 +1717,22 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa)
   const int tid = threadIdx.x;
   const int t0 = ta.seg_tile[s], t1 = ta.seg_tile[s + 1];
   if (tid < d.nmerges) ms[tid] = ta.merges[d.merge0 + tid];  // read by the walk, after the barrier below
+  // This thread's first group of every operand, loaded now so that the loads
+  // overlap the walk (where that takes few registers: up to 32 bytes per
+  // element over the operands).  A NULL operand reads operand 0, unused.
+  constexpr bool kPre = NB * sizeof(TIn) <= 32;
+  typename Elem<TIn>::Raw8 pre[kPre ? NB : 1];
+  const TileSpan sp = tile_part(tile, part_id, kSplit);
+  if constexpr (kPre) {
+    const int64_t g = sp.body_lo + (int64_t)tid * kGroup;
+    if (g < sp.body_hi) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const void* x = wa.x[k] != nullptr ? wa.x[k] : wa.x[0];
+        pre[k] = Elem<TIn>::load_raw8(static_cast<const TIn*>(x) + g);
+      }
+    }
+  }
   {
     // the tile partials: the segment's tiles cut into Q runs of consecutive
     // tiles (Q = kBlock / ne, at most kFusedRuns, at least 1); thread (q, e)
@@ -1731,7 +1772,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs wa)
   }
   if (tid < MO) wlo[tid] = w[tid].lo;
   __syncthreads();
-  wsum_tile_range<TIn, NB, TIn>(wa, 0, tile_part(tile, part_id, kSplit), wf, wlo, (f & 2u) != 0);
+  wsum_tile_range<TIn, NB, TIn, WsumArgs1, kPre>(wa, 0, sp, wf, wlo, (f & 2u) != 0, pre);
 }
 
 // ----------------------------------------------------------------- plain sum
@@ -1880,25 +1921,26 @@ struct RunSum {
   }
 };
 
-hipError_t run_gram_f64(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+template <typename GA = GramArgs>
+hipError_t run_gram_f64(int nbt, const GA& a, int ntiles, int njobs, hipStream_t st) {
   const dim3 grid(ntiles, njobs);
   // short tiles: at most kMinTile rows, 4 x 16 x (16 / nbt) x U rows per workgroup iteration
   static_assert(kMinTile <= 4 * 16 * 8 * 4 && kMinTile <= 4 * 16 * 4 * 8, "short tiles take one iteration per wave");
   switch (nbt) {
     case 2:
       if (a.short_tiles)
-        hipLaunchKernelGGL((gram_f64mfma_kernel<2, 4>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((gram_f64mfma_kernel<2, 4, GA>), grid, dim3(kBlock), 0, st, a);
       else
-        hipLaunchKernelGGL((gram_f64mfma_kernel<2>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((gram_f64mfma_kernel<2, kF64Unroll, GA>), grid, dim3(kBlock), 0, st, a);
       break;
     case 4:
       if (a.short_tiles)
-        hipLaunchKernelGGL((gram_f64mfma_kernel<4, 8>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((gram_f64mfma_kernel<4, 8, GA>), grid, dim3(kBlock), 0, st, a);
       else
-        hipLaunchKernelGGL((gram_f64mfma_kernel<4>), grid, dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((gram_f64mfma_kernel<4, kF64Unroll, GA>), grid, dim3(kBlock), 0, st, a);
       break;
-    case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8>), grid, dim3(kBlock), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16>), grid, dim3(kBlock), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gram_f64mfma_kernel<8, kF64Unroll, GA>), grid, dim3(kBlock), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((gram_f64mfma_kernel<16, kF64Unroll, GA>), grid, dim3(kBlock), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1921,15 +1963,21 @@ struct RunGramStage {
 
 template <typename T>
 struct RunGramMfma {
-  static hipError_t run(int nbt, const GramArgs& a, int ntiles, int njobs, hipStream_t st) {
+  template <typename GA = GramArgs>
+  static hipError_t run(int nbt, const GA& a, int ntiles, int njobs, hipStream_t st) {
     const dim3 grid(ntiles, njobs);
     switch (nbt) {
-      case 2: hipLaunchKernelGGL((gram_mfma_kernel<T, 2>), grid, dim3(kBlock), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((gram_mfma_kernel<T, 4>), grid, dim3(kBlock), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8>), grid, dim3(kBlock), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16>), grid, dim3(kBlock), 0, st, a); break;
-      case 32: hipLaunchKernelGGL((gram_mfma_kernel<T, 32>), grid, dim3(kBlock), 0, st, a); break;
-      case 64: hipLaunchKernelGGL((gram_mfma_kernel<T, 64>), grid, dim3(kBlock), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((gram_mfma_kernel<T, 2, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((gram_mfma_kernel<T, 4, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 32: hipLaunchKernelGGL((gram_mfma_kernel<T, 32, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 64:
+        if constexpr (std::is_same<GA, GramArgs>::value) {  // 64-operand blocks: never a one-job small launch
+          hipLaunchKernelGGL((gram_mfma_kernel<T, 64>), grid, dim3(kBlock), 0, st, a);
+          break;
+        }
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -2034,7 +2082,7 @@ struct RunExactFirst {
 
 template <typename TIn>
 struct RunFused {
-  static hipError_t run(int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st) {
+  static hipError_t run(int nbt, const TreeArgs& t, const WsumArgs1& w, int ntiles, hipStream_t st) {
     const dim3 grid((unsigned)ntiles * kFusedSplit);
     switch (nbt) {
       case 2: hipLaunchKernelGGL((fused_kernel<TIn, 2>), grid, dim3(kBlock), 0, st, t, w); break;
@@ -2082,8 +2130,18 @@ hipError_t launch_tree(const TreeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fused(DType in_t, int nbt, const TreeArgs& t, const WsumArgs& w, int ntiles, hipStream_t st) {
+hipError_t launch_fused(DType in_t, int nbt, const TreeArgs& t, const WsumArgs1& w, int ntiles, hipStream_t st) {
   return by_type<RunFused>(in_t, nbt, t, w, ntiles, st);
+}
+
+hipError_t launch_gram1(DType operand, int nbt, const GramArgs1& a, int ntiles, hipStream_t st) {
+  switch (operand) {
+    case DType::F32: return run_gram_f64<GramArgs1>(nbt, a, ntiles, 1, st);
+    case DType::F16: return RunGramMfma<_Float16>::run<GramArgs1>(nbt, a, ntiles, 1, st);
+    case DType::BF16: return RunGramMfma<bf16_t>::run<GramArgs1>(nbt, a, ntiles, 1, st);
+    case DType::F64: break;
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_tile_groups(const TreeArgs& a, int ntiles, hipStream_t st) {
