@@ -260,6 +260,8 @@ def other_workload(config, steps, warmup, dev, budget_s):
     log(f"other workload {config} ({WORKLOAD_NAMES[config]})")
     wl = W.make_workload(config, device=dev)
     K, N, esz = wl.K, wl.N, BYTES[wl.dtype]
+    if N < 1 << 22:
+        steps = max(steps, 200)  # a launch-bound combine of a few microseconds: more steps for a stable figure
     out = torch.empty_like(wl.grads[0])
     step = A.Combiner(wl.grads, wl.seg_offsets, out=out, return_coeffs=True)
     for _ in range(warmup):
@@ -414,7 +416,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of one-thread oracle time that bound the CPU baseline's sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--others", default="2,4",
+    ap.add_argument("--others", default="1,2,4",
                     help="comma-separated workloads also timed in the same run (compact records under "
                          "'other_workloads'); only with the default workload; '' for none")
     ap.add_argument("--cold", action="store_true",
