@@ -1715,7 +1715,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs1 wa
   const BlockDesc d = ta.descs[ta.desc0];
   const int ne = gram_entries(d.nbt);
   const int tid = threadIdx.x;
-  const int t0 = ta.seg_tile[s], t1 = ta.seg_tile[s + 1];
+  const int t0 = tile.seg_t0, t1 = tile.seg_t1;
   if (tid < d.nmerges) ms[tid] = ta.merges[d.merge0 + tid];  // read by the walk, after the barrier below
   // This thread's first group of every operand, loaded now so that the loads
   // overlap the walk (where that takes few registers: up to 32 bytes per

@@ -141,9 +141,10 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
       // the first tile absorbs the unaligned head; later tiles start aligned
       const int64_t body_start = align_up(a, kGroup);
       const int64_t end = std::min(hi, body_start + p.tile_rows);
-      p.tiles.push_back(Tile{a, (int32_t)(end - a), (int32_t)s});
+      p.tiles.push_back(Tile{a, (int32_t)(end - a), (int32_t)s, p.seg_tile[s], 0});
       a = end;
     }
+    for (size_t t = (size_t)p.seg_tile[s]; t < p.tiles.size(); ++t) p.tiles[t].seg_t1 = (int32_t)p.tiles.size();
   }
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
   const size_t ntiles = p.tiles.size();

@@ -103,10 +103,13 @@ constexpr int gram_entries(int n) { return n * (n + 1) / 2; }
 // Position of entry (i, j), i <= j, in the packed upper triangle (row-major).
 constexpr int gram_index(int n, int i, int j) { return i * n - i * (i - 1) / 2 + (j - i); }
 
-struct Tile {      // 16 bytes, read by every kernel from device memory
+struct Tile {      // 24 bytes, read by every kernel from device memory
   int64_t start;   // first element (global index into the N-element buffers)
   int32_t len;     // number of elements
   int32_t seg;     // owning segment
+  // the owning segment's tiles [seg_t0, seg_t1), so that a kernel that sums
+  // them needs no second dependent load (seg_tile[seg])
+  int32_t seg_t0, seg_t1;
 };
 
 // One tree node inside a block: node = Adasum(left, right), where left is

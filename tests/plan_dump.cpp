@@ -37,7 +37,8 @@ static void dump(const Plan& p, int dt, int sched, int K) {
   }
   printf("], \"tiles\": [");
   for (size_t t = 0; t < p.tiles.size(); ++t)
-    printf("%s[%lld,%d,%d]", t ? "," : "", (long long)p.tiles[t].start, p.tiles[t].len, p.tiles[t].seg);
+    printf("%s[%lld,%d,%d,%d,%d]", t ? "," : "", (long long)p.tiles[t].start, p.tiles[t].len, p.tiles[t].seg,
+           p.tiles[t].seg_t0, p.tiles[t].seg_t1);
   printf("], \"seg_tile\": [");
   for (size_t s = 0; s < p.seg_tile.size(); ++s) printf("%s%d", s ? "," : "", p.seg_tile[s]);
   printf("], \"gram_err\": [");

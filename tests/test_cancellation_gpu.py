@@ -114,3 +114,29 @@ def test_planted_cancellations_16bit(gpu, dtype, K):
     say(f"planted 16-bit {dtype} K={K}: relative L2 {ev['rel_l2']:.3g}, worst segment {ev['seg_worst']} at "
         f"{ev['seg_ratio']:.3g} of its budget, coefficient error {ev['coeff_err']:.3g}, {ev['exempt']} exempt")
     assert passes(ev, dtype)
+
+
+@pytest.mark.parametrize("K,schedule", [(4, "tree"), (16, "chain")])
+def test_small_combine_recomputes_flagged_pairs(gpu, K, schedule):
+    """A small one-block combine takes two launches: the Gram pass, then the
+    walk and weighted sum in one (each workgroup walks its own segment).  A
+    merge flagged there, here above fp32 pairs cancelling to eps^2 = 1e-12,
+    is recomputed exactly inside that launch: the Gram pass's rounding
+    (about 2^-44 of the entries' terms) would otherwise move the
+    coefficients above those pairs by about 2^-44 / 1e-12, far beyond the
+    1e-6 gate."""
+    from distributed_sgd_gradient_amd import _native
+    lengths = [5000, 300, 3]
+    wl = W.cancelling_pairs(K, lengths, np.sqrt(1e-12), dtype="f32", seed=900 + K)
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    _native.profile_begin()
+    try:
+        ev = evaluate(wl, schedule)
+    finally:
+        kinds = _native.profile_end()
+    launches = {k: v["launches"] for k, v in kinds.items()}
+    say(f"small combine K={K} {schedule}: launches {launches}, relative L2 {ev['rel_l2']:.3g}, worst segment "
+        f"{ev['seg_worst']} at {ev['seg_ratio']:.3g} of its budget, coefficient error {ev['coeff_err']:.3g}")
+    assert launches == {"gram": 1, "wsum": 1}, launches
+    assert ev["exempt"] == 0
+    assert passes(ev, "f32")

@@ -144,7 +144,7 @@ def test_tiles_cover_segments_exactly(plans):
         tiles = np.array(P["tiles"])
         assert tiles[0][0] == 0 and tiles[:, 1].sum() == 40
         assert np.all(tiles[1:, 0] == tiles[:-1, 0] + tiles[:-1, 1])   # contiguous
-        for start, length, seg in tiles:
+        for start, length, seg, _, _ in tiles:
             assert off[seg] <= start and start + length <= off[seg + 1]   # inside one segment
 
 
@@ -184,7 +184,7 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         tiles = P["tiles"]
         # tiles: in order, contiguous, inside their segment, bodies 8-aligned, bounded length
         pos = 0
-        for t, (start, length, seg) in enumerate(tiles):
+        for t, (start, length, seg, _, _) in enumerate(tiles):
             assert start == pos and length >= 1 and off[seg] <= start and start + length <= off[seg + 1]
             first_of_seg = start == off[seg]
             assert first_of_seg or start % 8 == 0
@@ -196,6 +196,8 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         assert len(st) == nseg + 1 and st[0] == 0 and st[-1] == len(tiles)
         for s in range(nseg):
             assert all(tiles[t][2] == s for t in range(st[s], st[s + 1]))
+            # every tile carries its segment's tile range
+            assert all(tiles[t][3:] == [st[s], st[s + 1]] for t in range(st[s], st[s + 1]))
             assert (st[s + 1] > st[s]) == (off[s + 1] > off[s])
         # small one-stage combines of one block of at most 32 operands, no
         # empty segment and few partials for every weighted-sum workgroup to
