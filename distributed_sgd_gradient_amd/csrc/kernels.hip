@@ -16,10 +16,12 @@
 //           256 rows: exact products summed in double-double); reduced
 //           across the workgroup in a fixed order;
 //   tree  - per segment: the tile partials summed in tile order, then the
-//           block's merges evaluated on the Gram matrix level by level:
+//           block's merges evaluated level by level on the Gram matrix:
 //           d = wL.G.wR, A = wL.G.wL, B = wR.G.wR, ca = 1 - d/(2A),
 //           cb = 1 - d/(2B) (coefficient 1 for a zero norm), and the
-//           weights of the merged operands scaled by ca and cb;
+//           weights of the merged operands scaled by ca and cb; the walk
+//           keeps these forms as the current nodes' dot products, each
+//           merge updating those of its result;
 //   wsum  - one pass: y = sum_k w_k x_k in fp64, rounded once.
 // Each block's Gram entries carry a known rounding bound; the walk flags the
 // (block, segment) pairs whose coefficients that rounding could move beyond
@@ -28,8 +30,8 @@
 // exact products, the walk is repeated for them alone on double-double tile
 // sums, and their weighted sums (with those of any block whose result is far
 // smaller than its parts) are summed in double-double.
-// The merge walk's quadratic forms are summed in double-double from exact
-// products, and the weighted sum uses separately rounded products and sums
+// The merge walk keeps its dot products in double-double (products of fp64
+// coefficients with double-double entries), and the weighted sum uses separately rounded products and sums
 // (no fused multiply-add); either way mirrored terms cancel exactly: an
 // operand pair (a, -a) gives an exactly zero node, as the plain definition
 // does.
@@ -1293,7 +1295,7 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // A segment of one short tile of 16-bit inputs has its Gram entries in
   // double-double (hi: that tile's partial, taken exactly above) from the
   // exact short-tile sums; a refined pair has all of them so.  The walk then
-  // forms its quadratic forms from both parts, so their rounding is not
+  // starts its node dot products from both parts, so their rounding is not
   // amplified by a merge that cancels.  Workgroup-uniform.
   const uint64_t all_inputs = d.nb >= 64 ? ~uint64_t(0) : (uint64_t(1) << d.nb) - 1u;
   const bool exact_g = kRefine || (a.partials_lo != nullptr && t1 - t0 == 1 && a.tiles[t0].len <= kExactRows &&
@@ -1688,9 +1690,9 @@ __device__ void segment_exact_gram(const void* const* table, int64_t lo, int64_t
 
 // A one-stage combine whose segments have few tiles, after its Gram pass,
 // in one launch instead of four (walk, exact recomputation, second walk,
-// weighted sum).  Each workgroup of the weighted sum first walks its own
-// segment's block on the segment's tile partials, summed as tree_kernel sums
-// them, so every workgroup of a segment takes the same walk and the same
+// weighted sum), one workgroup per tile.  Each workgroup first walks its
+// own segment's block on the segment's tile partials, summed in a fixed
+// order, so every workgroup of a segment takes the same walk and the same
 // weights; the segment's first workgroup writes the tables.  A pair the walk
 // flags is recomputed exactly by each of its workgroups over the whole
 // segment (rare, and bounded by the plan's limits on these combines) and

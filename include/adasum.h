@@ -69,10 +69,10 @@ extern "C" {
 #endif
 
 /* Element type of the inputs and of the result.  Inside a block of up to 16
- * operands (32 for at most 32 16-bit inputs) nothing intermediate is stored:
- * statistics are quadratic forms in the block's fp64 Gram matrix and the
- * block's result is one weighted sum; a block result that feeds a later
- * stage (K above 16, or above 32 for 16-bit inputs) is kept in fp64.
+ * operands (all of them for at most 64 16-bit inputs) nothing intermediate
+ * is stored: statistics are quadratic forms in the block's fp64 Gram matrix
+ * and the block's result is one weighted sum; a block result that feeds a
+ * later stage (K above 16, or above 64 for 16-bit inputs) is kept in fp64.
  * Statistics and coefficients are fp64. */
 typedef enum {
   ADASUM_F32 = 0,
@@ -146,8 +146,8 @@ ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int
  *   stats        device fp64 array [K-1][nseg][3] receiving (a.b, |a|^2,
  *                |b|^2) of every node in the same order, or NULL.
  *                Within each block of up to 16 operands (four tree levels;
- *                32 operands and five levels when at most 32 16-bit inputs
- *                make the whole tree one block) the statistics are evaluated
+ *                32 or 64 operands, five or six levels, when at most 64
+ *                16-bit inputs make the whole tree one block) the statistics are evaluated
  *                from the Gram matrix of the block's operands, accumulated
  *                in fp64 (double-double where a merge cancels deeply enough
  *                for the fp64 rounding to matter); above a block, from its
@@ -214,7 +214,8 @@ ADASUM_API int64_t adasum_sum_workspace_bytes(int K, int64_t N, int dtype);
  * most max_rows; rows may be NULL when max_rows is 0) or a negative code.
  */
 typedef struct {
-  char kernel[32];     /* "gram", "tree", "exact", "wsum", "sum" */
+  char kernel[32];     /* "gram", "tree", "exact", "wsum" (a small combine's
+                          fused walk and weighted sum counts here), "sum" */
   int launches;
   double milliseconds;
   double bytes;
