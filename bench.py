@@ -318,7 +318,13 @@ def probe(name, dev):
              alternating over two), so that each group's second read could
              come from the memory-side cache;
     launch - back-to-back plain sums of 8 elements (K = 1) in a graph: the
-             cost of a dependent launch."""
+             cost of a dependent launch;
+    host   - the small K = 2 workload (two launches per combine): host time
+             per eager `Combiner` call, per call of the C entry point with
+             marshalled arguments, and per `torch.cuda.current_stream()`
+             lookup, beside the GPU time per combine with no event in the
+             loop and as graph replays: whether such combines are bound by
+             the host or by the GPU."""
     import torch
 
     import distributed_sgd_gradient_amd as A
@@ -398,8 +404,37 @@ def probe(name, dev):
             for _ in range(100):
                 A.plain_sum([x], out=y)
         out_lines.append({"probe": "launch", "us_per_dependent_launch": _median_ms(g.replay) * 10})
+    elif name == "host":
+        import ctypes
+
+        import workloads as W
+
+        wl = W.make_workload(1, device=dev)
+        out = torch.empty_like(wl.grads[0])
+        step = A.Combiner(wl.grads, wl.seg_offsets, out=out, return_coeffs=True)
+        step()
+        torch.cuda.synchronize()
+        st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+        def host_us(fn, n):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            t1 = time.perf_counter()
+            torch.cuda.synchronize()
+            return (t1 - t0) / n * 1e6
+
+        rec = {"probe": "host", "workload": WORKLOAD_NAMES[1]}
+        for _ in range(2):  # the second pass is reported
+            rec["combiner_call_us"] = host_us(step, 200)
+            rec["c_entry_call_us"] = host_us(lambda: step._fn(*step._args, st), 200)
+            rec["current_stream_lookup_us"] = host_us(lambda: torch.cuda.current_stream(dev), 2000)
+            rec["gpu_us_without_events"] = time_bare(step, 200) * 1e3
+            rec["gpu_us_graph_replay"] = time_graph(step, 200) * 1e3
+        out_lines.append(rec)
     else:
-        raise SystemExit(f"unknown probe {name!r} (cache, groups, launch)")
+        raise SystemExit(f"unknown probe {name!r} (cache, groups, launch, host)")
     for ln in out_lines:
         print(json.dumps(ln), flush=True)
 
@@ -422,7 +457,7 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time each step alone after writing a 1 GiB scratch buffer (caches cold); "
                          "reported under 'cold', the headline value stays the back-to-back rate")
-    ap.add_argument("--probe", choices=["cache", "groups", "launch"], default=None,
+    ap.add_argument("--probe", choices=["cache", "groups", "launch", "host"], default=None,
                     help="instead of the benchmark, print the measurements behind a design decision (see probe())")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 3 plain fp32 copies of MIB MiB (read MIB, write MIB) "
