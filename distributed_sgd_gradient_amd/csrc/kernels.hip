@@ -954,6 +954,149 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GA args) {
   }
 }
 
+// The 64-operand block over fp16 inputs (33 to 64 of them, one stage),
+// loaded in runs of 256 bytes per operand and transposed through LDS.  In the
+// matrix cores' fragment layout a load instruction covers 64 bytes of each
+// of 16 operands, and with all 64 operands in flight per wave that pattern
+// reads at less than half the rate of 256-byte runs (2.8 against 6.0 TB/s,
+// measured at this kernel's occupancy).  So each wave loads its 128 rows of
+// all 64 operands as sixteen instructions of four operands (lane l of load
+// i: operand 4 i + l / 16, rows 8 (l % 16) of the 128), writes them to its
+// own LDS area (operand-major, rows contiguous, each operand padded by 16
+// bytes so that the fragment reads below are free of bank conflicts), and
+// reads each 32-row chunk back in fragment layout: lane l, group h, operand
+// 16 h + l % 16, rows 8 (l / 16) of the chunk.  The LDS area is the wave's
+// own, so no workgroup barrier is needed inside the loop, and the next
+// iteration's loads are issued as soon as this one's are in LDS, so that they
+// fly during its matrix work.  Per 32-row chunk the ten instructions and the
+// fp64 sums are those of gram_mfma_kernel; waves 1-3 then pass their sums
+// through LDS and wave 0 adds them in wave order.  (bf16 blocks of 64
+// operands stay on gram_mfma_kernel: their range check and scaled path do
+// not fit this kernel's registers at two waves per SIMD.)
+constexpr int kWideRows = 128;                   // rows per wave per iteration
+constexpr int kWideStride = 2 * kWideRows + 16;  // bytes per operand in a wave's LDS area
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(kBlock) void gram_wide_f16_kernel(GramArgs args) {
+  typedef _Float16 T;
+  static_assert(!Mfma<T>::kGuard, "every fp16 product is exact");
+  constexpr int NB = 64, NH = 4, NP = 10;
+  constexpr int C = kWideRows / 32;  // chunks per iteration
+  constexpr int L = NB / 4;          // load instructions per iteration
+  // the waves' staging areas; after the loop, the wave sums of waves 1-3
+  constexpr int kStage = kGramWaves * NB * kWideStride, kRed = (kGramWaves - 1) * NP * 4 * 64 * 8;
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRed ? kStage : kRed];
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const void* const* table = args.x + j * op_stride(NB);
+  if (tile.len <= kExactRows) {  // workgroup-uniform: a short tile, summed exactly
+    static_assert(sizeof(stage) >= sizeof(uint16_t) * NB * kExactRows, "staging fits the transpose buffer");
+    const int64_t at = args.poff[j] + (int64_t)tile_id * gram_entries(NB);
+    gram_exact_rows<T, NB>(table, lo, tile.len, args.partials + at,
+                           args.partials_lo != nullptr ? args.partials_lo + at : nullptr,
+                           reinterpret_cast<uint16_t*>(&stage[0]));
+    return;
+  }
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = lane & 15, grp = lane >> 4;  // fragment lane
+  const int sub = lane >> 4, rq = lane & 15;  // load lane: operand 4 i + sub, rows 8 rq
+  // Absent operands (a NULL slot) read operand 0 and are masked to zero.
+  const uint16_t* xp[L];
+  uint32_t live = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const void* p = table[4 * i + sub];
+    if (p != nullptr) live |= 1u << i;
+    xp[i] = static_cast<const uint16_t*>(p != nullptr ? p : table[0]);
+  }
+  unsigned char* const st = &stage[wave * NB * kWideStride];
+
+  double acc[NP][4];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[q][r] = 0.0;
+
+  v4u v[L];
+  auto load = [&](int64_t it) {
+    const int64_t r0 = first + it * kWideRows;
+    if (r0 >= lo && r0 + kWideRows <= hi) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) v[i] = gload(reinterpret_cast<const v4u*>(xp[i] + r0 + 8 * rq));
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; ++i) v[i] = load_raw_group(xp[i], r0 + 8 * rq, lo, hi);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      if (!((live >> i) & 1u)) v[i] = v4u{0u, 0u, 0u, 0u};
+  };
+
+  const int64_t niter = (hi - first + kWideRows - 1) / kWideRows;
+  if (wave < niter) load(wave);
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) *reinterpret_cast<v4u*>(st + (4 * i + sub) * kWideStride + 16 * rq) = v[i];
+    if (it + kGramWaves < niter) load(it + kGramWaves);  // in flight during this iteration's matrix work
+    wave_sync();  // the staged rows are visible to the whole wave
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      v4u f[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        f[h] = *reinterpret_cast<const v4u*>(st + (16 * h + op) * kWideStride + 2 * (32 * c + 8 * grp));
+      int q = 0;
+#pragma unroll
+      for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+        for (int h2 = h1; h2 < NH; ++h2, ++q) {
+          const f32x4 d = Mfma<T>::gram(f[h1], f[h2]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[q][r] += (double)d[r];
+        }
+    }
+    wave_sync();  // the fragments are read before the next iteration stages its rows
+  }
+
+  // Waves 1-3 pass their matrices through LDS; wave 0 adds them to its own in
+  // wave order and writes its lanes' entries of the packed triangle.
+  __syncthreads();  // every wave is done with its staging area
+  double(*red)[NP][4 * 64] = reinterpret_cast<double(*)[NP][4 * 64]>(&stage[0]);
+  if (wave > 0) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave - 1][q][r * 64 + lane] = acc[q][r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    double* out = args.partials + args.poff[j] + (int64_t)tile_id * gram_entries(NB);
+    int q = 0;
+#pragma unroll
+    for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+      for (int h2 = h1; h2 < NH; ++h2, ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * h1 + 4 * grp + r, k = 16 * h2 + op;
+          if (i > k) continue;
+          double sum = acc[q][r];
+#pragma unroll
+          for (int w = 0; w < kGramWaves - 1; ++w) sum += red[w][q][r * 64 + lane];
+          out[gram_index(NB, i, k)] = sum;
+        }
+  }
+}
+
 // ----------------------------------------------------------------- tree walk
 
 // Products and sums rounded separately, never fused, so that terms that
@@ -1976,7 +2119,10 @@ struct RunGramMfma {
       case 32: hipLaunchKernelGGL((gram_mfma_kernel<T, 32, GA>), grid, dim3(kBlock), 0, st, a); break;
       case 64:
         if constexpr (std::is_same<GA, GramArgs>::value) {  // 64-operand blocks: never a one-job small launch
-          hipLaunchKernelGGL((gram_mfma_kernel<T, 64>), grid, dim3(kBlock), 0, st, a);
+          if constexpr (std::is_same<T, _Float16>::value)
+            hipLaunchKernelGGL(gram_wide_f16_kernel, grid, dim3(kBlock), 0, st, a);
+          else
+            hipLaunchKernelGGL((gram_mfma_kernel<T, 64>), grid, dim3(kBlock), 0, st, a);
           break;
         }
         return hipErrorInvalidValue;
