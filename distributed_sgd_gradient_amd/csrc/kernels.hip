@@ -1097,6 +1097,190 @@ __global__ __launch_bounds__(kBlock) void gram_wide_f16_kernel(GramArgs args) {
   }
 }
 
+// Blocks of 16 and 32 16-bit operands (one or two 16-operand groups) with the
+// same loads: 256-byte runs per operand staged in each wave's LDS area and
+// read back in fragment layout, the next iteration's loads in flight during
+// the matrix work.  bf16 keeps the range check and scaled path of
+// gram_mfma_kernel, on the staged rows: per wave and iteration, every operand
+// scaled by the power of two that brings its largest value of the 128 rows
+// just below 2^61.  The waves' matrices are summed in wave order, as there.
+template <typename T, int NB, typename GA = GramArgs>
+__global__ __launch_bounds__(kBlock) void gram_tr_kernel(GA args) {
+  static_assert(NB == 16 || NB == 32, "one or two 16-operand groups");
+  constexpr int NH = NB / 16, NP = NH * (NH + 1) / 2, NE = gram_entries(NB);
+  constexpr int C = kWideRows / 32;  // chunks per iteration
+  constexpr int L = NB / 4;          // load instructions per iteration
+  constexpr int kStage = kGramWaves * NB * kWideStride, kRed = kGramWaves * NP * 64 * 4 * 8;
+  constexpr int kBytes = kStage > kRed ? kStage : kRed;
+  static_assert(kBytes >= (int)sizeof(uint16_t) * NB * kExactRows, "staging fits the short-tile rows");
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kBytes];
+  __shared__ int scale[kGramWaves][NB];  // bf16 scaled path: per-operand power of two of the wave's iteration
+  const int tile_id = blockIdx.x;
+  const int j = blockIdx.y;
+  const Tile tile = args.tiles[tile_id];
+  const int64_t lo = tile.start, hi = tile.start + tile.len;
+  const void* const* table = args.x + j * op_stride(NB);
+  if (tile.len <= kExactRows) {  // workgroup-uniform: a short tile, summed exactly
+    const int64_t at = args.poff[j] + (int64_t)tile_id * NE;
+    gram_exact_rows<T, NB>(table, lo, tile.len, args.partials + at,
+                           args.partials_lo != nullptr ? args.partials_lo + at : nullptr,
+                           reinterpret_cast<uint16_t*>(&stage[0]));
+    return;
+  }
+  const int64_t first = lo & ~int64_t(kGroup - 1);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int op = lane & 15, grp = lane >> 4;  // fragment lane
+  const int sub = lane >> 4, rq = lane & 15;  // load lane: operand 4 i + sub, rows 8 rq
+  // Absent operands (a NULL slot) read operand 0 and are masked to zero.
+  const uint16_t* xp[L];
+  uint32_t live = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const void* p = table[4 * i + sub];
+    if (p != nullptr) live |= 1u << i;
+    xp[i] = static_cast<const uint16_t*>(p != nullptr ? p : table[0]);
+  }
+  unsigned char* const st = &stage[wave * NB * kWideStride];
+
+  double acc[NP][4];
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[q][r] = 0.0;
+
+  v4u v[L];
+  auto load = [&](int64_t it) {
+    const int64_t r0 = first + it * kWideRows;
+    if (r0 >= lo && r0 + kWideRows <= hi) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) v[i] = gload(reinterpret_cast<const v4u*>(xp[i] + r0 + 8 * rq));
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; ++i) v[i] = load_raw_group(xp[i], r0 + 8 * rq, lo, hi);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      if (!((live >> i) & 1u)) v[i] = v4u{0u, 0u, 0u, 0u};
+  };
+  auto fragment = [&](int h, int c) {
+    return *reinterpret_cast<const v4u*>(st + (16 * h + op) * kWideStride + 2 * (32 * c + 8 * grp));
+  };
+
+  const int64_t niter = (hi - first + kWideRows - 1) / kWideRows;
+  if (wave < niter) load(wave);
+  for (int64_t it = wave; it < niter; it += kGramWaves) {
+    bool scaled = false;
+    if constexpr (Mfma<T>::kGuard) {
+      RangeU16 range;
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        range.add(v[i].x);
+        range.add(v[i].y);
+        range.add(v[i].z);
+        range.add(v[i].w);
+      }
+      scaled = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) != 0;  // wave-uniform
+      if (scaled) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+          const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          uint32_t m = 0;  // largest biased exponent among the lane's values
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m = max(m, max((w[e] >> 7) & 0xffu, (w[e] >> 23) & 0xffu));
+          // over the sixteen lanes that hold this operand's 128 rows
+          m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+          m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+          m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+          m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+          if (rq == 0) scale[wave][4 * i + sub] = kScaleTop - (int)(m == 0 ? 1 : m);  // all-zero: exponent 1
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) *reinterpret_cast<v4u*>(st + (4 * i + sub) * kWideStride + 16 * rq) = v[i];
+    if (it + kGramWaves < niter) load(it + kGramWaves);  // in flight during this iteration's matrix work
+    wave_sync();  // the staged rows (and scales) are visible to the whole wave
+    if (!scaled) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        v4u f[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) f[h] = fragment(h, c);
+        int q = 0;
+#pragma unroll
+        for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+          for (int h2 = h1; h2 < NH; ++h2, ++q) {
+            const f32x4 d = Mfma<T>::gram(f[h1], f[h2]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[q][r] += (double)d[r];
+          }
+      }
+    } else if constexpr (Mfma<T>::kGuard) {
+      // entry (row, col) of sub-block (h1, h2): row operand 16 h1 + 4 grp + r,
+      // column operand 16 h2 + op; every fragment scaled by its operand's
+      // power of two (exact), the results scaled back exactly in fp64
+      int sc[NH], back[NP][4];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) sc[h] = scale[wave][16 * h + op];
+      {
+        int q = 0;
+#pragma unroll
+        for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+          for (int h2 = h1; h2 < NH; ++h2, ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) back[q][r] = -(scale[wave][16 * h1 + 4 * grp + r] + sc[h2]);
+      }
+#pragma unroll 1
+      for (int c = 0; c < C; ++c) {
+        v4u f[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const v4u x = fragment(h, c);
+          f[h] = v4u{bf16x2_scale(x.x, sc[h]), bf16x2_scale(x.y, sc[h]), bf16x2_scale(x.z, sc[h]),
+                     bf16x2_scale(x.w, sc[h])};
+        }
+        int q = 0;
+#pragma unroll
+        for (int h1 = 0; h1 < NH; ++h1)
+#pragma unroll
+          for (int h2 = h1; h2 < NH; ++h2, ++q) {
+            const f32x4 d = Mfma<T>::gram(f[h1], f[h2]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[q][r] += __builtin_amdgcn_ldexp((double)d[r], back[q][r]);
+          }
+      }
+    }
+    wave_sync();  // the fragments and scales are read before the next iteration stages its own
+  }
+
+  // Sum the four waves' matrices in wave order; write the packed triangle.
+  __syncthreads();  // every wave is done with its staging area
+  double(*red)[NP][64 * 4] = reinterpret_cast<double(*)[NP][64 * 4]>(&stage[0]);
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][q][lane * 4 + r] = acc[q][r];
+  __syncthreads();
+  double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
+  for (int e = threadIdx.x; e < NE; e += kBlock) {
+    int i = 0, rem = e;
+    while (rem >= NB - i) {
+      rem -= NB - i;
+      ++i;
+    }
+    const int k = i + rem;  // entry (i, k), i <= k
+    const int q = (i >> 4) == 0 ? (k >> 4) : 2;  // (0,0) -> 0, (0,1) -> 1, (1,1) -> 2
+    const int src = ((k & 15) + 16 * ((i & 15) >> 2)) * 4 + (i & 3);
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kGramWaves; ++w) sum += red[w][q][src];
+    out[e] = sum;
+  }
+}
+
 // ----------------------------------------------------------------- tree walk
 
 // Products and sums rounded separately, never fused, so that terms that
@@ -2115,8 +2299,8 @@ struct RunGramMfma {
       case 2: hipLaunchKernelGGL((gram_mfma_kernel<T, 2, GA>), grid, dim3(kBlock), 0, st, a); break;
       case 4: hipLaunchKernelGGL((gram_mfma_kernel<T, 4, GA>), grid, dim3(kBlock), 0, st, a); break;
       case 8: hipLaunchKernelGGL((gram_mfma_kernel<T, 8, GA>), grid, dim3(kBlock), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((gram_mfma_kernel<T, 16, GA>), grid, dim3(kBlock), 0, st, a); break;
-      case 32: hipLaunchKernelGGL((gram_mfma_kernel<T, 32, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((gram_tr_kernel<T, 16, GA>), grid, dim3(kBlock), 0, st, a); break;
+      case 32: hipLaunchKernelGGL((gram_tr_kernel<T, 32, GA>), grid, dim3(kBlock), 0, st, a); break;
       case 64:
         if constexpr (std::is_same<GA, GramArgs>::value) {  // 64-operand blocks: never a one-job small launch
           if constexpr (std::is_same<T, _Float16>::value)
