@@ -12,8 +12,9 @@
 //           upper triangle) on the matrix cores: fp64 instructions on the
 //           widened values (exact products, fp64 sums) for fp32 operands and
 //           for the fp64 slots of later stages, 32-row sums of exact
-//           products added in fp64 for 16-bit operands (tiles of at most
-//           256 rows: exact products summed in double-double); reduced
+//           products added in fp64 for 16-bit operands, whose loads are
+//           transposed through LDS for blocks of 16 or more (tiles of at
+//           most 256 rows: exact products summed in double-double); reduced
 //           across the workgroup in a fixed order;
 //   tree  - per segment: the tile partials summed in tile order, then the
 //           block's merges evaluated level by level on the Gram matrix:
@@ -740,11 +741,15 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
   }
 }
 
-// Blocks of up to 16 operands use one 16-operand group; the 32-operand block
-// (at most 32 16-bit inputs, one stage) uses two, with three instructions
-// per 32-row chunk: the two diagonal 16 x 16 blocks and the cross block (A
-// from the first group, B from the second); the 64-operand block (33 to 64
-// 16-bit inputs, one stage) uses four, with ten instructions per chunk.
+// Loads in the matrix cores' fragment layout; the launches use this kernel
+// for blocks of 2 to 8 operands and for bf16 blocks of 64 (blocks of 16 and
+// 32, and fp16 blocks of 64, take the transposed loads of gram_tr_kernel and
+// gram_wide_f16_kernel below).  Blocks of up to 16 operands use one
+// 16-operand group; the 32-operand block (at most 32 16-bit inputs, one
+// stage) uses two, with three instructions per 32-row chunk: the two
+// diagonal 16 x 16 blocks and the cross block (A from the first group, B
+// from the second); the 64-operand block (33 to 64 16-bit inputs, one
+// stage) uses four, with ten instructions per chunk.
 // Lane l, output register r of sub-block q = (h1, h2) holds
 // G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].  A 64-operand wave keeps forty
 // fp64 sums, so it runs at two waves per SIMD, with eight chunks (32 KB) in
