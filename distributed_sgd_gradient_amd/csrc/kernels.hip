@@ -959,14 +959,15 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GA args) {
   }
 }
 
-// The 64-operand block over fp16 inputs (33 to 64 of them, one stage),
-// loaded in runs of 256 bytes per operand and transposed through LDS.  In the
+// The 64-operand block (33 to 64 16-bit inputs, one stage), loaded in runs
+// of 256 bytes per operand and transposed through LDS.  In the
 // matrix cores' fragment layout a load instruction covers 64 bytes of each
 // of 16 operands, and with all 64 operands in flight per wave that pattern
 // reads at less than half the rate of 256-byte runs (2.8 against 6.0 TB/s,
 // measured at this kernel's occupancy).  So each wave loads its 128 rows of
 // all 64 operands as sixteen instructions of four operands (lane l of load
-// i: operand 4 i + l / 16, rows 8 (l % 16) of the 128), writes them to its
+// i: operand 4 i + l / 16, rows 8 (l % 16) of the 128; bf16: 64 rows in
+// 128-byte runs, eight operands per instruction), writes them to its
 // own LDS area (operand-major, rows contiguous, each operand padded by 16
 // bytes so that the fragment reads below are free of bank conflicts), and
 // reads each 32-row chunk back in fragment layout: lane l, group h, operand
@@ -975,9 +976,13 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GA args) {
 // iteration's loads are issued as soon as this one's are in LDS, so that they
 // fly during its matrix work.  Per 32-row chunk the ten instructions and the
 // fp64 sums are those of gram_mfma_kernel; waves 1-3 then pass their sums
-// through LDS and wave 0 adds them in wave order.  (bf16 blocks of 64
-// operands stay on gram_mfma_kernel: their range check and scaled path do
-// not fit this kernel's registers at two waves per SIMD.)
+// through LDS and wave 0 adds them in wave order.  A bf16 iteration holding
+// a value outside the matrix cores' exact range (see gram_mfma_kernel) is
+// summed instead by each lane over its own forty entries, in fp64 from the
+// staged rows: a product of two bf16 values is exact in fp64, and each
+// entry adds its 128 products in row order.  That rare path takes few
+// registers, which keeps the kernel at two waves per SIMD (the scaled
+// matrix-core path of gram_mfma_kernel does not fit).
 constexpr int kWideRows = 128;                   // rows per wave per iteration
 constexpr int kWideStride = 2 * kWideRows + 16;  // bytes per operand in a wave's LDS area
 
@@ -987,14 +992,19 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(kBlock) void gram_wide_f16_kernel(GramArgs args) {
-  typedef _Float16 T;
-  static_assert(!Mfma<T>::kGuard, "every fp16 product is exact");
+template <typename T>
+__global__ __launch_bounds__(kBlock) void gram_wide_kernel(GramArgs args) {
   constexpr int NB = 64, NH = 4, NP = 10;
-  constexpr int C = kWideRows / 32;  // chunks per iteration
-  constexpr int L = NB / 4;          // load instructions per iteration
+  // rows per wave per iteration: 64 for bf16, whose range check and exact
+  // path need the registers that half the loads in flight free
+  constexpr int ROWS = Mfma<T>::kGuard ? 64 : kWideRows;
+  constexpr int STRIDE = 2 * ROWS + 16;  // bytes per operand in a wave's LDS area
+  constexpr int LPO = ROWS / 8;          // load lanes per operand
+  constexpr int OPI = 64 / LPO;          // operands per load instruction
+  constexpr int C = ROWS / 32;           // chunks per iteration
+  constexpr int L = NB / OPI;            // load instructions per iteration
   // the waves' staging areas; after the loop, the wave sums of waves 1-3
-  constexpr int kStage = kGramWaves * NB * kWideStride, kRed = (kGramWaves - 1) * NP * 4 * 64 * 8;
+  constexpr int kStage = kGramWaves * NB * STRIDE, kRed = (kGramWaves - 1) * NP * 4 * 64 * 8;
   __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRed ? kStage : kRed];
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
@@ -1013,17 +1023,17 @@ __global__ __launch_bounds__(kBlock) void gram_wide_f16_kernel(GramArgs args) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int op = lane & 15, grp = lane >> 4;  // fragment lane
-  const int sub = lane >> 4, rq = lane & 15;  // load lane: operand 4 i + sub, rows 8 rq
+  const int sub = lane / LPO, rq = lane % LPO;  // load lane: operand OPI i + sub, rows 8 rq
   // Absent operands (a NULL slot) read operand 0 and are masked to zero.
   const uint16_t* xp[L];
   uint32_t live = 0;
 #pragma unroll
   for (int i = 0; i < L; ++i) {
-    const void* p = table[4 * i + sub];
+    const void* p = table[OPI * i + sub];
     if (p != nullptr) live |= 1u << i;
     xp[i] = static_cast<const uint16_t*>(p != nullptr ? p : table[0]);
   }
-  unsigned char* const st = &stage[wave * NB * kWideStride];
+  unsigned char* const st = &stage[wave * NB * STRIDE];
 
   double acc[NP][4];
 #pragma unroll
@@ -1033,8 +1043,8 @@ __global__ __launch_bounds__(kBlock) void gram_wide_f16_kernel(GramArgs args) {
 
   v4u v[L];
   auto load = [&](int64_t it) {
-    const int64_t r0 = first + it * kWideRows;
-    if (r0 >= lo && r0 + kWideRows <= hi) {
+    const int64_t r0 = first + it * ROWS;
+    if (r0 >= lo && r0 + ROWS <= hi) {
 #pragma unroll
       for (int i = 0; i < L; ++i) v[i] = gload(reinterpret_cast<const v4u*>(xp[i] + r0 + 8 * rq));
     } else {
@@ -1046,19 +1056,65 @@ __global__ __launch_bounds__(kBlock) void gram_wide_f16_kernel(GramArgs args) {
       if (!((live >> i) & 1u)) v[i] = v4u{0u, 0u, 0u, 0u};
   };
 
-  const int64_t niter = (hi - first + kWideRows - 1) / kWideRows;
+  const int64_t niter = (hi - first + ROWS - 1) / ROWS;
   if (wave < niter) load(wave);
   for (int64_t it = wave; it < niter; it += kGramWaves) {
+    bool outside = false;  // bf16: some value of the iteration is outside the exact range
+    if constexpr (Mfma<T>::kGuard) {
+      RangeU16 range;
 #pragma unroll
-    for (int i = 0; i < L; ++i) *reinterpret_cast<v4u*>(st + (4 * i + sub) * kWideStride + 16 * rq) = v[i];
+      for (int i = 0; i < L; ++i) {
+        range.add(v[i].x);
+        range.add(v[i].y);
+        range.add(v[i].z);
+        range.add(v[i].w);
+      }
+      outside = __ballot(range.outside(Mfma<T>::kLoBits, Mfma<T>::kHiBits)) != 0;  // wave-uniform
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) *reinterpret_cast<v4u*>(st + (OPI * i + sub) * STRIDE + 16 * rq) = v[i];
     if (it + kGramWaves < niter) load(it + kGramWaves);  // in flight during this iteration's matrix work
     wave_sync();  // the staged rows are visible to the whole wave
+    if (outside) {
+      if constexpr (Mfma<T>::kGuard) {
+        // Entry (row, col) of sub-block (h1, h2): row operand 16 h1 + 4 grp + r,
+        // column operand 16 h2 + op.  One entry at a time (a runtime loop,
+        // so that this rare path holds few registers), added to its sum by
+        // a select over the lane's forty sums.
+#pragma unroll 1
+        for (int e = 0; e < NP * 4; ++e) {
+          const int q = e >> 2, r = e & 3;
+          const int h1 = q < 4 ? 0 : q < 7 ? 1 : q < 9 ? 2 : 3;  // (h1, h2), h1 <= h2, in order
+          const int h2 = h1 + q - (h1 == 0 ? 0 : h1 == 1 ? 4 : h1 == 2 ? 7 : 9);
+          const unsigned char* xi = st + (16 * h1 + 4 * grp + r) * STRIDE;
+          const unsigned char* xk = st + (16 * h2 + op) * STRIDE;
+          double sum = 0.0;
+#pragma unroll 1
+          for (int g = 0; g < ROWS / 8; ++g) {
+            const v4u a = *reinterpret_cast<const v4u*>(xi + 16 * g);
+            const v4u b = *reinterpret_cast<const v4u*>(xk + 16 * g);
+            const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              sum = fma(widen16<T>((uint16_t)(wa[x] & 0xffffu)), widen16<T>((uint16_t)(wb[x] & 0xffffu)), sum);
+              sum = fma(widen16<T>((uint16_t)(wa[x] >> 16)), widen16<T>((uint16_t)(wb[x] >> 16)), sum);
+            }
+          }
+#pragma unroll
+          for (int q2 = 0; q2 < NP; ++q2)
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) acc[q2][r2] = (4 * q2 + r2 == e) ? acc[q2][r2] + sum : acc[q2][r2];
+        }
+      }
+      wave_sync();  // the staged rows are read before the next iteration stages its own
+      continue;
+    }
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       v4u f[NH];
 #pragma unroll
       for (int h = 0; h < NH; ++h)
-        f[h] = *reinterpret_cast<const v4u*>(st + (16 * h + op) * kWideStride + 2 * (32 * c + 8 * grp));
+        f[h] = *reinterpret_cast<const v4u*>(st + (16 * h + op) * STRIDE + 2 * (32 * c + 8 * grp));
       int q = 0;
 #pragma unroll
       for (int h1 = 0; h1 < NH; ++h1)
@@ -2308,10 +2364,7 @@ struct RunGramMfma {
       case 32: hipLaunchKernelGGL((gram_tr_kernel<T, 32, GA>), grid, dim3(kBlock), 0, st, a); break;
       case 64:
         if constexpr (std::is_same<GA, GramArgs>::value) {  // 64-operand blocks: never a one-job small launch
-          if constexpr (std::is_same<T, _Float16>::value)
-            hipLaunchKernelGGL(gram_wide_f16_kernel, grid, dim3(kBlock), 0, st, a);
-          else
-            hipLaunchKernelGGL((gram_mfma_kernel<T, 64>), grid, dim3(kBlock), 0, st, a);
+          hipLaunchKernelGGL((gram_wide_kernel<T>), grid, dim3(kBlock), 0, st, a);
           break;
         }
         return hipErrorInvalidValue;
