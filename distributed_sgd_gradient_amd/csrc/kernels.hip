@@ -742,30 +742,23 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
 }
 
 // Loads in the matrix cores' fragment layout; the launches use this kernel
-// for blocks of 2 to 8 operands and for bf16 blocks of 64 (blocks of 16 and
-// 32, and fp16 blocks of 64, take the transposed loads of gram_tr_kernel and
-// gram_wide_f16_kernel below).  Blocks of up to 16 operands use one
-// 16-operand group; the 32-operand block (at most 32 16-bit inputs, one
-// stage) uses two, with three instructions per 32-row chunk: the two
-// diagonal 16 x 16 blocks and the cross block (A from the first group, B
-// from the second); the 64-operand block (33 to 64 16-bit inputs, one
-// stage) uses four, with ten instructions per chunk.
+// for blocks of 2 to 8 operands, whose few live streams read as fast in that
+// layout (blocks of 16, 32 and 64 take the transposed loads of
+// gram_tr_kernel and gram_wide_kernel below).  Blocks of up to 16 operands
+// use one 16-operand group; a 32-operand block uses two, with three
+// instructions per 32-row chunk: the two diagonal 16 x 16 blocks and the
+// cross block (A from the first group, B from the second).
 // Lane l, output register r of sub-block q = (h1, h2) holds
-// G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].  A 64-operand wave keeps forty
-// fp64 sums, so it runs at two waves per SIMD, with eight chunks (32 KB) in
-// flight per iteration to keep as many bytes in flight per CU as the
-// smaller blocks do at four waves per SIMD (bf16: four chunks, within the
-// registers that its range check and scaled path take).
-constexpr int kWideUnroll = 8;  // 32-row chunks per wave per iteration of a 64-operand block
+// G[16 h1 + 4 (l / 16) + r][16 h2 + l % 16].
 template <typename T, int NB, typename GA = GramArgs>
 __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GA args) {
-  constexpr int NH = NB > 32 ? 4 : NB > 16 ? 2 : 1;  // 16-operand groups
+  static_assert(NB <= 32, "one or two 16-operand groups");
+  constexpr int NH = NB > 16 ? 2 : 1;  // 16-operand groups
   constexpr int NP = NH * (NH + 1) / 2;  // sub-blocks (h1 <= h2)
-  constexpr int U = NB > 32 ? (Mfma<T>::kGuard ? kWideUnroll / 2 : kWideUnroll) : kMfmaUnroll / NH;  // chunks per wave per iteration
+  constexpr int U = kMfmaUnroll / NH;  // chunks per wave per iteration
   constexpr int R = 32 * U;            // rows per wave per iteration
   constexpr int NE = gram_entries(NB);
-  // the wave sums of every sub-block; for 64 operands those of waves 1-3 only
-  __shared__ double red[NB > 32 ? kGramWaves - 1 : kGramWaves][NP][64 * 4];
+  __shared__ double red[kGramWaves][NP][64 * 4];  // the wave sums of every sub-block
 
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
@@ -909,34 +902,6 @@ __global__ __launch_bounds__(kBlock) void gram_mfma_kernel(GA args) {
   }
 
   double* out = args.partials + args.poff[j] + (int64_t)tile_id * NE;
-  if constexpr (NB > 32) {
-    // Waves 1-3 pass their matrices through LDS; wave 0 adds them to its own
-    // in wave order and writes its lanes' entries of the packed triangle.
-    if (wave > 0) {
-#pragma unroll
-      for (int q = 0; q < NP; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave - 1][q][r * 64 + lane] = acc[q][r];
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int q = 0;
-#pragma unroll
-      for (int h1 = 0; h1 < NH; ++h1)
-#pragma unroll
-        for (int h2 = h1; h2 < NH; ++h2, ++q)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * h1 + 4 * grp + r, k = 16 * h2 + op;
-            if (i > k) continue;
-            double sum = acc[q][r];
-#pragma unroll
-            for (int w = 0; w < kGramWaves - 1; ++w) sum += red[w][q][r * 64 + lane];
-            out[gram_index(NB, i, k)] = sum;
-          }
-    }
-    return;
-  }
   // Sum the four waves' matrices in wave order; write the packed triangle.
 #pragma unroll
   for (int q = 0; q < NP; ++q)
