@@ -75,7 +75,7 @@ def test_bench_json_line(gpu):
     launches = {k: v["launches"] for k, v in rec["kernels"].items()}
     assert launches == {"gram": 3, "wsum": 3}, launches
     for key in ("mean", "median", "min", "max"):
-        assert rec["step_ms"][key] > 0 and rec["step_ms_without_launch_events"][key] > 0
+        assert rec["step_ms"][key] > 0 and rec["step_ms_with_launch_events"][key] > 0
     assert rec["step_ms"]["min"] <= rec["step_ms"]["median"] <= rec["step_ms"]["max"]
     # the same combines with no event inside the loop, and as graph replays
     assert rec["step_ms_without_events"] > 0 and rec["step_ms_graph_replay"] > 0
