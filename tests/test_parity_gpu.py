@@ -659,9 +659,9 @@ def test_random_shapes(gpu, case):
     full_check(wl, f"random case {case}: lengths={lengths}", schedule)
 
 
-@pytest.mark.parametrize("chunk", range(10))
+@pytest.mark.parametrize("chunk", range(20))
 def test_seeded_random_sweep(gpu, chunk):
-    """150 seeded random shapes, in ten chunks of 15: K log-uniform in [1, 400), all
+    """300 seeded random shapes, in twenty chunks of 15: K log-uniform in [1, 400), all
     three dtypes, tree and chain, i.i.d. / shared-component / per-segment
     scaled values, values at the edges of the format (fp16 subnormals, bf16
     near 2^-100 and 2^60) or worker pairs that nearly cancel (relative gap
