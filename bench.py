@@ -318,6 +318,14 @@ def probe(name, dev):
              after another (a HIP graph of all groups, on one stream and
              alternating over two), so that each group's second read could
              come from the memory-side cache;
+    seggroups - the same interleaving on the BERT-Large workload itself:
+             runs of consecutive segments whose K-operand footprint fits a
+             cap (64, 136 or 256 MiB) are packed into groups of at most the
+             cap, runs of larger segments are one call each, and the calls
+             replay one after another in a HIP graph (one stream, and
+             alternating over two), against the workload as one call;
+             printed with the step times, the number of calls and the
+             share of the input bytes that sits in groups;
     launch - back-to-back plain sums of 8 elements (K = 1) in a graph: the
              cost of a dependent launch;
     host   - the small K = 2 workload (two launches per combine): host time
@@ -395,6 +403,78 @@ def probe(name, dev):
                               "one_call_path_frac": bmin / (t_whole * 1e-3) / 1e9 / PEAK_HBM_GBS})
             del one, two, groups
             torch.cuda.synchronize()
+    elif name == "seggroups":
+        import workloads as W
+
+        wl = W.make_workload(3, device=dev)
+        grads, off = wl.grads, [int(x) for x in wl.seg_offsets]
+        K, nseg, N = len(grads), len(off) - 1, off[-1]
+        esz = grads[0].element_size()
+        bmin = (K + 1) * N * esz
+        out = torch.empty_like(grads[0])
+        ref = torch.empty_like(grads[0])
+        whole = A.Combiner(grads, off, out=ref)
+        whole()
+        torch.cuda.synchronize()
+        for cap_mib in (64, 136, 256):
+            cap = cap_mib << 20
+            fits = [K * esz * (off[s + 1] - off[s]) <= cap for s in range(nseg)]
+            runs, s = [], 0
+            while s < nseg:
+                e = s + 1
+                if fits[s]:
+                    while e < nseg and fits[e] and K * esz * (off[e + 1] - off[s]) <= cap:
+                        e += 1
+                else:
+                    while e < nseg and not fits[e]:
+                        e += 1
+                runs.append((s, e, fits[s]))
+                s = e
+            calls = []
+            for s, e, _ in runs:
+                lo, hi = off[s], off[e]
+                if lo % 4:  # 16-byte aligned bases only (every BERT tensor holds a multiple of 4 elements)
+                    raise SystemExit("segment group not 16-byte aligned")
+                calls.append(A.Combiner([g[lo:hi] for g in grads], [x - lo for x in off[s:e + 1]], out=out[lo:hi]))
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            diff = ((out.double() - ref.double()).norm() / ref.double().norm()).item()
+            one, two = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(one):
+                for c in calls:
+                    c()
+            side = torch.cuda.Stream()
+            with torch.cuda.graph(two):
+                cur = torch.cuda.current_stream()
+                side.wait_stream(cur)
+                for i, c in enumerate(calls):
+                    if i % 2:
+                        with torch.cuda.stream(side):
+                            c()
+                    else:
+                        c()
+                cur.wait_stream(side)
+            wg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(wg):
+                whole()
+            t = {"whole": [], "one": [], "two": []}
+            for _ in range(5):  # alternating, so that a drift of the box's rate hits all three alike
+                t["whole"].append(_median_ms(wg.replay, 3))
+                t["one"].append(_median_ms(one.replay, 3))
+                t["two"].append(_median_ms(two.replay, 3))
+            med = {k: sorted(v)[len(v) // 2] for k, v in t.items()}
+            grouped = sum(off[e] - off[s] for s, e, f in runs if f)
+            out_lines.append({"probe": "seggroups", "workload": WORKLOAD_NAMES[3], "cap_MiB": cap_mib,
+                              "calls": len(calls), "grouped_calls": sum(1 for r in runs if r[2]),
+                              "grouped_byte_share": grouped / N, "one_call_ms": med["whole"],
+                              "groups_one_stream_ms": med["one"], "groups_two_streams_ms": med["two"],
+                              "one_call_path_frac": bmin / (med["whole"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                              "rel_l2_vs_one_call": diff})
+            print(json.dumps(out_lines[-1]), flush=True)
+            del one, two, wg, calls
+            torch.cuda.synchronize()
+        out_lines = []
     elif name == "launch":
         x = torch.ones(8, device=dev)
         y = torch.empty_like(x)
@@ -435,7 +515,7 @@ def probe(name, dev):
             rec["gpu_us_graph_replay"] = time_graph(step, 200) * 1e3
         out_lines.append(rec)
     else:
-        raise SystemExit(f"unknown probe {name!r} (cache, groups, launch, host)")
+        raise SystemExit(f"unknown probe {name!r} (cache, groups, seggroups, launch, host)")
     for ln in out_lines:
         print(json.dumps(ln), flush=True)
 
@@ -458,7 +538,7 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time each step alone after writing a 1 GiB scratch buffer (caches cold); "
                          "reported under 'cold', the headline value stays the back-to-back rate")
-    ap.add_argument("--probe", choices=["cache", "groups", "launch", "host"], default=None,
+    ap.add_argument("--probe", choices=["cache", "groups", "seggroups", "launch", "host"], default=None,
                     help="instead of the benchmark, print the measurements behind a design decision (see probe())")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 3 plain fp32 copies of MIB MiB (read MIB, write MIB) "

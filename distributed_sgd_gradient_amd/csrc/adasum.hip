@@ -598,10 +598,13 @@ int enqueue(const Plan& p, const DeviceTables& dt, const CallBuffers& b, hipStre
         // cancellation); those pairs' tiles are then recomputed exactly and
         // walked again
         t.flags = flags;
-        if (p.descs[sg.blocks.front().desc].nbt > kArgOps) {
-          // 64-operand blocks (a stage of its own): tile groups of long segments
-          const double gbytes = 8.0 * gram_entries(kMaxOps) * ntiles * t.nblocks;
-          log_launch("groups", stage_no, ntiles, t.nblocks, kMaxOps, gbytes);
+        t.grouped = p.descs[sg.blocks.front().desc].nbt > kArgOps || p.tile_groups;
+        if (t.grouped) {
+          // 64-operand blocks (a stage of their own), or segments of many
+          // tiles: the walk reads tile-group sums, formed over many workgroups
+          double gbytes = 0;
+          for (const Block& bk : sg.blocks) gbytes += 8.0 * gram_entries(p.descs[bk.desc].nbt) * ntiles;
+          log_launch("groups", stage_no, ntiles, t.nblocks, 0, gbytes);
           const int pg = prof_start(kTree, gbytes, st);
           e = launch_tile_groups(t, ntiles, st);
           prof_stop(pg, st);

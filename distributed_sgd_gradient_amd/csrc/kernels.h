@@ -67,6 +67,7 @@ struct TreeArgs {
   uint32_t* flags;          // [nblocks total][nseg]
   int refine;
   int wide;                 // some block of the launch has 64 operands (nbt = 64)
+  int grouped;              // launch_tile_groups ran on this launch's partials
 };
 
 // Relative coefficient error bound above which a pair's Gram matrix is
@@ -140,10 +141,10 @@ struct SumArgs {
 hipError_t launch_gram(DType operand, DType narrow_t, int nbt, const GramArgs& a, int ntiles, int njobs,
                        hipStream_t st);
 hipError_t launch_tree(const TreeArgs& a, hipStream_t st);
-// For the 64-operand blocks of a launch (descs desc0 .. desc0 + nblocks - 1):
-// the Gram partials of each group of kTileGroup consecutive tiles of a
-// segment with more than one tile, added in tile order in fp64 into the
-// group's first tile.
+// For the blocks of a launch (descs desc0 .. desc0 + nblocks - 1): the Gram
+// partials of each group of kTileGroup consecutive tiles of a segment with
+// more than one tile, added in tile order in fp64 into the group's first
+// tile.  A tree launch on those partials then sets `grouped`.
 hipError_t launch_tile_groups(const TreeArgs& a, int ntiles, hipStream_t st);
 // The Gram partials of every tile of a flagged (block, segment) pair,
 // recomputed exactly: double-double sums of exact products in row order,

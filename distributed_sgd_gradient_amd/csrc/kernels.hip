@@ -1323,7 +1323,7 @@ constexpr int kTreeWaves = kBlock / 64;
 constexpr int kPartStride = gram_entries(kArgOps);
 static_assert(kTreeWaves * kPartStride >= gram_entries(kMaxOps), "a 64-operand Gram matrix fits the wave sums");
 
-// Groups of kTileGroup tiles of the segments of 64-operand blocks: see
+// Groups of kTileGroup tiles of the segments of a stage: see
 // launch_tile_groups.  One workgroup per (tile, block); a tile that starts
 // no group, or lies in a segment of one tile, returns at once.
 __global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
@@ -1553,14 +1553,17 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
   return kRefine ? 3u : fl;  // a refined pair is summed in double-double
 }
 
-// One workgroup per (block, segment).  Blocks of up to 32 operands: wave q
-// sums the tile partials of the q-th quarter of the segment's tiles (lanes
-// over Gram entries, tiles in order); the four quarter sums are then added
-// in wave order.  64-operand blocks: one thread per entry adds the
-// segment's tile groups in order (see launch_tile_groups).  Either way the
-// split depends only on the tile count, so the result is reproducible.  The
-// refining walk (kRefine) visits only flagged pairs, whose tiles hold
-// double-double entries, and sums them in double-double, tile by tile.
+// One workgroup per (block, segment).  The units summed are the segment's
+// tiles, or, where the launch formed tile groups (TreeArgs::grouped: always
+// for 64-operand blocks, else where some segment has many tiles), its tile
+// groups, whose sums sit in each group's first tile.  Blocks of up to 32
+// operands: wave q sums the q-th quarter of the units (lanes over Gram
+// entries, units in order); the four quarter sums are then added in wave
+// order.  64-operand blocks: one thread per entry adds the units in order.
+// Either way the split depends only on the shape, so the result is
+// reproducible.  The refining walk (kRefine) visits only flagged pairs,
+// whose tiles hold double-double entries, and sums them in double-double,
+// tile by tile.
 
 // kWide: the launch holds a 64-operand block (its Gram matrix takes 2080
 // entries of LDS; the other variant, 528, keeps more workgroups per CU).
@@ -1592,8 +1595,11 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // read, by the thread that read them, and above all wave sums' first
   // quarter-stride, so the space can be shared.
   double* const Glo = kRefine ? &part_lo[0] : &part[0];
+  // where tile groups were formed (see launch_tile_groups), the first tile
+  // of each group holds the group's sum; the refining walk reads the
+  // recomputed partials of every tile
+  const int step = (a.grouped && !kRefine && t1 - t0 > 1) ? kTileGroup : 1;
   if (kWide && n > kArgOps) {
-    const int step = (!kRefine && t1 - t0 > 1) ? kTileGroup : 1;
     for (int e = tid; e < ne; e += kBlock) {
       const double* p = a.partials + d.poff + e;
       if constexpr (kRefine) {
@@ -1611,21 +1617,26 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     }
     __syncthreads();
   } else {
+    // wave q sums a contiguous share of the segment's tiles (or groups)
     const int q = tid >> 6, lane = tid & 63;
-    const int chunk = (t1 - t0 + kTreeWaves - 1) / kTreeWaves;
-    const int q0 = min(t1, t0 + q * chunk), q1 = min(t1, q0 + chunk);
+    const int nu = (t1 - t0 + step - 1) / step;
+    const int chunk = (nu + kTreeWaves - 1) / kTreeWaves;
+    const int u0 = min(nu, q * chunk), u1 = min(nu, u0 + chunk);
     for (int e = lane; e < ne; e += 64) {
       const double* p = a.partials + d.poff + e;
       if constexpr (kRefine) {
         const double* pl = a.partials_lo + d.poff + e;
         DD sum{0.0, 0.0};
-        for (int t = q0; t < q1; ++t) sum = dd_add(sum, DD{p[(int64_t)t * ne], pl[(int64_t)t * ne]});
+        for (int u = u0; u < u1; ++u) {
+          const int64_t t = t0 + u;  // step is 1
+          sum = dd_add(sum, DD{p[t * ne], pl[t * ne]});
+        }
         part[q * kPartStride + e] = sum.hi;
         part_lo[q * kPartStride + e] = sum.lo;
       } else {
         double sum = 0.0;
 #pragma unroll 8
-        for (int t = q0; t < q1; ++t) sum += p[(int64_t)t * ne];
+        for (int u = u0; u < u1; ++u) sum += p[(int64_t)(t0 + u * step) * ne];
         part[q * kPartStride + e] = sum;
       }
     }

@@ -148,6 +148,8 @@ Plan build_plan(int K, const int64_t* offsets, int nseg, DType dtype, Schedule s
   }
   p.seg_tile[nseg] = (int32_t)p.tiles.size();
   const size_t ntiles = p.tiles.size();
+  for (int s = 0; s < nseg; ++s)
+    if (p.seg_tile[s + 1] - p.seg_tile[s] >= kGroupMinTiles) p.tile_groups = true;
 
   // ---- blocks, stage by stage.  An operand of a stage above the first is
   // an fp64 slot (the result of a lower block) or an input gradient that the

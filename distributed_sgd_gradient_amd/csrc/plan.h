@@ -46,11 +46,14 @@ constexpr int kMaxJobs = 8;      // blocks per launch (kernel-argument budget)
 constexpr int kArgOps = 32;
 constexpr int op_stride(int nbt) { return nbt > kArgOps ? 64 : kArgOps; }
 constexpr int max_jobs(int nbt) { return kArgOps * kMaxJobs / op_stride(nbt); }
-// The walk of a 64-operand block sums its 2080 Gram entries over the tiles
-// of a segment.  Where a segment has many tiles, a separate launch first
-// adds up groups of kTileGroup consecutive tiles, in place into each group's
-// first tile, so that the walk reads one partial per group.
+// The walk of a (block, segment) pair, one workgroup, sums the pair's Gram
+// entries over the segment's tiles.  Where that is long (64-operand blocks,
+// with 2080 entries; or a segment of at least kGroupMinTiles tiles) a
+// separate launch first adds up groups of kTileGroup consecutive tiles over
+// many workgroups, in place into each group's first tile, so that the walk
+// reads one partial per group.
 constexpr int kTileGroup = 16;
+constexpr int kGroupMinTiles = 128;
 // A one-stage plan of one block of at most 32 operands, with at most
 // kFusedMaxRows elements and no empty segment, runs its walk and weighted
 // sum in one launch after the Gram pass: every weighted-sum workgroup walks
@@ -167,6 +170,7 @@ struct Plan {
   std::vector<BlockDesc> descs;
   std::vector<Merge> merges;
   bool fused = false;             // see kFusedMaxRows
+  bool tile_groups = false;       // some segment has kGroupMinTiles tiles or more
   int nslots = 0;                 // fp64 vectors of N elements
   int nblocks = 0;                // rows of the leaf-weight table
   size_t partial_doubles = 0;     // largest per-stage Gram partials footprint

@@ -43,8 +43,8 @@ static void dump(const Plan& p, int dt, int sched, int K) {
   for (size_t s = 0; s < p.seg_tile.size(); ++s) printf("%s%d", s ? "," : "", p.seg_tile[s]);
   printf("], \"gram_err\": [");
   for (size_t b = 0; b < p.descs.size(); ++b) printf("%s%.17g", b ? "," : "", p.descs[b].gram_err);
-  printf("], \"fused\": %d, \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
-         (int)p.fused,
+  printf("], \"fused\": %d, \"tile_groups\": %d, \"partial_doubles\": %zu, \"ws\": [%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu,%zu], \"nblocks\": %d}\n",
+         (int)p.fused, (int)p.tile_groups,
          p.partial_doubles, p.ws_slots, p.ws_partials, p.ws_weights, p.ws_weights_lo, p.ws_leafnorm, p.ws_coeffs,
          p.ws_stats, p.ws_flags, p.ws_plo, p.ws_total, p.nblocks);
 }

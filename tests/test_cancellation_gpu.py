@@ -88,6 +88,23 @@ def test_planted_cancellations_are_gated(gpu, K, schedule, eps2):
     assert passes(ev, "f32")
 
 
+@pytest.mark.parametrize("K,schedule", [(12, "tree"), (20, "tree"), (16, "chain")])
+def test_planted_cancellations_in_grouped_segments(gpu, K, schedule):
+    """The same fp32 pairs cancelling to eps^2 = 1e-12, over a segment of 147
+    tiles, whose walk first reads sums of groups of 16 tiles.  The flagged
+    pairs' partials are then recomputed exactly for every tile and walked
+    again tile by tile in double-double, as in short segments."""
+    lengths = [300_000, 3000, 7]
+    wl = W.cancelling_pairs(K, lengths, np.sqrt(1e-12), dtype="f32", seed=750 + K)
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    ev = evaluate(wl, schedule)
+    say(f"planted grouped K={K} {schedule}: relative L2 {ev['rel_l2']:.3g}, worst segment "
+        f"{ev['seg_worst']} at {ev['seg_ratio']:.3g} of its budget, coefficient error {ev['coeff_err']:.3g}, "
+        f"{ev['exempt']} exempt")
+    assert ev["exempt"] == 0
+    assert passes(ev, "f32")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("K", [4, 32])
 def test_planted_cancellations_16bit(gpu, dtype, K):

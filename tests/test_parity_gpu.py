@@ -156,6 +156,21 @@ def test_wide_block_many_tiles(gpu, K, dtype, schedule):
     full_check(wl, f"wide K={K} {dtype} {schedule}", schedule)
 
 
+@pytest.mark.parametrize("K,dtype,schedule", [(16, "f32", "tree"), (16, "f32", "chain"), (40, "f32", "tree"),
+                                              (32, "bf16", "tree"), (12, "f16", "chain"), (9, "f32", "tree")])
+def test_long_segment_tile_groups(gpu, K, dtype, schedule):
+    """Blocks of up to 32 operands over a segment of 147 tiles: the walk
+    reads the sums of groups of 16 tiles, formed by a launch of their own
+    (a segment that long, summed by one workgroup tile by tile, would make
+    the walk the slowest step of a mid-sized call).  Segments of exactly
+    16 and of 18 tiles (group boundaries), a short tile and a few rows; one
+    and two stages; both schedules."""
+    lengths = [300_000, 16 * 2048, 17 * 2048 + 3, 300, 3]
+    wl = W.random_case(K, lengths, dtype=dtype, seed=350 + K, kind="shared")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"tile groups K={K} {dtype} {schedule}", schedule)
+
+
 @pytest.mark.parametrize("K", [8, 29, 50])
 def test_fp16_subnormal_scales(gpu, K):
     wl = W.random_case(K, [3000] * 16 + [7, 1], dtype="f16", seed=11, kind="scaled")

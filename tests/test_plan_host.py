@@ -210,6 +210,8 @@ def test_random_shapes_tiles_tree_and_workspace(plan_exe):
         if small:
             assert T <= 2048  # one weighted-sum workgroup per tile covers it in one vector step
         assert bool(P["fused"]) == small, (K, dt, sc, off[:5])
+        # the walk reads tile-group sums where some segment has 128 tiles or more
+        assert bool(P["tile_groups"]) == any(st[s + 1] - st[s] >= 128 for s in range(nseg)), (K, dt, sc)
         # the tree (or chain) is the oracle's, with the block size limits
         assert plan_nodes(P) == oracle_nodes(K, sc), (K, dt, sc)
         for si, stg in enumerate(P["stages"]):
