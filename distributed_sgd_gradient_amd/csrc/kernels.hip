@@ -1324,22 +1324,30 @@ constexpr int kPartStride = gram_entries(kArgOps);
 static_assert(kTreeWaves * kPartStride >= gram_entries(kMaxOps), "a 64-operand Gram matrix fits the wave sums");
 
 // Groups of kTileGroup tiles of the segments of a stage: see
-// launch_tile_groups.  One workgroup per (tile, block); a tile that starts
-// no group, or lies in a segment of one tile, returns at once.
-__global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a) {
-  const int t = blockIdx.x;
+// launch_tile_groups.  One workgroup per window of kTileGroup consecutive
+// tiles (and block) forms every group that starts in its window, one after
+// another: a window holds one group start of a long segment, or several of
+// short ones.  Each thread adds an entry's partials in tile order, all of
+// its loads in flight at once.
+__global__ __launch_bounds__(kBlock) void tile_group_kernel(TreeArgs a, int ntiles) {
   const BlockDesc d = a.descs[a.desc0 + blockIdx.y];
-  const int s = a.tiles[t].seg;
-  const int t0 = a.seg_tile[s], t1 = a.seg_tile[s + 1];
-  if (t1 - t0 < 2 || (t - t0) % kTileGroup != 0) return;  // workgroup-uniform
   const int ne = gram_entries(d.nbt);
-  const int n = min(t1 - t, kTileGroup);
-  // the partials live in the workspace; only the walk reads them as const
-  double* p = const_cast<double*>(a.partials) + d.poff + (int64_t)t * ne;
-  for (int e = threadIdx.x; e < ne; e += kBlock) {
-    double sum = 0.0;
-    for (int u = 0; u < n; ++u) sum += p[(int64_t)u * ne + e];
-    p[e] = sum;
+  const int w0 = blockIdx.x * kTileGroup, w1 = min(w0 + kTileGroup, ntiles);
+  for (int t = w0; t < w1; ++t) {
+    const Tile tile = a.tiles[t];
+    if (tile.seg_t1 - tile.seg_t0 < 2 || (t - tile.seg_t0) % kTileGroup != 0) continue;  // workgroup-uniform
+    const int n = min(tile.seg_t1 - t, kTileGroup);
+    // the partials live in the workspace; only the walk reads them as const
+    double* p = const_cast<double*>(a.partials) + d.poff + (int64_t)t * ne;
+    for (int e = threadIdx.x; e < ne; e += kBlock) {
+      double v[kTileGroup];
+#pragma unroll
+      for (int u = 0; u < kTileGroup; ++u) v[u] = u < n ? p[(int64_t)u * ne + e] : 0.0;
+      double sum = 0.0;
+#pragma unroll
+      for (int u = 0; u < kTileGroup; ++u) sum += v[u];
+      p[e] = sum;
+    }
   }
 }
 
@@ -2511,7 +2519,8 @@ hipError_t launch_gram1(DType operand, int nbt, const GramArgs1& a, int ntiles, 
 }
 
 hipError_t launch_tile_groups(const TreeArgs& a, int ntiles, hipStream_t st) {
-  hipLaunchKernelGGL(tile_group_kernel, dim3((unsigned)ntiles, (unsigned)a.nblocks), dim3(kBlock), 0, st, a);
+  const unsigned windows = (unsigned)((ntiles + kTileGroup - 1) / kTileGroup);
+  hipLaunchKernelGGL(tile_group_kernel, dim3(windows, (unsigned)a.nblocks), dim3(kBlock), 0, st, a, ntiles);
   return hipGetLastError();
 }
 
