@@ -1608,20 +1608,49 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
   // recomputed partials of every tile
   const int step = (a.grouped && !kRefine && t1 - t0 > 1) ? kTileGroup : 1;
   if (kWide && n > kArgOps) {
-    for (int e = tid; e < ne; e += kBlock) {
-      const double* p = a.partials + d.poff + e;
-      if constexpr (kRefine) {
+    if constexpr (kRefine) {
+      for (int e = tid; e < ne; e += kBlock) {
+        const double* p = a.partials + d.poff + e;
         const double* pl = a.partials_lo + d.poff + e;
         DD sum{0.0, 0.0};
         for (int t = t0; t < t1; ++t) sum = dd_add(sum, DD{p[(int64_t)t * ne], pl[(int64_t)t * ne]});
         G[e] = sum.hi;
         Glo[e] = sum.lo;
-      } else {
-        double sum = 0.0;
-#pragma unroll 8
-        for (int t = t0; t < t1; t += step) sum += p[(int64_t)t * ne];
-        G[e] = sum;
       }
+    } else {
+      // All of this thread's entries (2080 over 256 threads) at once, four
+      // units at a time, each entry's units added in order.  Entries past
+      // the last are read at the last one (in bounds, no branch), so every
+      // load of a step is in flight together; they are not stored.
+      constexpr int EPT = (gram_entries(kMaxOps) + kBlock - 1) / kBlock;
+      constexpr int UB = 4;
+      const double* pb = a.partials + d.poff;
+      int idx[EPT];
+      double acc[EPT];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        idx[i] = min(tid + i * kBlock, ne - 1);
+        acc[i] = 0.0;
+      }
+      int t = t0;
+      for (; t + (UB - 1) * step < t1; t += UB * step) {
+        double v[UB][EPT];
+#pragma unroll
+        for (int k = 0; k < UB; ++k)
+#pragma unroll
+          for (int i = 0; i < EPT; ++i) v[k][i] = pb[(int64_t)(t + k * step) * ne + idx[i]];
+#pragma unroll
+        for (int k = 0; k < UB; ++k)
+#pragma unroll
+          for (int i = 0; i < EPT; ++i) acc[i] += v[k][i];
+      }
+      for (; t < t1; t += step) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) acc[i] += pb[(int64_t)t * ne + idx[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if (tid + i * kBlock < ne) G[tid + i * kBlock] = acc[i];
     }
     __syncthreads();
   } else {
