@@ -1573,6 +1573,42 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
 // whose tiles hold double-double entries, and sums them in double-double,
 // tile by tile.
 
+// Sums over units u0 .. u1 - 1 (the tiles t0 + u * step) of a lane's Gram
+// entries lane, lane + 64, ... (EPL of them; ne entries per tile), each
+// entry's units added in order, UB units at a time.  Entries past the last
+// are read at the last one (in bounds, no branch), so every load of a step
+// is in flight together; they are not stored.
+template <int EPL, int UB>
+__device__ __forceinline__ void lane_unit_sums(const double* pb, int ne, int lane, int t0, int u0, int u1, int step,
+                                               double* out) {
+  int idx[EPL];
+  double acc[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    idx[i] = min(lane + 64 * i, ne - 1);
+    acc[i] = 0.0;
+  }
+  int u = u0;
+  for (; u + UB <= u1; u += UB) {
+    double v[UB][EPL];
+#pragma unroll
+    for (int k = 0; k < UB; ++k)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[k][i] = pb[(int64_t)(t0 + (u + k) * step) * ne + idx[i]];
+#pragma unroll
+    for (int k = 0; k < UB; ++k)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) acc[i] += v[k][i];
+  }
+  for (; u < u1; ++u) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] += pb[(int64_t)(t0 + u * step) * ne + idx[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + 64 * i < ne) out[lane + 64 * i] = acc[i];
+}
+
 // kWide: the launch holds a 64-operand block (its Gram matrix takes 2080
 // entries of LDS; the other variant, 528, keeps more workgroups per CU).
 template <bool kRefine, bool kWide>
@@ -1659,9 +1695,9 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
     const int nu = (t1 - t0 + step - 1) / step;
     const int chunk = (nu + kTreeWaves - 1) / kTreeWaves;
     const int u0 = min(nu, q * chunk), u1 = min(nu, u0 + chunk);
-    for (int e = lane; e < ne; e += 64) {
-      const double* p = a.partials + d.poff + e;
-      if constexpr (kRefine) {
+    if constexpr (kRefine) {
+      for (int e = lane; e < ne; e += 64) {
+        const double* p = a.partials + d.poff + e;
         const double* pl = a.partials_lo + d.poff + e;
         DD sum{0.0, 0.0};
         for (int u = u0; u < u1; ++u) {
@@ -1670,12 +1706,17 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
         }
         part[q * kPartStride + e] = sum.hi;
         part_lo[q * kPartStride + e] = sum.lo;
-      } else {
-        double sum = 0.0;
-#pragma unroll 8
-        for (int u = u0; u < u1; ++u) sum += p[(int64_t)(t0 + u * step) * ne];
-        part[q * kPartStride + e] = sum;
       }
+    } else {
+      // a lane's entries (1, 3 or 9 of them) together, several units at a time
+      const double* pb = a.partials + d.poff;
+      double* out = &part[q * kPartStride];
+      if (ne <= 64)
+        lane_unit_sums<1, 8>(pb, ne, lane, t0, u0, u1, step, out);
+      else if (ne <= 192)
+        lane_unit_sums<3, 4>(pb, ne, lane, t0, u0, u1, step, out);
+      else
+        lane_unit_sums<9, 1>(pb, ne, lane, t0, u0, u1, step, out);
     }
     __syncthreads();
     for (int e = tid; e < ne; e += kBlock) {
