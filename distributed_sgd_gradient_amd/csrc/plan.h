@@ -92,12 +92,17 @@ inline size_t dtype_size(DType t) { return t == DType::F64 ? 8 : t == DType::F32
 // Largest block of the first stage.  Blocks of 32 or 64 operands (16-bit
 // inputs only) pay off only where they finish the whole combine in one stage,
 // without the fp64 intermediates of a second: above 64 inputs the tree needs
-// a second stage anyway, and 16-operand blocks stream faster.  (A chain
-// takes the same blocks: its stages of 16 would write and read an fp64
-// running result between stages.)
-inline int first_stage_ops(DType t, int K, Schedule) {
+// a second stage anyway, and 16-operand blocks stream faster.  A chain takes
+// at most 32: inside a block the walk carries each node's squared norm from
+// merge to merge, and where an operand is much smaller than the running
+// result (the result then about halves), that update cancels about three
+// quarters of its terms.  Its double-double rounding is then amplified
+// about fourfold per merge.  Over 63 such merges that exceeds
+// double-double's reach; over 31 it stays near 2^-104 * 4^31, about 2^-42.
+// (The tree's six levels stay far below.)
+inline int first_stage_ops(DType t, int K, Schedule sc) {
   if (t == DType::F32 || K > kMaxOps) return kMaxOps32;
-  return K <= 32 ? 32 : kMaxOps;
+  return (K <= 32 || sc == Schedule::Chain) ? 32 : kMaxOps;
 }
 
 // Number of distinct entries of the symmetric n x n Gram matrix.

@@ -58,7 +58,8 @@ def test_config4_sampled_full_size(gpu):
 
 
 def test_config4_sampled_full_size_chain(gpu):
-    # 64 fp16 inputs as a left-to-right chain: one 64-operand block whose walk takes the 63 merges in order
+    # 64 fp16 inputs as a left-to-right chain: a block of the first 32, then stages of the running
+    # result (fp64) and up to 15 more inputs
     wl = W.make_workload(4, device=gpu)
     segs = _spread(wl.nseg, np.random.default_rng(41), extra=[0, 9, 13])
     sampled_check(wl, segs, "config4 chain", schedule="chain")
@@ -146,10 +147,11 @@ def test_multistage_K(gpu, K, dtype):
 
 @pytest.mark.parametrize("K,dtype,schedule", [(40, "f16", "tree"), (64, "bf16", "tree"), (33, "bf16", "chain")])
 def test_wide_block_many_tiles(gpu, K, dtype, schedule):
-    """33 to 64 16-bit inputs: one 64-operand block.  A segment of about 980
-    tiles (the walk reads its partials in groups of 16 tiles), segments of
-    exactly 16, 17 and 33 tiles (group boundaries), a short tile and a few
-    rows."""
+    """33 to 64 16-bit inputs: one 64-operand block in the tree (a chain of
+    33 takes a 32-operand block, then a second stage).  A segment of about
+    980 tiles (the walk reads its partials in groups of 16 tiles), segments
+    of exactly 16, 17 and 33 tiles (group boundaries), a short tile and a
+    few rows."""
     lengths = [2_000_000, 16 * 2048, 17 * 2048, 33 * 2048 + 5, 300, 3]
     wl = W.random_case(K, lengths, dtype=dtype, seed=300 + K, kind="shared")
     wl.grads = [g.to(gpu) for g in wl.grads]
@@ -305,6 +307,24 @@ def test_long_chain_one_element_segments(gpu, K, dtype, lengths, seed):
     wl = W.random_case(K, lengths, dtype=dtype, seed=seed, kind="shared")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"long chain K={K} {dtype}", "chain")
+
+
+@pytest.mark.parametrize("K,dtype,schedule,seed", [
+    (62, "bf16", "chain", 310050), (64, "f16", "chain", 310051), (48, "bf16", "chain", 310052),
+    (64, "bf16", "tree", 310050), (32, "f16", "chain", 310053),
+])
+def test_chain_of_widely_scaled_scalars(gpu, K, dtype, schedule, seed):
+    """One-element segments of 16-bit inputs with per-worker scales spread
+    over orders of magnitude.  Each merge averages two parallel values, and
+    where the new input is much smaller than the running result, the
+    update of the result's squared norm cancels about three quarters of its
+    terms.  A 62-input chain walked as one 64-operand block amplified its
+    double-double rounding to a 1.1e-4 coefficient error at the last merge
+    (case 310050 of a seeded sweep).  Chains now take blocks of at most 32
+    operands.  The tree's six levels are checked alongside."""
+    wl = W.random_case(K, [9, 1, 5, 1, 2], dtype=dtype, seed=seed, kind="scaled")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"scaled scalars K={K} {dtype} {schedule}", schedule)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

@@ -63,11 +63,11 @@ def oracle_nodes(K, schedule):
 
 
 def block_limit(stage, dtype, K, schedule=0):
-    """Largest block the planner may form: 16 operands, except the single
-    stage over at most 32 16-bit inputs (32) or at most 64 (64), in either
-    schedule."""
+    """Largest block the planner may form: 16 operands, except the first
+    stage over at most 64 16-bit inputs: 32 operands up to 32 inputs, and
+    above that 64 in the tree (the single stage) and 32 in the chain."""
     if stage == 0 and dtype != 0 and K <= 64:
-        return 32 if K <= 32 else 64
+        return 32 if (K <= 32 or schedule == 1) else 64
     return 16
 
 
@@ -116,25 +116,33 @@ def test_plan_nodes_match_oracle(plans, schedule, dtype):
 
 
 def test_16bit_blocks_are_larger(plans):
-    """Up to 64 16-bit inputs (fp16 or bf16) finish in one stage of one
-    block, of 32 operands up to 32 inputs and of 64 above, in both
-    schedules; beyond that the first stage uses 16-operand blocks."""
+    """Up to 32 16-bit inputs (fp16 or bf16) finish in one stage of one
+    32-operand block in both schedules, and up to 64 in one 64-operand block
+    in the tree.  A chain of 33 to 64 16-bit inputs starts with one block of
+    the first 32 and adds the rest 15 at a time (the walk's squared norms
+    would lose double-double precision over a longer chain).  Beyond 64
+    inputs the first stage uses 16-operand blocks."""
     seen = set()
     for P in plans:
         if P["K"] in (17, 32, 33, 64, 65):
-            K, dt = P["K"], P["dtype"]
-            one = dt != 0 and K <= 64
+            K, dt, sc = P["K"], P["dtype"], P["schedule"]
+            one = dt != 0 and (K <= 32 or (K <= 64 and sc == 0))
             nstages = len(P["stages"])
-            if P["schedule"] == 0:
+            if sc == 0:
                 assert nstages == (1 if one else 2), (K, dt, nstages)
             blocks = P["stages"][0]["blocks"]
             if one:
                 assert nstages == 1
                 assert len(blocks) == 1 and blocks[0]["nb"] == K and blocks[0]["nbt"] == (32 if K <= 32 else 64)
                 assert blocks[0]["leafmask"] == (1 << K) - 1
+            elif dt != 0 and K <= 64:
+                # chain of 33..64 16-bit inputs: 32, then the running result and up to 15 inputs per stage
+                assert len(blocks) == 1 and blocks[0]["nb"] == 32 and blocks[0]["nbt"] == 32
+                assert nstages == 1 + -(-(K - 32) // 15), (K, nstages)
+                assert all(b["nb"] <= 16 for st in P["stages"][1:] for b in st["blocks"])
             else:
                 assert all(b["nb"] <= 16 for b in blocks)
-            seen.add((K, dt, P["schedule"]))
+            seen.add((K, dt, sc))
     assert len(seen) == 30
 
 
