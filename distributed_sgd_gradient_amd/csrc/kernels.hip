@@ -406,6 +406,38 @@ __global__ __launch_bounds__(kBlock) void gram_f64mfma_kernel(GA args) {
 // chunk, as in the fp32 pass.
 constexpr int kStageUnroll = 8;  // 16-row chunks per wave per iteration
 
+// Zeros that the branch-free loads below read in place of the type an
+// operand does not have (cache hits).
+__device__ __align__(16) const double kZeroRow[4] = {0.0, 0.0, 0.0, 0.0};
+
+// Four consecutive rows [row, row + 4) (all inside the tile) of an fp64 slot
+// or, where narrow, a TN input, widened to fp64.  Both loads are issued
+// whatever the operand's type (one of them from kZeroRow) and the values
+// selected after, so that no branch separates the loads of an iteration:
+// with a branch per operand the compiler waits on each load before the
+// branch joins.
+template <typename TN>
+__device__ __forceinline__ void load_whole4(const void* p, bool narrow, int64_t row, double (&v)[4]) {
+  const double* pd = narrow ? kZeroRow : static_cast<const double*>(p) + row;
+  const v2d a = gload(reinterpret_cast<const v2d*>(pd));
+  const v2d b = gload(reinterpret_cast<const v2d*>(pd + 2));
+  double n[4];
+  if constexpr (std::is_same<TN, float>::value) {
+    const float* pf = narrow ? static_cast<const float*>(p) + row : reinterpret_cast<const float*>(kZeroRow);
+    const v4f f = gload(reinterpret_cast<const v4f*>(pf));
+    n[0] = f.x; n[1] = f.y; n[2] = f.z; n[3] = f.w;
+  } else {
+    const uint16_t* ph = narrow ? static_cast<const uint16_t*>(p) + row : reinterpret_cast<const uint16_t*>(kZeroRow);
+    const v2u w = gload(reinterpret_cast<const v2u*>(ph));
+    n[0] = narrow_to_f32<TN>(w.x & 0xffffu); n[1] = narrow_to_f32<TN>(w.x >> 16);
+    n[2] = narrow_to_f32<TN>(w.y & 0xffffu); n[3] = narrow_to_f32<TN>(w.y >> 16);
+  }
+  v[0] = narrow ? n[0] : a.x;
+  v[1] = narrow ? n[1] : a.y;
+  v[2] = narrow ? n[2] : b.x;
+  v[3] = narrow ? n[3] : b.y;
+}
+
 // Four consecutive rows [row, row + 4) of an fp64 slot or a TN input,
 // widened to fp64, zero outside [lo, hi).
 template <typename TN>
@@ -469,8 +501,13 @@ __global__ __launch_bounds__(kBlock) void gram_stage_kernel(GramArgs args) {
   for (int64_t it = wave; it < niter; it += kGramWaves) {
     const int64_t r0 = first + it * R;
     double v[U][4];
+    if (r0 >= lo && r0 + R <= hi) {  // wave-uniform: the iteration's rows are all in the tile
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_stage4<TN>(xp, narrow, r0 + u * RC + lane_row, lo, hi, v[u]);
+      for (int u = 0; u < U; ++u) load_whole4<TN>(xp, narrow, r0 + u * RC + lane_row, v[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_stage4<TN>(xp, narrow, r0 + u * RC + lane_row, lo, hi, v[u]);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -1992,24 +2029,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 // the job's narrow mask marks them, inputs of type TN carried up; the result
 // is an fp64 slot (TOut = double) or the output (TOut = TN).  Each thread
 // takes runs of four elements (the body starts at a multiple of kGroup, so
-// every fp64 run is 32-byte aligned); an operand's type is the same for the
-// whole workgroup.
-template <typename TN>
-__device__ __forceinline__ void load_run4(const void* p, bool narrow, int64_t g, double (&v)[4]) {
-  if (!narrow) {
-    const v2d a = gload(reinterpret_cast<const v2d*>(static_cast<const double*>(p) + g));
-    const v2d b = gload(reinterpret_cast<const v2d*>(static_cast<const double*>(p) + g + 2));
-    v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
-  } else if constexpr (std::is_same<TN, float>::value) {
-    const v4f f = gload(reinterpret_cast<const v4f*>(static_cast<const float*>(p) + g));
-    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-  } else {
-    const v2u w = gload(reinterpret_cast<const v2u*>(static_cast<const uint16_t*>(p) + g));
-    v[0] = narrow_to_f32<TN>(w.x & 0xffffu); v[1] = narrow_to_f32<TN>(w.x >> 16);
-    v[2] = narrow_to_f32<TN>(w.y & 0xffffu); v[3] = narrow_to_f32<TN>(w.y >> 16);
-  }
-}
-
+// every fp64 run is 32-byte aligned), loaded with load_whole4.
 template <int NB, typename TN, typename TOut>
 __global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
   constexpr int kSplit = kWsumSplitMax;
@@ -2063,7 +2083,7 @@ __global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
   for (int64_t g = sp.body_lo + (int64_t)tid * kRun; g < sp.body_hi; g += (int64_t)kBlock * kRun) {
     double v[NB][kRun];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) load_run4<TN>(xs[k], nk[k], g, v[k]);
+    for (int k = 0; k < NB; ++k) load_whole4<TN>(xs[k], nk[k], g, v[k]);
     double acc[kRun] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int k = 0; k < NB; ++k)

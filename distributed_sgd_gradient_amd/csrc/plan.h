@@ -93,16 +93,20 @@ inline size_t dtype_size(DType t) { return t == DType::F64 ? 8 : t == DType::F32
 // inputs only) pay off only where they finish the whole combine in one stage,
 // without the fp64 intermediates of a second: above 64 inputs the tree needs
 // a second stage anyway, and 16-operand blocks stream faster.  A chain takes
-// at most 32: inside a block the walk carries each node's squared norm from
-// merge to merge, and where an operand is much smaller than the running
-// result (the result then about halves), that update cancels about three
-// quarters of its terms.  Its double-double rounding is then amplified
-// about fourfold per merge.  Over 63 such merges that exceeds
-// double-double's reach; over 31 it stays near 2^-104 * 4^31, about 2^-42.
-// (The tree's six levels stay far below.)
+// 16 whatever the dtype.  Inside a block the walk carries each node's
+// squared norm from merge to merge: |P'|^2 = ca (ca A + cb d) + cb (ca d +
+// cb B).  Where the next operand is nearly parallel to the running result,
+// that update cancels most of its terms, and an error already in A grows
+// by the square of the merge's cancellation: about 4x per merge where the
+// operand is much smaller, more near an opposite one.  The coefficients do
+// not correct it (the node is what they define; the walk's record of its
+// norm drifts).  Over the 31 or 63 merges of a 32- or 64-operand chain,
+// segments of one to four random values reached coefficient errors of 1e-4
+// to 4e-2; over 15 the largest in about 400,000 such chains was 7e-8.  The
+// tree's five or six levels stay far below.
 inline int first_stage_ops(DType t, int K, Schedule sc) {
-  if (t == DType::F32 || K > kMaxOps) return kMaxOps32;
-  return (K <= 32 || sc == Schedule::Chain) ? 32 : kMaxOps;
+  if (t == DType::F32 || K > kMaxOps || sc == Schedule::Chain) return kMaxOps32;
+  return K <= 32 ? 32 : kMaxOps;
 }
 
 // Number of distinct entries of the symmetric n x n Gram matrix.

@@ -69,11 +69,11 @@ extern "C" {
 #endif
 
 /* Element type of the inputs and of the result.  Inside a block of up to 16
- * operands (all of them for at most 64 16-bit inputs in the tree, the first
- * 32 in the chain) nothing intermediate is stored: statistics are quadratic
+ * operands (all of them for at most 64 16-bit inputs in the tree) nothing
+ * intermediate is stored: statistics are quadratic
  * forms in the block's fp64 Gram matrix and the block's result is one
  * weighted sum; a block result that feeds a later stage (K above 16, or
- * above 64 (tree) or 32 (chain) for 16-bit inputs) is kept in fp64.
+ * above 64 for 16-bit inputs in the tree) is kept in fp64.
  * Statistics and coefficients are fp64. */
 typedef enum {
   ADASUM_F32 = 0,
@@ -148,8 +148,8 @@ ADASUM_API int64_t adasum_workspace_bytes(int K, const int64_t* seg_offsets, int
  *                |b|^2) of every node in the same order, or NULL.
  *                Within each block of up to 16 operands (four tree levels;
  *                32 or 64 operands, five or six levels, when at most 64
- *                16-bit inputs make the whole tree one block; the first 32
- *                inputs of a chain of 16-bit inputs) the statistics are evaluated
+ *                16-bit inputs make the whole tree one block; a chain
+ *                takes blocks of up to 16 whatever the dtype) the statistics are evaluated
  *                from the Gram matrix of the block's operands, accumulated
  *                in fp64 (double-double where a merge cancels deeply enough
  *                for the fp64 rounding to matter); above a block, from its

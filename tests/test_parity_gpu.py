@@ -58,7 +58,7 @@ def test_config4_sampled_full_size(gpu):
 
 
 def test_config4_sampled_full_size_chain(gpu):
-    # 64 fp16 inputs as a left-to-right chain: a block of the first 32, then stages of the running
+    # 64 fp16 inputs as a left-to-right chain: a block of the first 16, then stages of the running
     # result (fp64) and up to 15 more inputs
     wl = W.make_workload(4, device=gpu)
     segs = _spread(wl.nseg, np.random.default_rng(41), extra=[0, 9, 13])
@@ -148,7 +148,7 @@ def test_multistage_K(gpu, K, dtype):
 @pytest.mark.parametrize("K,dtype,schedule", [(40, "f16", "tree"), (64, "bf16", "tree"), (33, "bf16", "chain")])
 def test_wide_block_many_tiles(gpu, K, dtype, schedule):
     """33 to 64 16-bit inputs: one 64-operand block in the tree (a chain of
-    33 takes a 32-operand block, then a second stage).  A segment of about
+    33 takes blocks of 16 in three stages).  A segment of about
     980 tiles (the walk reads its partials in groups of 16 tiles), segments
     of exactly 16, 17 and 33 tiles (group boundaries), a short tile and a
     few rows."""
@@ -320,11 +320,34 @@ def test_chain_of_widely_scaled_scalars(gpu, K, dtype, schedule, seed):
     update of the result's squared norm cancels about three quarters of its
     terms.  A 62-input chain walked as one 64-operand block amplified its
     double-double rounding to a 1.1e-4 coefficient error at the last merge
-    (case 310050 of a seeded sweep).  Chains now take blocks of at most 32
-    operands.  The tree's six levels are checked alongside."""
+    (case 310050 of a seeded sweep), and 32-operand chains reached 4e-2 on
+    other seeds.  Chains now take blocks of 16 operands whatever the dtype.
+    The tree's six levels are checked alongside."""
     wl = W.random_case(K, [9, 1, 5, 1, 2], dtype=dtype, seed=seed, kind="scaled")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"scaled scalars K={K} {dtype} {schedule}", schedule)
+
+
+def scalar_chain_case(case):
+    """The shape seeded sweep case ``case`` of chains over short segments
+    draws: dtype, K (2..64 for 16-bit inputs, 2..39 for fp32), schedule
+    (chain three times in four) and 50-300 segments of 1-4 i.i.d. N(0,1)
+    values."""
+    rng = np.random.default_rng(case)
+    dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+    K = int(rng.integers(2, 65)) if dtype != "f32" else int(rng.integers(2, 40))
+    schedule = "chain" if rng.random() < 0.75 else "tree"
+    lengths = [int(x) for x in rng.integers(1, 5, size=int(rng.integers(50, 300)))]
+    return K, dtype, schedule, lengths
+
+
+# sweep cases whose chains missed the coefficient gate (1.2e-4, 1.6e-3, 4.2e-2) in blocks of 32 or 64
+@pytest.mark.parametrize("case", [400022, 400045, 400249])
+def test_chains_over_short_random_segments(gpu, case):
+    K, dtype, schedule, lengths = scalar_chain_case(case)
+    wl = W.random_case(K, lengths, dtype=dtype, seed=case, kind="normal")
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    full_check(wl, f"short-segment chain case {case} K={K} {dtype} {schedule}", schedule)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

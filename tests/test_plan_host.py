@@ -63,11 +63,11 @@ def oracle_nodes(K, schedule):
 
 
 def block_limit(stage, dtype, K, schedule=0):
-    """Largest block the planner may form: 16 operands, except the first
-    stage over at most 64 16-bit inputs: 32 operands up to 32 inputs, and
-    above that 64 in the tree (the single stage) and 32 in the chain."""
-    if stage == 0 and dtype != 0 and K <= 64:
-        return 32 if (K <= 32 or schedule == 1) else 64
+    """Largest block the planner may form: 16 operands, except the single
+    tree stage over at most 32 16-bit inputs (32) or at most 64 (64).
+    Chains take 16 whatever the dtype."""
+    if stage == 0 and dtype != 0 and K <= 64 and schedule == 0:
+        return 32 if K <= 32 else 64
     return 16
 
 
@@ -116,31 +116,27 @@ def test_plan_nodes_match_oracle(plans, schedule, dtype):
 
 
 def test_16bit_blocks_are_larger(plans):
-    """Up to 32 16-bit inputs (fp16 or bf16) finish in one stage of one
-    32-operand block in both schedules, and up to 64 in one 64-operand block
-    in the tree.  A chain of 33 to 64 16-bit inputs starts with one block of
-    the first 32 and adds the rest 15 at a time (the walk's squared norms
-    would lose double-double precision over a longer chain).  Beyond 64
-    inputs the first stage uses 16-operand blocks."""
+    """In the tree, up to 32 16-bit inputs (fp16 or bf16) finish in one
+    stage of one 32-operand block and up to 64 in one 64-operand block;
+    beyond that the first stage uses 16-operand blocks.  A chain takes
+    blocks of 16 whatever the dtype (the walk's squared norms lose
+    double-double precision over a longer chain): the first 16 inputs, then
+    the running result and up to 15 more inputs per stage."""
     seen = set()
     for P in plans:
         if P["K"] in (17, 32, 33, 64, 65):
             K, dt, sc = P["K"], P["dtype"], P["schedule"]
-            one = dt != 0 and (K <= 32 or (K <= 64 and sc == 0))
             nstages = len(P["stages"])
-            if sc == 0:
-                assert nstages == (1 if one else 2), (K, dt, nstages)
             blocks = P["stages"][0]["blocks"]
-            if one:
+            if sc == 1:
+                assert nstages == 1 + -(-(K - 16) // 15), (K, dt, nstages)
+                assert all(b["nb"] <= 16 for st in P["stages"] for b in st["blocks"])
+            elif dt != 0 and K <= 64:
                 assert nstages == 1
                 assert len(blocks) == 1 and blocks[0]["nb"] == K and blocks[0]["nbt"] == (32 if K <= 32 else 64)
                 assert blocks[0]["leafmask"] == (1 << K) - 1
-            elif dt != 0 and K <= 64:
-                # chain of 33..64 16-bit inputs: 32, then the running result and up to 15 inputs per stage
-                assert len(blocks) == 1 and blocks[0]["nb"] == 32 and blocks[0]["nbt"] == 32
-                assert nstages == 1 + -(-(K - 32) // 15), (K, nstages)
-                assert all(b["nb"] <= 16 for st in P["stages"][1:] for b in st["blocks"])
             else:
+                assert nstages == 2, (K, dt, nstages)
                 assert all(b["nb"] <= 16 for b in blocks)
             seen.add((K, dt, sc))
     assert len(seen) == 30
