@@ -341,8 +341,9 @@ def scalar_chain_case(case):
     return K, dtype, schedule, lengths
 
 
-# sweep cases whose chains missed the coefficient gate (1.2e-4, 1.6e-3, 4.2e-2) in blocks of 32 or 64
-@pytest.mark.parametrize("case", [400022, 400045, 400249])
+# sweep cases whose chains missed the coefficient gate (1.2e-4, 1.6e-3, 4.2e-2) in blocks of 32 or 64,
+# and 40 more seeds of the same sweep
+@pytest.mark.parametrize("case", [400022, 400045, 400249] + list(range(420000, 420040)))
 def test_chains_over_short_random_segments(gpu, case):
     K, dtype, schedule, lengths = scalar_chain_case(case)
     wl = W.random_case(K, lengths, dtype=dtype, seed=case, kind="normal")
