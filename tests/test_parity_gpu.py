@@ -314,15 +314,15 @@ def test_long_chain_one_element_segments(gpu, K, dtype, lengths, seed):
     (64, "bf16", "tree", 310050), (32, "f16", "chain", 310053),
 ])
 def test_chain_of_widely_scaled_scalars(gpu, K, dtype, schedule, seed):
-    """One-element segments of 16-bit inputs with per-worker scales spread
-    over orders of magnitude.  Each merge averages two parallel values, and
-    where the new input is much smaller than the running result, the
-    update of the result's squared norm cancels about three quarters of its
-    terms.  A 62-input chain walked as one 64-operand block amplified its
-    double-double rounding to a 1.1e-4 coefficient error at the last merge
-    (case 310050 of a seeded sweep), and 32-operand chains reached 4e-2 on
-    other seeds.  Chains now take blocks of 16 operands whatever the dtype.
-    The tree's six levels are checked alongside."""
+    """One-element segments of 16-bit inputs: i.i.d. normal values, each
+    segment scaled by its own factor in [1e-6, 1].  Each merge averages two
+    parallel values, and where the new input is much smaller than the
+    running result, the update of the result's squared norm cancels about
+    three quarters of its terms.  A 62-input chain walked as one 64-operand
+    block amplified its double-double rounding to a 1.1e-4 coefficient error
+    at the last merge (case 310050 of a seeded sweep), and 32-operand chains
+    reached 4e-2 on other seeds.  Chains now take blocks of 16 operands
+    whatever the dtype.  The tree's six levels are checked alongside."""
     wl = W.random_case(K, [9, 1, 5, 1, 2], dtype=dtype, seed=seed, kind="scaled")
     wl.grads = [g.to(gpu) for g in wl.grads]
     full_check(wl, f"scaled scalars K={K} {dtype} {schedule}", schedule)
