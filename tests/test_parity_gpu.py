@@ -591,13 +591,18 @@ def test_concurrent_calls_from_threads(gpu):
     assert not errors, errors
 
 
-def test_graph_capture_and_replay(gpu):
+@pytest.mark.parametrize("K,dtype,lengths", [
+    (7, "f32", [1000, 0, 65537, 300]),          # a small combine: Gram pass and one fused launch
+    (20, "f32", [300_000, 0, 5000, 3]),         # two stages, tile groups, the walk, exact and refining launches
+    (40, "f16", [300_000, 7]),                  # one 64-operand block over tile groups
+])
+def test_graph_capture_and_replay(gpu, K, dtype, lengths):
     """A prepared combine (plan and workspace made by an earlier call) is
     captured in a graph; each of five replays, with the inputs changed in
     place and eager work and synchronisations in between, equals the eager
     combine of the same inputs bit for bit."""
     A = _A()
-    wl = W.random_case(7, [1000, 0, 65537, 300], dtype="f32", seed=808, kind="shared")
+    wl = W.random_case(K, lengths, dtype=dtype, seed=808, kind="shared")
     grads = [g.to(gpu) for g in wl.grads]
     out = torch.empty_like(grads[0])
     step = A.Combiner(grads, wl.seg_offsets, out=out)
