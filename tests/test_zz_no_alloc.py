@@ -4,8 +4,9 @@ adasum_combine_noalloc runs the same kernels with its workspace and tables in
 a fixed device array; its output, coefficients, statistics and orthogonality
 ratios must equal those of adasum_combine_ex bit for bit, on two calls in a
 row, the second with a smaller input of another dtype and schedule (the array
-keeps the first call's contents), and on a third that needs fp32 slots of a
-second stage.
+keeps the first call's contents), then on a 64-operand block and on a chain
+whose second stage reads an fp64 slot, over a segment long enough for the
+walk to read tile groups.
 """
 
 import ctypes
@@ -42,6 +43,7 @@ CASES = [
     (16, "f32", "tree", [70000, 3, 0, 12345, 200000, 8191]),
     (5, "bf16", "chain", [1000, 7, 300]),
     (40, "f16", "tree", [20000, 1, 257, 9]),
+    (20, "f32", "chain", [300000, 5]),
 ]
 
 
