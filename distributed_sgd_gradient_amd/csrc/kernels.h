@@ -60,6 +60,7 @@ struct TreeArgs {
   // refine = 0: every pair is walked, and flags[wrow][segment] is written
   // (flags NULL: no flags): bit 0 where the Gram entries' rounding
   // (BlockDesc::gram_err) could move a coefficient by more than kRefineTol
+  // (kRefineTol16 over 16-bit inputs)
   // of it, bit 1 there too and where the block's result is at most
   // kSumCancel of its weighted parts in squared norm.  refine = 1: only pairs
   // with bit 0 are walked again, on the recomputed double-double entries.
@@ -71,8 +72,17 @@ struct TreeArgs {
 };
 
 // Relative coefficient error bound above which a pair's Gram matrix is
-// recomputed exactly (the coefficient gate is 1e-6).
-constexpr double kRefineTol = 2.5e-7;
+// recomputed exactly (the coefficient gate is 1e-6): blocks whose entries are
+// fp64 sums (fp32 inputs, fp64 slots).  A coefficient's error moves every
+// node built on it, and a chain that cancels again later can amplify it a
+// thousandfold by its end, so the bound sits well below the gate wherever
+// that costs nothing on ordinary data (an entry errs by about 2^-44 of its
+// terms there; the bound flags a merge only where its parts cancel to
+// below about 1/40 of their norm).  Blocks over 16-bit inputs, whose
+// entries carry the matrix cores' fp32 rounding (2^-24), would flag every
+// merge at that bound and keep kRefineTol16.
+constexpr double kRefineTol = 1e-10;
+constexpr double kRefineTol16 = 2.5e-7;
 
 // A block result whose squared norm is at most this fraction of
 // sum_k w_k^2 |x_k|^2 is summed in double-double: in fp64 its rounding would

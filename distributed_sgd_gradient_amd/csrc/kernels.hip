@@ -1483,9 +1483,10 @@ __device__ uint32_t walk_block(const TreeArgs& a, const BlockDesc& d, int s, con
         // estimate cannot tell from zero is flagged too.
         // (Compared multiplied out by A^2 and B^2, both positive there.)
         const double eA = gram_err * sl, eB = gram_err * sr, ed = gram_err * sqrt(fmax(sl * sr, 0.0));
+        const double tol = gram_err < 1e-10 ? kRefineTol : kRefineTol16;
         bool bad = (sl > 0.0 && A <= eA) || (sr > 0.0 && B <= eB);
-        if (A > eA) bad = bad || ed * A + fabs(dd) * eA > 2.0 * kRefineTol * fmax(1.0, fabs(ca)) * A * A;
-        if (B > eB) bad = bad || ed * B + fabs(dd) * eB > 2.0 * kRefineTol * fmax(1.0, fabs(cb)) * B * B;
+        if (A > eA) bad = bad || ed * A + fabs(dd) * eA > 2.0 * tol * fmax(1.0, fabs(ca)) * A * A;
+        if (B > eB) bad = bad || ed * B + fabs(dd) * eB > 2.0 * tol * fmax(1.0, fabs(cb)) * B * B;
         if (bad) unsure = 1;
       }
       S[L] = ca * ca * sl + cb * cb * sr;

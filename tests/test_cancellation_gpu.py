@@ -88,6 +88,47 @@ def test_planted_cancellations_are_gated(gpu, K, schedule, eps2):
     assert passes(ev, "f32")
 
 
+def nearly_parallel_case(case):
+    """The shape and inputs seeded sweep case ``case`` of nearly parallel
+    workers draws: g_k = s_k (v + eta n_k), with per-worker scales s_k
+    log-uniform over e^-8..1 (e^-3..1 for fp16) and random signs, eta
+    log-uniform in [1e-6, 1e-1], 1-5 segments up to 200,000 rows."""
+    import torch
+    rng = np.random.default_rng(case)
+    dtype = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+    K = int(np.exp(rng.uniform(np.log(2), np.log(100))))
+    schedule = "chain" if rng.random() < 0.5 else "tree"
+    lengths = [int(np.exp(rng.uniform(0, np.log(200000)))) for _ in range(int(rng.integers(1, 6)))]
+    while K * sum(lengths) > 2e7:
+        lengths = [max(1, n // 2) for n in lengths]
+    N = sum(lengths)
+    eta = float(np.exp(rng.uniform(np.log(1e-6), np.log(1e-1))))
+    span = 3.0 if dtype == "f16" else 8.0
+    s = np.exp(rng.uniform(-span, 0, size=K)) * rng.choice([-1.0, 1.0], size=K)
+    g = torch.Generator().manual_seed(case)
+    v = torch.randn(N, generator=g, dtype=torch.float64)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    grads = [(float(s[k]) * (v + eta * torch.randn(N, generator=g, dtype=torch.float64))).to(tdt) for k in range(K)]
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return W.Workload(K=K, dtype=dtype, seg_offsets=off, grads=grads, seed=case), schedule
+
+
+@pytest.mark.parametrize("case", [511121, 520000, 520001, 520002])
+def test_nearly_parallel_workers_with_random_scales(gpu, case):
+    """Nearly parallel workers of random sign and scale: the chain's running
+    result cancels against the next worker again and again, and each
+    coefficient's error moves the result every later merge builds on.  In
+    case 511121 (K = 98 fp32 chain) coefficients within 2.5e-7 of their own
+    nodes, the old refinement bound, ended 1.85e-6 off at node 84.  Blocks
+    over fp64 sums now refine below 1e-10."""
+    wl, schedule = nearly_parallel_case(case)
+    wl.grads = [g.to(gpu) for g in wl.grads]
+    ev = evaluate(wl, schedule)
+    say(f"nearly parallel case {case} K={wl.K} {wl.dtype} {schedule}: relative L2 {ev['rel_l2']:.3g}, "
+        f"coefficient error {ev['coeff_err']:.3g}, {ev['exempt']} exempt")
+    assert passes(ev, wl.dtype)
+
+
 @pytest.mark.parametrize("K,schedule", [(12, "tree"), (20, "tree"), (16, "chain")])
 def test_planted_cancellations_in_grouped_segments(gpu, K, schedule):
     """The same fp32 pairs cancelling to eps^2 = 1e-12, over a segment of 147
