@@ -1791,26 +1791,54 @@ __global__ __launch_bounds__(kBlock) void tree_kernel(TreeArgs a) {
 
 // A (block, segment) pair whose walk set bit 1 of its flag: every element's
 // sum_k w_k x_k in double-double, with the walk's double-double weights and
-// exact products, rounded once.  Operands one at a time (rare, so compact);
-// operand k is of type TIn, or TN where the job's narrow mask marks it.
+// exact products, rounded once.  Operand k is of type TIn, or TN where the
+// job's narrow mask marks it; a NULL operand adds nothing.  Up to 32
+// operands, every operand's load of an element is issued before the sums (a
+// NULL operand reads operand 0; an operand of the other type reads
+// kZeroRow), so they are all in flight together; 64 operands (whose kernel
+// keeps fewer registers) are read one at a time.  Either way the terms are
+// added in operand order.
 template <typename TIn, typename TN, int NB, typename TOut, typename WA = WsumArgs>
 __device__ void wsum_exact_range(const WA& args, int j, int64_t lo, int64_t hi, const double* w_hi,
                                  const double* w_lo) {
   TOut* __restrict__ y = static_cast<TOut*>(args.y[j]);
+  const void* x0 = args.x[j * op_stride(NB)];
   double unused;
   for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
     DD acc{0.0, 0.0};
+    if constexpr (NB > kArgOps) {
 #pragma unroll 1
-    for (int k = 0; k < NB; ++k) {
-      const void* x = args.x[j * op_stride(NB) + k];
-      if (x == nullptr) continue;
-      double v;
-      if constexpr (std::is_same<TIn, TN>::value) {
-        v = widen_any<TIn>(x, i);
-      } else {
-        v = ((args.narrow[j] >> k) & 1u) ? widen_any<TN>(x, i) : widen_any<TIn>(x, i);
+      for (int k = 0; k < NB; ++k) {
+        const void* x = args.x[j * op_stride(NB) + k];
+        if (x == nullptr) continue;
+        double v;
+        if constexpr (std::is_same<TIn, TN>::value) {
+          v = widen_any<TIn>(x, i);
+        } else {
+          v = ((args.narrow[j] >> k) & 1u) ? widen_any<TN>(x, i) : widen_any<TIn>(x, i);
+        }
+        acc = dd_add(acc, dd_mul(DD{w_hi[k], w_lo[k]}, DD{v, 0.0}));
       }
-      acc = dd_add(acc, dd_mul(DD{w_hi[k], w_lo[k]}, DD{v, 0.0}));
+    } else {
+      double v[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const void* xk = args.x[j * op_stride(NB) + k];
+        const void* x = xk != nullptr ? xk : x0;
+        if constexpr (std::is_same<TIn, TN>::value) {
+          v[k] = widen_any<TIn>(x, i);
+        } else {
+          const bool nk = (args.narrow[j] >> (xk != nullptr ? k : 0)) & 1u;
+          const double a = widen_any<TIn>(nk ? static_cast<const void*>(kZeroRow) : x, nk ? 0 : i);
+          const double n = widen_any<TN>(nk ? x : static_cast<const void*>(kZeroRow), nk ? i : 0);
+          v[k] = nk ? n : a;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const DD t = dd_add(acc, dd_mul(DD{w_hi[k], w_lo[k]}, DD{v[k], 0.0}));
+        if (args.x[j * op_stride(NB) + k] != nullptr) acc = t;
+      }
     }
     Elem<TOut>::store1(y + i, Elem<TOut>::round(acc.hi, &unused));  // normalised: hi is the rounded sum
   }
