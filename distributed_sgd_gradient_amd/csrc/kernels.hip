@@ -299,6 +299,20 @@ __device__ __forceinline__ DD dd_add(DD x, DD y) {
   return DD{hi, e - (hi - s)};
 }
 
+// s + x*y.  Products of fp32 or 16-bit values (widened) are exact in fp64,
+// at most 48 significant bits, so their low part is zero and the
+// fused multiply-add that would find it is skipped; products of fp64 values
+// carry their rounding error in the low part.  The two forms give the same
+// bits where both apply.
+template <bool kExactProducts>
+__device__ __forceinline__ DD dd_add_prod(DD s, double x, double y) {
+  if constexpr (kExactProducts) {
+    return dd_add(s, DD{x * y, 0.0});
+  } else {
+    return dd_add(s, dd_prod(x, y));
+  }
+}
+
 __device__ __forceinline__ DD dd_scale(DD x, double b) {
   DD p = dd_prod(x.hi, b);
   p.lo += x.lo * b;
@@ -721,7 +735,9 @@ template <typename TIn, typename TN, int NB>
 __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
   constexpr int NE = gram_entries(NB);
   constexpr int EPT = (NE + kBlock - 1) / kBlock;  // entries per thread
-  __shared__ double sh[NB][kExactChunk];
+  // rows padded by one double, so that the threads of a wave reading row r of
+  // different operands hit different LDS banks
+  __shared__ double sh[NB][kExactChunk + 1];
   const int tile_id = blockIdx.x;
   const int j = blockIdx.y;
   const Tile tile = args.tiles[tile_id];
@@ -764,7 +780,7 @@ __global__ __launch_bounds__(kBlock) void gram_exact_kernel(GramArgs args) {
       const double* x = sh[ei[q]];
       const double* y = sh[ek[q]];
       DD sum = acc[q];
-      for (int r = 0; r < n; ++r) sum = dd_add(sum, dd_prod(x[r], y[r]));
+      for (int r = 0; r < n; ++r) sum = dd_add_prod<!std::is_same<TIn, double>::value>(sum, x[r], y[r]);
       acc[q] = sum;
     }
   }
@@ -2129,8 +2145,11 @@ __global__ __launch_bounds__(kBlock) void wsum_stage_kernel(WsumArgs args) {
 // The double-double Gram matrix of rows [lo, hi) of the block's operands
 // (table; NULL: zero), every entry the row-order sum of exact products, high
 // parts into G and low parts into Glo; the rows pass through sh
-// (NB x kFusedChunk doubles).  Called by every thread of the workgroup.
+// (NB rows of kFusedStride doubles: kFusedChunk values and one of padding,
+// so that a wave's reads of one row index across operands hit different LDS
+// banks).  Called by every thread of the workgroup.
 constexpr int kFusedChunk = 64;
+constexpr int kFusedStride = kFusedChunk + 1;
 constexpr int kFusedRuns = 16;  // runs of tiles whose partials one workgroup sums in parallel
 
 template <typename TIn, int NB>
@@ -2158,16 +2177,16 @@ __device__ void segment_exact_gram(const void* const* table, int64_t lo, int64_t
     for (int idx = threadIdx.x; idx < NB * n; idx += kBlock) {
       const int k = idx / n, r = idx - k * n;
       const void* x = table[k];
-      sh[k * kFusedChunk + r] = x != nullptr ? widen_any<TIn>(x, c0 + r) : 0.0;
+      sh[k * kFusedStride + r] = x != nullptr ? widen_any<TIn>(x, c0 + r) : 0.0;
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
       if (threadIdx.x + q * kBlock >= NE) continue;
-      const double* x = sh + ei[q] * kFusedChunk;
-      const double* y = sh + ek[q] * kFusedChunk;
+      const double* x = sh + ei[q] * kFusedStride;
+      const double* y = sh + ek[q] * kFusedStride;
       DD sum = acc[q];
-      for (int r = 0; r < n; ++r) sum = dd_add(sum, dd_prod(x[r], y[r]));
+      for (int r = 0; r < n; ++r) sum = dd_add_prod<!std::is_same<TIn, double>::value>(sum, x[r], y[r]);
       acc[q] = sum;
     }
   }
@@ -2193,7 +2212,7 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(TreeArgs ta, WsumArgs1 wa
   constexpr int kSplit = kFusedSplit;
   constexpr int MO = kArgOps;
   static_assert(NB <= MO, "blocks of at most 32 operands");
-  static_assert(kTreeWaves * kPartStride >= NB * kFusedChunk, "the exact rows fit the wave sums");
+  static_assert(kTreeWaves * kPartStride >= NB * kFusedStride, "the exact rows fit the wave sums");
   __shared__ double part[kTreeWaves * kPartStride];
   __shared__ double G[gram_entries(MO)];
   __shared__ double glo[gram_entries(MO)];
